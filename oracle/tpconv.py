@@ -1,0 +1,236 @@
+"""Edge-conditioned CG tensor-product convolution, conventional schedule (fp64).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What is computed ("Sobek" page, abstract: equivariant GNNs apply
+edge-conditioned tensor-product convolutions over graph edges; conventional
+implementations materialise edge-specific weights, messages and adjoints).  For
+every directed edge e = (s -> v) of the receiver-sorted graph:
+
+  r_e = pos[s] - pos[v],  d = |r_e|,  r_hat = r_e / d
+  R_e[k]            radial basis (oracle.radial)
+  Y_e[l2, m2]       real spherical harmonics of r_hat (oracle.sh)
+  w_e[p, ci, co]  = sum_k R_e[k] W[k, p, ci, co]                (per-edge weights)
+  U_e[p, ci, m3]  = sum_{m1,m2} C^p[m1,m2,m3] x[s][l1, ci, m1] Y_e[l2, m2]
+  m_e[l3, co, m3] = sum_{p -> l3} sum_ci w_e[p, ci, co] U_e[p, ci, m3]   (message)
+  out[v]         += m_e                                          (scatter-add)
+
+This module deliberately keeps that order: it materialises w_e, U_e and m_e
+for a bounded chunk of edges at a time and scatter-adds with ``np.add.at``.
+The backward and double backward are written out by hand from the chain rule
+on the same materialised intermediates (adjoints g_w, g_U, g_Y, g_R per edge).
+
+Layouts (shared with the library's public header only as a data contract):
+  x   [N][D_in][C_in],  out [N][D_out][C_out]   rows ordered by irreps, l^2+l+m
+  W   [K][P][C_in][C_out]                        P paths in oracle.cg order
+  pos [N][3]
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import cg as _cg
+from . import radial as _radial
+from . import sh as _sh
+
+
+@dataclass
+class Problem:
+    irreps_in: str
+    irreps_out: str
+    sh_lmax: int
+    num_basis: int
+    cutoff: float = 5.0
+    envelope_p: int = 6
+    ir_in: list = field(init=False)
+    ir_out: list = field(init=False)
+    paths: list = field(init=False)
+
+    def __post_init__(self):
+        self.ir_in = _cg.parse_irreps(self.irreps_in)
+        self.ir_out = _cg.parse_irreps(self.irreps_out)
+        muls_in = {m for m, _, _ in self.ir_in}
+        muls_out = {m for m, _, _ in self.ir_out}
+        if len(muls_in) != 1 or len(muls_out) != 1:
+            raise ValueError("uniform multiplicity per irreps string is required")
+        self.C_in = muls_in.pop()
+        self.C_out = muls_out.pop()
+        self.D_in = _cg.irreps_dim(self.ir_in)
+        self.D_out = _cg.irreps_dim(self.ir_out)
+        self.off_in = _cg.irreps_offsets(self.ir_in)
+        self.off_out = _cg.irreps_offsets(self.ir_out)
+        self.paths = _cg.enumerate_paths(self.ir_in, self.sh_lmax, self.ir_out)
+        self.P = len(self.paths)
+        for p in self.paths:
+            p["C"] = _cg.real_cg(p["l1"], p["l2"], p["l3"])
+
+    @property
+    def w_shape(self):
+        return (self.num_basis, self.P, self.C_in, self.C_out)
+
+
+def csr_receivers(rowptr: np.ndarray) -> np.ndarray:
+    """Receiver id of every edge of a receiver-sorted CSR graph."""
+    rowptr = np.asarray(rowptr, dtype=np.int64)
+    return np.repeat(np.arange(len(rowptr) - 1), np.diff(rowptr))
+
+
+def _geometry(pos, s, v):
+    r = pos[s] - pos[v]
+    d = np.linalg.norm(r, axis=-1)
+    rhat = np.where((d > 0)[:, None], r / np.where(d > 0, d, 1.0)[:, None], 0.0)
+    return r, d, rhat
+
+
+def _chunks(prob: Problem, E: int):
+    per_edge = 8 * max(1, prob.P * prob.C_in * prob.C_out)
+    step = int(max(1, min(E, 48_000_000 // per_edge)))
+    for a in range(0, E, step):
+        yield a, min(E, a + step)
+
+
+def _edge_terms(prob, pos, s, v):
+    r, d, rhat = _geometry(pos, s, v)
+    R = _radial.bessel_radial(d, prob.num_basis, prob.cutoff, prob.envelope_p)
+    Y = _sh.spherical_harmonics(prob.sh_lmax, r)
+    return r, d, rhat, R, Y
+
+
+def _x_block(prob, x, s, p):
+    o = prob.off_in[p["i1"]]
+    return x[s, o:o + 2 * p["l1"] + 1, :]               # [e, m1, ci]
+
+
+def _y_block(Y, p):
+    l2 = p["l2"]
+    return Y[:, l2 * l2:(l2 + 1) * (l2 + 1)]            # [e, m2]
+
+
+def _out_rows(prob, p):
+    o = prob.off_out[p["i3"]]
+    return slice(o, o + 2 * p["l3"] + 1)
+
+
+def _in_rows(prob, p):
+    o = prob.off_in[p["i1"]]
+    return slice(o, o + 2 * p["l1"] + 1)
+
+
+def _coupling(C, xs, y):
+    """U[e, ci, m3] = sum_{m1,m2} C[m1,m2,m3] xs[e,m1,ci] y[e,m2]."""
+    return np.einsum("abc,eai,eb->eic", C, xs, y, optimize=True)
+
+
+def _as64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def forward(prob: Problem, pos, senders, receivers, x, W, num_nodes=None):
+    """out[v] = sum over edges into v of the materialised message m_e."""
+    pos, x, W = _as64(pos), _as64(x), _as64(W)
+    senders = np.asarray(senders, dtype=np.int64)
+    receivers = np.asarray(receivers, dtype=np.int64)
+    N = x.shape[0] if num_nodes is None else num_nodes
+    out = np.zeros((N, prob.D_out, prob.C_out))
+    for a, b in _chunks(prob, len(senders)):
+        s, v = senders[a:b], receivers[a:b]
+        _, _, _, R, Y = _edge_terms(prob, pos, s, v)
+        w_e = np.einsum("ek,kpio->epio", R, W, optimize=True)       # per-edge weights
+        for pi, p in enumerate(prob.paths):
+            U = _coupling(p["C"], _x_block(prob, x, s, p), _y_block(Y, p))
+            msg = np.einsum("eio,eic->eco", w_e[:, pi], U, optimize=True)   # message
+            np.add.at(out[:, _out_rows(prob, p), :], v, msg)
+    return out
+
+
+def backward(prob: Problem, pos, senders, receivers, x, W, g_out):
+    """Materialised adjoints; returns (g_x, g_W, g_pos) for the loss <g_out, out>."""
+    pos, x, W, g_out = _as64(pos), _as64(x), _as64(W), _as64(g_out)
+    senders = np.asarray(senders, dtype=np.int64)
+    receivers = np.asarray(receivers, dtype=np.int64)
+    N = x.shape[0]
+    K = prob.num_basis
+    g_x = np.zeros_like(x)
+    g_W = np.zeros_like(W)
+    g_pos = np.zeros_like(pos)
+    for a, b in _chunks(prob, len(senders)):
+        s, v = senders[a:b], receivers[a:b]
+        r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
+        dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
+        JY = _sh.sh_jacobian(prob.sh_lmax, r)                     # [e, Dsh, 3]
+        w_e = np.einsum("ek,kpio->epio", R, W, optimize=True)
+        g_m = g_out[v]                                           # message adjoint
+        g_w = np.zeros_like(w_e)
+        g_Y = np.zeros_like(Y)
+        for pi, p in enumerate(prob.paths):
+            C = p["C"]
+            xs = _x_block(prob, x, s, p)
+            y = _y_block(Y, p)
+            U = _coupling(C, xs, y)
+            gm = g_m[:, _out_rows(prob, p), :]                     # [e, m3, co]
+            g_w[:, pi] = np.einsum("eic,eco->eio", U, gm, optimize=True)
+            g_U = np.einsum("eio,eco->eic", w_e[:, pi], gm, optimize=True)
+            gx_e = np.einsum("abc,eb,eic->eai", C, y, g_U, optimize=True)
+            np.add.at(g_x[:, _in_rows(prob, p), :], s, gx_e)
+            l2 = p["l2"]
+            g_Y[:, l2 * l2:(l2 + 1) * (l2 + 1)] += np.einsum(
+                "abc,eai,eic->eb", C, xs, g_U, optimize=True)
+        g_W += np.einsum("ek,epio->kpio", R, g_w, optimize=True)
+        g_R = np.einsum("kpio,epio->ek", W, g_w, optimize=True)
+        g_r = (np.einsum("ek,ek->e", g_R, dR)[:, None] * rhat
+               + np.einsum("em,emj->ej", g_Y, JY))
+        np.add.at(g_pos, s, g_r)
+        np.add.at(g_pos, v, -g_r)
+    return g_x, g_W, g_pos
+
+
+def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos):
+    """Gradients of L_F = sum_n <gg_pos[n], g_pos[n]> w.r.t. W, x and g_out.
+
+    With phi_e = gg_pos[s] - gg_pos[v], L_F = sum_e <phi_e, g_r_e>, the
+    derivative of the edge energy <g_m_e, m_e> along phi_e.  The tangents are
+    R_dot = R'(d) (r_hat . phi), Y_dot = J_Y phi, U_dot = CG(x_s, Y_dot) and
+    w_dot = sum_k R_dot[k] W[k]; L_F is linear in W, x and g_out, so no second
+    derivatives of R or Y appear.  d/dpos (the Hessian term) is not computed.
+    """
+    pos, x, W = _as64(pos), _as64(x), _as64(W)
+    g_out, gg_pos = _as64(g_out), _as64(gg_pos)
+    senders = np.asarray(senders, dtype=np.int64)
+    receivers = np.asarray(receivers, dtype=np.int64)
+    K = prob.num_basis
+    d_W = np.zeros_like(W)
+    d_x = np.zeros_like(x)
+    d_gout = np.zeros_like(g_out)
+    for a, b in _chunks(prob, len(senders)):
+        s, v = senders[a:b], receivers[a:b]
+        r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
+        dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
+        JY = _sh.sh_jacobian(prob.sh_lmax, r)
+        phi = gg_pos[s] - gg_pos[v]
+        R_dot = dR * np.einsum("ej,ej->e", rhat, phi)[:, None]
+        Y_dot = np.einsum("emj,ej->em", JY, phi)
+        w_e = np.einsum("ek,kpio->epio", R, W, optimize=True)
+        w_dot = np.einsum("ek,kpio->epio", R_dot, W, optimize=True)
+        g_m = g_out[v]
+        for pi, p in enumerate(prob.paths):
+            C = p["C"]
+            xs = _x_block(prob, x, s, p)
+            y = _y_block(Y, p)
+            y_dot = _y_block(Y_dot, p)
+            U = _coupling(C, xs, y)
+            U_dot = _coupling(C, xs, y_dot)
+            gm = g_m[:, _out_rows(prob, p), :]
+            g_w = np.einsum("eic,eco->eio", U, gm, optimize=True)
+            g_U = np.einsum("eio,eco->eic", w_e[:, pi], gm, optimize=True)
+            gUdot_w = np.einsum("eio,eco->eic", w_dot[:, pi], gm, optimize=True)
+            d_W[:, pi] += (np.einsum("ek,eio->kio", R_dot, g_w, optimize=True)
+                           + np.einsum("ek,eic,eco->kio", R, U_dot, gm, optimize=True))
+            dx_e = (np.einsum("abc,eb,eic->eai", C, y_dot, g_U, optimize=True)
+                    + np.einsum("abc,eb,eic->eai", C, y, gUdot_w, optimize=True))
+            np.add.at(d_x[:, _in_rows(prob, p), :], s, dx_e)
+            dgo = (np.einsum("eio,eic->eco", w_dot[:, pi], U, optimize=True)
+                   + np.einsum("eio,eic->eco", w_e[:, pi], U_dot, optimize=True))
+            np.add.at(d_gout[:, _out_rows(prob, p), :], v, dgo)
+    return d_W, d_x, d_gout

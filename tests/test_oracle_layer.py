@@ -1,0 +1,258 @@
+"""Pins for oracle.tpconv (forward, backward, double backward), all fp64 on CPU.
+
+Each check is independent of the oracle's own formulas:
+  * schedule identity: the receiver-state reassociation (S = sum R x U, then W)
+    gives the materialised result (the Sobek abstract's central claim);
+  * scalar-only irreps reduce to a dense weighted-adjacency SpMM/GEMM;
+  * rotation equivariance, inversion parity, translation and edge-permutation
+    invariance, bilinearity in (x, W);
+  * single-edge closed forms: dot product, vector scaling and cross product;
+  * backward against central differences in random directions; sum of position
+    gradients is zero;
+  * double backward against central differences of <gg_pos, g_pos>.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from equivariant_gnn_tensor_receiver_amd import inputs
+from oracle import cg, radial, sh
+from oracle.tpconv import Problem, backward, csr_receivers, double_backward, forward
+
+from test_oracle_cg import random_rotation, wigner_from_sh
+
+
+def case(ir_in, ir_out, lsh, K, N=14, deg=6.0, seed=0, box=None):
+    prob = Problem(ir_in, ir_out, lsh, K)
+    pos, rowptr, snd, rng = inputs.random_graph(N, deg, seed, box=box)
+    rcv = csr_receivers(rowptr)
+    x = rng.standard_normal((N, prob.D_in, prob.C_in))
+    W = rng.standard_normal(prob.w_shape)
+    g_out = rng.standard_normal((N, prob.D_out, prob.C_out))
+    gg = rng.standard_normal((N, 3))
+    return prob, pos.astype(np.float64), snd.astype(np.int64), rcv, x, W, g_out, gg
+
+
+NAT2 = ("3x0e+3x1o+3x2e", "2x0e+2x1o+2x2e", 2, 4)
+MIXED = ("2x0e+2x1o+2x1e+2x2e", "2x0e+2x0o+2x1o+2x1e+2x2e+2x3o", 2, 3)
+
+
+def block_rotation(prob_irreps, D):
+    mats = [D[l] for _, l, _ in prob_irreps]
+    n = sum(m.shape[0] for m in mats)
+    out = np.zeros((n, n))
+    o = 0
+    for m in mats:
+        k = m.shape[0]
+        out[o:o + k, o:o + k] = m
+        o += k
+    return out
+
+
+def reassociated_forward(prob, pos, snd, rcv, x, W):
+    """S_v[k,p,ci,m3] = sum_e R_e[k] U_e[p,ci,m3]; out_v = sum_{k,p,ci} W S_v."""
+    N = x.shape[0]
+    r = pos[snd] - pos[rcv]
+    d = np.linalg.norm(r, axis=-1)
+    R = radial.bessel_radial(d, prob.num_basis, prob.cutoff)
+    Y = sh.spherical_harmonics(prob.sh_lmax, r)
+    out = np.zeros((N, prob.D_out, prob.C_out))
+    for pi, p in enumerate(prob.paths):
+        o1 = prob.off_in[p["i1"]]
+        xs = x[snd, o1:o1 + 2 * p["l1"] + 1]
+        y = Y[:, p["l2"] ** 2:(p["l2"] + 1) ** 2]
+        U = np.einsum("abc,eai,eb->eic", p["C"], xs, y)
+        S = np.zeros((N, prob.num_basis) + U.shape[1:])
+        np.add.at(S, rcv, R[:, :, None, None] * U[:, None])
+        o3 = prob.off_out[p["i3"]]
+        out[:, o3:o3 + 2 * p["l3"] + 1] += np.einsum("vkic,kio->vco", S, W[:, pi])
+    return out
+
+
+@pytest.mark.parametrize("spec", [NAT2, MIXED])
+def test_schedule_identity(spec):
+    prob, pos, snd, rcv, x, W, *_ = case(*spec)
+    a = forward(prob, pos, snd, rcv, x, W)
+    b = reassociated_forward(prob, pos, snd, rcv, x, W)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+def test_scalar_only_is_weighted_adjacency_gemm():
+    prob, pos, snd, rcv, x, W, *_ = case("5x0e", "4x0e", 0, 6, N=20, deg=5)
+    out = forward(prob, pos, snd, rcv, x, W)
+    N = x.shape[0]
+    d = np.linalg.norm(pos[snd] - pos[rcv], axis=-1)
+    R = radial.bessel_radial(d, 6, 5.0)
+    ref = np.zeros((N, 4))
+    for k in range(6):
+        A = np.zeros((N, N))
+        for e in range(len(snd)):
+            A[rcv[e], snd[e]] += R[e, k]
+        ref += A @ x[:, 0, :] @ W[k, 0]
+    assert np.abs(out[:, 0, :] - ref).max() < 1e-12 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("spec", [NAT2, MIXED, ("2x0e+2x1o+2x2e+2x3o", "2x0e+2x1o+2x2e+2x3o", 3, 2)])
+def test_rotation_equivariance(spec):
+    prob, pos, snd, rcv, x, W, *_ = case(*spec)
+    rng = np.random.default_rng(11)
+    rot = random_rotation(rng)
+    D = [wigner_from_sh(l, rot, rng) for l in range(4)]
+    Din = block_rotation(prob.ir_in, D)
+    Dout = block_rotation(prob.ir_out, D)
+    out = forward(prob, pos, snd, rcv, x, W)
+    out_rot = forward(prob, pos @ rot.T, snd, rcv, np.einsum("ab,nbc->nac", Din, x), W)
+    assert np.abs(out_rot - np.einsum("ab,nbc->nac", Dout, out)).max() < 1e-11 * np.abs(out).max()
+
+
+def test_inversion_translation_permutation_bilinearity():
+    prob, pos, snd, rcv, x, W, *_ = case(*MIXED)
+    out = forward(prob, pos, snd, rcv, x, W)
+    scale = np.abs(out).max()
+    p_in = np.concatenate([[p] * (2 * l + 1) for _, l, p in prob.ir_in])
+    p_out = np.concatenate([[p] * (2 * l + 1) for _, l, p in prob.ir_out])
+    inv = forward(prob, -pos, snd, rcv, x * p_in[None, :, None], W)
+    assert np.abs(inv - out * p_out[None, :, None]).max() < 1e-12 * scale
+    tr = forward(prob, pos + np.array([3.0, -7.0, 11.0]), snd, rcv, x, W)
+    assert np.abs(tr - out).max() < 1e-11 * scale
+    perm = np.random.default_rng(5).permutation(len(snd))
+    pm = forward(prob, pos, snd[perm], rcv[perm], x, W)
+    assert np.abs(pm - out).max() < 1e-12 * scale
+    rng = np.random.default_rng(6)
+    x2, W2 = rng.standard_normal(x.shape), rng.standard_normal(W.shape)
+    lin_x = forward(prob, pos, snd, rcv, 2.0 * x - 3.0 * x2, W)
+    ref_x = 2.0 * out - 3.0 * forward(prob, pos, snd, rcv, x2, W)
+    assert np.abs(lin_x - ref_x).max() < 1e-12 * np.abs(ref_x).max()
+    lin_w = forward(prob, pos, snd, rcv, x, 0.5 * W + 4.0 * W2)
+    ref_w = 0.5 * out + 4.0 * forward(prob, pos, snd, rcv, x, W2)
+    assert np.abs(lin_w - ref_w).max() < 1e-12 * np.abs(ref_w).max()
+
+
+def single_edge(ir_in, ir_out, K=5):
+    prob = Problem(ir_in, ir_out, 1, K)
+    rng = np.random.default_rng(21)
+    pos = np.array([[0.3, -0.2, 0.5], [1.9, 0.8, -1.1]])          # edge 1 -> 0
+    x = rng.standard_normal((2, prob.D_in, 1))
+    W = rng.standard_normal(prob.w_shape)
+    out = forward(prob, pos, np.array([1]), np.array([0]), x, W)
+    r = pos[1] - pos[0]
+    d = np.linalg.norm(r)
+    rhat = r / d
+    rw = float(radial.bessel_radial(np.array([d]), K, 5.0)[0] @ W[:, 0, 0, 0])
+    return out, x, rhat, rw
+
+
+def yzx(v):
+    return np.array([v[1], v[2], v[0]])
+
+
+def xyz(v):
+    return np.array([v[2], v[0], v[1]])
+
+
+def test_single_edge_closed_forms():
+    # 1o x 1o -> 0e: minus the dot product of the sender vector with r_hat
+    out, x, rhat, rw = single_edge("1x1o", "1x0e")
+    assert out[0, 0, 0] == pytest.approx(-rw * xyz(x[1, :, 0]) @ rhat, rel=1e-13)
+    assert np.all(out[1] == 0)                                   # empty segment
+    # 0e x 1o -> 1o: the scalar scales sqrt3 r_hat
+    out, x, rhat, rw = single_edge("1x0e", "1x1o")
+    assert np.abs(out[0, :, 0] - rw * x[1, 0, 0] * math.sqrt(3) * yzx(rhat)).max() < 1e-13 * abs(rw)
+    # 1o x 1o -> 1e (odd sum): the cross product, -sqrt(3/2) (x cross r_hat)
+    out, x, rhat, rw = single_edge("1x1o", "1x1e")
+    ref = -rw * math.sqrt(1.5) * yzx(np.cross(xyz(x[1, :, 0]), rhat))
+    assert np.abs(out[0, :, 0] - ref).max() < 1e-13 * np.abs(ref).max()
+
+
+def test_degenerate_edges():
+    prob = Problem("2x0e+2x1o", "2x0e+2x1o", 1, 3)
+    rng = np.random.default_rng(2)
+    pos = rng.standard_normal((3, 3))
+    x = rng.standard_normal((3, prob.D_in, 2))
+    W = rng.standard_normal(prob.w_shape)
+    # a self loop (d = 0): r_hat := 0, only l2 = 0 paths act, R at its limit
+    out = forward(prob, pos, np.array([2]), np.array([2]), x, W)
+    R0 = math.sqrt(2 / 5.0) * np.arange(1, 4) * math.pi / 5.0
+    assert np.abs(out[2, 0] - x[2, 0] @ np.einsum("k,kio->io", R0, W[:, 0])).max() < 1e-13
+    g = rng.standard_normal(out.shape)
+    _, _, gp = backward(prob, pos, np.array([2]), np.array([2]), x, W, g)
+    assert np.all(gp == 0)
+    # a duplicated edge counts twice; an edge at d >= cutoff contributes nothing
+    one = forward(prob, pos, np.array([0]), np.array([1]), x, W)
+    two = forward(prob, pos, np.array([0, 0]), np.array([1, 1]), x, W)
+    assert np.abs(two - 2 * one).max() < 1e-14 * np.abs(one).max()
+    far = pos.copy()
+    far[0] = far[1] + np.array([5.0, 0.0, 0.0])
+    assert np.all(forward(prob, far, np.array([0]), np.array([1]), x, W) == 0)
+
+
+@pytest.mark.parametrize("spec", [NAT2, MIXED])
+def test_backward_finite_differences(spec):
+    prob, pos, snd, rcv, x, W, g_out, _ = case(*spec, N=10, deg=5)
+    g_x, g_W, g_pos = backward(prob, pos, snd, rcv, x, W, g_out)
+    assert np.abs(g_pos.sum(0)).max() < 1e-12 * np.abs(g_pos).max()
+    rng = np.random.default_rng(99)
+
+    def L(px, pW, ppos):
+        return float((forward(prob, ppos, snd, rcv, px, pW) * g_out).sum())
+
+    h = 1e-5
+    for _ in range(3):
+        dx, dW, dp = rng.standard_normal(x.shape), rng.standard_normal(W.shape), rng.standard_normal(pos.shape)
+        fd_x = (L(x + h * dx, W, pos) - L(x - h * dx, W, pos)) / (2 * h)
+        fd_W = (L(x, W + h * dW, pos) - L(x, W - h * dW, pos)) / (2 * h)
+        fd_p = (L(x, W, pos + h * dp) - L(x, W, pos - h * dp)) / (2 * h)
+        assert fd_x == pytest.approx((g_x * dx).sum(), rel=1e-7)
+        assert fd_W == pytest.approx((g_W * dW).sum(), rel=1e-7)
+        assert fd_p == pytest.approx((g_pos * dp).sum(), rel=1e-6)
+    # element-wise on a few coordinates
+    for n, j in [(0, 0), (3, 2), (7, 1)]:
+        e = np.zeros_like(pos)
+        e[n, j] = h
+        fd = (L(x, W, pos + e) - L(x, W, pos - e)) / (2 * h)
+        assert fd == pytest.approx(g_pos[n, j], rel=1e-6, abs=1e-9)
+
+
+@pytest.mark.parametrize("spec", [NAT2, MIXED])
+def test_double_backward_finite_differences(spec):
+    prob, pos, snd, rcv, x, W, g_out, gg = case(*spec, N=10, deg=5)
+    d_W, d_x, d_gout = double_backward(prob, pos, snd, rcv, x, W, g_out, gg)
+
+    def LF(px, pW, pg):
+        return float((backward(prob, pos, snd, rcv, px, pW, pg)[2] * gg).sum())
+
+    rng = np.random.default_rng(123)
+    h = 1e-5
+    for _ in range(2):
+        dx, dW, dg = rng.standard_normal(x.shape), rng.standard_normal(W.shape), rng.standard_normal(g_out.shape)
+        fd_x = (LF(x + h * dx, W, g_out) - LF(x - h * dx, W, g_out)) / (2 * h)
+        fd_W = (LF(x, W + h * dW, g_out) - LF(x, W - h * dW, g_out)) / (2 * h)
+        fd_g = (LF(x, W, g_out + h * dg) - LF(x, W, g_out - h * dg)) / (2 * h)
+        assert fd_x == pytest.approx((d_x * dx).sum(), rel=1e-7)
+        assert fd_W == pytest.approx((d_W * dW).sum(), rel=1e-7)
+        assert fd_g == pytest.approx((d_gout * dg).sum(), rel=1e-7)
+
+
+def test_sampled_receivers_are_exact():
+    """Restricting to the in-edges of a receiver subset V* gives out[V*] exactly and,
+    with g_out zero outside V*, the full g_x, g_W, g_pos, d_W and d_x exactly and
+    d_grad_out on V* (the scheme used to check the full-size workloads)."""
+    prob, pos, snd, rcv, x, W, g_out, gg = case(*NAT2, N=30, deg=8)
+    Vs = np.array([2, 5, 11, 17, 29])
+    keep = np.isin(rcv, Vs)
+    out = forward(prob, pos, snd, rcv, x, W)
+    sub = forward(prob, pos, snd[keep], rcv[keep], x, W)
+    assert np.array_equal(out[Vs], sub[Vs])
+    gm = np.zeros_like(g_out)
+    gm[Vs] = g_out[Vs]
+    full = backward(prob, pos, snd, rcv, x, W, gm)
+    part = backward(prob, pos, snd[keep], rcv[keep], x, W, gm)
+    for a, b in zip(full, part):
+        assert np.abs(a - b).max() <= 1e-13 * max(1.0, np.abs(a).max())
+    fd = double_backward(prob, pos, snd, rcv, x, W, gm, gg)
+    pd = double_backward(prob, pos, snd[keep], rcv[keep], x, W, gm, gg)
+    for a, b in zip(fd[:2], pd[:2]):            # d_W, d_x: exact everywhere
+        assert np.abs(a - b).max() <= 1e-13 * max(1.0, np.abs(a).max())
+    # d_grad_out does not depend on g_out, so only its V* rows come from V*'s edges
+    assert np.abs(fd[2][Vs] - pd[2][Vs]).max() <= 1e-13 * np.abs(fd[2]).max()
