@@ -1,0 +1,87 @@
+"""Build libtpconv.so in-tree for gfx950.
+
+Steps: compile and run the CG code generator (host C++) to emit the device
+coupling code, compile every translation unit with hipcc in parallel, link
+the shared library next to this file.  Usage: python -m
+equivariant_gnn_tensor_receiver_amd.build [--jobs N]
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+GEN = os.path.join(BUILD, "gen")
+LIB = os.path.join(HERE, "libtpconv.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # packed fp32 VALU ops stay disabled: ordinary fp32 code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    "-munsafe-fp-atomics",
+]
+# (object name, source, extra defines)
+STREAM_VARIANTS = [
+    ("fwd_f32", "kFwd", "float"), ("fwd_bf16", "kFwd", "uint16_t"),
+    ("jvp_f32", "kJvp", "float"), ("jvp_bf16", "kJvp", "uint16_t"),
+    ("bpos_f32", "kBwdPos", "float"), ("bpos_bf16", "kBwdPos", "uint16_t"),
+    ("snd_f32", "kSnd", "float"), ("sndt_f32", "kSndT", "float"),
+]
+UNITS = ([(f"stream_{n}", "stream_inst.hip", [f"-DTP_MODE={m}", f"-DTP_FT={t}", f"-DTP_LAUNCHER=launch_stream_{n}"])
+          for n, m, t in STREAM_VARIANTS]
+         + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("graph", ".hip"), ("api", ".cpp"),
+                                             ("stream_dispatch", ".cpp"), ("plan", ".cpp"))])
+
+
+def run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}")
+    return r.stdout
+
+
+def generate():
+    os.makedirs(GEN, exist_ok=True)
+    exe = os.path.join(BUILD, "cg_codegen")
+    run(["g++", "-O2", "-std=c++17", os.path.join(CSRC, "cg_codegen.cpp"), os.path.join(CSRC, "plan.cpp"),
+         "-I", os.path.join(ROOT, "include"), "-o", exe])
+    run([exe, os.path.join(GEN, "cg_tables.inc")])
+
+
+def compile_one(unit):
+    name, src, defines = unit
+    obj = os.path.join(BUILD, name + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    run([HIPCC] + HIP_FLAGS + defines + ["-I", GEN, "-I", CSRC, "-I", os.path.join(ROOT, "include")] + lang +
+        ["-c", os.path.join(CSRC, src), "-o", obj])
+    return obj
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    generate()
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(compile_one, UNITS))
+    tmp = LIB + ".tmp"
+    run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    args = ap.parse_args()
+    build(args.jobs, verbose=True)
+    sys.exit(0)

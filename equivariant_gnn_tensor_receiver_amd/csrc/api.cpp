@@ -1,0 +1,489 @@
+// C ABI of the streaming CG tensor-product convolution (declared in include/tpconv.h).
+//
+// Pass structure (each step is one kernel launch on the caller's stream):
+//   forward          : receiver stream S_v = sum_e R_e (x) U_e  ->  out = S . W
+//   backward         : gS = g_out . W^T  ->  receiver stream for grad_pos
+//                      S^T . g_out (split, ordered sum) -> grad_W
+//                      sender stream T_s = sum_e R_e (x) CG'(g_out_v, Y_e)  ->  grad_x = T . W^T
+//   double backward  : receiver tangent stream S_dot (along phi_e = gg[s] - gg[v])
+//                      -> d_W = S_dot^T . g_out, d_grad_out = S_dot . W
+//                      sender tangent stream T_dot -> d_x = T_dot . W^T
+// Every intermediate is node-sized; nothing per edge is stored.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "../../include/tpconv.h"
+#include "kernels.h"
+#include "plan.h"
+
+struct tpconv_plan_s {
+  tpconv::Plan plan;
+};
+
+namespace tpconv {
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
+
+// Carves aligned sub-buffers out of the caller's workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  float* take(size_t count) {
+    float* p = reinterpret_cast<float*>(base ? base + used : nullptr);
+    used += align_up(count * sizeof(float));
+    return p;
+  }
+};
+
+int ct_log2_of(int C) {
+  int t = 0;
+  while (t < 6 && (C % (2 << t)) == 0) ++t;
+  return t;
+}
+
+int gw_splits(const Plan& p, int64_t N) {
+  int64_t tiles = 0, min_kr = INT64_MAX;
+  for (const auto& g : p.out_groups) {
+    if (g.paths.empty()) continue;
+    const int64_t M = (int64_t)p.K * g.paths.size() * p.C_in;
+    const int bn = p.C_out >= 64 ? 64 : 32;
+    const int bm = bn == 64 ? 64 : 128;
+    tiles += ((M + bm - 1) / bm) * ((p.C_out + bn - 1) / bn);
+    min_kr = std::min<int64_t>(min_kr, N * (2 * g.l + 1));
+  }
+  if (tiles == 0) return 1;
+  int64_t s = (2048 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, 64);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, min_kr / 256));
+  return (int)std::max<int64_t>(1, s);
+}
+
+size_t state_in_elems(const Plan& p, int64_t N) { return (size_t)(N * p.state_in_per_node); }
+size_t state_out_elems(const Plan& p, int64_t N) { return (size_t)(N * p.state_out_per_node); }
+size_t w_elems(const Plan& p) { return (size_t)p.K * p.P * p.C_in * p.C_out; }
+
+size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
+  return have_saved ? 0 : align_up(state_in_elems(p, N) * 4);
+}
+
+size_t ws_backward(const Plan& p, int64_t N) {
+  return align_up(state_in_elems(p, N) * 4) * 2 + align_up(state_out_elems(p, N) * 4) +
+         align_up((size_t)gw_splits(p, N) * w_elems(p) * 4);
+}
+
+size_t ws_double_backward(const Plan& p, int64_t N) {
+  return align_up(state_in_elems(p, N) * 4) + align_up(state_out_elems(p, N) * 4) +
+         align_up((size_t)gw_splits(p, N) * w_elems(p) * 4);
+}
+
+tpconv_status dev(hipError_t e) { return e == hipSuccess ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE; }
+
+tpconv_status check_graph(const tpconv_graph* g, bool need_csc) {
+  if (!g) return TPCONV_ERROR_INVALID_VALUE;
+  if (g->num_nodes < 0 || g->num_edges < 0 || g->num_nodes >= INT32_MAX || g->num_edges >= INT32_MAX)
+    return TPCONV_ERROR_INVALID_VALUE;
+  if (g->num_nodes > 0 && !g->rowptr) return TPCONV_ERROR_INVALID_VALUE;
+  if (g->num_edges > 0 && (!g->senders || g->num_nodes == 0)) return TPCONV_ERROR_INVALID_VALUE;
+  if (need_csc && g->num_nodes > 0 && (!g->csc_colptr || (g->num_edges > 0 && !g->csc_receivers)))
+    return TPCONV_ERROR_INVALID_VALUE;
+  return TPCONV_SUCCESS;
+}
+
+void fill_common(const Plan& p, StreamArgs& a, int64_t N, const float* pos) {
+  std::memset(&a, 0, sizeof(a));
+  a.num_nodes = (int32_t)N;
+  a.npaths = p.P;
+  a.env_p = p.env_p;
+  a.cutoff = p.cutoff;
+  a.inv_cutoff = 1.0f / p.cutoff;
+  a.pref = (float)std::sqrt(2.0 / p.cutoff);
+  const double e = p.env_p;
+  a.env_a = (float)((e + 1) * (e + 2) / 2);
+  a.env_b = (float)(e * (e + 2));
+  a.env_c = (float)(e * (e + 1) / 2);
+  a.env_d = (float)(e * (e + 1) * (e + 2) / 2);
+  a.pos = pos;
+}
+
+// Receiver-side stream over the CSR: gathered features x [N][D_in][C_in],
+// state S (or S_dot) in the output-group layout.
+void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const void* x) {
+  const int64_t N = g->num_nodes;
+  fill_common(p, a, N, pos);
+  a.ptr = g->rowptr;
+  a.nbr = g->senders;
+  a.feat = x;
+  a.feat_rows = p.D_in;
+  a.C = p.C_in;
+  a.ct_log2 = ct_log2_of(p.C_in);
+  a.ntiles = p.C_in >> a.ct_log2;
+  for (int i = 0; i < p.P; ++i) {
+    const Path& q = p.paths[i];
+    const Group& og = p.out_groups[q.i3];
+    a.paths[i] = StreamPath{q.l1, q.l2, q.l3, p.in_groups[q.i1].row_off, N * og.base_per_node,
+                            (int32_t)og.paths.size() * p.C_in, q.q_out};
+  }
+}
+
+// Sender-side stream over the CSC view: gathered features grad_out [N][D_out][C_out],
+// state T (or T_dot) in the input-group layout.
+void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const float* gout) {
+  const int64_t N = g->num_nodes;
+  fill_common(p, a, N, pos);
+  a.ptr = g->csc_colptr;
+  a.nbr = g->csc_receivers;
+  a.feat = gout;
+  a.feat_rows = p.D_out;
+  a.C = p.C_out;
+  a.ct_log2 = ct_log2_of(p.C_out);
+  a.ntiles = p.C_out >> a.ct_log2;
+  for (int i = 0; i < p.P; ++i) {
+    const Path& q = p.paths[i];
+    const Group& ig = p.in_groups[q.i1];
+    a.paths[i] = StreamPath{q.l1, q.l2, q.l3, p.out_groups[q.i3].row_off, N * ig.base_per_node,
+                            (int32_t)ig.paths.size() * p.C_out, q.q_in};
+  }
+}
+
+int64_t stream_items(const StreamArgs& a) { return (int64_t)a.num_nodes * a.ntiles * a.npaths; }
+
+// Groups of a GEMM over the output irreps (Out, Gs, Gw) or input irreps (Gx).
+int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
+  std::memset(&a, 0, sizeof(a));
+  a.P = p.P;
+  a.K = p.K;
+  a.C_in = p.C_in;
+  a.C_out = p.C_out;
+  a.splits = splits;
+  a.w_bf16 = p.w_dtype == TPCONV_BF16;
+  const bool in_side = kind == kGemmGx;
+  const auto& groups = in_side ? p.in_groups : p.out_groups;
+  a.D_feat = in_side ? p.D_in : p.D_out;
+  int npl = 0, ng = 0;
+  int64_t part = 0;
+  for (const auto& g : groups) {
+    const int npg = (int)g.paths.size();
+    if (npg == 0 && (kind == kGemmGs || kind == kGemmGw)) continue;
+    GemmGroup G{};
+    const int n = 2 * g.l + 1;
+    G.n = n;
+    G.row_off = g.row_off;
+    G.npg = npg;
+    G.plist = npl;
+    for (int q : g.paths) a.path_list[npl++] = q;
+    G.state_off = N * g.base_per_node;
+    switch (kind) {
+      case kGemmOut: G.M = (int)(N * n); G.N = p.C_out; G.Kr = p.K * npg * p.C_in; break;
+      case kGemmGs: G.M = (int)(N * n); G.N = p.K * npg * p.C_in; G.Kr = p.C_out; break;
+      case kGemmGx: G.M = (int)(N * n); G.N = p.C_in; G.Kr = p.K * npg * p.C_out; break;
+      case kGemmGw: G.M = p.K * npg * p.C_in; G.N = p.C_out; G.Kr = (int)(N * n); break;
+    }
+    G.part_off = part;
+    part += (int64_t)splits * G.M * G.N;
+    a.g[ng++] = G;
+  }
+  a.ngroups = ng;
+  const int bn = gemm_bn(kind, a);
+  const int bm = bn == 64 ? 64 : 128;
+  int max_tiles = 0;
+  for (int i = 0; i < ng; ++i) {
+    GemmGroup& G = a.g[i];
+    G.tiles_n = (G.N + bn - 1) / bn;
+    G.tiles = ((G.M + bm - 1) / bm) * G.tiles_n;
+    if (G.M == 0 || G.N == 0) G.tiles = 0;
+    max_tiles = std::max(max_tiles, G.tiles);
+  }
+  return max_tiles;
+}
+
+tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, const float* feat,
+                       const void* W, float* out, int splits, hipStream_t s) {
+  GemmArgs a;
+  const int tiles = gemm_setup(p, kind, N, a, splits);
+  a.state = state;
+  a.feat = feat;
+  a.W = W;
+  a.out = out;
+  return dev(launch_gemm(kind, a, tiles, s));
+}
+
+tpconv_status run_gw(const Plan& p, int64_t N, const float* state, const float* gout, float* part, float* gW,
+                     hipStream_t s) {
+  const int splits = gw_splits(p, N);
+  GemmArgs a;
+  const int tiles = gemm_setup(p, kGemmGw, N, a, splits);
+  a.state = state;
+  a.feat = gout;
+  a.out = part;
+  tpconv_status st = dev(launch_gemm(kGemmGw, a, tiles, s));
+  if (st != TPCONV_SUCCESS) return st;
+  ReduceArgs r;
+  std::memset(&r, 0, sizeof(r));
+  r.ngroups = a.ngroups;
+  r.splits = splits;
+  r.P = p.P;
+  r.C_in = p.C_in;
+  r.C_out = p.C_out;
+  r.part = part;
+  r.gw = gW;
+  std::memcpy(r.path_list, a.path_list, sizeof(r.path_list));
+  std::memcpy(r.g, a.g, sizeof(r.g));
+  int64_t total = 0;
+  for (int i = 0; i < a.ngroups; ++i) total += (int64_t)a.g[i].M * a.g[i].N;
+  if (total == 0) return dev(launch_fill(gW, (int64_t)w_elems(p), 0.f, s));
+  return dev(launch_gw_reduce(r, total, s));
+}
+
+}  // namespace
+}  // namespace tpconv
+
+using namespace tpconv;
+
+extern "C" {
+
+const char* tpconv_status_string(tpconv_status st) {
+  switch (st) {
+    case TPCONV_SUCCESS: return "success";
+    case TPCONV_ERROR_INVALID_VALUE: return "invalid value";
+    case TPCONV_ERROR_IRREPS: return "invalid irreps";
+    case TPCONV_ERROR_GRAPH: return "invalid graph";
+    case TPCONV_ERROR_WORKSPACE: return "workspace missing or too small";
+    case TPCONV_ERROR_UNSUPPORTED: return "unsupported configuration";
+    case TPCONV_ERROR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+tpconv_status tpconv_plan_create(tpconv_plan* out, const tpconv_desc* d) {
+  if (!out || !d) return TPCONV_ERROR_INVALID_VALUE;
+  *out = nullptr;
+  try {
+    auto* h = new (std::nothrow) tpconv_plan_s;
+    if (!h) return TPCONV_ERROR_INVALID_VALUE;
+    const int st = build_plan(d->irreps_in, d->irreps_out, d->sh_lmax, d->num_basis, d->cutoff, d->envelope_p,
+                              d->x_dtype, d->w_dtype, h->plan);
+    if (st != TPCONV_SUCCESS) {
+      delete h;
+      return (tpconv_status)st;
+    }
+    *out = h;
+    return TPCONV_SUCCESS;
+  } catch (...) {
+    return TPCONV_ERROR_INVALID_VALUE;
+  }
+}
+
+tpconv_status tpconv_plan_destroy(tpconv_plan plan) {
+  delete plan;
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_plan_info(tpconv_plan plan, int32_t* num_paths, int64_t* w_numel, int32_t* rows_in,
+                               int32_t* ch_in, int32_t* rows_out, int32_t* ch_out) {
+  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  const Plan& p = plan->plan;
+  if (num_paths) *num_paths = p.P;
+  if (w_numel) *w_numel = (int64_t)w_elems(p);
+  if (rows_in) *rows_in = p.D_in;
+  if (ch_in) *ch_in = p.C_in;
+  if (rows_out) *rows_out = p.D_out;
+  if (ch_out) *ch_out = p.C_out;
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_plan_path(tpconv_plan plan, int32_t path, int32_t* l123, int32_t* idx) {
+  if (!plan || path < 0 || path >= plan->plan.P) return TPCONV_ERROR_INVALID_VALUE;
+  const Path& q = plan->plan.paths[path];
+  if (l123) {
+    l123[0] = q.l1;
+    l123[1] = q.l2;
+    l123[2] = q.l3;
+  }
+  if (idx) {
+    idx[0] = q.i1;
+    idx[1] = q.i3;
+  }
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_plan_cg(tpconv_plan plan, int32_t path, double* out) {
+  if (!plan || !out || path < 0 || path >= plan->plan.P) return TPCONV_ERROR_INVALID_VALUE;
+  const auto& t = plan->plan.cg[path];
+  std::memcpy(out, t.data(), t.size() * sizeof(double));
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_state_size(tpconv_plan plan, int64_t N, size_t* bytes) {
+  if (!plan || !bytes || N < 0) return TPCONV_ERROR_INVALID_VALUE;
+  *bytes = state_in_elems(plan->plan, N) * sizeof(float);
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t N, int64_t E, size_t* bytes) {
+  if (!plan || !bytes || N < 0 || E < 0) return TPCONV_ERROR_INVALID_VALUE;
+  const Plan& p = plan->plan;
+  switch (op) {
+    case TPCONV_OP_FORWARD: *bytes = ws_forward(p, N, false); break;
+    case TPCONV_OP_BACKWARD: *bytes = ws_backward(p, N); break;
+    case TPCONV_OP_DOUBLE_BACKWARD: *bytes = ws_double_backward(p, N); break;
+    case TPCONV_OP_GRAPH_PREPARE: *bytes = graph_csc_workspace(N, E) + kAlign; break;
+    default: return TPCONV_ERROR_INVALID_VALUE;
+  }
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_graph_prepare(tpconv_plan plan, const tpconv_graph* g, int32_t* csc_colptr,
+                                   int32_t* csc_receivers, int32_t validate, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  tpconv_status st = check_graph(g, false);
+  if (st != TPCONV_SUCCESS) return st;
+  const int64_t N = g->num_nodes, E = g->num_edges;
+  if (!csc_colptr || (E > 0 && !csc_receivers)) return TPCONV_ERROR_INVALID_VALUE;
+  const size_t need = graph_csc_workspace(N, E) + kAlign;
+  if (!ws || ws_bytes < need) return TPCONV_ERROR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate && N > 0) {
+    int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + graph_csc_workspace(N, E));
+    if ((st = dev(launch_graph_validate(g->rowptr, g->senders, N, E, flag, s))) != TPCONV_SUCCESS) return st;
+    int32_t host_flag = 0;
+    if (hipMemcpyAsync(&host_flag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return TPCONV_ERROR_DEVICE;
+    if (host_flag) return TPCONV_ERROR_GRAPH;
+  }
+  if (N == 0) return TPCONV_SUCCESS;
+  return dev(graph_csc(g->rowptr, g->senders, N, E, csc_colptr, csc_receivers, ws, ws_bytes, s));
+}
+
+tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                             const void* W, float* out, float* saved_state, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  tpconv_status st = check_graph(g, false);
+  if (st != TPCONV_SUCCESS) return st;
+  const Plan& p = plan->plan;
+  const int64_t N = g->num_nodes;
+  if (N > 0 && (!pos || !x || !W || !out)) return TPCONV_ERROR_INVALID_VALUE;
+  const size_t need = ws_forward(p, N, saved_state != nullptr);
+  if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
+  if (N == 0) return TPCONV_SUCCESS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* S = saved_state ? saved_state : static_cast<float*>(ws);
+  StreamArgs a;
+  recv_args(p, a, g, pos, x);
+  a.state = S;
+  if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+      TPCONV_SUCCESS)
+    return st;
+  return run_gemm(p, kGemmOut, N, S, nullptr, W, out, 1, s);
+}
+
+tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                              const void* W, const float* grad_out, const float* saved_state, float* grad_x,
+                              float* grad_W, float* grad_pos, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  tpconv_status st = check_graph(g, grad_x != nullptr);
+  if (st != TPCONV_SUCCESS) return st;
+  if (!grad_x && !grad_W && !grad_pos) return TPCONV_ERROR_INVALID_VALUE;
+  const Plan& p = plan->plan;
+  const int64_t N = g->num_nodes;
+  if (N > 0 && (!pos || !x || !W || !grad_out)) return TPCONV_ERROR_INVALID_VALUE;
+  const size_t need = ws_backward(p, N);
+  if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    if (grad_W) return dev(launch_fill(grad_W, (int64_t)w_elems(p), 0.f, s));
+    return TPCONV_SUCCESS;
+  }
+  Carver c(ws);
+  float* S_ws = c.take(state_in_elems(p, N));
+  float* gS = c.take(state_in_elems(p, N));
+  float* T = c.take(state_out_elems(p, N));
+  float* part = c.take((size_t)gw_splits(p, N) * w_elems(p));
+
+  if (grad_W) {
+    const float* S = saved_state;
+    if (!S) {
+      StreamArgs a;
+      recv_args(p, a, g, pos, x);
+      a.state = S_ws;
+      if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+          TPCONV_SUCCESS)
+        return st;
+      S = S_ws;
+    }
+    if ((st = run_gw(p, N, S, grad_out, part, grad_W, s)) != TPCONV_SUCCESS) return st;
+  }
+  if (grad_pos) {
+    if ((st = run_gemm(p, kGemmGs, N, nullptr, grad_out, W, gS, 1, s)) != TPCONV_SUCCESS) return st;
+    if ((st = dev(launch_fill(grad_pos, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
+    StreamArgs a;
+    recv_args(p, a, g, pos, x);
+    a.gstate = gS;
+    a.gpos = grad_pos;
+    if ((st = dev(launch_stream(kBwdPos, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+        TPCONV_SUCCESS)
+      return st;
+  }
+  if (grad_x) {
+    StreamArgs a;
+    send_args(p, a, g, pos, grad_out);
+    a.state = T;
+    if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s))) != TPCONV_SUCCESS) return st;
+    if ((st = run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s)) != TPCONV_SUCCESS) return st;
+  }
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                                     const void* W, const float* grad_out, const float* gg_pos, float* d_W,
+                                     float* d_x, float* d_grad_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  tpconv_status st = check_graph(g, d_x != nullptr);
+  if (st != TPCONV_SUCCESS) return st;
+  if (!d_W && !d_x && !d_grad_out) return TPCONV_ERROR_INVALID_VALUE;
+  const Plan& p = plan->plan;
+  const int64_t N = g->num_nodes;
+  if (N > 0 && (!pos || !x || !W || !grad_out || !gg_pos)) return TPCONV_ERROR_INVALID_VALUE;
+  const size_t need = ws_double_backward(p, N);
+  if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N == 0) {
+    if (d_W) return dev(launch_fill(d_W, (int64_t)w_elems(p), 0.f, s));
+    return TPCONV_SUCCESS;
+  }
+  Carver c(ws);
+  float* Sd = c.take(state_in_elems(p, N));
+  float* Td = c.take(state_out_elems(p, N));
+  float* part = c.take((size_t)gw_splits(p, N) * w_elems(p));
+  if (d_W || d_grad_out) {
+    StreamArgs a;
+    recv_args(p, a, g, pos, x);
+    a.ggpos = gg_pos;
+    a.state = Sd;
+    if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+        TPCONV_SUCCESS)
+      return st;
+    if (d_W && (st = run_gw(p, N, Sd, grad_out, part, d_W, s)) != TPCONV_SUCCESS) return st;
+    if (d_grad_out && (st = run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s)) != TPCONV_SUCCESS)
+      return st;
+  }
+  if (d_x) {
+    StreamArgs a;
+    send_args(p, a, g, pos, grad_out);
+    a.ggpos = gg_pos;
+    a.state = Td;
+    if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s))) != TPCONV_SUCCESS) return st;
+    if ((st = run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s)) != TPCONV_SUCCESS) return st;
+  }
+  return TPCONV_SUCCESS;
+}
+
+}  // extern "C"

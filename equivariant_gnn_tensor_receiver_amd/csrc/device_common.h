@@ -1,0 +1,147 @@
+// Device helpers: feature loads, XCD-aware block order, edge geometry
+// (radial basis, real harmonics and their derivatives) in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tpconv {
+
+__device__ __forceinline__ float load_feat(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_feat(const uint16_t* p, int64_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+
+// Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// Remap so that consecutive work items share an XCD and therefore its L2:
+// item = (b % 8) * (grid / 8) + b / 8.  grid must be a multiple of 8.
+__device__ __forceinline__ int64_t xcd_item(int64_t b, int64_t grid) {
+  const int64_t per = grid >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
+// Bessel radial basis with the polynomial envelope, fp32.
+//   R_k(d)  = pref sin(k w d) / d * u(d / c),  w = pi / c
+//   R'_k(d) = pref [(k w) cos(k w d) / d - sin(k w d) / d^2] u + pref sin(k w d) / d * u'(d/c) / c
+// sin/cos of k w d come from one sincos and the angle-addition recurrence.
+template <int K, bool DERIV>
+__device__ __forceinline__ void radial(float d, float cutoff, float inv_cutoff, float pref, int p, float ea,
+                                       float eb, float ec, float ed, float* R, float* dR) {
+  const float w = 3.14159265358979f * inv_cutoff;
+  if (d <= 0.f) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      R[k] = pref * w * (float)(k + 1);
+      if (DERIV) dR[k] = 0.f;
+    }
+    return;
+  }
+  const float x = d * inv_cutoff;
+  if (x >= 1.f) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      R[k] = 0.f;
+      if (DERIV) dR[k] = 0.f;
+    }
+    return;
+  }
+  float xp1 = 1.f;  // x^(p-1)
+  for (int i = 0; i < p - 1; ++i) xp1 *= x;
+  const float xp = xp1 * x;
+  const float u = 1.f - ea * xp + eb * xp * x - ec * xp * x * x;
+  const float omx = 1.f - x;
+  const float du = -ed * xp1 * omx * omx * inv_cutoff;  // du/dd
+  float s1, c1;
+  __sincosf(w * d, &s1, &c1);
+  const float inv_d = 1.f / d;
+  float sk = s1, ck = c1;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float b = pref * sk * inv_d;
+    R[k] = b * u;
+    if (DERIV) {
+      const float db = pref * ((float)(k + 1) * w * ck * inv_d - sk * inv_d * inv_d);
+      dR[k] = db * u + b * du;
+    }
+    const float sn = sk * c1 + ck * s1;
+    const float cn = ck * c1 - sk * s1;
+    sk = sn;
+    ck = cn;
+  }
+}
+
+// Real harmonics of a unit vector (x, y, z), component normalised, rows l^2 + l + m.
+template <int L>
+__device__ __forceinline__ void sh_eval(float x, float y, float z, float* Y) {
+  Y[0] = 1.f;
+  if (L >= 1) {
+    const float s3 = 1.7320508075688772f;
+    Y[1] = s3 * y;
+    Y[2] = s3 * z;
+    Y[3] = s3 * x;
+  }
+  if (L >= 2) {
+    const float s15 = 3.872983346207417f, s5 = 2.23606797749979f;
+    Y[4] = s15 * x * y;
+    Y[5] = s15 * y * z;
+    Y[6] = 0.5f * s5 * (2.f * z * z - x * x - y * y);
+    Y[7] = s15 * x * z;
+    Y[8] = 0.5f * s15 * (x * x - y * y);
+  }
+  if (L >= 3) {
+    const float a = 0.25f * 8.366600265340756f, b = 0.25f * 6.48074069840786f, s105 = 10.246950765959598f,
+                s7 = 2.6457513110645907f;
+    Y[9] = a * y * (3.f * x * x - y * y);
+    Y[10] = s105 * x * y * z;
+    Y[11] = b * y * (4.f * z * z - x * x - y * y);
+    Y[12] = 0.5f * s7 * z * (2.f * z * z - 3.f * x * x - 3.f * y * y);
+    Y[13] = b * x * (4.f * z * z - x * x - y * y);
+    Y[14] = 0.5f * s105 * z * (x * x - y * y);
+    Y[15] = a * x * (x * x - 3.f * y * y);
+  }
+}
+
+// Gradients of the homogeneous polynomials P_lm at the unit vector: G[row][3].
+template <int L>
+__device__ __forceinline__ void sh_poly_grad(float x, float y, float z, float (*G)[3]) {
+  G[0][0] = G[0][1] = G[0][2] = 0.f;
+  if (L >= 1) {
+    const float s3 = 1.7320508075688772f;
+    G[1][0] = 0.f; G[1][1] = s3;  G[1][2] = 0.f;
+    G[2][0] = 0.f; G[2][1] = 0.f; G[2][2] = s3;
+    G[3][0] = s3;  G[3][1] = 0.f; G[3][2] = 0.f;
+  }
+  if (L >= 2) {
+    const float s15 = 3.872983346207417f, s5 = 2.23606797749979f;
+    G[4][0] = s15 * y;  G[4][1] = s15 * x;  G[4][2] = 0.f;
+    G[5][0] = 0.f;      G[5][1] = s15 * z;  G[5][2] = s15 * y;
+    G[6][0] = -s5 * x;  G[6][1] = -s5 * y;  G[6][2] = 2.f * s5 * z;
+    G[7][0] = s15 * z;  G[7][1] = 0.f;      G[7][2] = s15 * x;
+    G[8][0] = s15 * x;  G[8][1] = -s15 * y; G[8][2] = 0.f;
+  }
+  if (L >= 3) {
+    const float a = 0.25f * 8.366600265340756f, b = 0.25f * 6.48074069840786f, s105 = 10.246950765959598f,
+                h7 = 0.5f * 2.6457513110645907f, h105 = 0.5f * 10.246950765959598f;
+    G[9][0] = a * 6.f * x * y;  G[9][1] = a * 3.f * (x * x - y * y);  G[9][2] = 0.f;
+    G[10][0] = s105 * y * z;    G[10][1] = s105 * x * z;              G[10][2] = s105 * x * y;
+    G[11][0] = -2.f * b * x * y;
+    G[11][1] = b * (4.f * z * z - x * x - 3.f * y * y);
+    G[11][2] = 8.f * b * y * z;
+    G[12][0] = -6.f * h7 * x * z;
+    G[12][1] = -6.f * h7 * y * z;
+    G[12][2] = h7 * (6.f * z * z - 3.f * x * x - 3.f * y * y);
+    G[13][0] = b * (4.f * z * z - 3.f * x * x - y * y);
+    G[13][1] = -2.f * b * x * y;
+    G[13][2] = 8.f * b * x * z;
+    G[14][0] = 2.f * h105 * x * z;  G[14][1] = -2.f * h105 * y * z;  G[14][2] = h105 * (x * x - y * y);
+    G[15][0] = a * 3.f * (x * x - y * y);  G[15][1] = -a * 6.f * x * y;  G[15][2] = 0.f;
+  }
+}
+
+constexpr int sh_count(int L) { return (L + 1) * (L + 1); }
+constexpr int sh_degree_of_row(int row) {
+  return row == 0 ? 0 : row < 4 ? 1 : row < 9 ? 2 : 3;
+}
+
+}  // namespace tpconv

@@ -1,0 +1,109 @@
+// Kernel argument blocks and host launchers shared by the C-ABI layer and the
+// kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace tpconv {
+
+// Edge-stream kernel modes.  Receiver-side modes walk the receiver-sorted CSR
+// (self = receiver v, neighbour = sender s, gathered features = x[s]);
+// sender-side modes walk the sender-sorted view (self = s, neighbour = v,
+// gathered features = grad_out[v]).
+enum StreamMode : int {
+  kFwd = 0,      // S_v   += R (x) CG(x_s, Y)                      (receiver)
+  kJvp = 1,      // Sd_v  += Rd (x) CG(x_s, Y) + R (x) CG(x_s, Yd)  (receiver)
+  kSnd = 2,      // T_s   += R (x) CG'(g_v, Y)                      (sender)
+  kSndT = 3,     // Td_s  += R (x) CG'(g_v, Yd) + Rd (x) CG'(g_v, Y) (sender)
+  kBwdPos = 4,   // grad_pos from gS_v and the edge geometry        (receiver)
+};
+
+struct StreamPath {
+  int32_t l1, l2, l3;
+  int32_t feat_row;     // first row of the gathered block (x rows of l1, or grad_out rows of l3)
+  int64_t state_base;   // element offset of the group's state block
+  int32_t cols_per_k;   // (#paths of the group) * channels
+  int32_t q;            // path index inside its group
+};
+
+struct StreamArgs {
+  int32_t num_nodes;
+  int32_t npaths;
+  int32_t ct_log2;      // channel tile = 1 << ct_log2 (<= 64); edge slots per wave = 64 / tile
+  int32_t ntiles;       // channels / tile
+  int32_t feat_rows;    // rows per node of the gathered feature tensor
+  int32_t C;            // channels of the gathered features and of the state
+  int32_t env_p;
+  float cutoff, inv_cutoff, pref;          // pref = sqrt(2 / cutoff)
+  float env_a, env_b, env_c, env_d;        // u = 1 - a x^p + b x^(p+1) - c x^(p+2); u' = -d x^(p-1) (1-x)^2
+  const int32_t* ptr;   // [N+1] segment offsets of self
+  const int32_t* nbr;   // [E] neighbour of each edge
+  const float* pos;     // [N][3]
+  const float* ggpos;   // [N][3] tangent (kJvp, kSndT)
+  const void* feat;     // [N][feat_rows][C], fp32 or bf16
+  float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
+  const float* gstate;  // receiver-state cotangent gS (kBwdPos)
+  float* gpos;          // position gradient, accumulated (kBwdPos)
+  StreamPath paths[kMaxPaths];
+};
+
+// Dense contractions with W, one group per launch slice.
+enum GemmKind : int {
+  kGemmOut = 0,  // out[(v,m3), co]   = sum_j S_g[(v,m3), j] W[j -> (k,p,ci), co]
+  kGemmGs = 1,   // gS_g[(v,m3), j]   = sum_co g_out[(v,m3), co] W[j -> (k,p,ci), co]
+  kGemmGx = 2,   // g_x[(s,m1), ci]   = sum_j T_g[(s,m1), j] W[j -> (k,p,co), ci]
+  kGemmGw = 3,   // part[(k,p,ci), co] = sum_(v,m3) S_g[(v,m3), j] g_out[(v,m3), co]  (split over rows)
+};
+
+struct GemmGroup {
+  int32_t M, N, Kr;          // C[M][N] = sum_r A[M][r] B[r][N]
+  int32_t n;                 // 2l+1 of the group's irrep (rows per node)
+  int32_t row_off;           // row offset of the irrep in the feature tensor it touches
+  int32_t npg;               // paths in the group
+  int32_t plist;             // first entry of the group's path list in GemmArgs::path_list
+  int32_t tiles_n;           // column tiles
+  int32_t tiles;             // total tiles (row tiles * column tiles)
+  int64_t state_off;         // element offset of the group's state block
+  int64_t part_off;          // element offset of the group's split-K partials (kGemmGw)
+};
+
+struct GemmArgs {
+  int32_t ngroups;
+  int32_t P, K, C_in, C_out, D_feat;  // D_feat: rows per node of the feature tensor touched
+  int32_t splits;                     // kGemmGw: reduction splits
+  int32_t w_bf16;
+  const float* state;                 // S_g / T_g blocks (A for Out, Gx, Gw)
+  const float* feat;                  // g_out (A for Gs, B for Gw)
+  const void* W;                      // fp32 or bf16
+  float* out;                         // out / gS / g_x / partials
+  int32_t path_list[kMaxPaths];
+  GemmGroup g[kMaxGroups];
+};
+
+struct ReduceArgs {
+  int32_t ngroups, splits, P, C_in, C_out;
+  const float* part;
+  float* gw;
+  int32_t path_list[kMaxPaths];
+  GemmGroup g[kMaxGroups];
+};
+
+// Host launchers (return a hipError_t).
+hipError_t launch_stream(int mode, int lmax, int K, bool feat_bf16, const StreamArgs& a, int64_t items,
+                         hipStream_t s);
+hipError_t launch_gemm(int kind, const GemmArgs& a, int max_tiles, hipStream_t s);
+int gemm_bn(int kind, const GemmArgs& a);  // column tile (64 or 32); row tile = 4096 / (32 * bn) * 32
+hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
+hipError_t launch_zero_rows(float* base, int64_t N, int rows, int C, int row_off, int nrows, hipStream_t s);
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+hipError_t launch_graph_validate(const int32_t* rowptr, const int32_t* senders, int64_t N, int64_t E,
+                                 int32_t* flag, hipStream_t s);
+hipError_t graph_csc(const int32_t* rowptr, const int32_t* senders, int64_t N, int64_t E, int32_t* colptr,
+                     int32_t* receivers_out, void* ws, size_t ws_bytes, hipStream_t s);
+size_t graph_csc_workspace(int64_t N, int64_t E);
+
+}  // namespace tpconv

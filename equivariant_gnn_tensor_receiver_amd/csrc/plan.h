@@ -1,0 +1,70 @@
+// Host-side plan: irreps, parity-allowed paths, real CG tables and the layout
+// of the node-sized receiver / sender states.  Pure C++ (no device calls).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace tpconv {
+
+constexpr int kMaxL = 3;        // largest degree of any irrep or harmonic
+constexpr int kMaxPaths = 64;   // paths per plan (kernel argument tables)
+constexpr int kMaxGroups = 16;  // irreps per side
+
+struct Irrep {
+  int mul;
+  int l;
+  int parity;  // +1 even, -1 odd
+};
+
+// One parity-allowed coupling (input irrep i1 of degree l1) x (harmonic of
+// degree l2) -> (output irrep i3 of degree l3).
+struct Path {
+  int i1, l1, l2, i3, l3;
+  int q_out;  // index of the path among the paths of output irrep i3
+  int q_in;   // index of the path among the paths of input irrep i1
+};
+
+// Paths that write one output irrep (receiver state S) or read one input
+// irrep (sender state T).  The state of group g is a row-major matrix with
+// rows (node, m) and columns (k, q, channel):
+//   element (node, m, k, q, c) at base + ((node * n + m) * K + k) * cols_per_k + q * C + c
+// with n = 2l+1 and cols_per_k = (#paths in the group) * C.
+struct Group {
+  int irrep;                // irrep index on its side
+  int l;                    // its degree
+  int row_off;              // row offset of the irrep in the feature layout
+  std::vector<int> paths;   // plan path indices, in plan order
+  int64_t base_per_node;    // element offset of this group's state = N * base_per_node
+};
+
+struct Plan {
+  std::vector<Irrep> in, out;
+  int sh_lmax = 0, K = 0, env_p = 6;
+  float cutoff = 5.f;
+  int x_dtype = 0, w_dtype = 0;
+  int C_in = 0, C_out = 0, D_in = 0, D_out = 0, P = 0;
+  int lmax = 0;  // max degree over irreps and harmonics
+  std::vector<Path> paths;
+  std::vector<std::vector<double>> cg;  // dense [2l1+1][2l2+1][2l3+1] per path
+  std::vector<Group> out_groups;        // indexed by output irrep
+  std::vector<Group> in_groups;         // indexed by input irrep
+  int64_t state_in_per_node = 0;        // K * C_in * sum_p (2l3+1)
+  int64_t state_out_per_node = 0;       // K * C_out * sum_p (2l1+1)
+};
+
+// Parse "32x0e+32x1o"; returns false on a malformed string.
+bool parse_irreps(const std::string& s, std::vector<Irrep>& out);
+
+// <j1 m1 j2 m2 | J M> (Racah closed form, long double).
+long double cg_complex(int j1, int m1, int j2, int m2, int J, int M);
+
+// Real-basis table C[m1][m2][m3] (dense, row-major); false if the triangle rule fails.
+bool real_cg(int l1, int l2, int l3, std::vector<double>& out);
+
+// Returns 0 on success or a tpconv_status code.
+int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K, float cutoff,
+               int env_p, int x_dtype, int w_dtype, Plan& plan);
+
+}  // namespace tpconv

@@ -1,0 +1,120 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI
+and compare with the fp64 oracle on the same seeded inputs.
+
+Tolerances (per tensor, against the oracle's max magnitude):
+  forward:   max|gpu - oracle| <= 1e-4 * max|oracle|
+  gradients: max|gpu - oracle| <= 1e-3 * max|oracle|   (backward and double backward)
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from equivariant_gnn_tensor_receiver_amd import inputs
+from equivariant_gnn_tensor_receiver_amd import tpconv as tp
+from oracle import tpconv as otp
+
+FWD_TOL = 1e-4
+GRAD_TOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.abs(ref).max() if ref.size else 0.0
+    if scale == 0.0:
+        return float(np.abs(gpu).max() if gpu.size else 0.0)
+    return float(np.abs(gpu - ref).max() / scale)
+
+
+class DeviceCase:
+    """Seeded problem uploaded to cuda:0 plus the matching oracle Problem."""
+
+    def __init__(self, irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype="f32"):
+        import torch
+
+        self.dev = torch.device("cuda:0")
+        xd = tp.TPCONV_BF16 if dtype == "bf16" else tp.TPCONV_F32
+        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, 6, xd, xd)
+        self.prob = otp.Problem(irreps_in, irreps_out, sh_lmax, K)
+        assert self.plan.num_paths == self.prob.P
+        N = len(rowptr) - 1
+        t = inputs.make_tensors(rng, N, self.prob.D_in, self.prob.C_in, self.prob.D_out, self.prob.C_out, K,
+                                self.prob.P, dtype)
+        self.np = dict(pos=pos, rowptr=rowptr, senders=senders, **t)
+        self.receivers = otp.csr_receivers(rowptr)
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+        self.pos = to(pos.astype(np.float32))
+        self.rowptr = to(rowptr.astype(np.int32))
+        self.senders = to(senders.astype(np.int32)) if len(senders) else torch.zeros(1, dtype=torch.int32,
+                                                                                      device=self.dev)
+        if dtype == "bf16":
+            self.x = tp.to_device_bf16(t["x"], self.dev)
+            self.W = tp.to_device_bf16(t["W"], self.dev)
+        else:
+            self.x = to(t["x"])
+            self.W = to(t["W"])
+        self.g_out = to(t["g_out"])
+        self.gg = to(t["gg_pos"])
+        g = tp.Graph(self.rowptr, self.senders)
+        g.num_edges = len(senders)
+        self.graph = tp.tpconv_graph_prepare(self.plan, g, validate=True)
+
+    def forward(self, **kw):
+        import torch
+
+        out = tp.tpconv_forward(self.plan, self.graph, self.pos, self.x, self.W, **kw)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def backward(self, g_out=None, **kw):
+        import torch
+
+        go = self.g_out if g_out is None else g_out
+        r = tp.tpconv_backward(self.plan, self.graph, self.pos, self.x, self.W, go, **kw)
+        torch.cuda.synchronize()
+        return [None if a is None else a.cpu().numpy() for a in r]
+
+    def double_backward(self, g_out=None, **kw):
+        import torch
+
+        go = self.g_out if g_out is None else g_out
+        r = tp.tpconv_double_backward(self.plan, self.graph, self.pos, self.x, self.W, go, self.gg, **kw)
+        torch.cuda.synchronize()
+        return [None if a is None else a.cpu().numpy() for a in r]
+
+    # oracle side
+    def o_forward(self, snd=None, rcv=None):
+        n = self.np
+        snd = n["senders"] if snd is None else snd
+        rcv = self.receivers if rcv is None else rcv
+        return otp.forward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], num_nodes=len(n["rowptr"]) - 1)
+
+    def o_backward(self, g_out, snd=None, rcv=None):
+        n = self.np
+        snd = n["senders"] if snd is None else snd
+        rcv = self.receivers if rcv is None else rcv
+        return otp.backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out)
+
+    def o_double_backward(self, g_out, snd=None, rcv=None):
+        n = self.np
+        snd = n["senders"] if snd is None else snd
+        rcv = self.receivers if rcv is None else rcv
+        return otp.double_backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"])
+
+
+def small_case(irreps_in, irreps_out, sh_lmax, K, N, deg, seed, dtype="f32"):
+    pos, rowptr, senders, rng = inputs.random_graph(N, deg, seed)
+    return DeviceCase(irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype)
+
+
+def workload_case(name):
+    w = inputs.WORKLOADS[name]
+    pos, rowptr, senders, _, rng = inputs.make_graph(w)
+    return DeviceCase(w.irreps, w.irreps, w.lmax, w.num_basis, pos, rowptr, senders, rng, w.dtype)

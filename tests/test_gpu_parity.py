@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Element-wise at sizes the oracle finishes in seconds (several channel tiles,
+ragged edge batches, every path family), with edge cases; sampled receivers at
+the full workload sizes live in test_gpu_workloads.py.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+from gpu_cases import FWD_TOL, GRAD_TOL, DeviceCase, rel_err, say, small_case
+from equivariant_gnn_tensor_receiver_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, irreps_in, irreps_out, sh_lmax, K, N, deg, dtype
+    ("l1_c8", "8x0e+8x1o", "8x0e+8x1o", 1, 8, 60, 12, "f32"),
+    ("l2_c32", "32x0e+32x1o+32x2e", "32x0e+32x1o+32x2e", 2, 8, 150, 20, "f32"),
+    ("l2_c128_k16", "128x0e+128x1o+128x2e", "128x0e+128x1o+128x2e", 2, 16, 40, 14, "f32"),
+    ("l3_c16_bf16", "16x0e+16x1o+16x2e+16x3o", "16x0e+16x1o+16x2e+16x3o", 3, 8, 60, 14, "bf16"),
+    ("l3_c64_bf16", "64x0e+64x1o+64x2e+64x3o", "64x0e+64x1o+64x2e+64x3o", 3, 8, 30, 10, "bf16"),
+    ("mixed_cin_ne_cout", "16x0e+16x1o+16x1e+16x2e", "8x0e+8x0o+8x1o+8x1e+8x2e+8x3o", 2, 8, 50, 12, "f32"),
+    ("c3_odd_channels", "3x0e+3x1o+3x2e", "5x0e+5x1o", 2, 16, 40, 90, "f32"),
+    ("scalar_only", "24x0e", "40x0e", 0, 8, 70, 10, "f32"),
+]
+
+
+@pytest.fixture(scope="module", params=SMALL, ids=[c[0] for c in SMALL])
+def case(request):
+    name, ii, io, lsh, K, N, deg, dt = request.param
+    say(f"[case] {name}: N={N} deg~{deg} irreps_in={ii} irreps_out={io} lsh={lsh} K={K} {dt}")
+    return DeviceCase(ii, io, lsh, K, *inputs.random_graph(N, deg, seed=zlib.crc32(name.encode()) % 1000), dtype=dt)
+
+
+def test_forward(case):
+    say("[step] forward")
+    out = case.forward()
+    ref = case.o_forward()
+    e = rel_err(out, ref)
+    say(f"  fwd rel err {e:.2e}")
+    assert e <= FWD_TOL
+
+
+def test_forward_saved_state_and_determinism(case):
+    import torch
+
+    say("[step] forward with saved state, twice")
+    S = torch.empty(case.plan.state_size(case.graph.num_nodes) // 4, dtype=torch.float32, device=case.dev)
+    a = case.forward(saved_state=S)
+    b = case.forward()
+    assert np.array_equal(a, b)
+
+
+def test_backward(case):
+    say("[step] backward")
+    gx, gW, gp = case.backward()
+    rx, rW, rp = case.o_backward(case.np["g_out"])
+    ex, eW, ep = rel_err(gx, rx), rel_err(gW, rW), rel_err(gp, rp)
+    say(f"  bwd rel err x {ex:.2e} W {eW:.2e} pos {ep:.2e}")
+    assert ex <= GRAD_TOL and eW <= GRAD_TOL and ep <= GRAD_TOL
+
+
+def test_backward_with_saved_state_and_subsets(case):
+    import torch
+
+    say("[step] backward with saved state / partial outputs")
+    S = torch.empty(case.plan.state_size(case.graph.num_nodes) // 4, dtype=torch.float32, device=case.dev)
+    case.forward(saved_state=S)
+    gx, gW, gp = case.backward(saved_state=S)
+    gx2, gW2, gp2 = case.backward(want=("W",))
+    assert gx2 is None and gp2 is None
+    assert np.array_equal(gW, gW2)
+    _, _, gp3 = case.backward(want=("pos",))
+    assert rel_err(gp3, gp) <= 1e-6
+
+
+def test_double_backward(case):
+    say("[step] double backward")
+    dW, dx, dg = case.double_backward()
+    rW, rx, rg = case.o_double_backward(case.np["g_out"])
+    eW, ex, eg = rel_err(dW, rW), rel_err(dx, rx), rel_err(dg, rg)
+    say(f"  dbwd rel err W {eW:.2e} x {ex:.2e} g_out {eg:.2e}")
+    assert eW <= GRAD_TOL and ex <= GRAD_TOL and eg <= GRAD_TOL
+
+
+def test_tiny_workload_forward():
+    w = inputs.WORKLOADS["tiny"]
+    pos, rowptr, senders, _, rng = inputs.make_graph(w)
+    assert len(senders) == 512 and np.all(np.diff(rowptr) == 8)
+    say("[case] tiny workload: N=64 E=512")
+    c = DeviceCase(w.irreps, w.irreps, w.lmax, w.num_basis, pos, rowptr, senders, rng, w.dtype)
+    e = rel_err(c.forward(), c.o_forward())
+    say(f"  fwd rel err {e:.2e}")
+    assert e <= FWD_TOL
+
+
+def edge_case_graph(kind):
+    rng = np.random.default_rng(5)
+    N = 9
+    pos = (rng.random((N, 3)) * 4.0).astype(np.float32)
+    if kind == "empty":
+        snd, rcv = np.zeros(0, np.int64), np.zeros(0, np.int64)
+    elif kind == "self_loop_duplicates_isolated":
+        # node 8 has no edges at all; node 3 has a self loop; 1->2 appears twice
+        snd = np.array([1, 1, 3, 0, 4, 5, 6, 7, 2, 0])
+        rcv = np.array([2, 2, 3, 1, 0, 0, 5, 5, 7, 7])
+    elif kind == "one_node":
+        N = 1
+        pos = pos[:1]
+        snd, rcv = np.array([0]), np.array([0])
+    elif kind == "long_segment":
+        # one receiver with 150 in-edges (three batches, ragged) from coincident-free senders
+        N = 151
+        pos = (rng.random((N, 3)) * 3.0).astype(np.float32)
+        snd = np.arange(1, N)
+        rcv = np.zeros(N - 1, np.int64)
+    rowptr, senders = inputs.edges_to_csr(N, snd.astype(np.int64), rcv.astype(np.int64))
+    return pos, rowptr, senders, rng
+
+
+@pytest.mark.parametrize("kind", ["empty", "self_loop_duplicates_isolated", "one_node", "long_segment"])
+def test_edge_cases(kind):
+    say(f"[case] edge case {kind}")
+    pos, rowptr, senders, rng = edge_case_graph(kind)
+    c = DeviceCase("8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8, pos, rowptr, senders, rng)
+    out = c.forward()
+    ref = c.o_forward()
+    assert rel_err(out, ref) <= FWD_TOL
+    if kind != "empty":
+        assert np.all(out[np.diff(rowptr) == 0] == 0)
+    gx, gW, gp = c.backward()
+    rx, rW, rp = c.o_backward(c.np["g_out"])
+    assert rel_err(gx, rx) <= GRAD_TOL and rel_err(gW, rW) <= GRAD_TOL and rel_err(gp, rp) <= GRAD_TOL
+    dW, dx, dg = c.double_backward()
+    sW, sx, sg = c.o_double_backward(c.np["g_out"])
+    assert rel_err(dW, sW) <= GRAD_TOL and rel_err(dx, sx) <= GRAD_TOL and rel_err(dg, sg) <= GRAD_TOL
+
+
+def test_graph_prepare_matches_stable_sort_and_validation():
+    import torch
+    from equivariant_gnn_tensor_receiver_amd import tpconv as tp
+
+    say("[case] graph prepare")
+    pos, rowptr, senders, rng = inputs.random_graph(500, 25, seed=3)
+    c = DeviceCase("4x0e", "4x0e", 0, 8, pos, rowptr, senders, rng)
+    rcv = np.repeat(np.arange(500), np.diff(rowptr))
+    order = np.argsort(senders, kind="stable")
+    want_colptr = np.concatenate([[0], np.cumsum(np.bincount(senders, minlength=500))])
+    assert np.array_equal(c.graph.csc_colptr.cpu().numpy(), want_colptr)
+    assert np.array_equal(c.graph.csc_receivers.cpu().numpy()[:len(senders)], rcv[order])
+    # a CSR that fails validation: the call reports TPCONV_ERROR_GRAPH
+    bad_rowptr = torch.from_numpy(rowptr.astype(np.int32)).cuda()
+    bad_rowptr[-1] = bad_rowptr[-1] - 1
+    with pytest.raises(tp.TpconvError) as e:
+        g = tp.Graph(bad_rowptr, c.senders)
+        tp.tpconv_graph_prepare(c.plan, g, validate=True)
+    assert e.value.status == 3
+    bad_snd = c.senders.clone()
+    bad_snd[7] = 500
+    with pytest.raises(tp.TpconvError) as e:
+        tp.tpconv_graph_prepare(c.plan, tp.Graph(c.rowptr, bad_snd), validate=True)
+    assert e.value.status == 3
