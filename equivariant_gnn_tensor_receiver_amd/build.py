@@ -39,7 +39,8 @@ STREAM_VARIANTS = [
 UNITS = ([(f"stream_{n}", "stream_inst.hip", [f"-DTP_MODE={m}", f"-DTP_FT={t}", f"-DTP_LAUNCHER=launch_stream_{n}"])
           for n, m, t in STREAM_VARIANTS]
          + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("graph", ".hip"), ("api", ".cpp"),
-                                             ("stream_dispatch", ".cpp"), ("plan", ".cpp"))])
+                                             ("stream_dispatch", ".cpp"), ("plan", ".cpp"),
+                                             ("timing", ".cpp"))])
 
 
 def run(cmd):

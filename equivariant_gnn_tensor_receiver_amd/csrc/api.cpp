@@ -14,10 +14,12 @@
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "../../include/tpconv.h"
 #include "kernels.h"
 #include "plan.h"
+#include "timing.h"
 
 struct tpconv_plan_s {
   tpconv::Plan plan;
@@ -52,8 +54,8 @@ int gw_splits(const Plan& p, int64_t N) {
   for (const auto& g : p.out_groups) {
     if (g.paths.empty()) continue;
     const int64_t M = (int64_t)p.K * g.paths.size() * p.C_in;
-    const int bn = p.C_out >= 64 ? 64 : 32;
-    const int bm = bn == 64 ? 64 : 128;
+    const int bn = p.C_out > 64 ? 128 : (p.C_out > 32 ? 64 : 32);
+    const int bm = gemm_bm();
     tiles += ((M + bm - 1) / bm) * ((p.C_out + bn - 1) / bn);
     min_kr = std::min<int64_t>(min_kr, N * (2 * g.l + 1));
   }
@@ -111,6 +113,13 @@ void fill_common(const Plan& p, StreamArgs& a, int64_t N, const float* pos) {
   a.pos = pos;
 }
 
+void set_units(const Plan& p, StreamArgs& a, const std::vector<std::vector<int>>& units) {
+  a.nunits = (int32_t)units.size();
+  a.bundled = p.natural ? 1 : 0;
+  for (size_t u = 0; u < units.size(); ++u)
+    for (size_t i = 0; i < units[u].size(); ++i) a.unit_paths[u][i] = (int8_t)units[u][i];
+}
+
 // Receiver-side stream over the CSR: gathered features x [N][D_in][C_in],
 // state S (or S_dot) in the output-group layout.
 void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const void* x) {
@@ -129,6 +138,7 @@ void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
     a.paths[i] = StreamPath{q.l1, q.l2, q.l3, p.in_groups[q.i1].row_off, N * og.base_per_node,
                             (int32_t)og.paths.size() * p.C_in, q.q_out};
   }
+  set_units(p, a, p.recv_units);
 }
 
 // Sender-side stream over the CSC view: gathered features grad_out [N][D_out][C_out],
@@ -149,9 +159,11 @@ void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
     a.paths[i] = StreamPath{q.l1, q.l2, q.l3, p.out_groups[q.i3].row_off, N * ig.base_per_node,
                             (int32_t)ig.paths.size() * p.C_out, q.q_in};
   }
+  set_units(p, a, p.send_units);
 }
 
-int64_t stream_items(const StreamArgs& a) { return (int64_t)a.num_nodes * a.ntiles * a.npaths; }
+// Work items of a stream launch: one wave per (node, channel tile, unit).
+int64_t stream_items(const StreamArgs& a) { return (int64_t)a.num_nodes * a.ntiles * a.nunits; }
 
 // Groups of a GEMM over the output irreps (Out, Gs, Gw) or input irreps (Gx).
 int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
@@ -162,6 +174,7 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
   a.C_out = p.C_out;
   a.splits = splits;
   a.w_bf16 = p.w_dtype == TPCONV_BF16;
+  a.vec = (p.C_in % 16 == 0) && (p.C_out % 16 == 0);
   const bool in_side = kind == kGemmGx;
   const auto& groups = in_side ? p.in_groups : p.out_groups;
   a.D_feat = in_side ? p.D_in : p.D_out;
@@ -190,7 +203,7 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
   }
   a.ngroups = ng;
   const int bn = gemm_bn(kind, a);
-  const int bm = bn == 64 ? 64 : 128;
+  const int bm = gemm_bm();
   int max_tiles = 0;
   for (int i = 0; i < ng; ++i) {
     GemmGroup& G = a.g[i];
@@ -483,6 +496,20 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
     if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s))) != TPCONV_SUCCESS) return st;
     if ((st = run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s)) != TPCONV_SUCCESS) return st;
   }
+  return TPCONV_SUCCESS;
+}
+
+tpconv_status tpconv_kernel_timing(int32_t enable) {
+  return timing_set(enable != 0) ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE;
+}
+
+tpconv_status tpconv_kernel_timing_read(int32_t kernel, int64_t* launches, double* total_ms) {
+  if (kernel < 0 || kernel >= kcCount || !launches || !total_ms) return TPCONV_ERROR_INVALID_VALUE;
+  long long n = 0;
+  double ms = 0.0;
+  if (!timing_read(kernel, &n, &ms)) return TPCONV_ERROR_DEVICE;
+  *launches = n;
+  *total_ms = ms;
   return TPCONV_SUCCESS;
 }
 

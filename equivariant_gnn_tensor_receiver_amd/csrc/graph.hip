@@ -8,6 +8,7 @@
 // only receiver ids, the sorted segment is unique and the result is
 // deterministic even though the scatter order is not.
 #include "kernels.h"
+#include "timing.h"
 
 namespace tpconv {
 
@@ -116,6 +117,7 @@ hipError_t launch_graph_validate(const int32_t* rowptr, const int32_t* senders, 
 hipError_t graph_csc(const int32_t* rowptr, const int32_t* senders, int64_t N, int64_t E, int32_t* colptr,
                      int32_t* receivers_out, void* ws, size_t ws_bytes, hipStream_t s) {
   if (ws_bytes < graph_csc_workspace(N, E)) return hipErrorInvalidValue;
+  TimingScope ts(kcGraph, s);
   int32_t* cursor = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(fill_i32, dim3(blocks(N + 1, 256)), dim3(256), 0, s, colptr, N + 1, 0);
   if (E > 0) hipLaunchKernelGGL(histogram_kernel, dim3(blocks(E, 256)), dim3(256), 0, s, senders, E, colptr);

@@ -30,9 +30,13 @@ struct StreamPath {
   int32_t q;            // path index inside its group
 };
 
+constexpr int kMaxUnitPaths = 8;  // member paths per stream work unit
+
 struct StreamArgs {
   int32_t num_nodes;
   int32_t npaths;
+  int32_t nunits;       // work units per (node, tile)
+  int32_t bundled;      // units are the compile-time bundles of the natural path list
   int32_t ct_log2;      // channel tile = 1 << ct_log2 (<= 64); edge slots per wave = 64 / tile
   int32_t ntiles;       // channels / tile
   int32_t feat_rows;    // rows per node of the gathered feature tensor
@@ -49,6 +53,7 @@ struct StreamArgs {
   const float* gstate;  // receiver-state cotangent gS (kBwdPos)
   float* gpos;          // position gradient, accumulated (kBwdPos)
   StreamPath paths[kMaxPaths];
+  int8_t unit_paths[kMaxPaths][kMaxUnitPaths];  // plan path indices of each unit's members
 };
 
 // Dense contractions with W, one group per launch slice.
@@ -76,6 +81,7 @@ struct GemmArgs {
   int32_t P, K, C_in, C_out, D_feat;  // D_feat: rows per node of the feature tensor touched
   int32_t splits;                     // kGemmGw: reduction splits
   int32_t w_bf16;
+  int32_t vec;                        // channel counts allow float4 operand loads
   const float* state;                 // S_g / T_g blocks (A for Out, Gx, Gw)
   const float* feat;                  // g_out (A for Gs, B for Gw)
   const void* W;                      // fp32 or bf16
@@ -96,7 +102,8 @@ struct ReduceArgs {
 hipError_t launch_stream(int mode, int lmax, int K, bool feat_bf16, const StreamArgs& a, int64_t items,
                          hipStream_t s);
 hipError_t launch_gemm(int kind, const GemmArgs& a, int max_tiles, hipStream_t s);
-int gemm_bn(int kind, const GemmArgs& a);  // column tile (64 or 32); row tile = 4096 / (32 * bn) * 32
+int gemm_bn(int kind, const GemmArgs& a);  // column tile (32, 64 or 128)
+int gemm_bm();                             // row tile
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 hipError_t launch_zero_rows(float* base, int64_t N, int rows, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);

@@ -140,6 +140,40 @@ bool real_cg(int l1, int l2, int l3, std::vector<double>& out) {
   return true;
 }
 
+std::vector<Path> natural_paths(int L) {
+  std::vector<Path> out;
+  for (int l1 = 0; l1 <= L; ++l1)
+    for (int l2 = 0; l2 <= L; ++l2)
+      for (int l3 = 0; l3 <= L; ++l3)
+        if (l3 >= std::abs(l1 - l2) && l3 <= l1 + l2 && (l1 + l2 + l3) % 2 == 0)
+          out.push_back(Path{l1, l1, l2, l3, l3, 0, 0});
+  return out;
+}
+
+std::vector<std::vector<int>> natural_bundles(int L, int K, bool receiver_side) {
+  const std::vector<Path> paths = natural_paths(L);
+  const int cap = std::max(1, kUnitAccumulators / K);
+  std::vector<std::vector<int>> bundles;
+  for (int g = 0; g <= L; ++g) {
+    std::vector<int> cur;
+    int sum = 0;
+    for (int i = 0; i < (int)paths.size(); ++i) {
+      const Path& p = paths[i];
+      if ((receiver_side ? p.l1 : p.l3) != g) continue;
+      const int n = 2 * (receiver_side ? p.l3 : p.l1) + 1;
+      if (!cur.empty() && sum + n > cap) {
+        bundles.push_back(cur);
+        cur.clear();
+        sum = 0;
+      }
+      cur.push_back(i);
+      sum += n;
+    }
+    if (!cur.empty()) bundles.push_back(cur);
+  }
+  return bundles;
+}
+
 int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K, float cutoff,
                int env_p, int x_dtype, int w_dtype, Plan& plan) {
   if (!irreps_in || !irreps_out) return TPCONV_ERROR_INVALID_VALUE;
@@ -214,6 +248,29 @@ int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K
     off += (int64_t)(2 * g.l + 1) * K * (int64_t)g.paths.size() * p.C_out;
   }
   p.state_out_per_node = off;
+  // natural irreps: irrep i has degree i and parity (-1)^i on both sides, harmonics up to L
+  auto is_natural = [&](const std::vector<Irrep>& v) {
+    if ((int)v.size() != lmax + 1) return false;
+    for (int i = 0; i <= lmax; ++i)
+      if (v[i].l != i || v[i].parity != ((i % 2) ? -1 : 1)) return false;
+    return true;
+  };
+  p.natural = is_natural(p.in) && is_natural(p.out) && sh_lmax == lmax;
+  if (p.natural) {
+    p.recv_units = natural_bundles(lmax, K, true);
+    p.send_units = natural_bundles(lmax, K, false);
+    for (const auto* us : {&p.recv_units, &p.send_units})
+      for (const auto& u : *us)
+        if ((int)u.size() > 8) p.natural = false;  // more members than a unit holds
+  }
+  if (!p.natural) {
+    p.recv_units.clear();
+    p.send_units.clear();
+    for (int i = 0; i < p.P; ++i) {
+      p.recv_units.push_back({i});
+      p.send_units.push_back({i});
+    }
+  }
   plan = std::move(p);
   return TPCONV_SUCCESS;
 }

@@ -11,6 +11,7 @@ namespace tpconv {
 constexpr int kMaxL = 3;        // largest degree of any irrep or harmonic
 constexpr int kMaxPaths = 64;   // paths per plan (kernel argument tables)
 constexpr int kMaxGroups = 16;  // irreps per side
+constexpr int kUnitAccumulators = 128;  // state accumulators per lane in a stream work unit
 
 struct Irrep {
   int mul;
@@ -52,7 +53,21 @@ struct Plan {
   std::vector<Group> in_groups;         // indexed by input irrep
   int64_t state_in_per_node = 0;        // K * C_in * sum_p (2l3+1)
   int64_t state_out_per_node = 0;       // K * C_out * sum_p (2l1+1)
+  // Work units of the edge streams.  With the natural irreps (one irrep per
+  // degree 0..L on both sides, harmonics up to L) paths that gather the same
+  // feature block are packed into bundles; otherwise every path is its own unit.
+  bool natural = false;
+  std::vector<std::vector<int>> recv_units;  // path indices per unit, receiver-side streams
+  std::vector<std::vector<int>> send_units;  // path indices per unit, sender-side streams
 };
+
+// Paths (l1, l2, l3) of the natural irreps of degree <= L, in plan order.
+std::vector<Path> natural_paths(int L);
+
+// Bundles over natural_paths(L): paths grouped by the degree of the gathered
+// block (l1 on the receiver side, l3 on the sender side), packed in order so
+// that K * (sum of output degrees 2l+1) <= kUnitAccumulators per lane.
+std::vector<std::vector<int>> natural_bundles(int L, int K, bool receiver_side);
 
 // Parse "32x0e+32x1o"; returns false on a malformed string.
 bool parse_irreps(const std::string& s, std::vector<Irrep>& out);

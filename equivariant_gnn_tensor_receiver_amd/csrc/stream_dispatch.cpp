@@ -1,5 +1,6 @@
 // Host dispatch of the edge-stream kernels to their per-(mode, dtype) instantiations.
 #include "kernels.h"
+#include "timing.h"
 
 namespace tpconv {
 
@@ -16,6 +17,7 @@ TP_DECL(launch_stream_sndt_f32)
 
 hipError_t launch_stream(int mode, int lmax, int K, bool bf16, const StreamArgs& a, int64_t items,
                          hipStream_t s) {
+  TimingScope ts(kcStreamFwd + mode, s);
   switch (mode) {
     case kFwd: return bf16 ? launch_stream_fwd_bf16(lmax, K, a, items, s) : launch_stream_fwd_f32(lmax, K, a, items, s);
     case kJvp: return bf16 ? launch_stream_jvp_bf16(lmax, K, a, items, s) : launch_stream_jvp_f32(lmax, K, a, items, s);

@@ -2,17 +2,23 @@
 // accumulation of the Sobek reassociation ("Sobek" page, abstract: edge-local
 // products consumed directly into bounded receiver-side state).
 //
-// Work decomposition: one wavefront per (node, channel tile, path).  The node's
-// edges are streamed in batches; lane j of the wave computes the geometry of
-// edge j of the batch (radial basis, harmonics and, where needed, their
-// derivatives) into wave-private LDS.  Then lanes map to (channel, edge slot):
-// each lane gathers the neighbour's feature rows of its path for its channel
-// (coalesced across channels), forms the CG coupling with the baked table on
-// VALU, and accumulates the outer product with R into registers.  Edge slots
-// are summed with cross-lane shuffles at the end; the state of a (node, path,
-// channel) is written once.  No per-edge value is ever written to memory and
-// no atomics touch the state.
+// Work decomposition: one wavefront per (node, channel tile, unit).  A unit is
+// a compile-time bundle of paths that gather the same feature block (the same
+// l1 on the receiver side, the same l3 on the sender side); plans whose irreps
+// are not the natural ones use single-path units.  The node's edges are
+// streamed in batches; lane j of the wave computes the geometry of edge j of
+// the batch (radial basis, harmonics and, where needed, their derivatives)
+// into wave-private LDS.  Then lanes map to (channel, edge slot): each lane
+// gathers the neighbour's feature rows for its channel (coalesced across
+// channels; the next edge's rows are loaded while the current one is used),
+// forms every member path's CG coupling with the baked tables on VALU and
+// accumulates the outer product with R into registers.  Edge slots are summed
+// across lanes at the end and each (node, path, channel) state entry is
+// written once.  No per-edge value is ever written to memory and no atomics
+// touch the state.
 #pragma once
+
+#include <type_traits>
 
 #include "cg_tables.inc"
 #include "device_common.h"
@@ -28,24 +34,27 @@ struct ModeTraits {
   static constexpr int batch = (MODE == kFwd || MODE == kSnd) ? 64 : 32;
 };
 
-template <int K, int NSH, int MODE>
-struct EdgeLds {
+// Wave-private geometry of one batch of edges.  Harmonic blocks are padded to
+// 8 floats per degree and Jacobian rows to 4 so that reads are 16-byte aligned.
+template <int K, int LMAX, int MODE>
+struct __attribute__((aligned(16))) EdgeLds {
   static constexpr int B = ModeTraits<MODE>::batch;
+  static constexpr int NSH = sh_count(LMAX);
   static constexpr int BT = ModeTraits<MODE>::tangent ? B : 1;
   static constexpr int BP = ModeTraits<MODE>::bwdpos ? B : 1;
   int nbr[B];
   float R[B][K];
-  float Y[B][NSH];
+  float Y[B][LMAX + 1][8];
   float Rd[(ModeTraits<MODE>::tangent || ModeTraits<MODE>::bwdpos) ? B : 1][K];  // R_dot or R'
-  float Yd[BT][NSH];
-  float J[BP][NSH][3];
-  float rhat[BP][3];
+  float Yd[BT][LMAX + 1][8];
+  float J[BP][NSH][4];
+  float rhat[BP][4];
 };
 
 // Geometry of one edge into LDS slot j.
 template <int LMAX, int K, int MODE>
 __device__ __forceinline__ void edge_prep(const StreamArgs& a, int self, float psx, float psy, float psz, int e,
-                                          int j, EdgeLds<K, sh_count(LMAX), MODE>& L) {
+                                          int j, EdgeLds<K, LMAX, MODE>& L) {
   constexpr int NSH = sh_count(LMAX);
   constexpr bool RECV = ModeTraits<MODE>::recv;
   constexpr bool DER = ModeTraits<MODE>::tangent || ModeTraits<MODE>::bwdpos;
@@ -71,7 +80,10 @@ __device__ __forceinline__ void edge_prep(const StreamArgs& a, int self, float p
 #pragma unroll
   for (int k = 0; k < K; ++k) L.R[j][k] = R[k];
 #pragma unroll
-  for (int i = 0; i < NSH; ++i) L.Y[j][i] = Y[i];
+  for (int i = 0; i < NSH; ++i) {
+    const int l = sh_degree_of_row(i);
+    L.Y[j][l][i - l * l] = Y[i];
+  }
   if constexpr (DER) {
     float G[NSH][3];
     sh_poly_grad<LMAX>(ux, uy, uz, G);
@@ -85,8 +97,8 @@ __device__ __forceinline__ void edge_prep(const StreamArgs& a, int self, float p
       for (int k = 0; k < K; ++k) L.Rd[j][k] = dR[k] * rphi;
 #pragma unroll
       for (int i = 0; i < NSH; ++i) {
-        const float l = (float)sh_degree_of_row(i);
-        L.Yd[j][i] = (G[i][0] * fx + G[i][1] * fy + G[i][2] * fz - l * Y[i] * rphi) * inv_d;
+        const int l = sh_degree_of_row(i);
+        L.Yd[j][l][i - l * l] = (G[i][0] * fx + G[i][1] * fy + G[i][2] * fz - (float)l * Y[i] * rphi) * inv_d;
       }
     } else {
 #pragma unroll
@@ -105,155 +117,237 @@ __device__ __forceinline__ void edge_prep(const StreamArgs& a, int self, float p
   }
 }
 
-template <int LMAX, int K, int MODE, typename FT, int L1, int L2, int L3>
-__device__ __forceinline__ void run_path(const StreamArgs& a, const StreamPath& P, int node, int tile,
-                                         EdgeLds<K, sh_count(LMAX), MODE>& L) {
-  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  constexpr bool RECV = ModeTraits<MODE>::recv;
-  constexpr int NIN = RECV ? N1 : N3;
-  constexpr int NOUT = RECV ? N3 : N1;
-  constexpr int B = ModeTraits<MODE>::batch;
-  constexpr int Y0 = L2 * L2;
-  using Tab = CG<L1, L2, L3>;
-
-  const int lane = threadIdx.x;
-  const int ctl = a.ct_log2;
-  const int CT = 1 << ctl;
-  const int ES = 64 >> ctl;
-  const int cl = lane & (CT - 1);
-  const int es = lane >> ctl;
-  const int c = tile * CT + cl;
-  const int C = a.C;
-  const FT* feat = static_cast<const FT*>(a.feat);
-
-  float acc[K][NOUT];
-#pragma unroll
-  for (int k = 0; k < K; ++k)
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) acc[k][o] = 0.f;
-
-  float gs[ModeTraits<MODE>::bwdpos ? K : 1][N3];
-  float vself[3] = {0.f, 0.f, 0.f};
-  if constexpr (ModeTraits<MODE>::bwdpos) {
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-      for (int o = 0; o < N3; ++o)
-        gs[k][o] = a.gstate[P.state_base + ((int64_t)(node * N3 + o) * K + k) * P.cols_per_k + P.q * C + c];
+// Sum over the edge slots of a wave (lanes c, c + CT, c + 2 CT, ...).
+__device__ __forceinline__ float edge_slot_sum(float v, int ct_log2) {
+  if (ct_log2 >= 6) return v;
+  if (ct_log2 == 5) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-
-  const float psx = a.pos[3 * (int64_t)node], psy = a.pos[3 * (int64_t)node + 1],
-              psz = a.pos[3 * (int64_t)node + 2];
-  const int e0 = a.ptr[node], e1 = a.ptr[node + 1];
-  for (int b0 = e0; b0 < e1; b0 += B) {
-    const int nb = min(B, e1 - b0);
-    __syncthreads();
-    if (lane < nb) edge_prep<LMAX, K, MODE>(a, node, psx, psy, psz, b0 + lane, lane, L);
-    __syncthreads();
-    for (int j0 = 0; j0 < nb; j0 += ES) {
-      const int j = j0 + es;
-      if (j >= nb) continue;
-      const int nbv = L.nbr[j];
-      float av[NIN];
-      const int64_t fbase = ((int64_t)nbv * a.feat_rows + P.feat_row) * C + c;
-#pragma unroll
-      for (int i = 0; i < NIN; ++i) av[i] = load_feat(feat, fbase + (int64_t)i * C);
-      float y[N2];
-#pragma unroll
-      for (int i = 0; i < N2; ++i) y[i] = L.Y[j][Y0 + i];
-      float r[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) r[k] = L.R[j][k];
-
-      if constexpr (MODE == kFwd || MODE == kSnd) {
-        float u[NOUT];
-        if constexpr (RECV) Tab::fwd(av, y, u); else Tab::snd(av, y, u);
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-          for (int o = 0; o < NOUT; ++o) acc[k][o] = __builtin_fmaf(r[k], u[o], acc[k][o]);
-      } else if constexpr (MODE == kJvp || MODE == kSndT) {
-        float yd[N2], rd[K];
-#pragma unroll
-        for (int i = 0; i < N2; ++i) yd[i] = L.Yd[j][Y0 + i];
-#pragma unroll
-        for (int k = 0; k < K; ++k) rd[k] = L.Rd[j][k];
-        float u[NOUT], ud[NOUT];
-        if constexpr (RECV) {
-          Tab::fwd(av, y, u);
-          Tab::fwd(av, yd, ud);
-        } else {
-          Tab::snd(av, y, u);
-          Tab::snd(av, yd, ud);
-        }
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-          for (int o = 0; o < NOUT; ++o)
-            acc[k][o] = __builtin_fmaf(rd[k], u[o], __builtin_fmaf(r[k], ud[o], acc[k][o]));
-      } else {  // kBwdPos
-        float u[N3];
-        Tab::fwd(av, y, u);
-        float alpha = 0.f;
-        float gU[N3];
-#pragma unroll
-        for (int o = 0; o < N3; ++o) gU[o] = 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          float gR = 0.f;
-#pragma unroll
-          for (int o = 0; o < N3; ++o) {
-            gR = __builtin_fmaf(gs[k][o], u[o], gR);
-            gU[o] = __builtin_fmaf(r[k], gs[k][o], gU[o]);
-          }
-          alpha = __builtin_fmaf(gR, L.Rd[j][k], alpha);
-        }
-        float gy[N2];
-#pragma unroll
-        for (int i = 0; i < N2; ++i) gy[i] = 0.f;
-        Tab::ybar(av, gU, gy);
-        float vec[3];
-#pragma unroll
-        for (int cc = 0; cc < 3; ++cc) {
-          float v = alpha * L.rhat[j][cc];
-#pragma unroll
-          for (int i = 0; i < N2; ++i) v = __builtin_fmaf(gy[i], L.J[j][Y0 + i][cc], v);
-          vec[cc] = v;
-        }
-        for (int off = 1; off < CT; off <<= 1)
-#pragma unroll
-          for (int cc = 0; cc < 3; ++cc) vec[cc] += __shfl_xor(vec[cc], off);
-        if (cl == 0) {
-#pragma unroll
-          for (int cc = 0; cc < 3; ++cc) {
-            atomicAdd(&a.gpos[3 * (int64_t)nbv + cc], vec[cc]);
-            vself[cc] -= vec[cc];
-          }
-        }
-      }
-    }
-  }
-
-  if constexpr (ModeTraits<MODE>::bwdpos) {
-    for (int off = CT; off < 64; off <<= 1)
-#pragma unroll
-      for (int cc = 0; cc < 3; ++cc) vself[cc] += __shfl_xor(vself[cc], off);
-    if (lane == 0 && e1 > e0) {
-#pragma unroll
-      for (int cc = 0; cc < 3; ++cc) atomicAdd(&a.gpos[3 * (int64_t)node + cc], vself[cc]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-      for (int o = 0; o < NOUT; ++o) {
-        float v = acc[k][o];
-        for (int off = CT; off < 64; off <<= 1) v += __shfl_xor(v, off);
-        if (es == 0)
-          a.state[P.state_base + ((int64_t)(node * NOUT + o) * K + k) * P.cols_per_k + P.q * C + c] = v;
-      }
-  }
+  for (int off = 1 << ct_log2; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
 }
+
+// Sum over the channel lanes of one edge slot (lanes c = 0..CT-1).
+__device__ __forceinline__ float channel_sum(float v, int ct) {
+  for (int off = 1; off < ct; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <class P0, class... Ps>
+struct First {
+  using type = P0;
+};
+
+template <int MODE, class P>
+constexpr int out_dim() {
+  return ModeTraits<MODE>::recv ? 2 * P::l3 + 1 : 2 * P::l1 + 1;
+}
+
+// The kernel arguments travel as an explicit reference parameter through the
+// (inlined) call chain; storing a reference to them in this object would make
+// the compiler copy the whole argument block to scratch memory.
+template <int MODE, typename FT, int LMAX, int K>
+struct StreamCtx {
+  int node, tile, unit;
+  EdgeLds<K, LMAX, MODE>& L;
+
+  static constexpr bool RECV = ModeTraits<MODE>::recv;
+  static constexpr bool BPOS = ModeTraits<MODE>::bwdpos;
+  static constexpr bool TAN = ModeTraits<MODE>::tangent;
+
+  // One edge for the member paths OFF.. of the unit (compile-time recursion).
+  template <int OFF, int TOT, int NIN, class P, class... Rest>
+  __device__ __forceinline__ void edge(const StreamArgs& a, const float (&av)[NIN], int j, const float (&r)[K], const float (&rd)[K],
+                                       float (&acc)[BPOS ? 1 : K][TOT], const float (&gs)[BPOS ? K : 1][TOT],
+                                       float& alpha, float (&vec)[3]) {
+    constexpr int N2 = 2 * P::l2 + 1;
+    constexpr int NO = out_dim<MODE, P>();
+    using Tab = CG<P::l1, P::l2, P::l3>;
+    float y[N2];
+#pragma unroll
+    for (int i = 0; i < N2; ++i) y[i] = L.Y[j][P::l2][i];
+    float u[NO];
+    if constexpr (RECV) Tab::fwd(av, y, u); else Tab::snd(av, y, u);
+    if constexpr (MODE == kFwd || MODE == kSnd) {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int o = 0; o < NO; ++o) acc[k][OFF + o] = __builtin_fmaf(r[k], u[o], acc[k][OFF + o]);
+    } else if constexpr (TAN) {
+      float yd[N2], ud[NO];
+#pragma unroll
+      for (int i = 0; i < N2; ++i) yd[i] = L.Yd[j][P::l2][i];
+      if constexpr (RECV) Tab::fwd(av, yd, ud); else Tab::snd(av, yd, ud);
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+          acc[k][OFF + o] = __builtin_fmaf(rd[k], u[o], __builtin_fmaf(r[k], ud[o], acc[k][OFF + o]));
+    } else {  // position gradient: alpha += sum_k R'_k <gS[k], U>, vec += J^T CG^T(x, sum_k R_k gS[k])
+      float gU[NO];
+#pragma unroll
+      for (int o = 0; o < NO; ++o) gU[o] = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        float gR = 0.f;
+#pragma unroll
+        for (int o = 0; o < NO; ++o) {
+          gR = __builtin_fmaf(gs[k][OFF + o], u[o], gR);
+          gU[o] = __builtin_fmaf(r[k], gs[k][OFF + o], gU[o]);
+        }
+        alpha = __builtin_fmaf(gR, rd[k], alpha);
+      }
+      float gy[N2];
+#pragma unroll
+      for (int i = 0; i < N2; ++i) gy[i] = 0.f;
+      Tab::ybar(av, gU, gy);
+#pragma unroll
+      for (int i = 0; i < N2; ++i) {
+        const int row = P::l2 * P::l2 + i;
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc) vec[cc] = __builtin_fmaf(gy[i], L.J[j][row][cc], vec[cc]);
+      }
+    }
+    if constexpr (sizeof...(Rest) > 0)
+      edge<OFF + NO, TOT, NIN, Rest...>(a, av, j, r, rd, acc, gs, alpha, vec);
+  }
+
+  // Load the receiver-state cotangent of the member paths (position gradient).
+  template <int I, int OFF, int TOT, class P, class... Rest>
+  __device__ __forceinline__ void load_gs(const StreamArgs& a, float (&gs)[K][TOT], int c) {
+    constexpr int NO = out_dim<MODE, P>();
+    const StreamPath& Q = a.paths[a.unit_paths[unit][I]];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int o = 0; o < NO; ++o)
+        gs[k][OFF + o] = a.gstate[Q.state_base + ((int64_t)(node * NO + o) * K + k) * Q.cols_per_k + Q.q * a.C + c];
+    if constexpr (sizeof...(Rest) > 0) load_gs<I + 1, OFF + NO, TOT, Rest...>(a, gs, c);
+  }
+
+  // Sum edge slots and write the member paths' state (each entry once).
+  template <int I, int OFF, int TOT, class P, class... Rest>
+  __device__ __forceinline__ void store(const StreamArgs& a, const float (&acc)[K][TOT], int c, int es) {
+    constexpr int NO = out_dim<MODE, P>();
+    const StreamPath& Q = a.paths[a.unit_paths[unit][I]];
+    const int ctl = a.ct_log2;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        const float v = edge_slot_sum(acc[k][OFF + o], ctl);
+        if (es == 0) a.state[Q.state_base + ((int64_t)(node * NO + o) * K + k) * Q.cols_per_k + Q.q * a.C + c] = v;
+      }
+    if constexpr (sizeof...(Rest) > 0) store<I + 1, OFF + NO, TOT, Rest...>(a, acc, c, es);
+  }
+
+  template <class... Ps>
+  __device__ __forceinline__ void run(const StreamArgs& a) {
+    using P0 = typename First<Ps...>::type;
+    constexpr int NIN = RECV ? 2 * P0::l1 + 1 : 2 * P0::l3 + 1;
+    constexpr int TOT = (out_dim<MODE, Ps>() + ...);
+    constexpr int B = ModeTraits<MODE>::batch;
+    const int lane = threadIdx.x;
+    const int ctl = a.ct_log2;
+    const int CT = 1 << ctl;
+    const int ES = 64 >> ctl;
+    const int cl = lane & (CT - 1);
+    const int es = lane >> ctl;
+    const int c = tile * CT + cl;
+    const int C = a.C;
+    const FT* feat = static_cast<const FT*>(a.feat);
+    const int64_t fcol = (int64_t)a.paths[a.unit_paths[unit][0]].feat_row * C + c;
+
+    float acc[BPOS ? 1 : K][TOT];
+    float gs[BPOS ? K : 1][TOT];
+    if constexpr (!BPOS) {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int o = 0; o < TOT; ++o) acc[k][o] = 0.f;
+    } else {
+      load_gs<0, 0, TOT, Ps...>(a, gs, c);
+    }
+    float vs0 = 0.f, vs1 = 0.f, vs2 = 0.f;  // receiver share of the position gradient
+
+    const float psx = a.pos[3 * (int64_t)node], psy = a.pos[3 * (int64_t)node + 1],
+                psz = a.pos[3 * (int64_t)node + 2];
+    const int e0 = a.ptr[node], e1 = a.ptr[node + 1];
+    for (int b0 = e0; b0 < e1; b0 += B) {
+      const int nb = min(B, e1 - b0);
+      __syncthreads();
+      if (lane < nb) edge_prep<LMAX, K, MODE>(a, node, psx, psy, psz, b0 + lane, lane, L);
+      __syncthreads();
+      // Branch-free edge loop: the gathers for the next edge slot are issued
+      // before the current slot is used (edge indices clamped into the batch,
+      // so every load is unconditional), and a slot past the last edge is
+      // masked by zeroing R.  The loop is unrolled by two over alternating
+      // buffers so that no register copy waits on a load in flight; divergent
+      // branches or such copies would make the compiler wait for every
+      // outstanding gather.
+      const int last = nb - 1;
+      const int nslots = (nb + ES - 1) / ES;
+      auto gather = [&](int slot, float (&v)[NIN]) {
+        const int64_t f = (int64_t)L.nbr[min(slot * ES + es, last)] * a.feat_rows * C + fcol;
+#pragma unroll
+        for (int i = 0; i < NIN; ++i) v[i] = load_feat(feat, f + (int64_t)i * C);
+      };
+      auto step = [&](int slot, const float (&av)[NIN]) {
+        const int j = slot * ES + es;
+        const bool valid = j < nb;
+        const int jj = min(j, last);
+        const float mask = valid ? 1.f : 0.f;  // multiply, not select: no branch around the reads
+        float r[K], rd[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) r[k] = L.R[jj][k] * mask;
+        if constexpr (TAN || BPOS) {
+#pragma unroll
+          for (int k = 0; k < K; ++k) rd[k] = L.Rd[jj][k] * mask;
+        }
+        float alpha = 0.f;
+        float vec[3] = {0.f, 0.f, 0.f};
+        edge<0, TOT, NIN, Ps...>(a, av, jj, r, rd, acc, gs, alpha, vec);
+        if constexpr (BPOS) {
+          // this unit's share of the edge vector g_r, summed over the channel lanes
+#pragma unroll
+          for (int cc = 0; cc < 3; ++cc) vec[cc] = channel_sum(__builtin_fmaf(alpha, L.rhat[jj][cc], vec[cc]) * mask, CT);
+          if (valid && cl == 0) {
+            const int64_t s3 = 3 * (int64_t)L.nbr[jj];
+            atomicAdd(&a.gpos[s3 + 0], vec[0]);
+            atomicAdd(&a.gpos[s3 + 1], vec[1]);
+            atomicAdd(&a.gpos[s3 + 2], vec[2]);
+            vs0 -= vec[0];
+            vs1 -= vec[1];
+            vs2 -= vec[2];
+          }
+        }
+      };
+      float bA[NIN], bB[NIN];
+      gather(0, bA);
+      for (int t = 0; t < nslots; t += 2) {  // an odd last slot is masked
+        gather(t + 1, bB);
+        step(t, bA);
+        gather(t + 2, bA);
+        step(t + 1, bB);
+      }
+    }
+    if constexpr (BPOS) {
+      for (int off = 1; off < 64; off <<= 1) {
+        vs0 += __shfl_xor(vs0, off);
+        vs1 += __shfl_xor(vs1, off);
+        vs2 += __shfl_xor(vs2, off);
+      }
+      if (lane == 0 && e1 > e0) {
+        atomicAdd(&a.gpos[3 * (int64_t)node + 0], vs0);
+        atomicAdd(&a.gpos[3 * (int64_t)node + 1], vs1);
+        atomicAdd(&a.gpos[3 * (int64_t)node + 2], vs2);
+      }
+    } else {
+      store<0, 0, TOT, Ps...>(a, acc, c, es);
+    }
+  }
+};
 
 #define TPCONV_PATH_CASES(X)                                                                                  \
   X(0, 0, 0) X(0, 1, 1) X(0, 2, 2) X(0, 3, 3) X(1, 0, 1) X(1, 1, 0) X(1, 1, 1) X(1, 1, 2) X(1, 2, 1)          \
@@ -261,21 +355,31 @@ __device__ __forceinline__ void run_path(const StreamArgs& a, const StreamPath& 
   X(2, 2, 1) X(2, 2, 2) X(2, 2, 3) X(2, 3, 1) X(2, 3, 2) X(2, 3, 3) X(3, 0, 3) X(3, 1, 2) X(3, 1, 3)          \
   X(3, 2, 1) X(3, 2, 2) X(3, 2, 3) X(3, 3, 0) X(3, 3, 1) X(3, 3, 2) X(3, 3, 3)
 
+// The argument block is read in place from the kernel-argument segment (it is
+// the first argument, at offset 0).  Naming the by-value parameter instead
+// would let the compiler copy the whole 2.7 KB block to scratch memory when
+// the inlined code reads it in many places.
 template <int LMAX, int K, int MODE, typename FT>
-__global__ __launch_bounds__(64) void stream_kernel(const StreamArgs a, int64_t items) {
-  __shared__ EdgeLds<K, sh_count(LMAX), MODE> L;
+__global__ __launch_bounds__(64) void stream_kernel(const StreamArgs /*args*/, int64_t items) {
+  const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  __shared__ EdgeLds<K, LMAX, MODE> L;
   const int64_t item = xcd_item(blockIdx.x, gridDim.x);
   if (item >= items) return;
-  const int p = (int)(item % a.npaths);
-  const int64_t t = item / a.npaths;
+  const int unit = (int)(item % a.nunits);
+  const int64_t t = item / a.nunits;
   const int tile = (int)(t % a.ntiles);
   const int node = (int)(t / a.ntiles);
-  const StreamPath& P = a.paths[p];
+  StreamCtx<MODE, FT, LMAX, K> ctx{node, tile, unit, L};
+  if (a.bundled) {
+    Bundles<LMAX, K, ModeTraits<MODE>::recv>::run(unit, ctx, a);
+    return;
+  }
+  const StreamPath& P = a.paths[a.unit_paths[unit][0]];
   switch (P.l1 * 16 + P.l2 * 4 + P.l3) {
-#define TPCONV_CASE(A, B, C)                                                    \
-  case A * 16 + B * 4 + C:                                                      \
-    if constexpr (A <= LMAX && B <= LMAX && C <= LMAX)                          \
-      run_path<LMAX, K, MODE, FT, A, B, C>(a, P, node, tile, L);                \
+#define TPCONV_CASE(A, B, C)                                 \
+  case A * 16 + B * 4 + C:                                   \
+    if constexpr (A <= LMAX && B <= LMAX && C <= LMAX)       \
+      ctx.template run<P3<A, B, C>>(a);                      \
     break;
     TPCONV_PATH_CASES(TPCONV_CASE)
 #undef TPCONV_CASE

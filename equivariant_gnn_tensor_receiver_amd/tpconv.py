@@ -24,7 +24,10 @@ STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "IRREPS", 3: "GRAPH", 4: "WORKSPA
 
 EXPORTS = ("tpconv_plan_create", "tpconv_plan_destroy", "tpconv_plan_info", "tpconv_plan_path",
            "tpconv_plan_cg", "tpconv_workspace_size", "tpconv_state_size", "tpconv_graph_prepare",
-           "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string")
+           "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string",
+           "tpconv_kernel_timing", "tpconv_kernel_timing_read")
+KERNELS = ("stream_fwd", "stream_jvp", "stream_snd", "stream_sndt", "stream_bwdpos", "gemm_out", "gemm_gs",
+           "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph")
 
 
 class TpconvError(RuntimeError):
@@ -65,6 +68,8 @@ def _lib():
         L.tpconv_forward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, c_size_t, P]
         L.tpconv_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
         L.tpconv_double_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
+        L.tpconv_kernel_timing.argtypes = [c_int32]
+        L.tpconv_kernel_timing_read.argtypes = [c_int32, POINTER(c_int64), POINTER(c_double)]
         L.tpconv_status_string.argtypes = [c_int32]
         L.tpconv_status_string.restype = c_char_p
         for name in EXPORTS:
@@ -190,40 +195,61 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
 
 
 def tpconv_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, saved_state=None, want=("x", "W", "pos"),
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, grad_x=None, grad_W=None, grad_pos=None):
     import torch
 
     dev = pos.device
     N = graph.num_nodes
-    gx = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev) if "x" in want else None
-    gW = torch.empty(plan.w_shape, dtype=torch.float32, device=dev) if "W" in want else None
-    gp = torch.empty((N, 3), dtype=torch.float32, device=dev) if "pos" in want else None
+    if grad_x is None and "x" in want:
+        grad_x = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev)
+    if grad_W is None and "W" in want:
+        grad_W = torch.empty(plan.w_shape, dtype=torch.float32, device=dev)
+    if grad_pos is None and "pos" in want:
+        grad_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_BACKWARD, N, graph.num_edges), dev)
     g = graph.c()
     _check(_lib().tpconv_backward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(grad_out),
-                                  _ptr(saved_state), _ptr(gx), _ptr(gW), _ptr(gp), _ptr(workspace),
+                                  _ptr(saved_state), _ptr(grad_x), _ptr(grad_W), _ptr(grad_pos), _ptr(workspace),
                                   workspace.numel(), _stream(stream)), "tpconv_backward")
-    return gx, gW, gp
+    return grad_x, grad_W, grad_pos
 
 
 def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos, want=("W", "x", "grad_out"),
-                           workspace=None, stream=None):
+                           workspace=None, stream=None, d_W=None, d_x=None, d_grad_out=None):
     import torch
 
     dev = pos.device
     N = graph.num_nodes
-    dW = torch.empty(plan.w_shape, dtype=torch.float32, device=dev) if "W" in want else None
-    dx = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev) if "x" in want else None
-    dg = torch.empty((N, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev) if "grad_out" in want else None
+    if d_W is None and "W" in want:
+        d_W = torch.empty(plan.w_shape, dtype=torch.float32, device=dev)
+    if d_x is None and "x" in want:
+        d_x = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev)
+    if d_grad_out is None and "grad_out" in want:
+        d_grad_out = torch.empty((N, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_DOUBLE_BACKWARD, N, graph.num_edges), dev)
     g = graph.c()
     _check(_lib().tpconv_double_backward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W),
-                                         _ptr(grad_out), _ptr(gg_pos), _ptr(dW), _ptr(dx), _ptr(dg),
+                                         _ptr(grad_out), _ptr(gg_pos), _ptr(d_W), _ptr(d_x), _ptr(d_grad_out),
                                          _ptr(workspace), workspace.numel(), _stream(stream)),
            "tpconv_double_backward")
-    return dW, dx, dg
+    return d_W, d_x, d_grad_out
+
+
+def tpconv_kernel_timing(enable: bool):
+    _check(_lib().tpconv_kernel_timing(int(enable)), "tpconv_kernel_timing")
+
+
+def tpconv_kernel_timing_read():
+    """{kernel name: (launches, total ms)} for every class with at least one launch."""
+    out = {}
+    for i, name in enumerate(KERNELS):
+        n, ms = c_int64(), c_double()
+        _check(_lib().tpconv_kernel_timing_read(i, ctypes.byref(n), ctypes.byref(ms)), "tpconv_kernel_timing_read")
+        if n.value:
+            out[name] = (n.value, ms.value)
+    return out
 
 
 def to_device_bf16(a: np.ndarray, device):

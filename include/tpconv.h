@@ -181,6 +181,34 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
                                      float* d_grad_out, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/* Kernel classes for tpconv_kernel_timing_read. */
+typedef enum {
+  TPCONV_KERNEL_STREAM_FWD = 0,    /* receiver stream: S */
+  TPCONV_KERNEL_STREAM_JVP = 1,    /* receiver stream: S_dot */
+  TPCONV_KERNEL_STREAM_SND = 2,    /* sender stream: T */
+  TPCONV_KERNEL_STREAM_SNDT = 3,   /* sender stream: T_dot */
+  TPCONV_KERNEL_STREAM_BWDPOS = 4, /* receiver stream: grad_pos */
+  TPCONV_KERNEL_GEMM_OUT = 5,      /* out = S . W  (also d_grad_out) */
+  TPCONV_KERNEL_GEMM_GS = 6,       /* gS = grad_out . W^T */
+  TPCONV_KERNEL_GEMM_GX = 7,       /* grad_x = T . W^T  (also d_x) */
+  TPCONV_KERNEL_GEMM_GW = 8,       /* grad_W partials = S^T . grad_out  (also d_W) */
+  TPCONV_KERNEL_GW_REDUCE = 9,     /* ordered sum of the grad_W partials */
+  TPCONV_KERNEL_FILL = 10,         /* zero fills */
+  TPCONV_KERNEL_GRAPH = 11,        /* sender-sorted view construction */
+  TPCONV_KERNEL_COUNT = 12
+} tpconv_kernel;
+
+/* Diagnostics for roofline measurements (not needed for computing).
+ * tpconv_kernel_timing(1) clears the table and starts bracketing every
+ * library launch with two HIP events recorded on the launch's own stream;
+ * tpconv_kernel_timing(0) stops (and clears).  Timing adds event packets
+ * between launches, so time end-to-end throughput with it disabled.
+ * tpconv_kernel_timing_read waits for the recorded events of one kernel class
+ * and returns the number of launches and their summed duration (ms).
+ * Process-global; not meant for concurrent use from several threads. */
+tpconv_status tpconv_kernel_timing(int32_t enable);
+tpconv_status tpconv_kernel_timing_read(int32_t kernel, int64_t* launches, double* total_ms);
+
 /* Static description of a status code. */
 const char* tpconv_status_string(tpconv_status status);
 

@@ -29,7 +29,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(tp.LIB_PATH)
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     assert sorted(names) == sorted(tp.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
