@@ -49,20 +49,20 @@ int ct_log2_of(int C) {
   return t;
 }
 
+// Reduction splits of the gW product over blocks: enough waves to fill the
+// chip (with up to 4 waves per block) while each split keeps >= 512 reductions.
 int gw_splits(const Plan& p, int64_t N) {
   int64_t tiles = 0, min_kr = INT64_MAX;
   for (const auto& g : p.out_groups) {
     if (g.paths.empty()) continue;
     const int64_t M = (int64_t)p.K * g.paths.size() * p.C_in;
-    const int bn = p.C_out > 64 ? 128 : (p.C_out > 32 ? 64 : 32);
-    const int bm = gemm_bm();
-    tiles += ((M + bm - 1) / bm) * ((p.C_out + bn - 1) / bn);
+    tiles += gemm_wave_tiles((int)M, p.C_out, p.C_out);
     min_kr = std::min<int64_t>(min_kr, N * (2 * g.l + 1));
   }
   if (tiles == 0) return 1;
-  int64_t s = (2048 + tiles - 1) / tiles;
+  int64_t s = (1024 + tiles - 1) / tiles;
   s = std::min<int64_t>(s, 64);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, min_kr / 256));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, min_kr / 512));
   return (int)std::max<int64_t>(1, s);
 }
 
@@ -174,7 +174,6 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
   a.C_out = p.C_out;
   a.splits = splits;
   a.w_bf16 = p.w_dtype == TPCONV_BF16;
-  a.vec = (p.C_in % 16 == 0) && (p.C_out % 16 == 0);
   const bool in_side = kind == kGemmGx;
   const auto& groups = in_side ? p.in_groups : p.out_groups;
   a.D_feat = in_side ? p.D_in : p.D_out;
@@ -202,39 +201,39 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
     a.g[ng++] = G;
   }
   a.ngroups = ng;
-  const int bn = gemm_bn(kind, a);
-  const int bm = gemm_bm();
-  int max_tiles = 0;
-  for (int i = 0; i < ng; ++i) {
-    GemmGroup& G = a.g[i];
-    G.tiles_n = (G.N + bn - 1) / bn;
-    G.tiles = ((G.M + bm - 1) / bm) * G.tiles_n;
-    if (G.M == 0 || G.N == 0) G.tiles = 0;
-    max_tiles = std::max(max_tiles, G.tiles);
-  }
-  return max_tiles;
+  return ng;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// 16-byte operand loads need channel counts that are multiples of 16 and
+// 16-byte aligned base pointers.
+void set_vec(const Plan& p, GemmArgs& a) {
+  a.vec = (p.C_in % 16 == 0) && (p.C_out % 16 == 0) && aligned16(a.state) && aligned16(a.feat) && aligned16(a.W);
 }
 
 tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, const float* feat,
                        const void* W, float* out, int splits, hipStream_t s) {
   GemmArgs a;
-  const int tiles = gemm_setup(p, kind, N, a, splits);
+  gemm_setup(p, kind, N, a, splits);
   a.state = state;
   a.feat = feat;
   a.W = W;
   a.out = out;
-  return dev(launch_gemm(kind, a, tiles, s));
+  set_vec(p, a);
+  return dev(launch_gemm(kind, a, s));
 }
 
 tpconv_status run_gw(const Plan& p, int64_t N, const float* state, const float* gout, float* part, float* gW,
                      hipStream_t s) {
   const int splits = gw_splits(p, N);
   GemmArgs a;
-  const int tiles = gemm_setup(p, kGemmGw, N, a, splits);
+  gemm_setup(p, kGemmGw, N, a, splits);
   a.state = state;
   a.feat = gout;
   a.out = part;
-  tpconv_status st = dev(launch_gemm(kGemmGw, a, tiles, s));
+  set_vec(p, a);
+  tpconv_status st = dev(launch_gemm(kGemmGw, a, s));
   if (st != TPCONV_SUCCESS) return st;
   ReduceArgs r;
   std::memset(&r, 0, sizeof(r));

@@ -8,13 +8,21 @@
 //   gS_g = g_out . W^T    rows (v, m3), reduction co, columns (k, q, ci)
 //   g_x  = T_g . W^T      rows (s, m1), reduction (k, q, co), columns ci
 //   gW   = S_g^T . g_out  rows (k, q, ci), reduction (v, m3), columns co (split, then summed in order)
-// One kernel template covers the four kinds through accessor functions.  A
-// block of 2 waves computes a 64 x BN tile; each wave owns 32 rows and BN/32
-// v_mfma_f32_32x32x2f32 accumulators (fp32 in, fp32 accumulate).  Tiles of 16
-// reduction steps are double-buffered in LDS (k-major, so each MFMA operand
-// read is 32 consecutive floats) and the next tile's global loads are issued
-// before the current tile is multiplied.  Global loads are float4 along each
-// operand's contiguous dimension when channel counts are multiples of 16.
+//
+// These products are skinny (32..128 columns) and stream a node-sized
+// operand once, so the kernel is built for bytes in flight rather than for
+// LDS reuse.  Every wave owns a 32-row x (32*NT)-column tile and loads its
+// operands straight into registers: for v_mfma_f32_32x32x2f32 lane (i, h)
+// (i = lane % 32, h = lane / 32) supplies A[i][kk = h] and B[kk = h][i], and
+// the reduction order inside a chunk of 2*VH indices is permuted so that lane
+// half h takes the VH consecutive indices r0 + VH*h + t (t = 0..VH-1), step t
+// of the chunk summing r0 + t and r0 + VH + t.  An operand that is contiguous
+// along the reduction is then read as 16-byte vectors per lane; one that is
+// contiguous along its row or column index is read as 128-byte coalesced
+// rows.  The next chunk is loaded while the current one is multiplied.  Small
+// problems split the reduction over the 1, 2 or 4 waves of a block; the waves'
+// partial tiles are summed in a fixed order through LDS, so results do not
+// depend on timing.
 #include "device_common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -26,16 +34,13 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 16;
-constexpr int BM = 64;
-constexpr int kThreads = 128;
+constexpr int kTargetWaves = 4096;  // 4 waves per SIMD
+constexpr int kMaxWaveSplit = 4;
 
-template <bool WBF16>
-__device__ __forceinline__ float load_w(const void* W, int64_t i) {
-  if constexpr (WBF16)
-    return load_feat(static_cast<const uint16_t*>(W), i);
-  else
-    return static_cast<const float*>(W)[i];
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ float load_w(const void* W, int64_t i, bool bf16) {
+  return bf16 ? load_feat(static_cast<const uint16_t*>(W), i) : static_cast<const float*>(W)[i];
 }
 
 template <bool WBF16>
@@ -49,70 +54,133 @@ __device__ __forceinline__ floatx4 load_w4(const void* W, int64_t i) {
   }
 }
 
-// Contiguous dimension of each operand: A along k (reduction) or m; B along n or k.
-template <int KIND> struct KindTraits;
-template <> struct KindTraits<kGemmOut> { static constexpr bool a_k = true, b_n = true; };
-template <> struct KindTraits<kGemmGs> { static constexpr bool a_k = true, b_n = false; };
-template <> struct KindTraits<kGemmGx> { static constexpr bool a_k = true, b_n = false; };
-template <> struct KindTraits<kGemmGw> { static constexpr bool a_k = false, b_n = true; };
+// VH consecutive floats p[0..VH), zero unless `ok`.  The VEC form reads
+// 16-byte vectors from an address that is valid either way (`p` or `safe`) and
+// selects afterwards, so the loads are not predicated.  The scalar form
+// (channel counts that are not multiples of 16) reads the first `valid` values.
+template <int VH, bool VEC>
+__device__ __forceinline__ void load_run(const float* p, const float* safe, bool ok, int valid, float (&v)[VH]) {
+  if constexpr (VEC) {
+    const float* q = ok ? p : safe;
+#pragma unroll
+    for (int j = 0; j < VH / 4; ++j) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(q + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = ok ? x[e] : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < VH; ++t) v[t] = t < valid ? p[t] : 0.f;
+  }
+}
 
-// Element offset of A(m, r) and B(r, n) in their tensors.
-template <int KIND>
-__device__ __forceinline__ int64_t a_index(const GemmArgs& a, const GemmGroup& G, int m, int r) {
+// Path index and channel of a reduction/column index (k, q, c) of a group.
+__device__ __forceinline__ int64_t w_row(const GemmArgs& a, const GemmGroup& G, int kqc, int C, int& c) {
+  const int cpk = G.npg * C;
+  const int k = kqc / cpk, rem = kqc - k * cpk, q = rem / C;
+  c = rem - q * C;
+  return (int64_t)k * a.P + a.path_list[G.plist + q];
+}
+
+// A operand: values t = 0..VH-1 of row m at reductions rs + t (< r_end).
+template <int KIND, int VH, bool VEC>
+__device__ __forceinline__ void load_a(const GemmArgs& a, const GemmGroup& G, int m, int rs, int r_end,
+                                       float (&v)[VH]) {
   if constexpr (KIND == kGemmOut || KIND == kGemmGx) {
-    return G.state_off + (int64_t)m * G.Kr + r;
+    const float* row = a.state + G.state_off + (int64_t)m * G.Kr;
+    load_run<VH, VEC>(row + rs, row, rs < r_end, r_end - rs, v);
   } else if constexpr (KIND == kGemmGs) {
-    const int v = m / G.n, mm = m - v * G.n;
-    return ((int64_t)v * a.D_feat + G.row_off + mm) * a.C_out + r;
-  } else {  // Gw: A(j, r) = S_g[r][j]
-    return G.state_off + (int64_t)r * G.M + m;
+    const int node = m / G.n, mm = m - node * G.n;
+    const float* row = a.feat + ((int64_t)node * a.D_feat + G.row_off + mm) * a.C_out;
+    load_run<VH, VEC>(row + rs, row, rs < r_end, r_end - rs, v);
+  } else {  // Gw: A(j, r) = S_g[r][j], contiguous along j across the lanes
+    const float* p = a.state + G.state_off + m;
+#pragma unroll
+    for (int t = 0; t < VH; ++t) {
+      const float x = p[(int64_t)min(rs + t, G.Kr - 1) * G.M];
+      v[t] = rs + t < r_end ? x : 0.f;
+    }
   }
 }
 
-template <int KIND>
-__device__ __forceinline__ int64_t b_index(const GemmArgs& a, const GemmGroup& G, int r, int n) {
-  if constexpr (KIND == kGemmOut) {  // W[(k,q,ci) = r][co = n]
-    const int cpk = G.npg * a.C_in;
-    const int k = r / cpk, rem = r - k * cpk, q = rem / a.C_in, ci = rem - q * a.C_in;
-    return (((int64_t)k * a.P + a.path_list[G.plist + q]) * a.C_in + ci) * a.C_out + n;
-  } else if constexpr (KIND == kGemmGs) {  // W[(k,q,ci) = n][co = r]
-    const int cpk = G.npg * a.C_in;
-    const int k = n / cpk, rem = n - k * cpk, q = rem / a.C_in, ci = rem - q * a.C_in;
-    return (((int64_t)k * a.P + a.path_list[G.plist + q]) * a.C_in + ci) * a.C_out + r;
-  } else if constexpr (KIND == kGemmGx) {  // W[(k,q,co) = r][ci = n]
-    const int cpk = G.npg * a.C_out;
-    const int k = r / cpk, rem = r - k * cpk, q = rem / a.C_out, co = rem - q * a.C_out;
-    return (((int64_t)k * a.P + a.path_list[G.plist + q]) * a.C_in + n) * a.C_out + co;
-  } else {  // Gw: g_out[(v, m3) = r][co = n]
-    const int v = r / G.n, mm = r - v * G.n;
-    return ((int64_t)v * a.D_feat + G.row_off + mm) * a.C_out + n;
+// B operand: values t = 0..VH-1 of column n at reductions rs + t (< r_end).
+template <int KIND, int VH, bool WBF16, bool VEC>
+__device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, int n, int rs, int r_end,
+                                       float (&v)[VH]) {
+  if constexpr (KIND == kGemmOut) {  // B(r = (k,q,ci), n = co) = W[k][p][ci][co]
+    if constexpr (VEC) {  // the VH reductions share (k, q): C_in is a multiple of 16
+      int ci;
+      const bool ok = rs < r_end;
+      const int64_t kp = w_row(a, G, ok ? rs : 0, a.C_in, ci);
+      const int64_t base = (kp * a.C_in + ci) * a.C_out + n;
+#pragma unroll
+      for (int t = 0; t < VH; ++t) {
+        const float x = load_w(a.W, base + (int64_t)t * a.C_out, WBF16);
+        v[t] = ok ? x : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < VH; ++t) {
+        int ci;
+        const int r = min(rs + t, G.Kr - 1);
+        const int64_t kp = w_row(a, G, r, a.C_in, ci);
+        v[t] = rs + t < r_end ? load_w(a.W, (kp * a.C_in + ci) * a.C_out + n, WBF16) : 0.f;
+      }
+    }
+  } else if constexpr (KIND == kGemmGs) {  // B(r = co, n = (k,q,ci)) = W[k][p][ci][co]
+    int ci;
+    const int64_t kp = w_row(a, G, n, a.C_in, ci);
+    const int64_t row = (kp * a.C_in + ci) * a.C_out;
+    if constexpr (VEC) {
+      const bool ok = rs < r_end;
+      const int64_t base = row + (ok ? rs : 0);
+#pragma unroll
+      for (int j = 0; j < VH / 4; ++j) {
+        const floatx4 x = load_w4<WBF16>(a.W, base + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = ok ? x[e] : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < VH; ++t) v[t] = rs + t < r_end ? load_w(a.W, row + rs + t, WBF16) : 0.f;
+    }
+  } else if constexpr (KIND == kGemmGx) {  // B(r = (k,q,co), n = ci) = W[k][p][ci][co]
+    if constexpr (VEC) {  // the VH reductions share (k, q): C_out is a multiple of 16
+      int co;
+      const bool ok = rs < r_end;
+      const int64_t kp = w_row(a, G, ok ? rs : 0, a.C_out, co);
+      const int64_t base = (kp * a.C_in + n) * a.C_out + co;
+#pragma unroll
+      for (int j = 0; j < VH / 4; ++j) {
+        const floatx4 x = load_w4<WBF16>(a.W, base + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = ok ? x[e] : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < VH; ++t) {
+        int co;
+        const int r = min(rs + t, G.Kr - 1);
+        const int64_t kp = w_row(a, G, r, a.C_out, co);
+        v[t] = rs + t < r_end ? load_w(a.W, (kp * a.C_in + n) * a.C_out + co, WBF16) : 0.f;
+      }
+    }
+  } else {  // Gw: B(r = (v, m3), n = co) = g_out[v][row_off + m3][co]; rows stepped without division
+    const int r0 = min(rs, G.Kr - 1);
+    int node = r0 / G.n, mm = r0 - node * G.n;
+    const float* base = a.feat + (int64_t)G.row_off * a.C_out + n;
+#pragma unroll
+    for (int t = 0; t < VH; ++t) {
+      const float x = base[((int64_t)node * a.D_feat + mm) * a.C_out];
+      v[t] = rs + t < r_end ? x : 0.f;
+      // next row; past the end of the reduction the last row is read again
+      const bool adv = rs + t + 1 < G.Kr;
+      const bool wrap = mm + 1 == G.n;
+      const int mm2 = wrap ? 0 : mm + 1, node2 = wrap ? node + 1 : node;
+      mm = adv ? mm2 : mm;
+      node = adv ? node2 : node;
+    }
   }
-}
-
-template <int KIND, bool WBF16>
-__device__ __forceinline__ float load_a1(const GemmArgs& a, const GemmGroup& G, int m, int r) {
-  const int64_t i = a_index<KIND>(a, G, m, r);
-  return (KIND == kGemmGs) ? a.feat[i] : a.state[i];
-}
-
-template <int KIND, bool WBF16>
-__device__ __forceinline__ float load_b1(const GemmArgs& a, const GemmGroup& G, int r, int n) {
-  const int64_t i = b_index<KIND>(a, G, r, n);
-  if constexpr (KIND == kGemmGw) return a.feat[i];
-  return load_w<WBF16>(a.W, i);
-}
-
-template <int KIND, bool WBF16>
-__device__ __forceinline__ floatx4 load_a4(const GemmArgs& a, const GemmGroup& G, int m, int r) {
-  const int64_t i = a_index<KIND>(a, G, m, r);
-  return *reinterpret_cast<const floatx4*>(((KIND == kGemmGs) ? a.feat : a.state) + i);
-}
-
-template <int KIND, bool WBF16>
-__device__ __forceinline__ floatx4 load_b4(const GemmArgs& a, const GemmGroup& G, int r, int n) {
-  const int64_t i = b_index<KIND>(a, G, r, n);
-  if constexpr (KIND == kGemmGw) return *reinterpret_cast<const floatx4*>(a.feat + i);
-  return load_w4<WBF16>(a.W, i);
 }
 
 template <int KIND>
@@ -130,175 +198,98 @@ __device__ __forceinline__ void store_c(const GemmArgs& a, const GemmGroup& G, i
   }
 }
 
-// Register staging of one BM x BK (A) and BK x BN (B) tile.
-template <int BN>
-struct Stage {
-  static constexpr int NA = BM * BK / 4 / kThreads;  // float4 per thread
-  static constexpr int NB = (BN * BK / 4 + kThreads - 1) / kThreads;
-  floatx4 a[NA];
-  floatx4 b[NB];
+template <int KIND, int NT, int VH, bool WBF16, bool VEC>
+struct Chunk {
+  float a[VH];
+  float b[NT][VH];
+  __device__ __forceinline__ void load(const GemmArgs& ar, const GemmGroup& G, int m, const int (&n)[NT], int rs,
+                                       int r_end) {
+    load_a<KIND, VH, VEC>(ar, G, m, rs, r_end, a);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) load_b<KIND, VH, WBF16, VEC>(ar, G, n[j], rs, r_end, b[j]);
+  }
+  __device__ __forceinline__ void mul(floatx16 (&acc)[NT]) const {
+#pragma unroll
+    for (int t = 0; t < VH; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[j][t], acc[j], 0, 0, 0);
+  }
 };
 
-template <int KIND, int BN, bool WBF16>
-__device__ __forceinline__ void load_tile(const GemmArgs& a, const GemmGroup& G, int m0, int n0, int k0, int r_end,
-                                          bool vec, Stage<BN>& st) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < Stage<BN>::NA; ++i) {
-    const int idx = t + i * kThreads;  // float4 index in the tile
-    int m, k;
-    if constexpr (KindTraits<KIND>::a_k) {
-      m = idx / (BK / 4);
-      k = (idx % (BK / 4)) * 4;
-    } else {
-      k = idx / (BM / 4);
-      m = (idx % (BM / 4)) * 4;
-    }
-    const int gm = m0 + m, gk = k0 + k;
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (KindTraits<KIND>::a_k) {
-      if (vec && gm < G.M && gk + 3 < r_end) {
-        v = load_a4<KIND, WBF16>(a, G, gm, gk);
-      } else if (gm < G.M) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (gk + e < r_end) v[e] = load_a1<KIND, WBF16>(a, G, gm, gk + e);
-      }
-    } else {
-      if (vec && gm + 3 < G.M && gk < r_end) {
-        v = load_a4<KIND, WBF16>(a, G, gm, gk);
-      } else if (gk < r_end) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (gm + e < G.M) v[e] = load_a1<KIND, WBF16>(a, G, gm + e, gk);
-      }
-    }
-    st.a[i] = v;
-  }
-#pragma unroll
-  for (int i = 0; i < Stage<BN>::NB; ++i) {
-    const int idx = t + i * kThreads;
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (idx < BN * BK / 4) {
-      int n, k;
-      if constexpr (KindTraits<KIND>::b_n) {
-        k = idx / (BN / 4);
-        n = (idx % (BN / 4)) * 4;
-      } else {
-        n = idx / (BK / 4);
-        k = (idx % (BK / 4)) * 4;
-      }
-      const int gn = n0 + n, gk = k0 + k;
-      if constexpr (KindTraits<KIND>::b_n) {
-        if (vec && gn + 3 < G.N && gk < r_end) {
-          v = load_b4<KIND, WBF16>(a, G, gk, gn);
-        } else if (gk < r_end) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (gn + e < G.N) v[e] = load_b1<KIND, WBF16>(a, G, gk, gn + e);
-        }
-      } else {
-        if (vec && gn < G.N && gk + 3 < r_end) {
-          v = load_b4<KIND, WBF16>(a, G, gk, gn);
-        } else if (gn < G.N) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (gk + e < r_end) v[e] = load_b1<KIND, WBF16>(a, G, gk + e, gn);
-        }
-      }
-    }
-    st.b[i] = v;
-  }
-}
-
-template <int KIND, int BN>
-__device__ __forceinline__ void store_tile(const Stage<BN>& st, float (*As)[BM + 4], float (*Bs)[BN + 4]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < Stage<BN>::NA; ++i) {
-    const int idx = t + i * kThreads;
-    if constexpr (KindTraits<KIND>::a_k) {
-      const int m = idx / (BK / 4), k = (idx % (BK / 4)) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) As[k + e][m] = st.a[i][e];
-    } else {
-      const int k = idx / (BM / 4), m = (idx % (BM / 4)) * 4;
-      *reinterpret_cast<floatx4*>(&As[k][m]) = st.a[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < Stage<BN>::NB; ++i) {
-    const int idx = t + i * kThreads;
-    if (idx >= BN * BK / 4) continue;
-    if constexpr (KindTraits<KIND>::b_n) {
-      const int k = idx / (BN / 4), n = (idx % (BN / 4)) * 4;
-      *reinterpret_cast<floatx4*>(&Bs[k][n]) = st.b[i];
-    } else {
-      const int n = idx / (BK / 4), k = (idx % (BK / 4)) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Bs[k + e][n] = st.b[i][e];
-    }
-  }
-}
-
-template <int KIND, int BN, bool WBF16>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
-  constexpr int NT = BN / 32;  // 32x32 accumulators per wave
-  const int gi = blockIdx.z;
-  if (gi >= a.ngroups) return;
+template <int KIND, int NT, int VH, bool WBF16, bool VEC>
+__global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs /*args*/) {
+  // Read the arguments in place: a by-value copy indexed by a runtime group
+  // would be spilled to scratch.
+  const GemmArgs& a = *(const GemmArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  extern __shared__ float red[];  // (waves - 1) x NT x 16 x 64 partial tiles
+  const int b = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < a.ngroups && b >= a.g[gi + 1].tile_begin) ++gi;
   const GemmGroup& G = a.g[gi];
-  const int tile = blockIdx.x;
-  if (tile >= G.tiles) return;
+  const int tile = b - G.tile_begin;
+  if (tile >= G.tiles) return;  // uniform over the block
   const int tm = tile / G.tiles_n, tn = tile - tm * G.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
-  int r_begin = 0, r_end = G.Kr;
+  const int m0 = tm * 32, n0 = tn * 32 * NT;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int i = lane & 31, h = lane >> 5;
+  constexpr int KC = 2 * VH;
+
+  int rb = 0, re = G.Kr;
   if constexpr (KIND == kGemmGw) {
-    const int per = ((G.Kr + a.splits - 1) / a.splits + BK - 1) / BK * BK;
-    r_begin = blockIdx.y * per;
-    r_end = min(G.Kr, r_begin + per);
-  } else {
-    if (blockIdx.y != 0) return;
+    const int per = ceil_div(ceil_div(G.Kr, a.splits), KC) * KC;
+    rb = min(G.Kr, (int)blockIdx.y * per);
+    re = min(G.Kr, rb + per);
   }
-  __shared__ __attribute__((aligned(16))) float As[2][BK][BM + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + 4];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const bool vec = a.vec != 0;
+  {
+    const int per = ceil_div(ceil_div(re - rb, nw), KC) * KC;
+    rb = min(re, rb + w * per);
+    re = min(re, rb + per);
+  }
+  const int m = min(m0 + i, G.M - 1);
+  int n[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) n[j] = min(n0 + 32 * j + i, G.N - 1);
+
   floatx16 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
-  const int nk = r_end > r_begin ? (r_end - r_begin + BK - 1) / BK : 0;
-  Stage<BN> st;
-  if (nk > 0) {
-    load_tile<KIND, BN, WBF16>(a, G, m0, n0, r_begin, r_end, vec, st);
-    store_tile<KIND, BN>(st, As[0], Bs[0]);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load_tile<KIND, BN, WBF16>(a, G, m0, n0, r_begin + (kt + 1) * BK, r_end, vec, st);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      const float av = As[buf][kk + (lane >> 5)][w * 32 + (lane & 31)];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const float bv = Bs[buf][kk + (lane >> 5)][j * 32 + (lane & 31)];
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[j], 0, 0, 0);
-      }
+  const int nch = re > rb ? ceil_div(re - rb, KC) : 0;
+  Chunk<KIND, NT, VH, WBF16, VEC> c0, c1;
+  if (nch > 0) c0.load(a, G, m, n, rb + VH * h, re);
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) c1.load(a, G, m, n, rb + (c + 1) * KC + VH * h, re);
+    c0.mul(acc);
+    if (c + 1 < nch) {
+      if (c + 2 < nch) c0.load(a, G, m, n, rb + (c + 2) * KC + VH * h, re);
+      c1.mul(acc);
     }
-    if (more) store_tile<KIND, BN>(st, As[buf ^ 1], Bs[buf ^ 1]);
+  }
+
+  if (nw > 1) {  // fixed-order sum of the waves' partial tiles
+    if (w > 0) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(((w - 1) * NT + j) * 16 + r) * 64 + lane] = acc[j][r];
+    }
     __syncthreads();
+    if (w > 0) return;
+    for (int ww = 1; ww < nw; ++ww)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] += red[(((ww - 1) * NT + j) * 16 + r) * 64 + lane];
   }
   // D layout of 32x32x2: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int gm = m0 + w * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int gn = n0 + j * 32 + (lane & 31);
+      const int gm = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int gn = n0 + 32 * j + i;
       if (gm < G.M && gn < G.N) store_c<KIND>(a, G, gm, gn, acc[j][r]);
     }
 }
@@ -329,39 +320,66 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
   if (i < n) p[i] = v;
 }
 
-template <int KIND, bool WBF16>
-hipError_t launch_kind(const GemmArgs& a, int max_tiles, int bn, hipStream_t s) {
-  const dim3 grid((unsigned)max_tiles, (unsigned)(KIND == kGemmGw ? a.splits : 1), (unsigned)a.ngroups);
-  if (bn == 128)
-    hipLaunchKernelGGL((gemm_kernel<KIND, 128, WBF16>), grid, dim3(kThreads), 0, s, a);
-  else if (bn == 64)
-    hipLaunchKernelGGL((gemm_kernel<KIND, 64, WBF16>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<KIND, 32, WBF16>), grid, dim3(kThreads), 0, s, a);
+int nt_for(int max_cols) { return max_cols > 64 ? 4 : (max_cols > 32 ? 2 : 1); }
+
+template <int KIND, int NT, bool WBF16, bool VEC>
+hipError_t launch_inst(const GemmArgs& a, dim3 grid, int waves, hipStream_t s) {
+  constexpr int VH = NT == 4 ? 8 : 16;
+  const size_t lds = (size_t)(waves - 1) * NT * 16 * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemm_kernel<KIND, NT, VH, WBF16, VEC>), grid, dim3(64 * waves), lds, s, a);
   return hipGetLastError();
+}
+
+template <int KIND, bool WBF16>
+hipError_t launch_kind(const GemmArgs& a, int nt, dim3 grid, int waves, hipStream_t s) {
+  const bool vec = a.vec != 0;
+  switch (nt) {
+    case 4: return vec ? launch_inst<KIND, 4, WBF16, true>(a, grid, waves, s) : launch_inst<KIND, 4, WBF16, false>(a, grid, waves, s);
+    case 2: return vec ? launch_inst<KIND, 2, WBF16, true>(a, grid, waves, s) : launch_inst<KIND, 2, WBF16, false>(a, grid, waves, s);
+    default: return vec ? launch_inst<KIND, 1, WBF16, true>(a, grid, waves, s) : launch_inst<KIND, 1, WBF16, false>(a, grid, waves, s);
+  }
 }
 
 }  // namespace
 
-int gemm_bm() { return BM; }
-
-int gemm_bn(int kind, const GemmArgs& a) {
-  int ncols = 0;
-  for (int g = 0; g < a.ngroups; ++g) ncols = a.g[g].N > ncols ? a.g[g].N : ncols;
-  (void)kind;
-  return ncols > 64 ? 128 : (ncols > 32 ? 64 : 32);
+int64_t gemm_wave_tiles(int M, int N, int max_cols) {
+  if (M <= 0 || N <= 0) return 0;
+  const int cols = 32 * nt_for(max_cols);
+  return (int64_t)ceil_div(M, 32) * ceil_div(N, cols);
 }
 
-hipError_t launch_gemm(int kind, const GemmArgs& a, int max_tiles, hipStream_t s) {
-  if (max_tiles <= 0 || a.ngroups <= 0) return hipSuccess;
-  const int bn = gemm_bn(kind, a);
+hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
+  if (a.ngroups <= 0) return hipSuccess;
+  int max_cols = 0, min_kr = INT32_MAX;
+  for (int g = 0; g < a.ngroups; ++g) max_cols = a.g[g].N > max_cols ? a.g[g].N : max_cols;
+  const int nt = nt_for(max_cols);
+  int64_t total = 0;
+  for (int g = 0; g < a.ngroups; ++g) {
+    GemmGroup& G = a.g[g];
+    G.tiles_n = G.N > 0 ? ceil_div(G.N, 32 * nt) : 0;
+    G.tiles = (G.M > 0 && G.N > 0) ? ceil_div(G.M, 32) * G.tiles_n : 0;
+    G.tile_begin = (int32_t)total;
+    total += G.tiles;
+    if (G.tiles > 0 && G.Kr < min_kr) min_kr = G.Kr;
+  }
+  if (total == 0) return hipSuccess;
+  if (total > INT32_MAX) return hipErrorInvalidValue;
+  const int splits = kind == kGemmGw ? a.splits : 1;
+  // Split the reduction over the waves of a block while the launch is small
+  // and every wave keeps at least four chunks of the reduction.
+  const int kc = nt == 4 ? 16 : 32;
+  int waves = 1;
+  while (waves < kMaxWaveSplit && total * splits * waves < kTargetWaves &&
+         (int64_t)min_kr >= (int64_t)splits * waves * 2 * 4 * kc)
+    waves *= 2;
+  const dim3 grid((unsigned)total, (unsigned)splits, 1);
   const bool wb = a.w_bf16 != 0;
   TimingScope ts(kcGemmOut + kind, s);
   switch (kind) {
-    case kGemmOut: return wb ? launch_kind<kGemmOut, true>(a, max_tiles, bn, s) : launch_kind<kGemmOut, false>(a, max_tiles, bn, s);
-    case kGemmGs: return wb ? launch_kind<kGemmGs, true>(a, max_tiles, bn, s) : launch_kind<kGemmGs, false>(a, max_tiles, bn, s);
-    case kGemmGx: return wb ? launch_kind<kGemmGx, true>(a, max_tiles, bn, s) : launch_kind<kGemmGx, false>(a, max_tiles, bn, s);
-    case kGemmGw: return launch_kind<kGemmGw, false>(a, max_tiles, bn, s);
+    case kGemmOut: return wb ? launch_kind<kGemmOut, true>(a, nt, grid, waves, s) : launch_kind<kGemmOut, false>(a, nt, grid, waves, s);
+    case kGemmGs: return wb ? launch_kind<kGemmGs, true>(a, nt, grid, waves, s) : launch_kind<kGemmGs, false>(a, nt, grid, waves, s);
+    case kGemmGx: return wb ? launch_kind<kGemmGx, true>(a, nt, grid, waves, s) : launch_kind<kGemmGx, false>(a, nt, grid, waves, s);
+    case kGemmGw: return launch_kind<kGemmGw, false>(a, nt, grid, waves, s);
     default: return hipErrorInvalidValue;
   }
 }

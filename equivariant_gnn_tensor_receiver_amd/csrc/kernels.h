@@ -72,6 +72,7 @@ struct GemmGroup {
   int32_t plist;             // first entry of the group's path list in GemmArgs::path_list
   int32_t tiles_n;           // column tiles
   int32_t tiles;             // total tiles (row tiles * column tiles)
+  int32_t tile_begin;        // first block of the group in the flattened launch
   int64_t state_off;         // element offset of the group's state block
   int64_t part_off;          // element offset of the group's split-K partials (kGemmGw)
 };
@@ -101,9 +102,10 @@ struct ReduceArgs {
 // Host launchers (return a hipError_t).
 hipError_t launch_stream(int mode, int lmax, int K, bool feat_bf16, const StreamArgs& a, int64_t items,
                          hipStream_t s);
-hipError_t launch_gemm(int kind, const GemmArgs& a, int max_tiles, hipStream_t s);
-int gemm_bn(int kind, const GemmArgs& a);  // column tile (32, 64 or 128)
-int gemm_bm();                             // row tile
+// Fills the tiling fields of a.g[] (tiles, tiles_n, tile_begin) and launches.
+hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s);
+// Wave tiles of a C[M][N] product (32 rows x up to 128 columns per wave).
+int64_t gemm_wave_tiles(int M, int N, int max_cols);
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 hipError_t launch_zero_rows(float* base, int64_t N, int rows, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
