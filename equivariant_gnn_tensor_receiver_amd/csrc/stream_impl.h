@@ -118,19 +118,59 @@ __device__ __forceinline__ void edge_prep(const StreamArgs& a, int self, float p
 }
 
 // Sum over the edge slots of a wave (lanes c, c + CT, c + 2 CT, ...).
-__device__ __forceinline__ float edge_slot_sum(float v, int ct_log2) {
-  if (ct_log2 >= 6) return v;
-  if (ct_log2 == 5) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  for (int off = 1 << ct_log2; off < 64; off <<= 1) v += __shfl_xor(v, off);
-  return v;
+// v + (v read through the DPP lane pattern CTRL): one VALU op, no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the channel lanes of one edge slot (lanes c = 0..CT-1).
-__device__ __forceinline__ float channel_sum(float v, int ct) {
-  for (int off = 1; off < ct; off <<= 1) v += __shfl_xor(v, off);
+// v + the same lane of the other 16-lane row of its 32-lane half.
+__device__ __forceinline__ float row16_add(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// v + the same lane of the other 32-lane half.
+__device__ __forceinline__ float half32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the edge slots (lanes with the same channel, lane % CT): rotations
+// within each 16-lane row by CT, 2CT, .. 8, then across rows and halves.  The
+// launch-uniform ct_log2 makes every branch scalar.
+__device__ __forceinline__ float edge_slot_sum(float v, int ct_log2) {
+  if (ct_log2 >= 6) return v;
+  if (ct_log2 <= 0) v = dpp_add<0x121>(v);  // row_ror:1
+  if (ct_log2 <= 1) v = dpp_add<0x122>(v);  // row_ror:2
+  if (ct_log2 <= 2) v = dpp_add<0x124>(v);  // row_ror:4
+  if (ct_log2 <= 3) v = dpp_add<0x128>(v);  // row_ror:8
+  if (ct_log2 <= 4) v = row16_add(v);
+  return half32_add(v);
+}
+
+// channel_sum of three values, interleaved so that one scalar branch covers a
+// step and the DPP read-after-write waits of one value overlap the others.
+__device__ __forceinline__ void channel_sum3(float (&v)[3], int ct_log2) {
+  if (ct_log2 >= 1) { v[0] = dpp_add<0xB1>(v[0]); v[1] = dpp_add<0xB1>(v[1]); v[2] = dpp_add<0xB1>(v[2]); }
+  if (ct_log2 >= 2) { v[0] = dpp_add<0x4E>(v[0]); v[1] = dpp_add<0x4E>(v[1]); v[2] = dpp_add<0x4E>(v[2]); }
+  if (ct_log2 >= 3) { v[0] = dpp_add<0x141>(v[0]); v[1] = dpp_add<0x141>(v[1]); v[2] = dpp_add<0x141>(v[2]); }
+  if (ct_log2 >= 4) { v[0] = dpp_add<0x140>(v[0]); v[1] = dpp_add<0x140>(v[1]); v[2] = dpp_add<0x140>(v[2]); }
+  if (ct_log2 >= 5) { v[0] = row16_add(v[0]); v[1] = row16_add(v[1]); v[2] = row16_add(v[2]); }
+  if (ct_log2 >= 6) { v[0] = half32_add(v[0]); v[1] = half32_add(v[1]); v[2] = half32_add(v[2]); }
+}
+
+// Sum over the channel lanes of one edge slot (lanes c = 0..CT-1 of a group),
+// every lane of the group receiving the sum.  After the two quad steps each
+// quad is uniform, so the half-row and row mirrors pair it with the right
+// neighbours.
+__device__ __forceinline__ float channel_sum(float v, int ct_log2) {
+  if (ct_log2 >= 1) v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (ct_log2 >= 2) v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (ct_log2 >= 3) v = dpp_add<0x141>(v);  // row_half_mirror
+  if (ct_log2 >= 4) v = dpp_add<0x140>(v);  // row_mirror
+  if (ct_log2 >= 5) v = row16_add(v);
+  if (ct_log2 >= 6) v = half32_add(v);
   return v;
 }
 
@@ -156,11 +196,29 @@ struct StreamCtx {
   static constexpr bool BPOS = ModeTraits<MODE>::bwdpos;
   static constexpr bool TAN = ModeTraits<MODE>::tangent;
 
+  static constexpr int NSH = (LMAX + 1) * (LMAX + 1);
+
+  // vec += J^T gy over the harmonic degrees L2.. that a member path uses.
+  template <int L2, class... Ps>
+  __device__ __forceinline__ void apply_jacobian(const float (&gy)[NSH], int j, float (&vec)[3]) {
+    if constexpr (L2 <= LMAX) {
+      if constexpr (((Ps::l2 == L2) || ...)) {
+#pragma unroll
+        for (int i = 0; i < 2 * L2 + 1; ++i) {
+          const int row = L2 * L2 + i;
+#pragma unroll
+          for (int cc = 0; cc < 3; ++cc) vec[cc] = __builtin_fmaf(gy[row], L.J[j][row][cc], vec[cc]);
+        }
+      }
+      apply_jacobian<L2 + 1, Ps...>(gy, j, vec);
+    }
+  }
+
   // One edge for the member paths OFF.. of the unit (compile-time recursion).
   template <int OFF, int TOT, int NIN, class P, class... Rest>
   __device__ __forceinline__ void edge(const StreamArgs& a, const float (&av)[NIN], int j, const float (&r)[K], const float (&rd)[K],
                                        float (&acc)[BPOS ? 1 : K][TOT], const float (&gs)[BPOS ? K : 1][TOT],
-                                       float& alpha, float (&vec)[3]) {
+                                       float& alpha, float (&gy)[BPOS ? (LMAX + 1) * (LMAX + 1) : 1]) {
     constexpr int N2 = 2 * P::l2 + 1;
     constexpr int NO = out_dim<MODE, P>();
     using Tab = CG<P::l1, P::l2, P::l3>;
@@ -184,7 +242,7 @@ struct StreamCtx {
 #pragma unroll
         for (int o = 0; o < NO; ++o)
           acc[k][OFF + o] = __builtin_fmaf(rd[k], u[o], __builtin_fmaf(r[k], ud[o], acc[k][OFF + o]));
-    } else {  // position gradient: alpha += sum_k R'_k <gS[k], U>, vec += J^T CG^T(x, sum_k R_k gS[k])
+    } else {  // position gradient: alpha += sum_k R'_k <gS[k], U>, gy[l2] += CG^T(x, sum_k R_k gS[k])
       float gU[NO];
 #pragma unroll
       for (int o = 0; o < NO; ++o) gU[o] = 0.f;
@@ -198,19 +256,10 @@ struct StreamCtx {
         }
         alpha = __builtin_fmaf(gR, rd[k], alpha);
       }
-      float gy[N2];
-#pragma unroll
-      for (int i = 0; i < N2; ++i) gy[i] = 0.f;
-      Tab::ybar(av, gU, gy);
-#pragma unroll
-      for (int i = 0; i < N2; ++i) {
-        const int row = P::l2 * P::l2 + i;
-#pragma unroll
-        for (int cc = 0; cc < 3; ++cc) vec[cc] = __builtin_fmaf(gy[i], L.J[j][row][cc], vec[cc]);
-      }
+      if constexpr (P::l2 > 0) Tab::ybar(av, gU, gy + P::l2 * P::l2);  // Y_00 is constant
     }
     if constexpr (sizeof...(Rest) > 0)
-      edge<OFF + NO, TOT, NIN, Rest...>(a, av, j, r, rd, acc, gs, alpha, vec);
+      edge<OFF + NO, TOT, NIN, Rest...>(a, av, j, r, rd, acc, gs, alpha, gy);
   }
 
   // Load the receiver-state cotangent of the member paths (position gradient).
@@ -297,21 +346,31 @@ struct StreamCtx {
         const int j = slot * ES + es;
         const bool valid = j < nb;
         const int jj = min(j, last);
-        const float mask = valid ? 1.f : 0.f;  // multiply, not select: no branch around the reads
+        // multiply, not select: no branch around the reads.  The accumulating
+        // modes mask the radial values; the position gradient masks its result.
+        const float mask = valid ? 1.f : 0.f;
         float r[K], rd[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) r[k] = L.R[jj][k] * mask;
+        for (int k = 0; k < K; ++k) r[k] = BPOS ? L.R[jj][k] : L.R[jj][k] * mask;
         if constexpr (TAN || BPOS) {
 #pragma unroll
-          for (int k = 0; k < K; ++k) rd[k] = L.Rd[jj][k] * mask;
+          for (int k = 0; k < K; ++k) rd[k] = BPOS ? L.Rd[jj][k] : L.Rd[jj][k] * mask;
         }
         float alpha = 0.f;
-        float vec[3] = {0.f, 0.f, 0.f};
-        edge<0, TOT, NIN, Ps...>(a, av, jj, r, rd, acc, gs, alpha, vec);
-        if constexpr (BPOS) {
-          // this unit's share of the edge vector g_r, summed over the channel lanes
+        float gy[BPOS ? NSH : 1];
 #pragma unroll
-          for (int cc = 0; cc < 3; ++cc) vec[cc] = channel_sum(__builtin_fmaf(alpha, L.rhat[jj][cc], vec[cc]) * mask, CT);
+        for (int i = 0; i < (BPOS ? NSH : 1); ++i) gy[i] = 0.f;
+        edge<0, TOT, NIN, Ps...>(a, av, jj, r, rd, acc, gs, alpha, gy);
+        if constexpr (BPOS) {
+          // this unit's share of the edge vector g_r = alpha r_hat + J^T gy,
+          // summed over the channel lanes
+          float vec[3];
+#pragma unroll
+          for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * L.rhat[jj][cc];
+          apply_jacobian<1, Ps...>(gy, jj, vec);
+#pragma unroll
+          for (int cc = 0; cc < 3; ++cc) vec[cc] *= mask;
+          channel_sum3(vec, ctl);
           if (valid && cl == 0) {
             const int64_t s3 = 3 * (int64_t)L.nbr[jj];
             atomicAdd(&a.gpos[s3 + 0], vec[0]);
@@ -333,11 +392,9 @@ struct StreamCtx {
       }
     }
     if constexpr (BPOS) {
-      for (int off = 1; off < 64; off <<= 1) {
-        vs0 += __shfl_xor(vs0, off);
-        vs1 += __shfl_xor(vs1, off);
-        vs2 += __shfl_xor(vs2, off);
-      }
+      vs0 = channel_sum(vs0, 6);
+      vs1 = channel_sum(vs1, 6);
+      vs2 = channel_sum(vs2, 6);
       if (lane == 0 && e1 > e0) {
         atomicAdd(&a.gpos[3 * (int64_t)node + 0], vs0);
         atomicAdd(&a.gpos[3 * (int64_t)node + 1], vs1);
