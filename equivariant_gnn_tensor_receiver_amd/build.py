@@ -36,7 +36,11 @@ STREAM_VARIANTS = [
     ("bpos_f32", "kBwdPos", "float"), ("bpos_bf16", "kBwdPos", "uint16_t"),
     ("snd_f32", "kSnd", "float"), ("sndt_f32", "kSndT", "float"),
 ]
-UNITS = ([(f"stream_{n}", "stream_inst.hip", [f"-DTP_MODE={m}", f"-DTP_FT={t}", f"-DTP_LAUNCHER=launch_stream_{n}"])
+# The edge streams keep their 4x4 outer-product accumulators in ordinary VGPRs
+# (the accumulation registers would otherwise be copied back and forth).
+STREAM_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+UNITS = ([(f"stream_{n}", "stream_inst.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f"-DTP_FT={t}",
+                                                            f"-DTP_LAUNCHER=launch_stream_{n}"])
           for n, m, t in STREAM_VARIANTS]
          + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("graph", ".hip"), ("api", ".cpp"),
                                              ("stream_dispatch", ".cpp"), ("plan", ".cpp"),

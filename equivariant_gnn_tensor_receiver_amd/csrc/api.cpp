@@ -43,10 +43,13 @@ struct Carver {
   }
 };
 
+// log2 of the channel tile of the edge streams: the largest power of two
+// dividing C, at most 64 and at least 4 (lanes are paired in fours by the
+// 4x4 outer products; a tile past C is masked).
 int ct_log2_of(int C) {
   int t = 0;
   while (t < 6 && (C % (2 << t)) == 0) ++t;
-  return t;
+  return t < 2 ? 2 : t;
 }
 
 // Reduction splits of the gW product over blocks: enough waves to fill the
@@ -131,7 +134,7 @@ void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
   a.feat_rows = p.D_in;
   a.C = p.C_in;
   a.ct_log2 = ct_log2_of(p.C_in);
-  a.ntiles = p.C_in >> a.ct_log2;
+  a.ntiles = (p.C_in + (1 << a.ct_log2) - 1) >> a.ct_log2;
   for (int i = 0; i < p.P; ++i) {
     const Path& q = p.paths[i];
     const Group& og = p.out_groups[q.i3];
@@ -152,7 +155,7 @@ void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
   a.feat_rows = p.D_out;
   a.C = p.C_out;
   a.ct_log2 = ct_log2_of(p.C_out);
-  a.ntiles = p.C_out >> a.ct_log2;
+  a.ntiles = (p.C_out + (1 << a.ct_log2) - 1) >> a.ct_log2;
   for (int i = 0; i < p.P; ++i) {
     const Path& q = p.paths[i];
     const Group& ig = p.in_groups[q.i1];

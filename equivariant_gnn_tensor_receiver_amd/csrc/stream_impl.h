@@ -26,6 +26,9 @@
 
 namespace tpconv {
 
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+
 template <int MODE>
 struct ModeTraits {
   static constexpr bool recv = (MODE == kFwd || MODE == kJvp || MODE == kBwdPos);
@@ -136,17 +139,35 @@ __device__ __forceinline__ float half32_add(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the edge slots (lanes with the same channel, lane % CT): rotations
-// within each 16-lane row by CT, 2CT, .. 8, then across rows and halves.  The
-// launch-uniform ct_log2 makes every branch scalar.
-__device__ __forceinline__ float edge_slot_sum(float v, int ct_log2) {
-  if (ct_log2 >= 6) return v;
-  if (ct_log2 <= 0) v = dpp_add<0x121>(v);  // row_ror:1
-  if (ct_log2 <= 1) v = dpp_add<0x122>(v);  // row_ror:2
-  if (ct_log2 <= 2) v = dpp_add<0x124>(v);  // row_ror:4
-  if (ct_log2 <= 3) v = dpp_add<0x128>(v);  // row_ror:8
-  if (ct_log2 <= 4) v = row16_add(v);
-  return half32_add(v);
+// Sum over the edge slots (lanes with the same channel, lane % CT) of every
+// value in v: rotations within each 16-lane row by CT, 2CT, .. 8, then across
+// rows and halves.  The launch-uniform ct_log2 makes every branch scalar, one
+// per stage for all values.
+template <int N>
+__device__ __forceinline__ void edge_slot_sum(float (&v)[N], int ct_log2) {
+  if (ct_log2 >= 6) return;
+  if (ct_log2 <= 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = dpp_add<0x121>(v[i]);  // row_ror:1
+  }
+  if (ct_log2 <= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = dpp_add<0x122>(v[i]);  // row_ror:2
+  }
+  if (ct_log2 <= 2) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = dpp_add<0x124>(v[i]);  // row_ror:4
+  }
+  if (ct_log2 <= 3) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = dpp_add<0x128>(v[i]);  // row_ror:8
+  }
+  if (ct_log2 <= 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = row16_add(v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = half32_add(v[i]);
 }
 
 // channel_sum of three values, interleaved so that one scalar branch covers a
@@ -217,7 +238,7 @@ struct StreamCtx {
   // One edge for the member paths OFF.. of the unit (compile-time recursion).
   template <int OFF, int TOT, int NIN, class P, class... Rest>
   __device__ __forceinline__ void edge(const StreamArgs& a, const float (&av)[NIN], int j, const float (&r)[K], const float (&rd)[K],
-                                       float (&acc)[BPOS ? 1 : K][TOT], const float (&gs)[BPOS ? K : 1][TOT],
+                                       floatx4 (&acc)[BPOS ? 1 : K / 4][TOT], const float (&gs)[BPOS ? K : 1][TOT],
                                        float& alpha, float (&gy)[BPOS ? (LMAX + 1) * (LMAX + 1) : 1]) {
     constexpr int N2 = 2 * P::l2 + 1;
     constexpr int NO = out_dim<MODE, P>();
@@ -228,20 +249,24 @@ struct StreamCtx {
     float u[NO];
     if constexpr (RECV) Tab::fwd(av, y, u); else Tab::snd(av, y, u);
     if constexpr (MODE == kFwd || MODE == kSnd) {
+      // state += R (x) U on the matrix cores: r[kq] holds R[4 kq + lane % 4]
 #pragma unroll
-      for (int k = 0; k < K; ++k)
+      for (int kq = 0; kq < K / 4; ++kq)
 #pragma unroll
-        for (int o = 0; o < NO; ++o) acc[k][OFF + o] = __builtin_fmaf(r[k], u[o], acc[k][OFF + o]);
+        for (int o = 0; o < NO; ++o)
+          acc[kq][OFF + o] = __builtin_amdgcn_mfma_f32_4x4x1f32(r[kq], u[o], acc[kq][OFF + o], 0, 0, 0);
     } else if constexpr (TAN) {
       float yd[N2], ud[NO];
 #pragma unroll
       for (int i = 0; i < N2; ++i) yd[i] = L.Yd[j][P::l2][i];
       if constexpr (RECV) Tab::fwd(av, yd, ud); else Tab::snd(av, yd, ud);
 #pragma unroll
-      for (int k = 0; k < K; ++k)
+      for (int kq = 0; kq < K / 4; ++kq)
 #pragma unroll
-        for (int o = 0; o < NO; ++o)
-          acc[k][OFF + o] = __builtin_fmaf(rd[k], u[o], __builtin_fmaf(r[k], ud[o], acc[k][OFF + o]));
+        for (int o = 0; o < NO; ++o) {
+          acc[kq][OFF + o] = __builtin_amdgcn_mfma_f32_4x4x1f32(r[kq], ud[o], acc[kq][OFF + o], 0, 0, 0);
+          acc[kq][OFF + o] = __builtin_amdgcn_mfma_f32_4x4x1f32(rd[kq], u[o], acc[kq][OFF + o], 0, 0, 0);
+        }
     } else {  // position gradient: alpha += sum_k R'_k <gS[k], U>, gy[l2] += CG^T(x, sum_k R_k gS[k])
       float gU[NO];
 #pragma unroll
@@ -275,20 +300,20 @@ struct StreamCtx {
     if constexpr (sizeof...(Rest) > 0) load_gs<I + 1, OFF + NO, TOT, Rest...>(a, gs, c);
   }
 
-  // Sum edge slots and write the member paths' state (each entry once).
+  // Write the member paths' slot-summed state (each entry once).
   template <int I, int OFF, int TOT, class P, class... Rest>
-  __device__ __forceinline__ void store(const StreamArgs& a, const float (&acc)[K][TOT], int c, int es) {
+  __device__ __forceinline__ void store(const StreamArgs& a, const float (&v)[K * TOT], int c, bool owner) {
     constexpr int NO = out_dim<MODE, P>();
     const StreamPath& Q = a.paths[a.unit_paths[unit][I]];
-    const int ctl = a.ct_log2;
+    if (owner) {
 #pragma unroll
-    for (int k = 0; k < K; ++k)
+      for (int k = 0; k < K; ++k)
 #pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        const float v = edge_slot_sum(acc[k][OFF + o], ctl);
-        if (es == 0) a.state[Q.state_base + ((int64_t)(node * NO + o) * K + k) * Q.cols_per_k + Q.q * a.C + c] = v;
-      }
-    if constexpr (sizeof...(Rest) > 0) store<I + 1, OFF + NO, TOT, Rest...>(a, acc, c, es);
+        for (int o = 0; o < NO; ++o)
+          a.state[Q.state_base + ((int64_t)(node * NO + o) * K + k) * Q.cols_per_k + Q.q * a.C + c] =
+              v[k * TOT + OFF + o];
+    }
+    if constexpr (sizeof...(Rest) > 0) store<I + 1, OFF + NO, TOT, Rest...>(a, v, c, owner);
   }
 
   template <class... Ps>
@@ -303,18 +328,23 @@ struct StreamCtx {
     const int ES = 64 >> ctl;
     const int cl = lane & (CT - 1);
     const int es = lane >> ctl;
-    const int c = tile * CT + cl;
     const int C = a.C;
+    // Channel tiles have at least 4 lanes (the 4x4 outer products pair lanes
+    // in fours); lanes past the last channel read channel C-1 and write nothing.
+    const int c_lane = tile * CT + cl;
+    const bool c_ok = c_lane < C;
+    const int c = c_ok ? c_lane : C - 1;
+    const int q4 = lane & 3;
     const FT* feat = static_cast<const FT*>(a.feat);
     const int64_t fcol = (int64_t)a.paths[a.unit_paths[unit][0]].feat_row * C + c;
 
-    float acc[BPOS ? 1 : K][TOT];
+    floatx4 acc[BPOS ? 1 : K / 4][TOT];
     float gs[BPOS ? K : 1][TOT];
     if constexpr (!BPOS) {
 #pragma unroll
-      for (int k = 0; k < K; ++k)
+      for (int kq = 0; kq < K / 4; ++kq)
 #pragma unroll
-        for (int o = 0; o < TOT; ++o) acc[k][o] = 0.f;
+        for (int o = 0; o < TOT; ++o) acc[kq][o] = floatx4{0.f, 0.f, 0.f, 0.f};
     } else {
       load_gs<0, 0, TOT, Ps...>(a, gs, c);
     }
@@ -350,11 +380,18 @@ struct StreamCtx {
         // modes mask the radial values; the position gradient masks its result.
         const float mask = valid ? 1.f : 0.f;
         float r[K], rd[K];
+        if constexpr (BPOS) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) r[k] = BPOS ? L.R[jj][k] : L.R[jj][k] * mask;
-        if constexpr (TAN || BPOS) {
+          for (int k = 0; k < K; ++k) {
+            r[k] = L.R[jj][k];
+            rd[k] = L.Rd[jj][k];
+          }
+        } else {  // the matrix-core operand of this lane: R[4 kq + lane % 4]
 #pragma unroll
-          for (int k = 0; k < K; ++k) rd[k] = BPOS ? L.Rd[jj][k] : L.Rd[jj][k] * mask;
+          for (int kq = 0; kq < K / 4; ++kq) {
+            r[kq] = L.R[jj][4 * kq + q4] * mask;
+            if constexpr (TAN) rd[kq] = L.Rd[jj][4 * kq + q4] * mask;
+          }
         }
         float alpha = 0.f;
         float gy[BPOS ? NSH : 1];
@@ -368,8 +405,9 @@ struct StreamCtx {
 #pragma unroll
           for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * L.rhat[jj][cc];
           apply_jacobian<1, Ps...>(gy, jj, vec);
+          const float vmask = (valid && c_ok) ? 1.f : 0.f;
 #pragma unroll
-          for (int cc = 0; cc < 3; ++cc) vec[cc] *= mask;
+          for (int cc = 0; cc < 3; ++cc) vec[cc] *= vmask;
           channel_sum3(vec, ctl);
           if (valid && cl == 0) {
             const int64_t s3 = 3 * (int64_t)L.nbr[jj];
@@ -401,7 +439,13 @@ struct StreamCtx {
         atomicAdd(&a.gpos[3 * (int64_t)node + 2], vs2);
       }
     } else {
-      store<0, 0, TOT, Ps...>(a, acc, c, es);
+      float v[K * TOT];
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int o = 0; o < TOT; ++o) v[k * TOT + o] = acc[k >> 2][o][k & 3];
+      edge_slot_sum(v, ctl);
+      store<0, 0, TOT, Ps...>(a, v, c, es == 0 && c_ok);
     }
   }
 };
