@@ -441,6 +441,7 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
     if ((st = dev(launch_fill(grad_pos, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
     StreamArgs a;
     recv_args(p, a, g, pos, x);
+    set_units(p, a, p.pos_units);
     a.gstate = gS;
     a.gpos = grad_pos;
     if ((st = dev(launch_stream(kBwdPos, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=

@@ -12,6 +12,22 @@ __device__ __forceinline__ float load_feat(const float* p, int64_t i) { return p
 __device__ __forceinline__ float load_feat(const uint16_t* p, int64_t i) {
   return __uint_as_float(((uint32_t)p[i]) << 16);
 }
+// Four consecutive features p[i..i+3]; i must be a multiple of 4.
+__device__ __forceinline__ void load_feat4(const float* p, int64_t i, float (&v)[4]) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 x = *reinterpret_cast<const f4*>(p + i);
+  v[0] = x[0];
+  v[1] = x[1];
+  v[2] = x[2];
+  v[3] = x[3];
+}
+__device__ __forceinline__ void load_feat4(const uint16_t* p, int64_t i, float (&v)[4]) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  v[0] = __uint_as_float(u.x << 16);
+  v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16);
+  v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
 
 // Blocks are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Remap so that consecutive work items share an XCD and therefore its L2:

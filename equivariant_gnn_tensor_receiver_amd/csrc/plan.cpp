@@ -150,9 +150,10 @@ std::vector<Path> natural_paths(int L) {
   return out;
 }
 
-std::vector<std::vector<int>> natural_bundles(int L, int K, bool receiver_side) {
+std::vector<std::vector<int>> natural_bundles(int L, int K, int side) {
   const std::vector<Path> paths = natural_paths(L);
-  const int cap = std::max(1, kUnitAccumulators / K);
+  const bool receiver_side = side != kUnitsSend;
+  const int cap = std::max(1, (side == kUnitsPos ? kPosUnitAccumulators : kUnitAccumulators) / K);
   std::vector<std::vector<int>> bundles;
   for (int g = 0; g <= L; ++g) {
     std::vector<int> cur;
@@ -257,18 +258,21 @@ int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K
   };
   p.natural = is_natural(p.in) && is_natural(p.out) && sh_lmax == lmax;
   if (p.natural) {
-    p.recv_units = natural_bundles(lmax, K, true);
-    p.send_units = natural_bundles(lmax, K, false);
-    for (const auto* us : {&p.recv_units, &p.send_units})
+    p.recv_units = natural_bundles(lmax, K, kUnitsRecv);
+    p.send_units = natural_bundles(lmax, K, kUnitsSend);
+    p.pos_units = natural_bundles(lmax, K, kUnitsPos);
+    for (const auto* us : {&p.recv_units, &p.send_units, &p.pos_units})
       for (const auto& u : *us)
         if ((int)u.size() > 8) p.natural = false;  // more members than a unit holds
   }
   if (!p.natural) {
     p.recv_units.clear();
     p.send_units.clear();
+    p.pos_units.clear();
     for (int i = 0; i < p.P; ++i) {
       p.recv_units.push_back({i});
       p.send_units.push_back({i});
+      p.pos_units.push_back({i});
     }
   }
   plan = std::move(p);

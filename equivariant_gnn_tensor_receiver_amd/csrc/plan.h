@@ -11,7 +11,11 @@ namespace tpconv {
 constexpr int kMaxL = 3;        // largest degree of any irrep or harmonic
 constexpr int kMaxPaths = 64;   // paths per plan (kernel argument tables)
 constexpr int kMaxGroups = 16;  // irreps per side
-constexpr int kUnitAccumulators = 128;  // state accumulators per lane in a stream work unit
+constexpr int kUnitAccumulators = 128;    // state accumulators per lane in a stream work unit
+constexpr int kPosUnitAccumulators = 96;  // state cotangents per lane in a position-gradient unit
+
+// Which stream a list of work units is for.
+enum UnitSide { kUnitsRecv = 0, kUnitsSend = 1, kUnitsPos = 2 };
 
 struct Irrep {
   int mul;
@@ -59,15 +63,17 @@ struct Plan {
   bool natural = false;
   std::vector<std::vector<int>> recv_units;  // path indices per unit, receiver-side streams
   std::vector<std::vector<int>> send_units;  // path indices per unit, sender-side streams
+  std::vector<std::vector<int>> pos_units;   // path indices per unit, position-gradient stream
 };
 
 // Paths (l1, l2, l3) of the natural irreps of degree <= L, in plan order.
 std::vector<Path> natural_paths(int L);
 
 // Bundles over natural_paths(L): paths grouped by the degree of the gathered
-// block (l1 on the receiver side, l3 on the sender side), packed in order so
-// that K * (sum of output degrees 2l+1) <= kUnitAccumulators per lane.
-std::vector<std::vector<int>> natural_bundles(int L, int K, bool receiver_side);
+// block (l1 on the receiver side and in the position gradient, l3 on the
+// sender side), packed in order so that K * (sum of output degrees 2l+1) stays
+// within kUnitAccumulators (kPosUnitAccumulators for the position gradient).
+std::vector<std::vector<int>> natural_bundles(int L, int K, int side);
 
 // Parse "32x0e+32x1o"; returns false on a malformed string.
 bool parse_irreps(const std::string& s, std::vector<Irrep>& out);

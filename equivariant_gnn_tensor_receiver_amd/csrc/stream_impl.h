@@ -181,6 +181,26 @@ __device__ __forceinline__ void channel_sum3(float (&v)[3], int ct_log2) {
   if (ct_log2 >= 6) { v[0] = half32_add(v[0]); v[1] = half32_add(v[1]); v[2] = half32_add(v[2]); }
 }
 
+// Sum over the channel quads of one edge slot (lanes with the same lane % 4
+// within the slot's CT lanes), every such lane receiving the sum.
+__device__ __forceinline__ void quad_sum3(float (&v)[3], int ct_log2) {
+  if (ct_log2 == 3) {  // two quads: partner lane ^ 4 (shift right into banks 1, 3; left into banks 0, 2)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int x = __float_as_int(v[i]);
+      int p = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xA, false);  // row_shr:4
+      p = __builtin_amdgcn_update_dpp(p, x, 0x104, 0xF, 0x5, false);      // row_shl:4
+      v[i] += __int_as_float(p);
+    }
+  }
+  if (ct_log2 >= 4) {
+    v[0] = dpp_add<0x124>(v[0]); v[1] = dpp_add<0x124>(v[1]); v[2] = dpp_add<0x124>(v[2]);  // row_ror:4
+    v[0] = dpp_add<0x128>(v[0]); v[1] = dpp_add<0x128>(v[1]); v[2] = dpp_add<0x128>(v[2]);  // row_ror:8
+  }
+  if (ct_log2 >= 5) { v[0] = row16_add(v[0]); v[1] = row16_add(v[1]); v[2] = row16_add(v[2]); }
+  if (ct_log2 >= 6) { v[0] = half32_add(v[0]); v[1] = half32_add(v[1]); v[2] = half32_add(v[2]); }
+}
+
 // Sum over the channel lanes of one edge slot (lanes c = 0..CT-1 of a group),
 // every lane of the group receiving the sum.  After the two quad steps each
 // quad is uniform, so the half-row and row mirrors pair it with the right
@@ -235,11 +255,11 @@ struct StreamCtx {
     }
   }
 
-  // One edge for the member paths OFF.. of the unit (compile-time recursion).
+  // One edge for the member paths OFF.. of the unit (compile-time recursion);
+  // accumulating modes.
   template <int OFF, int TOT, int NIN, class P, class... Rest>
-  __device__ __forceinline__ void edge(const StreamArgs& a, const float (&av)[NIN], int j, const float (&r)[K], const float (&rd)[K],
-                                       floatx4 (&acc)[BPOS ? 1 : K / 4][TOT], const float (&gs)[BPOS ? K : 1][TOT],
-                                       float& alpha, float (&gy)[BPOS ? (LMAX + 1) * (LMAX + 1) : 1]) {
+  __device__ __forceinline__ void edge(const float (&av)[NIN], int j, const float (&r)[K / 4],
+                                       const float (&rd)[K / 4], floatx4 (&acc)[K / 4][TOT]) {
     constexpr int N2 = 2 * P::l2 + 1;
     constexpr int NO = out_dim<MODE, P>();
     using Tab = CG<P::l1, P::l2, P::l3>;
@@ -248,14 +268,14 @@ struct StreamCtx {
     for (int i = 0; i < N2; ++i) y[i] = L.Y[j][P::l2][i];
     float u[NO];
     if constexpr (RECV) Tab::fwd(av, y, u); else Tab::snd(av, y, u);
-    if constexpr (MODE == kFwd || MODE == kSnd) {
+    if constexpr (!TAN) {
       // state += R (x) U on the matrix cores: r[kq] holds R[4 kq + lane % 4]
 #pragma unroll
       for (int kq = 0; kq < K / 4; ++kq)
 #pragma unroll
         for (int o = 0; o < NO; ++o)
           acc[kq][OFF + o] = __builtin_amdgcn_mfma_f32_4x4x1f32(r[kq], u[o], acc[kq][OFF + o], 0, 0, 0);
-    } else if constexpr (TAN) {
+    } else {
       float yd[N2], ud[NO];
 #pragma unroll
       for (int i = 0; i < N2; ++i) yd[i] = L.Yd[j][P::l2][i];
@@ -267,24 +287,52 @@ struct StreamCtx {
           acc[kq][OFF + o] = __builtin_amdgcn_mfma_f32_4x4x1f32(r[kq], ud[o], acc[kq][OFF + o], 0, 0, 0);
           acc[kq][OFF + o] = __builtin_amdgcn_mfma_f32_4x4x1f32(rd[kq], u[o], acc[kq][OFF + o], 0, 0, 0);
         }
-    } else {  // position gradient: alpha += sum_k R'_k <gS[k], U>, gy[l2] += CG^T(x, sum_k R_k gS[k])
-      float gU[NO];
+    }
+    if constexpr (sizeof...(Rest) > 0) edge<OFF + NO, TOT, NIN, Rest...>(av, j, r, rd, acc);
+  }
+
+  // Position gradient, one edge per lane and four channels per lane (compile-
+  // time recursion over the member paths).  xv[i] holds the gathered block of
+  // channel c0 + i, where c0 is the first channel of the lane's quad; gs is
+  // the lane's own channel's state cotangent, the A operand of the matrix
+  // cores, and r / rd this lane's edge's R and R', the B operand.  A chain of
+  // K 4x4x1 outer products then leaves in register i of lane 4b + j
+  //   sum_k gS[k][o](channel c0 + i) * R_k(edge of lane 4b + j),
+  // i.e. sum_k R_k gS[k] for the lane's own edge and its quad's channels.
+  template <int OFF, int TOT, int NIN, class P, class... Rest>
+  __device__ __forceinline__ void pos_edge(const float (&xv)[4][NIN], int j, const float (&r)[K],
+                                           const float (&rd)[K], const float (&gs)[K][TOT], float& alpha,
+                                           float (&gy)[NSH]) {
+    constexpr int N2 = 2 * P::l2 + 1;
+    constexpr int NO = 2 * P::l3 + 1;
+    using Tab = CG<P::l1, P::l2, P::l3>;
+    float y[N2];
 #pragma unroll
-      for (int o = 0; o < NO; ++o) gU[o] = 0.f;
+    for (int i = 0; i < N2; ++i) y[i] = L.Y[j][P::l2][i];
+    float u[4][NO];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Tab::fwd(xv[i], y, u[i]);
+    float gU[4][NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      floatx4 g = {0.f, 0.f, 0.f, 0.f}, gd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        float gR = 0.f;
-#pragma unroll
-        for (int o = 0; o < NO; ++o) {
-          gR = __builtin_fmaf(gs[k][OFF + o], u[o], gR);
-          gU[o] = __builtin_fmaf(r[k], gs[k][OFF + o], gU[o]);
-        }
-        alpha = __builtin_fmaf(gR, rd[k], alpha);
+        g = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], r[k], g, 0, 0, 0);
+        gd = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], rd[k], gd, 0, 0, 0);
       }
-      if constexpr (P::l2 > 0) Tab::ybar(av, gU, gy + P::l2 * P::l2);  // Y_00 is constant
+      // alpha += sum_k R'_k <gS[k], U>;  gU = sum_k R_k gS[k]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        alpha = __builtin_fmaf(u[i][o], gd[i], alpha);
+        gU[i][o] = g[i];
+      }
     }
-    if constexpr (sizeof...(Rest) > 0)
-      edge<OFF + NO, TOT, NIN, Rest...>(a, av, j, r, rd, acc, gs, alpha, gy);
+    if constexpr (P::l2 > 0) {  // Y_00 is constant
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tab::ybar(xv[i], gU[i], gy + P::l2 * P::l2);
+    }
+    if constexpr (sizeof...(Rest) > 0) pos_edge<OFF + NO, TOT, NIN, Rest...>(xv, j, r, rd, gs, alpha, gy);
   }
 
   // Load the receiver-state cotangent of the member paths (position gradient).
@@ -318,6 +366,17 @@ struct StreamCtx {
 
   template <class... Ps>
   __device__ __forceinline__ void run(const StreamArgs& a) {
+    if constexpr (BPOS) {
+      run_pos<Ps...>(a);
+    } else {
+      run_acc<Ps...>(a);
+    }
+  }
+
+  // Accumulating modes: lanes are (channel, edge slot); each lane gathers its
+  // channel of one edge per step and accumulates S[k, q, c, m] in registers.
+  template <class... Ps>
+  __device__ __forceinline__ void run_acc(const StreamArgs& a) {
     using P0 = typename First<Ps...>::type;
     constexpr int NIN = RECV ? 2 * P0::l1 + 1 : 2 * P0::l3 + 1;
     constexpr int TOT = (out_dim<MODE, Ps>() + ...);
@@ -338,17 +397,11 @@ struct StreamCtx {
     const FT* feat = static_cast<const FT*>(a.feat);
     const int64_t fcol = (int64_t)a.paths[a.unit_paths[unit][0]].feat_row * C + c;
 
-    floatx4 acc[BPOS ? 1 : K / 4][TOT];
-    float gs[BPOS ? K : 1][TOT];
-    if constexpr (!BPOS) {
+    floatx4 acc[K / 4][TOT];
 #pragma unroll
-      for (int kq = 0; kq < K / 4; ++kq)
+    for (int kq = 0; kq < K / 4; ++kq)
 #pragma unroll
-        for (int o = 0; o < TOT; ++o) acc[kq][o] = floatx4{0.f, 0.f, 0.f, 0.f};
-    } else {
-      load_gs<0, 0, TOT, Ps...>(a, gs, c);
-    }
-    float vs0 = 0.f, vs1 = 0.f, vs2 = 0.f;  // receiver share of the position gradient
+      for (int o = 0; o < TOT; ++o) acc[kq][o] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     const float psx = a.pos[3 * (int64_t)node], psy = a.pos[3 * (int64_t)node + 1],
                 psz = a.pos[3 * (int64_t)node + 2];
@@ -374,51 +427,16 @@ struct StreamCtx {
       };
       auto step = [&](int slot, const float (&av)[NIN]) {
         const int j = slot * ES + es;
-        const bool valid = j < nb;
         const int jj = min(j, last);
-        // multiply, not select: no branch around the reads.  The accumulating
-        // modes mask the radial values; the position gradient masks its result.
-        const float mask = valid ? 1.f : 0.f;
-        float r[K], rd[K];
-        if constexpr (BPOS) {
+        const float mask = j < nb ? 1.f : 0.f;  // multiply, not select: no branch around the reads
+        // the matrix-core operand of this lane: R[4 kq + lane % 4]
+        float r[K / 4], rd[K / 4];
 #pragma unroll
-          for (int k = 0; k < K; ++k) {
-            r[k] = L.R[jj][k];
-            rd[k] = L.Rd[jj][k];
-          }
-        } else {  // the matrix-core operand of this lane: R[4 kq + lane % 4]
-#pragma unroll
-          for (int kq = 0; kq < K / 4; ++kq) {
-            r[kq] = L.R[jj][4 * kq + q4] * mask;
-            if constexpr (TAN) rd[kq] = L.Rd[jj][4 * kq + q4] * mask;
-          }
+        for (int kq = 0; kq < K / 4; ++kq) {
+          r[kq] = L.R[jj][4 * kq + q4] * mask;
+          rd[kq] = TAN ? L.Rd[jj][4 * kq + q4] * mask : 0.f;
         }
-        float alpha = 0.f;
-        float gy[BPOS ? NSH : 1];
-#pragma unroll
-        for (int i = 0; i < (BPOS ? NSH : 1); ++i) gy[i] = 0.f;
-        edge<0, TOT, NIN, Ps...>(a, av, jj, r, rd, acc, gs, alpha, gy);
-        if constexpr (BPOS) {
-          // this unit's share of the edge vector g_r = alpha r_hat + J^T gy,
-          // summed over the channel lanes
-          float vec[3];
-#pragma unroll
-          for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * L.rhat[jj][cc];
-          apply_jacobian<1, Ps...>(gy, jj, vec);
-          const float vmask = (valid && c_ok) ? 1.f : 0.f;
-#pragma unroll
-          for (int cc = 0; cc < 3; ++cc) vec[cc] *= vmask;
-          channel_sum3(vec, ctl);
-          if (valid && cl == 0) {
-            const int64_t s3 = 3 * (int64_t)L.nbr[jj];
-            atomicAdd(&a.gpos[s3 + 0], vec[0]);
-            atomicAdd(&a.gpos[s3 + 1], vec[1]);
-            atomicAdd(&a.gpos[s3 + 2], vec[2]);
-            vs0 -= vec[0];
-            vs1 -= vec[1];
-            vs2 -= vec[2];
-          }
-        }
+        edge<0, TOT, NIN, Ps...>(av, jj, r, rd, acc);
       };
       float bA[NIN], bB[NIN];
       gather(0, bA);
@@ -429,23 +447,129 @@ struct StreamCtx {
         step(t + 1, bB);
       }
     }
-    if constexpr (BPOS) {
-      vs0 = channel_sum(vs0, 6);
-      vs1 = channel_sum(vs1, 6);
-      vs2 = channel_sum(vs2, 6);
-      if (lane == 0 && e1 > e0) {
-        atomicAdd(&a.gpos[3 * (int64_t)node + 0], vs0);
-        atomicAdd(&a.gpos[3 * (int64_t)node + 1], vs1);
-        atomicAdd(&a.gpos[3 * (int64_t)node + 2], vs2);
+    float v[K * TOT];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int o = 0; o < TOT; ++o) v[k * TOT + o] = acc[k >> 2][o][k & 3];
+    edge_slot_sum(v, ctl);
+    store<0, 0, TOT, Ps...>(a, v, c, es == 0 && c_ok);
+  }
+
+  // Position gradient: lanes are (channel quad, edge slot, edge j4 = lane % 4).
+  // Each lane takes one edge and the four channels of its quad per step (four
+  // edges per slot per step), so the K-contractions with the state cotangent
+  // become 4x4x1 outer-product chains on the matrix cores, and the per-edge
+  // vector g_r is summed over the quads of the tile.  Sender shares go out as
+  // atomic adds; the receiver's share is reduced over the wave.
+  template <class... Ps>
+  __device__ __forceinline__ void run_pos(const StreamArgs& a) {
+    using P0 = typename First<Ps...>::type;
+    constexpr int NIN = 2 * P0::l1 + 1;
+    constexpr int TOT = (out_dim<MODE, Ps>() + ...);
+    constexpr int B = ModeTraits<MODE>::batch;
+    const int lane = threadIdx.x;
+    const int ctl = a.ct_log2;
+    const int CT = 1 << ctl;
+    const int ES = 64 >> ctl;
+    const int cl = lane & (CT - 1);
+    const int es = lane >> ctl;
+    const int j4 = lane & 3;
+    const int quad = cl >> 2;
+    const int C = a.C;
+    const int c_own = min(tile * CT + cl, C - 1);  // this lane's channel of the cotangent
+    const int c0 = tile * CT + 4 * quad;           // the quad's first channel
+    const bool vec4 = (C & 3) == 0;                 // whole quads, 16-byte aligned rows
+    const FT* feat = static_cast<const FT*>(a.feat);
+    const int64_t frow = (int64_t)a.paths[a.unit_paths[unit][0]].feat_row * C;
+
+    float gs[K][TOT];
+    load_gs<0, 0, TOT, Ps...>(a, gs, c_own);
+    float vs0 = 0.f, vs1 = 0.f, vs2 = 0.f;  // receiver share of the position gradient
+
+    const float psx = a.pos[3 * (int64_t)node], psy = a.pos[3 * (int64_t)node + 1],
+                psz = a.pos[3 * (int64_t)node + 2];
+    const int e0 = a.ptr[node], e1 = a.ptr[node + 1];
+    const int per_step = 4 * ES;
+    for (int b0 = e0; b0 < e1; b0 += B) {
+      const int nb = min(B, e1 - b0);
+      __syncthreads();
+      if (lane < nb) edge_prep<LMAX, K, MODE>(a, node, psx, psy, psz, b0 + lane, lane, L);
+      __syncthreads();
+      const int last = nb - 1;
+      const int nsteps = (nb + per_step - 1) / per_step;
+      // gathered block of the lane's edge for the quad's channels (clamped
+      // edge index: unconditional loads, as in the accumulating modes)
+      auto gather = [&](int t, float (&v)[4][NIN]) {
+        const int jl = min(t * per_step + 4 * es + j4, last);
+        const int64_t base = (int64_t)L.nbr[jl] * a.feat_rows * C + frow;
+        if (vec4) {
+#pragma unroll
+          for (int m = 0; m < NIN; ++m) {
+            float q[4];
+            load_feat4(feat, base + (int64_t)m * C + c0, q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i][m] = q[i];
+          }
+        } else {  // a quad past the channel count reads channel C-1 and is zeroed
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float ok = c0 + i < C ? 1.f : 0.f;
+            const int ci = min(c0 + i, C - 1);
+#pragma unroll
+            for (int m = 0; m < NIN; ++m) v[i][m] = load_feat(feat, base + (int64_t)m * C + ci) * ok;
+          }
+        }
+      };
+      auto step = [&](int t, const float (&xv)[4][NIN]) {
+        const int jl = t * per_step + 4 * es + j4;
+        const int jj = min(jl, last);
+        float r[K], rd[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          r[k] = L.R[jj][k];
+          rd[k] = L.Rd[jj][k];
+        }
+        float alpha = 0.f;
+        float gy[NSH];
+#pragma unroll
+        for (int i = 0; i < NSH; ++i) gy[i] = 0.f;
+        pos_edge<0, TOT, NIN, Ps...>(xv, jj, r, rd, gs, alpha, gy);
+        // this unit's share of g_r = alpha r_hat + J^T gy for the quad's channels
+        float vec[3];
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * L.rhat[jj][cc];
+        apply_jacobian<1, Ps...>(gy, jj, vec);
+        const float mask = jl < nb ? 1.f : 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc) vec[cc] *= mask;
+        quad_sum3(vec, ctl);
+        if (jl < nb && quad == 0) {
+          const int64_t s3 = 3 * (int64_t)L.nbr[jj];
+          atomicAdd(&a.gpos[s3 + 0], vec[0]);
+          atomicAdd(&a.gpos[s3 + 1], vec[1]);
+          atomicAdd(&a.gpos[s3 + 2], vec[2]);
+          vs0 -= vec[0];
+          vs1 -= vec[1];
+          vs2 -= vec[2];
+        }
+      };
+      float bA[4][NIN], bB[4][NIN];
+      gather(0, bA);
+      for (int t = 0; t < nsteps; t += 2) {  // an odd last step is masked
+        gather(t + 1, bB);
+        step(t, bA);
+        gather(t + 2, bA);
+        step(t + 1, bB);
       }
-    } else {
-      float v[K * TOT];
-#pragma unroll
-      for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int o = 0; o < TOT; ++o) v[k * TOT + o] = acc[k >> 2][o][k & 3];
-      edge_slot_sum(v, ctl);
-      store<0, 0, TOT, Ps...>(a, v, c, es == 0 && c_ok);
+    }
+    vs0 = channel_sum(vs0, 6);
+    vs1 = channel_sum(vs1, 6);
+    vs2 = channel_sum(vs2, 6);
+    if (lane == 0 && e1 > e0) {
+      atomicAdd(&a.gpos[3 * (int64_t)node + 0], vs0);
+      atomicAdd(&a.gpos[3 * (int64_t)node + 1], vs1);
+      atomicAdd(&a.gpos[3 * (int64_t)node + 2], vs2);
     }
   }
 };
@@ -472,7 +596,7 @@ __global__ __launch_bounds__(64) void stream_kernel(const StreamArgs /*args*/, i
   const int node = (int)(t / a.ntiles);
   StreamCtx<MODE, FT, LMAX, K> ctx{node, tile, unit, L};
   if (a.bundled) {
-    Bundles<LMAX, K, ModeTraits<MODE>::recv>::run(unit, ctx, a);
+    Bundles<LMAX, K, ModeTraits<MODE>::bwdpos ? 2 : (ModeTraits<MODE>::recv ? 0 : 1)>::run(unit, ctx, a);
     return;
   }
   const StreamPath& P = a.paths[a.unit_paths[unit][0]];
