@@ -14,7 +14,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload molecular
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -26,15 +25,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "edges/sec fwd and fwd+bwd per config; % of HBM/MFMA roofline; peak bytes"
 PEAK = {"hbm": (8000.0, "GB/s"), "mfma": (157.3, "TFLOP/s"), "alu": (157.3, "TFLOP/s")}
-KERNEL_SOURCES = ("stream_impl.h", "stream_inst.hip", "device_common.h", "gemm.hip", "kernels.h", "cg_codegen.cpp")
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "equivariant_gnn_tensor_receiver_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def plan_counts(plan):
@@ -97,6 +87,8 @@ def load_traffic(workload, kernel):
         return None
     with open(path) as fh:
         t = json.load(fh)
+    from equivariant_gnn_tensor_receiver_amd.profiling import kernel_source_hash
+
     if t.get("source_hash") != kernel_source_hash():
         return None  # the kernel changed since the counters were taken
     return t.get("hbm_bytes_per_launch")
@@ -285,8 +277,9 @@ def main():
         "setup_s": {"inputs": round(t_gen, 2), "graph_prepare": round(t_prep, 4)},
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample_edges or {"tiny": 512, "molecular": 20000, "wide_l": 3000,
-                                           "edge_scaling": 20000, "force": 800}[w.name]
+        # about 10-30 s of oracle work on the machine's host cores
+        sample = args.cpu_sample_edges or {"tiny": 512, "molecular": 80000, "wide_l": 4000,
+                                           "edge_scaling": 80000, "force": 2000}[w.name]
         res["cpu_baseline"] = cpu_baseline(w.name, w, data, plan, sample)
     print(json.dumps(res), flush=True)
 

@@ -352,7 +352,9 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   if (a.ngroups <= 0) return hipSuccess;
   int max_cols = 0, min_kr = INT32_MAX;
   for (int g = 0; g < a.ngroups; ++g) max_cols = a.g[g].N > max_cols ? a.g[g].N : max_cols;
-  const int nt = nt_for(max_cols);
+  // gS has a short reduction (C_out) and a wide output: one 32-column tile per
+  // wave keeps registers low and many waves resident for the store stream.
+  const int nt = kind == kGemmGs ? 1 : nt_for(max_cols);
   int64_t total = 0;
   for (int g = 0; g < a.ngroups; ++g) {
     GemmGroup& G = a.g[g];

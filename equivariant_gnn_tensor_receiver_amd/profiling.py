@@ -1,0 +1,101 @@
+"""HBM traffic of one kernel from rocprofv3 counter runs, calibrated on a copy.
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are collected in two separate
+rocprofv3 --pmc runs of the same command.  Their scale is checked on a plain
+device copy of known size (this module's ``copy`` mode), so the reported bytes
+are counter * (bytes the copy moves / what the counter reads for the copy).
+
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_fetch -o run -- \
+      python3 -m equivariant_gnn_tensor_receiver_amd.profiling copy
+  rocprofv3 --pmc WRITE_SIZE ... (same, copy_write)
+  rocprofv3 --pmc FETCH_SIZE ... -d OUT/wl_fetch -- python3 bench.py --workload W --steps 2 --warmup 1 --no-cpu-baseline
+  rocprofv3 --pmc WRITE_SIZE ... -d OUT/wl_write -- (same)
+  python3 -m equivariant_gnn_tensor_receiver_amd.profiling summarize OUT W KERNEL_SUBSTRING NAME > traffic.json
+
+The summary records the hash of the kernel sources it was taken with; bench.py
+ignores it once the sources change.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+COPY_BYTES = 1 << 30  # 1 GiB read and 1 GiB written per copy
+COPY_REPS = 4
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("stream_impl.h", "stream_inst.hip", "device_common.h", "gemm.hip", "kernels.h", "cg_codegen.cpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe():
+    import torch
+
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x {COPY_REPS}", flush=True)
+
+
+def _per_dispatch(run_dir: str, counter: str, match) -> list[float]:
+    """Counter value (summed over rows of one dispatch) per matching dispatch."""
+    tot = defaultdict(float)
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter or not match(row["Kernel_Name"]):
+                continue
+            tot[row.get("Dispatch_Id") or row.get("Correlation_Id")] += float(row["Counter_Value"])
+    return list(tot.values())
+
+
+def summarize(out_dir: str, workload: str, kernel_substr: str, name: str) -> dict:
+    res = {"workload": workload, "kernel": name, "kernel_match": kernel_substr,
+           "source_hash": kernel_source_hash()}
+    scale = {}
+    for counter, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        copy = _per_dispatch(os.path.join(out_dir, f"copy_{tag}"), counter,
+                             lambda k: "copy" in k.lower() or "elementwise" in k.lower())
+        big = [v for v in copy if v * 1024 > COPY_BYTES / 4]  # the 1 GiB copies, not setup kernels
+        if not big:
+            raise SystemExit(f"no copy dispatch found for {counter}")
+        kib = sum(big) / len(big)
+        scale[tag] = COPY_BYTES / (kib * 1024)
+        vals = _per_dispatch(os.path.join(out_dir, f"{workload}_{tag}"), counter, lambda k: kernel_substr in k)
+        if not vals:
+            raise SystemExit(f"no dispatch of {kernel_substr!r} found for {counter}")
+        res[f"{tag}_kib_per_dispatch"] = sum(vals) / len(vals)
+        res[f"{tag}_dispatches"] = len(vals)
+        res[f"copy_{tag}_kib"] = kib
+        res[f"{tag}_scale"] = scale[tag]
+    res["hbm_bytes_per_launch"] = int(res["fetch_kib_per_dispatch"] * 1024 * scale["fetch"]
+                                      + res["write_kib_per_dispatch"] * 1024 * scale["write"])
+    return res
+
+
+def main(argv):
+    if len(argv) >= 1 and argv[0] == "copy":
+        copy_probe()
+    elif len(argv) == 5 and argv[0] == "summarize":
+        print(json.dumps(summarize(*argv[1:]), indent=1))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
