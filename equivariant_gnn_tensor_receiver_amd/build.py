@@ -8,6 +8,7 @@ equivariant_gnn_tensor_receiver_amd.build [--jobs N]
 from __future__ import annotations
 
 import argparse
+import glob
 import os
 import subprocess
 import sys
@@ -62,20 +63,31 @@ def generate():
     run([exe, os.path.join(GEN, "cg_tables.inc")])
 
 
-def compile_one(unit):
+def _newest_input(src: str) -> float:
+    """Newest of a unit's source, every header, the generated tables and this script."""
+    files = ([os.path.join(CSRC, src), os.path.join(ROOT, "include", "tpconv.h"), __file__]
+             + glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(GEN, "*")))
+    return max(os.path.getmtime(f) for f in files if os.path.isfile(f))
+
+
+def compile_one(unit, incremental=False):
     name, src, defines = unit
     obj = os.path.join(BUILD, name + ".o")
+    if incremental and os.path.exists(obj) and os.path.getmtime(obj) > _newest_input(src):
+        return obj
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     run([HIPCC] + HIP_FLAGS + defines + ["-I", GEN, "-I", CSRC, "-I", os.path.join(ROOT, "include")] + lang +
         ["-c", os.path.join(CSRC, src), "-o", obj])
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
+def build(jobs: int = 8, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every unit (incremental=True skips objects newer than all sources) and link."""
     os.makedirs(BUILD, exist_ok=True)
-    generate()
+    if not (incremental and os.path.exists(os.path.join(GEN, "cg_tables.inc"))):
+        generate()
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, UNITS))
+        objs = list(ex.map(lambda u: compile_one(u, incremental), UNITS))
     tmp = LIB + ".tmp"
     run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs)
     os.replace(tmp, LIB)
@@ -87,6 +99,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("--incremental", action="store_true", help="skip objects newer than every source")
     args = ap.parse_args()
-    build(args.jobs, verbose=True)
+    build(args.jobs, verbose=True, incremental=args.incremental)
     sys.exit(0)

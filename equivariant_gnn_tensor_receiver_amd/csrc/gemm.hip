@@ -54,115 +54,115 @@ __device__ __forceinline__ floatx4 load_w4(const void* W, int64_t i) {
   }
 }
 
-// VH consecutive floats p[0..VH), zero unless `ok`.  The VEC form reads
-// 16-byte vectors from an address that is valid either way (`p` or `safe`) and
-// selects afterwards, so the loads are not predicated.  The scalar form
-// (channel counts that are not multiples of 16) reads the first `valid` values.
+// VH consecutive floats p[0..VH) (16-byte loads when VEC).  Loads are never
+// predicated and their values are not touched here: the caller clamps `p`
+// into the tensor, and a reduction index past the end is zeroed in A just
+// before the multiply (B may then hold any finite value).  A select right
+// after a load would make the compiler wait for it, which defeats the
+// one-chunk-ahead prefetch.
 template <int VH, bool VEC>
-__device__ __forceinline__ void load_run(const float* p, const float* safe, bool ok, int valid, float (&v)[VH]) {
+__device__ __forceinline__ void load_run(const float* p, int valid, float (&v)[VH]) {
   if constexpr (VEC) {
-    const float* q = ok ? p : safe;
 #pragma unroll
     for (int j = 0; j < VH / 4; ++j) {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(q + 4 * j);
+      const floatx4 x = *reinterpret_cast<const floatx4*>(p + 4 * j);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * j + e] = ok ? x[e] : 0.f;
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
     }
   } else {
+    const int last = valid > 0 ? valid - 1 : 0;
 #pragma unroll
-    for (int t = 0; t < VH; ++t) v[t] = t < valid ? p[t] : 0.f;
+    for (int t = 0; t < VH; ++t) v[t] = p[t < last ? t : last];
   }
 }
 
-// Path index and channel of a reduction/column index (k, q, c) of a group.
-__device__ __forceinline__ int64_t w_row(const GemmArgs& a, const GemmGroup& G, int kqc, int C, int& c) {
+// Row k * P + path of W and channel c for a reduction/column index (k, q, c)
+// of a group.  `pl` holds, in lane i, the group's i-th path index (read once
+// per kernel), so the lookup is a lane shuffle, not a memory load.
+__device__ __forceinline__ int64_t w_row(const GemmArgs& a, const GemmGroup& G, int kqc, int C, int pl, int& c) {
   const int cpk = G.npg * C;
   const int k = kqc / cpk, rem = kqc - k * cpk, q = rem / C;
   c = rem - q * C;
-  return (int64_t)k * a.P + a.path_list[G.plist + q];
+  return (int64_t)k * a.P + __shfl(pl, q);
 }
 
-// A operand: values t = 0..VH-1 of row m at reductions rs + t (< r_end).
+// A operand: values t = 0..VH-1 of row m at reductions rs + t; indices past
+// the end of the reduction read inside the tensor (zeroed later).
 template <int KIND, int VH, bool VEC>
 __device__ __forceinline__ void load_a(const GemmArgs& a, const GemmGroup& G, int m, int rs, int r_end,
                                        float (&v)[VH]) {
-  if constexpr (KIND == kGemmOut || KIND == kGemmGx) {
-    const float* row = a.state + G.state_off + (int64_t)m * G.Kr;
-    load_run<VH, VEC>(row + rs, row, rs < r_end, r_end - rs, v);
-  } else if constexpr (KIND == kGemmGs) {
-    const int node = m / G.n, mm = m - node * G.n;
-    const float* row = a.feat + ((int64_t)node * a.D_feat + G.row_off + mm) * a.C_out;
-    load_run<VH, VEC>(row + rs, row, rs < r_end, r_end - rs, v);
+  if constexpr (KIND == kGemmOut || KIND == kGemmGx || KIND == kGemmGs) {
+    const float* row;
+    if constexpr (KIND == kGemmGs) {
+      const int node = m / G.n, mm = m - node * G.n;
+      row = a.feat + ((int64_t)node * a.D_feat + G.row_off + mm) * a.C_out;
+    } else {
+      row = a.state + G.state_off + (int64_t)m * G.Kr;
+    }
+    // VEC: Kr is a multiple of 16 and rs of VH, so a whole run is in or out
+    const int rc = VEC ? (rs < r_end ? rs : r_end - VH) : (rs < r_end ? rs : r_end - 1);
+    load_run<VH, VEC>(row + (rc > 0 ? rc : 0), r_end - rs, v);
   } else {  // Gw: A(j, r) = S_g[r][j], contiguous along j across the lanes
     const float* p = a.state + G.state_off + m;
 #pragma unroll
-    for (int t = 0; t < VH; ++t) {
-      const float x = p[(int64_t)min(rs + t, G.Kr - 1) * G.M];
-      v[t] = rs + t < r_end ? x : 0.f;
-    }
+    for (int t = 0; t < VH; ++t) v[t] = p[(int64_t)min(rs + t, G.Kr - 1) * G.M];
   }
 }
 
 // B operand: values t = 0..VH-1 of column n at reductions rs + t (< r_end).
 template <int KIND, int VH, bool WBF16, bool VEC>
-__device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, int n, int rs, int r_end,
+__device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, int n, int rs, int r_end, int pl,
                                        float (&v)[VH]) {
   if constexpr (KIND == kGemmOut) {  // B(r = (k,q,ci), n = co) = W[k][p][ci][co]
     if constexpr (VEC) {  // the VH reductions share (k, q): C_in is a multiple of 16
       int ci;
-      const bool ok = rs < r_end;
-      const int64_t kp = w_row(a, G, ok ? rs : 0, a.C_in, ci);
+      const int64_t kp = w_row(a, G, rs < r_end ? rs : 0, a.C_in, pl, ci);
       const int64_t base = (kp * a.C_in + ci) * a.C_out + n;
 #pragma unroll
-      for (int t = 0; t < VH; ++t) {
-        const float x = load_w(a.W, base + (int64_t)t * a.C_out, WBF16);
-        v[t] = ok ? x : 0.f;
-      }
+      for (int t = 0; t < VH; ++t) v[t] = load_w(a.W, base + (int64_t)t * a.C_out, WBF16);
     } else {
 #pragma unroll
       for (int t = 0; t < VH; ++t) {
         int ci;
         const int r = min(rs + t, G.Kr - 1);
-        const int64_t kp = w_row(a, G, r, a.C_in, ci);
-        v[t] = rs + t < r_end ? load_w(a.W, (kp * a.C_in + ci) * a.C_out + n, WBF16) : 0.f;
+        const int64_t kp = w_row(a, G, r, a.C_in, pl, ci);
+        v[t] = load_w(a.W, (kp * a.C_in + ci) * a.C_out + n, WBF16);
       }
     }
   } else if constexpr (KIND == kGemmGs) {  // B(r = co, n = (k,q,ci)) = W[k][p][ci][co]
     int ci;
-    const int64_t kp = w_row(a, G, n, a.C_in, ci);
+    const int64_t kp = w_row(a, G, n, a.C_in, pl, ci);
     const int64_t row = (kp * a.C_in + ci) * a.C_out;
     if constexpr (VEC) {
-      const bool ok = rs < r_end;
-      const int64_t base = row + (ok ? rs : 0);
+      const int64_t base = row + (rs < r_end ? rs : 0);
 #pragma unroll
       for (int j = 0; j < VH / 4; ++j) {
         const floatx4 x = load_w4<WBF16>(a.W, base + 4 * j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * j + e] = ok ? x[e] : 0.f;
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < VH; ++t) v[t] = rs + t < r_end ? load_w(a.W, row + rs + t, WBF16) : 0.f;
+      for (int t = 0; t < VH; ++t) v[t] = load_w(a.W, row + min(rs + t, r_end - 1), WBF16);
     }
   } else if constexpr (KIND == kGemmGx) {  // B(r = (k,q,co), n = ci) = W[k][p][ci][co]
     if constexpr (VEC) {  // the VH reductions share (k, q): C_out is a multiple of 16
       int co;
-      const bool ok = rs < r_end;
-      const int64_t kp = w_row(a, G, ok ? rs : 0, a.C_out, co);
+      const int64_t kp = w_row(a, G, rs < r_end ? rs : 0, a.C_out, pl, co);
       const int64_t base = (kp * a.C_in + n) * a.C_out + co;
 #pragma unroll
       for (int j = 0; j < VH / 4; ++j) {
         const floatx4 x = load_w4<WBF16>(a.W, base + 4 * j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * j + e] = ok ? x[e] : 0.f;
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
       }
     } else {
 #pragma unroll
       for (int t = 0; t < VH; ++t) {
         int co;
         const int r = min(rs + t, G.Kr - 1);
-        const int64_t kp = w_row(a, G, r, a.C_out, co);
-        v[t] = rs + t < r_end ? load_w(a.W, (kp * a.C_in + n) * a.C_out + co, WBF16) : 0.f;
+        const int64_t kp = w_row(a, G, r, a.C_out, pl, co);
+        v[t] = load_w(a.W, (kp * a.C_in + n) * a.C_out + co, WBF16);
       }
     }
   } else {  // Gw: B(r = (v, m3), n = co) = g_out[v][row_off + m3][co]; rows stepped without division
@@ -171,8 +171,7 @@ __device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, in
     const float* base = a.feat + (int64_t)G.row_off * a.C_out + n;
 #pragma unroll
     for (int t = 0; t < VH; ++t) {
-      const float x = base[((int64_t)node * a.D_feat + mm) * a.C_out];
-      v[t] = rs + t < r_end ? x : 0.f;
+      v[t] = base[((int64_t)node * a.D_feat + mm) * a.C_out];
       // next row; past the end of the reduction the last row is read again
       const bool adv = rs + t + 1 < G.Kr;
       const bool wrap = mm + 1 == G.n;
@@ -202,17 +201,21 @@ template <int KIND, int NT, int VH, bool WBF16, bool VEC>
 struct Chunk {
   float a[VH];
   float b[NT][VH];
+  int valid;  // reductions of this lane half inside the range (<= 0: none)
   __device__ __forceinline__ void load(const GemmArgs& ar, const GemmGroup& G, int m, const int (&n)[NT], int rs,
-                                       int r_end) {
+                                       int r_end, int pl) {
+    valid = r_end - rs;
     load_a<KIND, VH, VEC>(ar, G, m, rs, r_end, a);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) load_b<KIND, VH, WBF16, VEC>(ar, G, n[j], rs, r_end, b[j]);
+    for (int j = 0; j < NT; ++j) load_b<KIND, VH, WBF16, VEC>(ar, G, n[j], rs, r_end, pl, b[j]);
   }
   __device__ __forceinline__ void mul(floatx16 (&acc)[NT]) const {
 #pragma unroll
-    for (int t = 0; t < VH; ++t)
+    for (int t = 0; t < VH; ++t) {
+      const float av = t < valid ? a[t] : 0.f;  // past the end of the reduction
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[j][t], acc[j], 0, 0, 0);
+      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[j][t], acc[j], 0, 0, 0);
+    }
   }
 };
 
@@ -230,7 +233,9 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
   if (tile >= G.tiles) return;  // uniform over the block
   const int tm = tile / G.tiles_n, tn = tile - tm * G.tiles_n;
   const int m0 = tm * 32, n0 = tn * 32 * NT;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  // wave index and loop bounds in scalar registers: the chunk loop then needs
+  // no exec masking and the accumulators stay in place across iterations
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
   const int i = lane & 31, h = lane >> 5;
   constexpr int KC = 2 * VH;
 
@@ -256,15 +261,37 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
+  // the group's path list, one entry per lane, for the W row lookups
+  const int pl = (KIND == kGemmGw || G.npg <= 0) ? 0 : a.path_list[G.plist + min(lane, G.npg - 1)];
   const int nch = re > rb ? ceil_div(re - rb, KC) : 0;
-  Chunk<KIND, NT, VH, WBF16, VEC> c0, c1;
-  if (nch > 0) c0.load(a, G, m, n, rb + VH * h, re);
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) c1.load(a, G, m, n, rb + (c + 1) * KC + VH * h, re);
-    c0.mul(acc);
-    if (c + 1 < nch) {
-      if (c + 2 < nch) c0.load(a, G, m, n, rb + (c + 2) * KC + VH * h, re);
-      c1.mul(acc);
+  auto at = [&](int c) { return rb + c * KC + VH * h; };
+  if constexpr (KIND == kGemmGs) {
+    // short reduction (C_out): one chunk ahead, loads guarded so that no
+    // chunk past the end is fetched
+    Chunk<KIND, NT, VH, WBF16, VEC> c0, c1;
+    if (0 < nch) c0.load(a, G, m, n, at(0), re, pl);
+    for (int c = 0; c < nch; c += 2) {
+      if (c + 1 < nch) c1.load(a, G, m, n, at(c + 1), re, pl);
+      c0.mul(acc);
+      if (c + 2 < nch) c0.load(a, G, m, n, at(c + 2), re, pl);
+      if (c + 1 < nch) c1.mul(acc);
+    }
+  } else {
+    // Three chunk buffers: chunks c+1 and c+2 are in flight while chunk c is
+    // multiplied.  Every load is issued unconditionally (a chunk past the end
+    // has no valid reductions and reads clamped addresses) and only the
+    // multiplies are guarded: guarded loads make the compiler copy the
+    // accumulators around the branches.
+    Chunk<KIND, NT, VH, WBF16, VEC> c0, c1, c2;
+    c0.load(a, G, m, n, at(0), re, pl);
+    c1.load(a, G, m, n, at(1), re, pl);
+    for (int c = 0; c < nch; c += 3) {
+      c2.load(a, G, m, n, at(c + 2), re, pl);
+      c0.mul(acc);
+      c0.load(a, G, m, n, at(c + 3), re, pl);
+      if (c + 1 < nch) c1.mul(acc);
+      c1.load(a, G, m, n, at(c + 4), re, pl);
+      if (c + 2 < nch) c2.mul(acc);
     }
   }
 
