@@ -309,10 +309,7 @@ struct StreamCtx {
     float y[N2];
 #pragma unroll
     for (int i = 0; i < N2; ++i) y[i] = L.Y[j][P::l2][i];
-    float u[4][NO];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Tab::fwd(xv[i], y, u[i]);
-    float gU[4][NO];
+    float gU[4][NO], gD[4][NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) {
       floatx4 g = {0.f, 0.f, 0.f, 0.f}, gd = {0.f, 0.f, 0.f, 0.f};
@@ -321,16 +318,42 @@ struct StreamCtx {
         g = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], r[k], g, 0, 0, 0);
         gd = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], rd[k], gd, 0, 0, 0);
       }
-      // alpha += sum_k R'_k <gS[k], U>;  gU = sum_k R_k gS[k]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        alpha = __builtin_fmaf(u[i][o], gd[i], alpha);
-        gU[i][o] = g[i];
+        gU[i][o] = g[i];   // sum_k R_k gS[k]
+        gD[i][o] = gd[i];  // sum_k R'_k gS[k]
       }
     }
-    if constexpr (P::l2 > 0) {  // Y_00 is constant
+    // The quad's channels are summed before the coupling table is applied:
+    //   alpha += <U, gD> = sum c y[m2] p[m1][m3],  p[m1][m3] = sum_i x_i[m1] gD_i[m3]
+    //   gy    += CG^T(x, gU)   via q[m1][m3] = sum_i x_i[m1] gU_i[m3] when that is cheaper
+    float pq[NIN * NO];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Tab::ybar(xv[i], gU[i], gy + P::l2 * P::l2);
+    for (int m1 = 0; m1 < NIN; ++m1)
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        float t = xv[0][m1] * gD[0][o];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[i][m1], gD[i][o], t);
+        pq[m1 * NO + o] = t;
+      }
+    alpha = Tab::ydot(y, pq, alpha);
+    if constexpr (P::l2 > 0) {  // Y_00 is constant
+      if constexpr (4 * NIN * NO + Tab::kNnz < 4 * Tab::kYbarOps) {
+#pragma unroll
+        for (int m1 = 0; m1 < NIN; ++m1)
+#pragma unroll
+          for (int o = 0; o < NO; ++o) {
+            float t = xv[0][m1] * gU[0][o];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[i][m1], gU[i][o], t);
+            pq[m1 * NO + o] = t;
+          }
+        Tab::qbar(pq, gy + P::l2 * P::l2);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Tab::ybar(xv[i], gU[i], gy + P::l2 * P::l2);
+      }
     }
     if constexpr (sizeof...(Rest) > 0) pos_edge<OFF + NO, TOT, NIN, Rest...>(xv, j, r, rd, gs, alpha, gy);
   }
