@@ -12,6 +12,81 @@ __device__ __forceinline__ float load_feat(const float* p, int64_t i) { return p
 __device__ __forceinline__ float load_feat(const uint16_t* p, int64_t i) {
   return __uint_as_float(((uint32_t)p[i]) << 16);
 }
+// Gathered features are kept in their stored form until they are used, and
+// widened to fp32 only there: a conversion placed at the load would make the
+// compiler wait for that load and defeat the prefetch pipelines.
+template <typename FT> struct FeatRaw;
+template <> struct FeatRaw<float> {
+  typedef float type;
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static float f32(float v) { return v; }
+};
+template <> struct FeatRaw<uint16_t> {
+  typedef uint32_t type;
+  __device__ static uint32_t load(const uint16_t* p, int64_t i) { return p[i]; }
+  __device__ static float f32(uint32_t v) { return __uint_as_float(v << 16); }
+};
+
+// Four consecutive channels of NIN rows, raw.  `base` indexes the first row's
+// first channel; with vec4 (C a multiple of 4, c0 too) each row is one 16-byte
+// (fp32) or 8-byte (bf16) load, otherwise channel c0+i reads min(c0+i, C-1).
+template <typename FT, int NIN> struct Quads;
+template <int NIN> struct Quads<float, NIN> {
+  float v[NIN][4];
+  __device__ __forceinline__ void load(const float* p, int64_t base, int C, int c0, bool vec4) {
+    if (vec4) {
+      typedef float f4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int m = 0; m < NIN; ++m) {
+        const f4 x = *reinterpret_cast<const f4*>(p + base + (int64_t)m * C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[m][i] = x[i];
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NIN; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[m][i] = p[base + (int64_t)m * C + min(i, C - 1 - c0)];
+    }
+  }
+  __device__ __forceinline__ void get(float (&x)[4][NIN]) const {
+#pragma unroll
+    for (int m = 0; m < NIN; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i][m] = v[m][i];
+  }
+};
+template <int NIN> struct Quads<uint16_t, NIN> {
+  uint32_t w[NIN][2];  // channels (c0, c0+1) and (c0+2, c0+3), low half first
+  __device__ __forceinline__ void load(const uint16_t* p, int64_t base, int C, int c0, bool vec4) {
+    if (vec4) {
+#pragma unroll
+      for (int m = 0; m < NIN; ++m) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p + base + (int64_t)m * C);
+        w[m][0] = u.x;
+        w[m][1] = u.y;
+      }
+    } else {  // rare: pack four clamped channels
+#pragma unroll
+      for (int m = 0; m < NIN; ++m) {
+        const uint16_t* r = p + base + (int64_t)m * C;
+        const int l = C - 1 - c0;
+        w[m][0] = (uint32_t)r[0] | ((uint32_t)r[min(1, l)] << 16);
+        w[m][1] = (uint32_t)r[min(2, l)] | ((uint32_t)r[min(3, l)] << 16);
+      }
+    }
+  }
+  __device__ __forceinline__ void get(float (&x)[4][NIN]) const {
+#pragma unroll
+    for (int m = 0; m < NIN; ++m) {
+      x[0][m] = __uint_as_float(w[m][0] << 16);
+      x[1][m] = __uint_as_float(w[m][0] & 0xffff0000u);
+      x[2][m] = __uint_as_float(w[m][1] << 16);
+      x[3][m] = __uint_as_float(w[m][1] & 0xffff0000u);
+    }
+  }
+};
+
 // Four consecutive features p[i..i+3]; i must be a multiple of 4.
 __device__ __forceinline__ void load_feat4(const float* p, int64_t i, float (&v)[4]) {
   typedef float f4 __attribute__((ext_vector_type(4)));

@@ -443,12 +443,16 @@ struct StreamCtx {
       // outstanding gather.
       const int last = nb - 1;
       const int nslots = (nb + ES - 1) / ES;
-      auto gather = [&](int slot, float (&v)[NIN]) {
+      using Raw = FeatRaw<FT>;
+      auto gather = [&](int slot, typename Raw::type (&v)[NIN]) {
         const int64_t f = (int64_t)L.nbr[min(slot * ES + es, last)] * a.feat_rows * C + fcol;
 #pragma unroll
-        for (int i = 0; i < NIN; ++i) v[i] = load_feat(feat, f + (int64_t)i * C);
+        for (int i = 0; i < NIN; ++i) v[i] = Raw::load(feat, f + (int64_t)i * C);
       };
-      auto step = [&](int slot, const float (&av)[NIN]) {
+      auto step = [&](int slot, const typename Raw::type (&raw)[NIN]) {
+        float av[NIN];
+#pragma unroll
+        for (int i = 0; i < NIN; ++i) av[i] = Raw::f32(raw[i]);
         const int j = slot * ES + es;
         const int jj = min(j, last);
         const float mask = j < nb ? 1.f : 0.f;  // multiply, not select: no branch around the reads
@@ -461,7 +465,7 @@ struct StreamCtx {
         }
         edge<0, TOT, NIN, Ps...>(av, jj, r, rd, acc);
       };
-      float bA[NIN], bB[NIN];
+      typename Raw::type bA[NIN], bB[NIN];
       gather(0, bA);
       for (int t = 0; t < nslots; t += 2) {  // an odd last slot is masked
         gather(t + 1, bB);
@@ -508,6 +512,12 @@ struct StreamCtx {
 
     float gs[K][TOT];
     load_gs<0, 0, TOT, Ps...>(a, gs, c_own);
+    if (tile * CT + cl >= C) {  // a lane past the channel count contributes nothing
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int o = 0; o < TOT; ++o) gs[k][o] = 0.f;
+    }
     float vs0 = 0.f, vs1 = 0.f, vs2 = 0.f;  // receiver share of the position gradient
 
     const float psx = a.pos[3 * (int64_t)node], psy = a.pos[3 * (int64_t)node + 1],
@@ -523,28 +533,14 @@ struct StreamCtx {
       const int nsteps = (nb + per_step - 1) / per_step;
       // gathered block of the lane's edge for the quad's channels (clamped
       // edge index: unconditional loads, as in the accumulating modes)
-      auto gather = [&](int t, float (&v)[4][NIN]) {
+      // (channels past C read channel C-1; their cotangents are zero)
+      auto gather = [&](int t, Quads<FT, NIN>& v) {
         const int jl = min(t * per_step + 4 * es + j4, last);
-        const int64_t base = (int64_t)L.nbr[jl] * a.feat_rows * C + frow;
-        if (vec4) {
-#pragma unroll
-          for (int m = 0; m < NIN; ++m) {
-            float q[4];
-            load_feat4(feat, base + (int64_t)m * C + c0, q);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i][m] = q[i];
-          }
-        } else {  // a quad past the channel count reads channel C-1 and is zeroed
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float ok = c0 + i < C ? 1.f : 0.f;
-            const int ci = min(c0 + i, C - 1);
-#pragma unroll
-            for (int m = 0; m < NIN; ++m) v[i][m] = load_feat(feat, base + (int64_t)m * C + ci) * ok;
-          }
-        }
+        v.load(feat, (int64_t)L.nbr[jl] * a.feat_rows * C + frow + min(c0, C - 1), C, min(c0, C - 1), vec4);
       };
-      auto step = [&](int t, const float (&xv)[4][NIN]) {
+      auto step = [&](int t, const Quads<FT, NIN>& raw) {
+        float xv[4][NIN];
+        raw.get(xv);
         const int jl = t * per_step + 4 * es + j4;
         const int jj = min(jl, last);
         float r[K], rd[K];
@@ -577,7 +573,7 @@ struct StreamCtx {
           vs2 -= vec[2];
         }
       };
-      float bA[4][NIN], bB[4][NIN];
+      Quads<FT, NIN> bA, bB;
       gather(0, bA);
       for (int t = 0; t < nsteps; t += 2) {  // an odd last step is masked
         gather(t + 1, bB);
