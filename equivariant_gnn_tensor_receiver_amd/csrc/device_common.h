@@ -29,7 +29,9 @@ template <> struct FeatRaw<uint16_t> {
 
 // Four consecutive channels of NIN rows, raw.  `base` indexes the first row's
 // first channel; with vec4 (C a multiple of 4, c0 too) each row is one 16-byte
-// (fp32) or 8-byte (bf16) load, otherwise channel c0+i reads min(c0+i, C-1).
+// (fp32) or 8-byte (bf16) load.  Otherwise each channel is read on its own and
+// channels past C are zero (that path waits for its loads; it only serves
+// channel counts that are not multiples of 4).
 template <typename FT, int NIN> struct Quads;
 template <int NIN> struct Quads<float, NIN> {
   float v[NIN][4];
@@ -46,15 +48,12 @@ template <int NIN> struct Quads<float, NIN> {
 #pragma unroll
       for (int m = 0; m < NIN; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[m][i] = p[base + (int64_t)m * C + min(i, C - 1 - c0)];
+        for (int i = 0; i < 4; ++i)
+          v[m][i] = c0 + i < C ? p[base + (int64_t)m * C + min(i, C - 1 - c0)] : 0.f;
     }
   }
-  __device__ __forceinline__ void get(float (&x)[4][NIN]) const {
-#pragma unroll
-    for (int m = 0; m < NIN; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i][m] = v[m][i];
-  }
+  // fp32: the raw rows already are the values, [row][channel]
+  __device__ __forceinline__ const float (&get(float (&)[NIN][4]) const)[NIN][4] { return v; }
 };
 template <int NIN> struct Quads<uint16_t, NIN> {
   uint32_t w[NIN][2];  // channels (c0, c0+1) and (c0+2, c0+3), low half first
@@ -71,19 +70,21 @@ template <int NIN> struct Quads<uint16_t, NIN> {
       for (int m = 0; m < NIN; ++m) {
         const uint16_t* r = p + base + (int64_t)m * C;
         const int l = C - 1 - c0;
-        w[m][0] = (uint32_t)r[0] | ((uint32_t)r[min(1, l)] << 16);
-        w[m][1] = (uint32_t)r[min(2, l)] | ((uint32_t)r[min(3, l)] << 16);
+        w[m][0] = (uint32_t)r[0] | (l >= 1 ? (uint32_t)r[1] << 16 : 0u);
+        w[m][1] = (l >= 2 ? (uint32_t)r[2] : 0u) | (l >= 3 ? (uint32_t)r[3] << 16 : 0u);
       }
     }
   }
-  __device__ __forceinline__ void get(float (&x)[4][NIN]) const {
+  // bf16: widen into x, [row][channel]
+  __device__ __forceinline__ const float (&get(float (&x)[NIN][4]) const)[NIN][4] {
 #pragma unroll
     for (int m = 0; m < NIN; ++m) {
-      x[0][m] = __uint_as_float(w[m][0] << 16);
-      x[1][m] = __uint_as_float(w[m][0] & 0xffff0000u);
-      x[2][m] = __uint_as_float(w[m][1] << 16);
-      x[3][m] = __uint_as_float(w[m][1] & 0xffff0000u);
+      x[m][0] = __uint_as_float(w[m][0] << 16);
+      x[m][1] = __uint_as_float(w[m][0] & 0xffff0000u);
+      x[m][2] = __uint_as_float(w[m][1] << 16);
+      x[m][3] = __uint_as_float(w[m][1] & 0xffff0000u);
     }
+    return x;
   }
 };
 

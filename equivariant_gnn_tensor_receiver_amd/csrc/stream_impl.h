@@ -292,15 +292,15 @@ struct StreamCtx {
   }
 
   // Position gradient, one edge per lane and four channels per lane (compile-
-  // time recursion over the member paths).  xv[i] holds the gathered block of
-  // channel c0 + i, where c0 is the first channel of the lane's quad; gs is
+  // time recursion over the member paths).  xv[m][i] holds row m of the gathered
+  // block for channel c0 + i, where c0 is the first channel of the lane's quad; gs is
   // the lane's own channel's state cotangent, the A operand of the matrix
   // cores, and r / rd this lane's edge's R and R', the B operand.  A chain of
   // K 4x4x1 outer products then leaves in register i of lane 4b + j
   //   sum_k gS[k][o](channel c0 + i) * R_k(edge of lane 4b + j),
   // i.e. sum_k R_k gS[k] for the lane's own edge and its quad's channels.
   template <int OFF, int TOT, int NIN, class P, class... Rest>
-  __device__ __forceinline__ void pos_edge(const float (&xv)[4][NIN], int j, const float (&r)[K],
+  __device__ __forceinline__ void pos_edge(const float (&xv)[NIN][4], int j, const float (&r)[K],
                                            const float (&rd)[K], const float (&gs)[K][TOT], float& alpha,
                                            float (&gy)[NSH]) {
     constexpr int N2 = 2 * P::l2 + 1;
@@ -332,9 +332,9 @@ struct StreamCtx {
     for (int m1 = 0; m1 < NIN; ++m1)
 #pragma unroll
       for (int o = 0; o < NO; ++o) {
-        float t = xv[0][m1] * gD[0][o];
+        float t = xv[m1][0] * gD[0][o];
 #pragma unroll
-        for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[i][m1], gD[i][o], t);
+        for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], gD[i][o], t);
         pq[m1 * NO + o] = t;
       }
     alpha = Tab::ydot(y, pq, alpha);
@@ -344,15 +344,20 @@ struct StreamCtx {
         for (int m1 = 0; m1 < NIN; ++m1)
 #pragma unroll
           for (int o = 0; o < NO; ++o) {
-            float t = xv[0][m1] * gU[0][o];
+            float t = xv[m1][0] * gU[0][o];
 #pragma unroll
-            for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[i][m1], gU[i][o], t);
+            for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], gU[i][o], t);
             pq[m1 * NO + o] = t;
           }
         Tab::qbar(pq, gy + P::l2 * P::l2);
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Tab::ybar(xv[i], gU[i], gy + P::l2 * P::l2);
+        for (int i = 0; i < 4; ++i) {
+          float xi[NIN];
+#pragma unroll
+          for (int m1 = 0; m1 < NIN; ++m1) xi[m1] = xv[m1][i];
+          Tab::ybar(xi, gU[i], gy + P::l2 * P::l2);
+        }
       }
     }
     if constexpr (sizeof...(Rest) > 0) pos_edge<OFF + NO, TOT, NIN, Rest...>(xv, j, r, rd, gs, alpha, gy);
@@ -512,12 +517,6 @@ struct StreamCtx {
 
     float gs[K][TOT];
     load_gs<0, 0, TOT, Ps...>(a, gs, c_own);
-    if (tile * CT + cl >= C) {  // a lane past the channel count contributes nothing
-#pragma unroll
-      for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int o = 0; o < TOT; ++o) gs[k][o] = 0.f;
-    }
     float vs0 = 0.f, vs1 = 0.f, vs2 = 0.f;  // receiver share of the position gradient
 
     const float psx = a.pos[3 * (int64_t)node], psy = a.pos[3 * (int64_t)node + 1],
@@ -533,14 +532,14 @@ struct StreamCtx {
       const int nsteps = (nb + per_step - 1) / per_step;
       // gathered block of the lane's edge for the quad's channels (clamped
       // edge index: unconditional loads, as in the accumulating modes)
-      // (channels past C read channel C-1; their cotangents are zero)
+      // (channels past C, only when C is not a multiple of 4, read as zero)
       auto gather = [&](int t, Quads<FT, NIN>& v) {
         const int jl = min(t * per_step + 4 * es + j4, last);
         v.load(feat, (int64_t)L.nbr[jl] * a.feat_rows * C + frow + min(c0, C - 1), C, min(c0, C - 1), vec4);
       };
       auto step = [&](int t, const Quads<FT, NIN>& raw) {
-        float xv[4][NIN];
-        raw.get(xv);
+        float tmp[NIN][4];
+        const float(&xv)[NIN][4] = raw.get(tmp);
         const int jl = t * per_step + 4 * es + j4;
         const int jj = min(jl, last);
         float r[K], rd[K];
