@@ -12,7 +12,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -88,6 +91,80 @@ size_t ws_double_backward(const Plan& p, int64_t N) {
 }
 
 tpconv_status dev(hipError_t e) { return e == hipSuccess ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE; }
+
+// Independent chains of one call (the position gradient, the input gradient
+// and the weight gradient) run concurrently: a second stream per device,
+// created on first use with the default priority, is forked from the
+// caller's stream with an event and joined back before the call returns.
+// The mutex keeps the record/wait pairs of concurrent callers on one device
+// from interleaving.  While kernel timing is on, or with TPCONV_OVERLAP=0 in
+// the environment, everything stays on the caller's stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+SideStream* side_stream() {
+  static std::mutex mu;
+  static std::map<int, SideStream*> per_device;
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = per_device.find(d);
+  if (it != per_device.end()) return it->second;
+  SideStream* ss = new (std::nothrow) SideStream();
+  if (!ss) return nullptr;
+  if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
+    delete ss;  // (a failed creation leaves the call on one stream)
+    return nullptr;
+  }
+  per_device[d] = ss;
+  return ss;
+}
+
+bool overlap_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("TPCONV_OVERLAP");
+    return !(e && e[0] == '0');
+  }();
+  return on && !timing_enabled();
+}
+
+class Fork {
+ public:
+  explicit Fork(hipStream_t main) : main_(main), side_(main) {
+    if (!overlap_enabled()) return;
+    ss_ = side_stream();
+    if (!ss_) return;
+    ss_->mu.lock();
+    if (hipEventRecord(ss_->fork, main_) != hipSuccess || hipStreamWaitEvent(ss_->s, ss_->fork, 0) != hipSuccess) {
+      ss_->mu.unlock();
+      ss_ = nullptr;
+      return;
+    }
+    side_ = ss_->s;
+  }
+  hipStream_t side() const { return side_; }
+  // Makes the caller's stream wait for the side stream; idempotent.
+  tpconv_status join() {
+    if (!ss_) return TPCONV_SUCCESS;
+    hipError_t e = hipEventRecord(ss_->join, side_);
+    if (e == hipSuccess) e = hipStreamWaitEvent(main_, ss_->join, 0);
+    ss_->mu.unlock();
+    ss_ = nullptr;
+    return dev(e);
+  }
+  ~Fork() { join(); }
+  Fork(const Fork&) = delete;
+  Fork& operator=(const Fork&) = delete;
+
+ private:
+  hipStream_t main_, side_;
+  SideStream* ss_ = nullptr;
+};
 
 tpconv_status check_graph(const tpconv_graph* g, bool need_csc) {
   if (!g) return TPCONV_ERROR_INVALID_VALUE;
@@ -423,20 +500,29 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
   float* T = c.take(state_out_elems(p, N));
   float* part = c.take((size_t)gw_splits(p, N) * w_elems(p));
 
-  if (grad_W) {
-    const float* S = saved_state;
-    if (!S) {
-      StreamArgs a;
-      recv_args(p, a, g, pos, x);
-      a.state = S_ws;
-      if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
-          TPCONV_SUCCESS)
-        return st;
-      S = S_ws;
-    }
-    if ((st = run_gw(p, N, S, grad_out, part, grad_W, s)) != TPCONV_SUCCESS) return st;
+  const float* S = saved_state;
+  if (grad_W && !S) {  // recompute the receiver state for the weight gradient
+    StreamArgs a;
+    recv_args(p, a, g, pos, x);
+    a.state = S_ws;
+    if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+        TPCONV_SUCCESS)
+      return st;
+    S = S_ws;
   }
-  if (grad_pos) {
+  Fork fork(s);
+  const hipStream_t s2 = fork.side();
+  if (grad_x) {  // side stream: sender stream, then g_x = T W^T
+    StreamArgs a;
+    send_args(p, a, g, pos, grad_out);
+    a.state = T;
+    if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
+    if ((st = run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s2)) != TPCONV_SUCCESS) return st;
+  }
+  if (grad_W) {  // side stream: gW = S^T g_out
+    if ((st = run_gw(p, N, S, grad_out, part, grad_W, s2)) != TPCONV_SUCCESS) return st;
+  }
+  if (grad_pos) {  // caller's stream: gS = g_out W^T, then the position gradient
     if ((st = run_gemm(p, kGemmGs, N, nullptr, grad_out, W, gS, 1, s)) != TPCONV_SUCCESS) return st;
     if ((st = dev(launch_fill(grad_pos, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
     StreamArgs a;
@@ -448,14 +534,7 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
         TPCONV_SUCCESS)
       return st;
   }
-  if (grad_x) {
-    StreamArgs a;
-    send_args(p, a, g, pos, grad_out);
-    a.state = T;
-    if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s))) != TPCONV_SUCCESS) return st;
-    if ((st = run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s)) != TPCONV_SUCCESS) return st;
-  }
-  return TPCONV_SUCCESS;
+  return fork.join();
 }
 
 tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
@@ -479,7 +558,17 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
   float* Sd = c.take(state_in_elems(p, N));
   float* Td = c.take(state_out_elems(p, N));
   float* part = c.take((size_t)gw_splits(p, N) * w_elems(p));
-  if (d_W || d_grad_out) {
+  Fork fork(s);
+  const hipStream_t s2 = fork.side();
+  if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
+    StreamArgs a;
+    send_args(p, a, g, pos, grad_out);
+    a.ggpos = gg_pos;
+    a.state = Td;
+    if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
+    if ((st = run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s2)) != TPCONV_SUCCESS) return st;
+  }
+  if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
     StreamArgs a;
     recv_args(p, a, g, pos, x);
     a.ggpos = gg_pos;
@@ -491,15 +580,7 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
     if (d_grad_out && (st = run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s)) != TPCONV_SUCCESS)
       return st;
   }
-  if (d_x) {
-    StreamArgs a;
-    send_args(p, a, g, pos, grad_out);
-    a.ggpos = gg_pos;
-    a.state = Td;
-    if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s))) != TPCONV_SUCCESS) return st;
-    if ((st = run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s)) != TPCONV_SUCCESS) return st;
-  }
-  return TPCONV_SUCCESS;
+  return fork.join();
 }
 
 tpconv_status tpconv_kernel_timing(int32_t enable) {

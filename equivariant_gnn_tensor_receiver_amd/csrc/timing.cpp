@@ -63,6 +63,8 @@ TimingScope::~TimingScope() {
   g_records.push_back({cls_, start_, stop});
 }
 
+bool timing_enabled() { return g_enabled.load(); }
+
 bool timing_set(bool enable) {
   std::lock_guard<std::mutex> lk(g_mu);
   for (auto& r : g_records)

@@ -27,6 +27,7 @@ class TimingScope {
 };
 
 bool timing_set(bool enable);  // clears the table; returns false on a HIP error
+bool timing_enabled();
 bool timing_read(int cls, long long* launches, double* total_ms);
 
 }  // namespace tpconv
