@@ -20,9 +20,16 @@ for a bounded chunk of edges at a time and scatter-adds with ``np.add.at``.
 The backward and double backward are written out by hand from the chain rule
 on the same materialised intermediates (adjoints g_w, g_U, g_Y, g_R per edge).
 
+Two connections of the channels are covered.  Fully connected ("uvw"): one
+C_in x C_out matrix per (k, path), W[k, p, ci, co].  Channel-wise ("uvu",
+C_in = C_out = C): one weight per (k, path, channel), W[k, p, c], so
+w_e[p, c] = sum_k R_e[k] W[k, p, c] and m_e[l3, c, m3] = sum_p w_e[p, c]
+U_e[p, c, m3] (the Sobek page's abstract names two operator families; this
+reading takes the channel-wise product as the second).
+
 Layouts (shared with the library's public header only as a data contract):
   x   [N][D_in][C_in],  out [N][D_out][C_out]   rows ordered by irreps, l^2+l+m
-  W   [K][P][C_in][C_out]                        P paths in oracle.cg order
+  W   [K][P][C_in][C_out] (uvw) or [K][P][C] (uvu), P paths in oracle.cg order
   pos [N][3]
 """
 from __future__ import annotations
@@ -44,6 +51,7 @@ class Problem:
     num_basis: int
     cutoff: float = 5.0
     envelope_p: int = 6
+    channelwise: bool = False
     ir_in: list = field(init=False)
     ir_out: list = field(init=False)
     paths: list = field(init=False)
@@ -57,6 +65,8 @@ class Problem:
             raise ValueError("uniform multiplicity per irreps string is required")
         self.C_in = muls_in.pop()
         self.C_out = muls_out.pop()
+        if self.channelwise and self.C_in != self.C_out:
+            raise ValueError("the channel-wise product needs equal multiplicities")
         self.D_in = _cg.irreps_dim(self.ir_in)
         self.D_out = _cg.irreps_dim(self.ir_out)
         self.off_in = _cg.irreps_offsets(self.ir_in)
@@ -68,7 +78,19 @@ class Problem:
 
     @property
     def w_shape(self):
+        if self.channelwise:
+            return (self.num_basis, self.P, self.C_in)
         return (self.num_basis, self.P, self.C_in, self.C_out)
+
+    # einsum forms of the weight contractions.  Index letters: e edge, k basis,
+    # p path, i input channel, o output channel, c (in U) the m3 component.
+    @property
+    def ops(self):
+        if self.channelwise:  # w_e[e, p, i]; messages and adjoints keep the channel i
+            return dict(w="ek,kpi->epi", msg="ei,eic->eci", g_w="eic,eci->ei", g_U="ei,eci->eic",
+                        g_W="ek,epi->kpi", g_R="kpi,epi->ek", dW_a="ek,ei->ki", dW_b="ek,eic,eci->ki")
+        return dict(w="ek,kpio->epio", msg="eio,eic->eco", g_w="eic,eco->eio", g_U="eio,eco->eic",
+                    g_W="ek,epio->kpio", g_R="kpio,epio->ek", dW_a="ek,eio->kio", dW_b="ek,eic,eco->kio")
 
 
 def csr_receivers(rowptr: np.ndarray) -> np.ndarray:
@@ -137,10 +159,11 @@ def forward(prob: Problem, pos, senders, receivers, x, W, num_nodes=None):
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
         _, _, _, R, Y = _edge_terms(prob, pos, s, v)
-        w_e = np.einsum("ek,kpio->epio", R, W, optimize=True)       # per-edge weights
+        ops = prob.ops
+        w_e = np.einsum(ops["w"], R, W, optimize=True)              # per-edge weights
         for pi, p in enumerate(prob.paths):
             U = _coupling(p["C"], _x_block(prob, x, s, p), _y_block(Y, p))
-            msg = np.einsum("eio,eic->eco", w_e[:, pi], U, optimize=True)   # message
+            msg = np.einsum(ops["msg"], w_e[:, pi], U, optimize=True)      # message
             np.add.at(out[:, _out_rows(prob, p), :], v, msg)
     return out
 
@@ -160,7 +183,8 @@ def backward(prob: Problem, pos, senders, receivers, x, W, g_out):
         r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
         dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
         JY = _sh.sh_jacobian(prob.sh_lmax, r)                     # [e, Dsh, 3]
-        w_e = np.einsum("ek,kpio->epio", R, W, optimize=True)
+        ops = prob.ops
+        w_e = np.einsum(ops["w"], R, W, optimize=True)
         g_m = g_out[v]                                           # message adjoint
         g_w = np.zeros_like(w_e)
         g_Y = np.zeros_like(Y)
@@ -170,15 +194,15 @@ def backward(prob: Problem, pos, senders, receivers, x, W, g_out):
             y = _y_block(Y, p)
             U = _coupling(C, xs, y)
             gm = g_m[:, _out_rows(prob, p), :]                     # [e, m3, co]
-            g_w[:, pi] = np.einsum("eic,eco->eio", U, gm, optimize=True)
-            g_U = np.einsum("eio,eco->eic", w_e[:, pi], gm, optimize=True)
+            g_w[:, pi] = np.einsum(ops["g_w"], U, gm, optimize=True)
+            g_U = np.einsum(ops["g_U"], w_e[:, pi], gm, optimize=True)
             gx_e = np.einsum("abc,eb,eic->eai", C, y, g_U, optimize=True)
             np.add.at(g_x[:, _in_rows(prob, p), :], s, gx_e)
             l2 = p["l2"]
             g_Y[:, l2 * l2:(l2 + 1) * (l2 + 1)] += np.einsum(
                 "abc,eai,eic->eb", C, xs, g_U, optimize=True)
-        g_W += np.einsum("ek,epio->kpio", R, g_w, optimize=True)
-        g_R = np.einsum("kpio,epio->ek", W, g_w, optimize=True)
+        g_W += np.einsum(ops["g_W"], R, g_w, optimize=True)
+        g_R = np.einsum(ops["g_R"], W, g_w, optimize=True)
         g_r = (np.einsum("ek,ek->e", g_R, dR)[:, None] * rhat
                + np.einsum("em,emj->ej", g_Y, JY))
         np.add.at(g_pos, s, g_r)
@@ -211,8 +235,9 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
         phi = gg_pos[s] - gg_pos[v]
         R_dot = dR * np.einsum("ej,ej->e", rhat, phi)[:, None]
         Y_dot = np.einsum("emj,ej->em", JY, phi)
-        w_e = np.einsum("ek,kpio->epio", R, W, optimize=True)
-        w_dot = np.einsum("ek,kpio->epio", R_dot, W, optimize=True)
+        ops = prob.ops
+        w_e = np.einsum(ops["w"], R, W, optimize=True)
+        w_dot = np.einsum(ops["w"], R_dot, W, optimize=True)
         g_m = g_out[v]
         for pi, p in enumerate(prob.paths):
             C = p["C"]
@@ -222,15 +247,15 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
             U = _coupling(C, xs, y)
             U_dot = _coupling(C, xs, y_dot)
             gm = g_m[:, _out_rows(prob, p), :]
-            g_w = np.einsum("eic,eco->eio", U, gm, optimize=True)
-            g_U = np.einsum("eio,eco->eic", w_e[:, pi], gm, optimize=True)
-            gUdot_w = np.einsum("eio,eco->eic", w_dot[:, pi], gm, optimize=True)
-            d_W[:, pi] += (np.einsum("ek,eio->kio", R_dot, g_w, optimize=True)
-                           + np.einsum("ek,eic,eco->kio", R, U_dot, gm, optimize=True))
+            g_w = np.einsum(ops["g_w"], U, gm, optimize=True)
+            g_U = np.einsum(ops["g_U"], w_e[:, pi], gm, optimize=True)
+            gUdot_w = np.einsum(ops["g_U"], w_dot[:, pi], gm, optimize=True)
+            d_W[:, pi] += (np.einsum(ops["dW_a"], R_dot, g_w, optimize=True)
+                           + np.einsum(ops["dW_b"], R, U_dot, gm, optimize=True))
             dx_e = (np.einsum("abc,eb,eic->eai", C, y_dot, g_U, optimize=True)
                     + np.einsum("abc,eb,eic->eai", C, y, gUdot_w, optimize=True))
             np.add.at(d_x[:, _in_rows(prob, p), :], s, dx_e)
-            dgo = (np.einsum("eio,eic->eco", w_dot[:, pi], U, optimize=True)
-                   + np.einsum("eio,eic->eco", w_e[:, pi], U_dot, optimize=True))
+            dgo = (np.einsum(ops["msg"], w_dot[:, pi], U, optimize=True)
+                   + np.einsum(ops["msg"], w_e[:, pi], U_dot, optimize=True))
             np.add.at(d_gout[:, _out_rows(prob, p), :], v, dgo)
     return d_W, d_x, d_gout
