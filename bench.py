@@ -60,6 +60,9 @@ def algorithmic(plan, paths, N, E, xbytes):
         "gemm_gs": (2 * N * K * Ci * Co * M3, go + Wb + S),
         "gemm_gx": (2 * N * K * Ci * Co * M1, T + Wb + x // xbytes * 4),
         "gemm_gw": (2 * N * K * Ci * Co * M3, S + go + 4 * plan.w_numel),
+        # channel-wise contractions (out side shown; the input side is the same size for these path sets)
+        "cw_contract": (2 * N * K * Ci * M3, S + Wb + go),
+        "cw_gw": (2 * N * K * Ci * M3, S + go),
     }
 
 
@@ -105,7 +108,7 @@ def cpu_baseline(name, w, data, plan, sample_edges):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = 1
-    prob = otp.Problem(w.irreps, w.irreps, w.lmax, w.num_basis)
+    prob = otp.Problem(w.irreps, w.irreps, w.lmax, w.num_basis, channelwise=w.channelwise)
     rowptr = data["rowptr"]
     nrecv = int(np.searchsorted(rowptr, sample_edges, side="right") - 1)
     nrecv = max(1, min(nrecv, w.num_nodes))
@@ -147,7 +150,8 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     dt_code = tp.TPCONV_BF16 if w.dtype == "bf16" else tp.TPCONV_F32
-    plan = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis, inputs.CUTOFF, 6, dt_code, dt_code)
+    plan = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis, inputs.CUTOFF, 6, dt_code, dt_code,
+                   tp.CHANNELWISE if w.channelwise else tp.FULLY_CONNECTED)
     t0 = time.perf_counter()
     data = inputs.make_workload(args.workload, plan.num_paths)
     t_gen = time.perf_counter() - t0
@@ -262,7 +266,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "num_nodes": N, "num_edges": E, "mean_degree": round(E / N, 2),
                    "irreps": w.irreps, "sh_lmax": w.lmax, "num_basis": w.num_basis, "paths": plan.num_paths,
-                   "step": "+".join(w.passes), "cutoff": inputs.CUTOFF, "box": round(data["box"], 4)},
+                   "step": "+".join(w.passes), "cutoff": inputs.CUTOFF, "box": round(data["box"], 4),
+                   "connection": "channelwise" if w.channelwise else "fully_connected"},
         "passes": passes,
         "peak_bytes": {"workspace_fwd": plan.workspace_size(tp.OP_FORWARD, N, E),
                        "workspace_bwd": plan.workspace_size(tp.OP_BACKWARD, N, E),
@@ -279,7 +284,8 @@ def main():
     if not args.no_cpu_baseline:
         # about 10-30 s of oracle work on the machine's host cores
         sample = args.cpu_sample_edges or {"tiny": 512, "molecular": 80000, "wide_l": 4000,
-                                           "edge_scaling": 80000, "force": 2000}[w.name]
+                                           "edge_scaling": 80000, "force": 2000,
+                                           "molecular_uvu": 120000}[w.name]
         res["cpu_baseline"] = cpu_baseline(w.name, w, data, plan, sample)
     print(json.dumps(res), flush=True)
 

@@ -43,7 +43,7 @@ STREAM_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 UNITS = ([(f"stream_{n}", "stream_inst.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f"-DTP_FT={t}",
                                                             f"-DTP_LAUNCHER=launch_stream_{n}"])
           for n, m, t in STREAM_VARIANTS]
-         + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("graph", ".hip"), ("api", ".cpp"),
+         + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("channelwise", ".hip"), ("graph", ".hip"), ("api", ".cpp"),
                                              ("stream_dispatch", ".cpp"), ("plan", ".cpp"),
                                              ("timing", ".cpp"))])
 

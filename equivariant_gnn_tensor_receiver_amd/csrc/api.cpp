@@ -74,20 +74,41 @@ int gw_splits(const Plan& p, int64_t N) {
 
 size_t state_in_elems(const Plan& p, int64_t N) { return (size_t)(N * p.state_in_per_node); }
 size_t state_out_elems(const Plan& p, int64_t N) { return (size_t)(N * p.state_out_per_node); }
-size_t w_elems(const Plan& p) { return (size_t)p.K * p.P * p.C_in * p.C_out; }
+bool channelwise(const Plan& p) { return p.connection == TPCONV_CHANNELWISE; }
+size_t w_elems(const Plan& p) { return (size_t)p.K * p.P * p.C_in * (channelwise(p) ? 1 : p.C_out); }
+
+// Row splits of the channel-wise weight gradient: about 256k threads, each
+// summing at least 16 rows of the smallest group.
+int cw_splits(const Plan& p, int64_t N) {
+  const int64_t elems = (int64_t)w_elems(p);
+  int64_t min_rows = INT64_MAX;
+  for (const auto& g : p.out_groups)
+    if (!g.paths.empty()) min_rows = std::min<int64_t>(min_rows, N * (2 * g.l + 1));
+  if (elems == 0 || min_rows == INT64_MAX) return 1;
+  int64_t s = (262144 + elems - 1) / elems;
+  s = std::min<int64_t>(s, 1024);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, min_rows / 16));
+  return (int)std::max<int64_t>(1, s);
+}
+
+// Partial sums of the weight gradient (either connection).
+size_t part_elems(const Plan& p, int64_t N) {
+  return (size_t)(channelwise(p) ? cw_splits(p, N) : gw_splits(p, N)) * w_elems(p);
+}
 
 size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
   return have_saved ? 0 : align_up(state_in_elems(p, N) * 4);
 }
 
 size_t ws_backward(const Plan& p, int64_t N) {
-  return align_up(state_in_elems(p, N) * 4) * 2 + align_up(state_out_elems(p, N) * 4) +
-         align_up((size_t)gw_splits(p, N) * w_elems(p) * 4);
+  // S (recomputed when not saved), gS (fully connected only), T, gW partials
+  return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
+         align_up(part_elems(p, N) * 4);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
   return align_up(state_in_elems(p, N) * 4) + align_up(state_out_elems(p, N) * 4) +
-         align_up((size_t)gw_splits(p, N) * w_elems(p) * 4);
+         align_up(part_elems(p, N) * 4);
 }
 
 tpconv_status dev(hipError_t e) { return e == hipSuccess ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE; }
@@ -216,7 +237,7 @@ void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
     const Path& q = p.paths[i];
     const Group& og = p.out_groups[q.i3];
     a.paths[i] = StreamPath{q.l1, q.l2, q.l3, p.in_groups[q.i1].row_off, N * og.base_per_node,
-                            (int32_t)og.paths.size() * p.C_in, q.q_out};
+                            (int32_t)og.paths.size() * p.C_in, q.q_out, i, og.row_off};
   }
   set_units(p, a, p.recv_units);
 }
@@ -237,7 +258,7 @@ void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
     const Path& q = p.paths[i];
     const Group& ig = p.in_groups[q.i1];
     a.paths[i] = StreamPath{q.l1, q.l2, q.l3, p.out_groups[q.i3].row_off, N * ig.base_per_node,
-                            (int32_t)ig.paths.size() * p.C_out, q.q_in};
+                            (int32_t)ig.paths.size() * p.C_out, q.q_in, i, p.in_groups[q.i1].row_off};
   }
   set_units(p, a, p.send_units);
 }
@@ -332,6 +353,81 @@ tpconv_status run_gw(const Plan& p, int64_t N, const float* state, const float* 
   return dev(launch_gw_reduce(r, total, s));
 }
 
+// Channel-wise contraction of a state over one side's groups into a feature
+// tensor: out / d_grad_out from S or S_dot (output side), g_x / d_x from T or
+// T_dot (input side).
+tpconv_status run_cw_contract(const Plan& p, bool out_side, int64_t N, const float* state, const void* W,
+                              float* dst, hipStream_t s) {
+  CwArgs a;
+  std::memset(&a, 0, sizeof(a));
+  const auto& groups = out_side ? p.out_groups : p.in_groups;
+  a.K = p.K;
+  a.P = p.P;
+  a.C = p.C_in;
+  a.N = N;
+  a.D_feat = out_side ? p.D_out : p.D_in;
+  a.w_bf16 = p.w_dtype == TPCONV_BF16;
+  a.state = state;
+  a.W = W;
+  a.dst = dst;
+  int npl = 0;
+  int64_t total = 0;
+  for (const auto& g : groups) {
+    CwGroup G{};
+    G.n = 2 * g.l + 1;
+    G.row_off = g.row_off;
+    G.npg = (int)g.paths.size();
+    G.plist = npl;
+    for (int q : g.paths) a.path_list[npl++] = q;
+    G.state_off = N * g.base_per_node;
+    G.first = total;
+    total += N * G.n * p.C_in;
+    a.g[a.ngroups++] = G;
+  }
+  a.total = total;
+  return dev(launch_cw_contract(a, s));
+}
+
+// Channel-wise weight gradient dW[k, p, c] = sum_{v, m3} state * grad_out over
+// the output groups (S for grad_W, S_dot for d_W), split over rows and summed
+// in a fixed order.
+tpconv_status run_cw_gw(const Plan& p, int64_t N, const float* state, const float* gout, float* part, float* gW,
+                        hipStream_t s) {
+  CwArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.K = p.K;
+  a.P = p.P;
+  a.C = p.C_in;
+  a.N = N;
+  a.D_feat = p.D_out;
+  a.splits = cw_splits(p, N);
+  a.state = state;
+  a.gout = gout;
+  a.dst = part;
+  int npl = 0;
+  int64_t elems = 0;
+  for (const auto& g : p.out_groups) {
+    if (g.paths.empty()) continue;
+    CwGroup G{};
+    G.n = 2 * g.l + 1;
+    G.row_off = g.row_off;
+    G.npg = (int)g.paths.size();
+    G.plist = npl;
+    for (int q : g.paths) a.path_list[npl++] = q;
+    G.state_off = N * g.base_per_node;
+    G.elem_off = elems;
+    elems += (int64_t)p.K * G.npg * p.C_in;
+    a.g[a.ngroups++] = G;
+  }
+  a.elems = elems;
+  if (elems == 0) return dev(launch_fill(gW, (int64_t)w_elems(p), 0.f, s));
+  tpconv_status st = dev(launch_cw_gw(a, s));
+  if (st != TPCONV_SUCCESS) return st;
+  a.part = part;
+  a.dst = gW;
+  return dev(launch_cw_reduce(a, s));
+}
+
 }  // namespace
 }  // namespace tpconv
 
@@ -359,7 +455,7 @@ tpconv_status tpconv_plan_create(tpconv_plan* out, const tpconv_desc* d) {
     auto* h = new (std::nothrow) tpconv_plan_s;
     if (!h) return TPCONV_ERROR_INVALID_VALUE;
     const int st = build_plan(d->irreps_in, d->irreps_out, d->sh_lmax, d->num_basis, d->cutoff, d->envelope_p,
-                              d->x_dtype, d->w_dtype, h->plan);
+                              d->x_dtype, d->w_dtype, d->connection, h->plan);
     if (st != TPCONV_SUCCESS) {
       delete h;
       return (tpconv_status)st;
@@ -474,6 +570,7 @@ tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const floa
   if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
       TPCONV_SUCCESS)
     return st;
+  if (channelwise(p)) return run_cw_contract(p, true, N, S, W, out, s);
   return run_gemm(p, kGemmOut, N, S, nullptr, W, out, 1, s);
 }
 
@@ -494,11 +591,12 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
     if (grad_W) return dev(launch_fill(grad_W, (int64_t)w_elems(p), 0.f, s));
     return TPCONV_SUCCESS;
   }
+  const bool cw = channelwise(p);
   Carver c(ws);
   float* S_ws = c.take(state_in_elems(p, N));
-  float* gS = c.take(state_in_elems(p, N));
+  float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
   float* T = c.take(state_out_elems(p, N));
-  float* part = c.take((size_t)gw_splits(p, N) * w_elems(p));
+  float* part = c.take(part_elems(p, N));
 
   const float* S = saved_state;
   if (grad_W && !S) {  // recompute the receiver state for the weight gradient
@@ -517,19 +615,28 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
     send_args(p, a, g, pos, grad_out);
     a.state = T;
     if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    if ((st = run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s2)) != TPCONV_SUCCESS) return st;
+    st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2) : run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s2);
+    if (st != TPCONV_SUCCESS) return st;
   }
   if (grad_W) {  // side stream: gW = S^T g_out
-    if ((st = run_gw(p, N, S, grad_out, part, grad_W, s2)) != TPCONV_SUCCESS) return st;
+    st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, grad_out, part, grad_W, s2);
+    if (st != TPCONV_SUCCESS) return st;
   }
-  if (grad_pos) {  // caller's stream: gS = g_out W^T, then the position gradient
-    if ((st = run_gemm(p, kGemmGs, N, nullptr, grad_out, W, gS, 1, s)) != TPCONV_SUCCESS) return st;
+  if (grad_pos) {  // caller's stream: gS = g_out W^T (formed in registers when channel-wise), then the stream
+    if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, grad_out, W, gS, 1, s)) != TPCONV_SUCCESS) return st;
     if ((st = dev(launch_fill(grad_pos, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
     StreamArgs a;
     recv_args(p, a, g, pos, x);
     set_units(p, a, p.pos_units);
     a.gstate = gS;
     a.gpos = grad_pos;
+    if (cw) {
+      a.cw = 1;
+      a.W = W;
+      a.w_bf16 = p.w_dtype == TPCONV_BF16;
+      a.gout = grad_out;
+      a.gout_rows = p.D_out;
+    }
     if ((st = dev(launch_stream(kBwdPos, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
         TPCONV_SUCCESS)
       return st;
@@ -554,10 +661,11 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
     if (d_W) return dev(launch_fill(d_W, (int64_t)w_elems(p), 0.f, s));
     return TPCONV_SUCCESS;
   }
+  const bool cw = channelwise(p);
   Carver c(ws);
   float* Sd = c.take(state_in_elems(p, N));
   float* Td = c.take(state_out_elems(p, N));
-  float* part = c.take((size_t)gw_splits(p, N) * w_elems(p));
+  float* part = c.take(part_elems(p, N));
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
@@ -566,7 +674,8 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
     a.ggpos = gg_pos;
     a.state = Td;
     if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    if ((st = run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s2)) != TPCONV_SUCCESS) return st;
+    st = cw ? run_cw_contract(p, false, N, Td, W, d_x, s2) : run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s2);
+    if (st != TPCONV_SUCCESS) return st;
   }
   if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
     StreamArgs a;
@@ -576,9 +685,15 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
     if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
         TPCONV_SUCCESS)
       return st;
-    if (d_W && (st = run_gw(p, N, Sd, grad_out, part, d_W, s)) != TPCONV_SUCCESS) return st;
-    if (d_grad_out && (st = run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s)) != TPCONV_SUCCESS)
-      return st;
+    if (d_W) {
+      st = cw ? run_cw_gw(p, N, Sd, grad_out, part, d_W, s) : run_gw(p, N, Sd, grad_out, part, d_W, s);
+      if (st != TPCONV_SUCCESS) return st;
+    }
+    if (d_grad_out) {
+      st = cw ? run_cw_contract(p, true, N, Sd, W, d_grad_out, s)
+              : run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s);
+      if (st != TPCONV_SUCCESS) return st;
+    }
   }
   return fork.join();
 }

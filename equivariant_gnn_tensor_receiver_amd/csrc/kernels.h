@@ -28,6 +28,8 @@ struct StreamPath {
   int64_t state_base;   // element offset of the group's state block
   int32_t cols_per_k;   // (#paths of the group) * channels
   int32_t q;            // path index inside its group
+  int32_t path;         // plan path index (row k * P + path of W)
+  int32_t out_row;      // first row of the path's output irrep in grad_out (channel-wise cotangent)
 };
 
 constexpr int kMaxUnitPaths = 8;  // member paths per stream work unit
@@ -50,8 +52,15 @@ struct StreamArgs {
   const float* ggpos;   // [N][3] tangent (kJvp, kSndT)
   const void* feat;     // [N][feat_rows][C], fp32 or bf16
   float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
-  const float* gstate;  // receiver-state cotangent gS (kBwdPos)
+  const float* gstate;  // receiver-state cotangent gS (kBwdPos, fully connected)
   float* gpos;          // position gradient, accumulated (kBwdPos)
+  // kBwdPos with channel-wise weights: the cotangent gS[k, p, c, m3] =
+  // W[k, p, c] grad_out[v][out_row + m3][c] is formed in registers
+  int32_t cw;           // 1: channel-wise cotangent from W and grad_out
+  int32_t w_bf16;
+  int32_t gout_rows;    // rows per node of grad_out
+  const void* W;        // [K][P][C], fp32 or bf16
+  const float* gout;    // [N][gout_rows][C]
   StreamPath paths[kMaxPaths];
   int8_t unit_paths[kMaxPaths][kMaxUnitPaths];  // plan path indices of each unit's members
 };
@@ -91,6 +100,34 @@ struct GemmArgs {
   GemmGroup g[kMaxGroups];
 };
 
+// Channel-wise (diagonal) contractions over one side's irrep groups:
+//   contract: dst[node][row_off + m][c] = sum_{q, k} W[k][path q][c] state_g[(node, m)][(k, q, c)]
+//   gw:       part[split][elem_off + (k, q, c)] = sum_{(v, m) in split} state_g[(v, m)][(k, q, c)] gout[v][row_off + m][c]
+//   reduce:   gW[k][path q][c] = sum over splits of part (fixed order)
+struct CwGroup {
+  int32_t n;         // 2l+1 rows per node
+  int32_t row_off;   // row offset of the irrep in the feature tensor
+  int32_t npg;       // paths in the group
+  int32_t plist;     // first entry in CwArgs::path_list
+  int64_t state_off; // element offset of the group's state block
+  int64_t first;     // first flattened work index of the group
+  int64_t elem_off;  // offset of the group's (k, q, c) block in the partials
+};
+
+struct CwArgs {
+  int32_t ngroups, K, P, C, D_feat, splits, w_bf16;
+  int64_t N;
+  int64_t total;      // flattened work items (contract: rows x C; gw/reduce: elements)
+  int64_t elems;      // sum over groups of K * npg * C
+  const float* state;
+  const float* gout;
+  const void* W;
+  float* dst;         // contract output, gw partials, or reduced gW
+  const float* part;  // reduce input
+  int32_t path_list[kMaxPaths];
+  CwGroup g[kMaxGroups];
+};
+
 struct ReduceArgs {
   int32_t ngroups, splits, P, C_in, C_out;
   const float* part;
@@ -109,6 +146,9 @@ int64_t gemm_wave_tiles(int M, int N, int max_cols);
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 hipError_t launch_zero_rows(float* base, int64_t N, int rows, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+hipError_t launch_cw_contract(const CwArgs& a, hipStream_t s);
+hipError_t launch_cw_gw(const CwArgs& a, hipStream_t s);
+hipError_t launch_cw_reduce(const CwArgs& a, hipStream_t s);
 hipError_t launch_graph_validate(const int32_t* rowptr, const int32_t* senders, int64_t N, int64_t E,
                                  int32_t* flag, hipStream_t s);
 hipError_t graph_csc(const int32_t* rowptr, const int32_t* senders, int64_t N, int64_t E, int32_t* colptr,

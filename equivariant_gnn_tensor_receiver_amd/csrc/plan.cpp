@@ -176,7 +176,8 @@ std::vector<std::vector<int>> natural_bundles(int L, int K, int side) {
 }
 
 int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K, float cutoff,
-               int env_p, int x_dtype, int w_dtype, Plan& plan) {
+               int env_p, int x_dtype, int w_dtype, int connection, Plan& plan) {
+  if (connection != TPCONV_FULLY_CONNECTED && connection != TPCONV_CHANNELWISE) return TPCONV_ERROR_INVALID_VALUE;
   if (!irreps_in || !irreps_out) return TPCONV_ERROR_INVALID_VALUE;
   if (K != 8 && K != 16) return TPCONV_ERROR_INVALID_VALUE;
   if (!(cutoff > 0.f) || !std::isfinite(cutoff) || env_p < 2 || env_p > 64) return TPCONV_ERROR_INVALID_VALUE;
@@ -201,6 +202,8 @@ int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K
   p.w_dtype = w_dtype;
   p.C_in = p.in[0].mul;
   p.C_out = p.out[0].mul;
+  p.connection = connection;
+  if (connection == TPCONV_CHANNELWISE && p.C_in != p.C_out) return TPCONV_ERROR_IRREPS;
   p.lmax = lmax;
   p.D_in = p.D_out = 0;
   p.in_groups.resize(p.in.size());

@@ -49,6 +49,7 @@ struct Plan {
   int sh_lmax = 0, K = 0, env_p = 6;
   float cutoff = 5.f;
   int x_dtype = 0, w_dtype = 0;
+  int connection = 0;  // tpconv_connection
   int C_in = 0, C_out = 0, D_in = 0, D_out = 0, P = 0;
   int lmax = 0;  // max degree over irreps and harmonics
   std::vector<Path> paths;
@@ -86,6 +87,6 @@ bool real_cg(int l1, int l2, int l3, std::vector<double>& out);
 
 // Returns 0 on success or a tpconv_status code.
 int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K, float cutoff,
-               int env_p, int x_dtype, int w_dtype, Plan& plan);
+               int env_p, int x_dtype, int w_dtype, int connection, Plan& plan);
 
 }  // namespace tpconv

@@ -368,11 +368,24 @@ struct StreamCtx {
   __device__ __forceinline__ void load_gs(const StreamArgs& a, float (&gs)[K][TOT], int c) {
     constexpr int NO = out_dim<MODE, P>();
     const StreamPath& Q = a.paths[a.unit_paths[unit][I]];
+    if (a.cw) {  // channel-wise: gS[k][o] = W[k, path, c] grad_out[node][out_row + o][c]
+      float go[NO];
 #pragma unroll
-    for (int k = 0; k < K; ++k)
+      for (int o = 0; o < NO; ++o) go[o] = a.gout[((int64_t)node * a.gout_rows + Q.out_row + o) * a.C + c];
 #pragma unroll
-      for (int o = 0; o < NO; ++o)
-        gs[k][OFF + o] = a.gstate[Q.state_base + ((int64_t)(node * NO + o) * K + k) * Q.cols_per_k + Q.q * a.C + c];
+      for (int k = 0; k < K; ++k) {
+        const int64_t wi = ((int64_t)k * a.npaths + Q.path) * a.C + c;
+        const float w = a.w_bf16 ? load_feat(static_cast<const uint16_t*>(a.W), wi) : static_cast<const float*>(a.W)[wi];
+#pragma unroll
+        for (int o = 0; o < NO; ++o) gs[k][OFF + o] = w * go[o];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+          gs[k][OFF + o] = a.gstate[Q.state_base + ((int64_t)(node * NO + o) * K + k) * Q.cols_per_k + Q.q * a.C + c];
+    }
     if constexpr (sizeof...(Rest) > 0) load_gs<I + 1, OFF + NO, TOT, Rest...>(a, gs, c);
   }
 

@@ -8,7 +8,8 @@ namespace tpconv {
 // Kernel classes; the numbering matches tpconv_kernel in include/tpconv.h.
 enum KernelClass : int {
   kcStreamFwd = 0, kcStreamJvp, kcStreamSnd, kcStreamSndT, kcStreamBwdPos,
-  kcGemmOut, kcGemmGs, kcGemmGx, kcGemmGw, kcGwReduce, kcFill, kcGraph, kcCount
+  kcGemmOut, kcGemmGs, kcGemmGx, kcGemmGw, kcGwReduce, kcFill, kcGraph,
+  kcCwContract, kcCwGw, kcCwReduce, kcCount
 };
 
 // While timing is enabled, brackets the launches issued in its lifetime with

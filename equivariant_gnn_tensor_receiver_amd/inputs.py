@@ -7,8 +7,9 @@ tensors and builds receiver-sorted CSR edge lists.  Shapes that depend on the
 path count are passed in by the caller.
 
 Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this
-order): positions U[0,1)^{N x 3}; x ~ N(0,1); W ~ N(0, 1/(K*C_in)); g_out ~
-N(0,1); gg_pos ~ N(0,1).  bf16 workloads round x and W to bf16 (round to
+order): positions U[0,1)^{N x 3}; x ~ N(0,1); W ~ N(0, 1/(K*C_in)) for the
+fully connected weights [K][P][C_in][C_out], or N(0, 1/K) for the channel-wise
+weights [K][P][C]; g_out ~ N(0,1); gg_pos ~ N(0,1).  bf16 workloads round x and W to bf16 (round to
 nearest even) and use the exact bf16 values on both sides.
 
 Graphs are directed radius graphs with cutoff c = 5 Angstrom, edges sorted by
@@ -42,6 +43,7 @@ class Workload:
     passes: tuple
     knn_cap: int = 0
     box: float = 0.0          # fixed cube side (Tiny)
+    channelwise: bool = False  # W[k, p, c] ("uvu") instead of W[k, p, ci, co]
 
     @property
     def irreps(self) -> str:
@@ -59,6 +61,8 @@ WORKLOADS = {
     "wide_l": Workload("wide_l", 2, 16384, 64, 64, 3, 8, "bf16", ("fwd", "bwd")),
     "edge_scaling": Workload("edge_scaling", 3, 32768, 256, 32, 2, 8, "f32", ("fwd", "bwd")),
     "force": Workload("force", 4, 8192, 64, 128, 2, 16, "f32", ("fwd", "bwd", "dbwd")),
+    # the Molecular graph and features with the channel-wise connection
+    "molecular_uvu": Workload("molecular_uvu", 1, 4096, 32, 32, 2, 8, "f32", ("fwd", "bwd"), channelwise=True),
 }
 
 
@@ -155,11 +159,16 @@ def make_graph(w: Workload):
     return pos, rowptr, senders, L, rng
 
 
-def make_tensors(rng, num_nodes, rows_in, c_in, rows_out, c_out, num_basis, num_paths, dtype="f32"):
-    """x [N,rows_in,c_in], W [K,P,c_in,c_out], g_out [N,rows_out,c_out], gg_pos [N,3]."""
+def make_tensors(rng, num_nodes, rows_in, c_in, rows_out, c_out, num_basis, num_paths, dtype="f32",
+                 channelwise=False):
+    """x [N,rows_in,c_in], W [K,P,c_in,c_out] (or [K,P,c_in] channel-wise), g_out [N,rows_out,c_out], gg_pos [N,3]."""
     x = rng.standard_normal((num_nodes, rows_in, c_in), dtype=np.float32)
-    W = (rng.standard_normal((num_basis, num_paths, c_in, c_out), dtype=np.float32)
-         * np.float32(math.sqrt(1.0 / (num_basis * c_in))))
+    if channelwise:
+        W = (rng.standard_normal((num_basis, num_paths, c_in), dtype=np.float32)
+             * np.float32(math.sqrt(1.0 / num_basis)))
+    else:
+        W = (rng.standard_normal((num_basis, num_paths, c_in, c_out), dtype=np.float32)
+             * np.float32(math.sqrt(1.0 / (num_basis * c_in))))
     g_out = rng.standard_normal((num_nodes, rows_out, c_out), dtype=np.float32)
     gg_pos = rng.standard_normal((num_nodes, 3), dtype=np.float32)
     if dtype == "bf16":
@@ -173,7 +182,7 @@ def make_workload(name: str, num_paths: int):
     w = WORKLOADS[name]
     pos, rowptr, senders, L, rng = make_graph(w)
     t = make_tensors(rng, w.num_nodes, w.rows, w.channels, w.rows, w.channels,
-                     w.num_basis, num_paths, w.dtype)
+                     w.num_basis, num_paths, w.dtype, channelwise=w.channelwise)
     return dict(workload=w, pos=pos, rowptr=rowptr, senders=senders, box=L, **t)
 
 

@@ -18,6 +18,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.so")
 
 TPCONV_F32, TPCONV_BF16 = 0, 1
+FULLY_CONNECTED, CHANNELWISE = 0, 1  # tpconv_connection
 OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_GRAPH_PREPARE = 0, 1, 2, 3
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "IRREPS", 3: "GRAPH", 4: "WORKSPACE", 5: "UNSUPPORTED",
           6: "DEVICE"}
@@ -27,7 +28,7 @@ EXPORTS = ("tpconv_plan_create", "tpconv_plan_destroy", "tpconv_plan_info", "tpc
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string",
            "tpconv_kernel_timing", "tpconv_kernel_timing_read")
 KERNELS = ("stream_fwd", "stream_jvp", "stream_snd", "stream_sndt", "stream_bwdpos", "gemm_out", "gemm_gs",
-           "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph")
+           "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce")
 
 
 class TpconvError(RuntimeError):
@@ -38,7 +39,8 @@ class TpconvError(RuntimeError):
 
 class TpconvDesc(ctypes.Structure):
     _fields_ = [("irreps_in", c_char_p), ("irreps_out", c_char_p), ("sh_lmax", c_int32), ("num_basis", c_int32),
-                ("cutoff", c_float), ("envelope_p", c_int32), ("x_dtype", c_int32), ("w_dtype", c_int32)]
+                ("cutoff", c_float), ("envelope_p", c_int32), ("x_dtype", c_int32), ("w_dtype", c_int32),
+                ("connection", c_int32)]
 
 
 class TpconvGraph(ctypes.Structure):
@@ -99,9 +101,12 @@ class Plan:
     """Owning handle of a tpconv_plan (host-side tables; no device memory)."""
 
     def __init__(self, irreps_in: str, irreps_out: str, sh_lmax: int, num_basis: int, cutoff: float = 5.0,
-                 envelope_p: int = 6, x_dtype: int = TPCONV_F32, w_dtype: int = TPCONV_F32):
+                 envelope_p: int = 6, x_dtype: int = TPCONV_F32, w_dtype: int = TPCONV_F32,
+                 connection: int = FULLY_CONNECTED):
         self._keep = (irreps_in.encode(), irreps_out.encode())
-        desc = TpconvDesc(self._keep[0], self._keep[1], sh_lmax, num_basis, cutoff, envelope_p, x_dtype, w_dtype)
+        desc = TpconvDesc(self._keep[0], self._keep[1], sh_lmax, num_basis, cutoff, envelope_p, x_dtype, w_dtype,
+                          connection)
+        self.connection = connection
         h = c_void_p()
         _check(_lib().tpconv_plan_create(ctypes.byref(h), ctypes.byref(desc)), "tpconv_plan_create")
         self.handle = h
@@ -143,6 +148,8 @@ class Plan:
 
     @property
     def w_shape(self):
+        if self.connection == CHANNELWISE:
+            return (self.num_basis, self.num_paths, self.ch_in)
         return (self.num_basis, self.num_paths, self.ch_in, self.ch_out)
 
 

@@ -72,6 +72,14 @@ typedef enum {
 
 typedef enum { TPCONV_F32 = 0, TPCONV_BF16 = 1 } tpconv_dtype;
 
+/* How the shared weights mix channels (the Sobek page's abstract names two
+ * operator families of the edge-conditioned tensor-product convolution).
+ *   FULLY_CONNECTED ("uvw"): W[K][P][C_in][C_out], one C_in x C_out matrix per
+ *                            (radial function, path).
+ *   CHANNELWISE     ("uvu"): W[K][P][C], C_in = C_out = C, one weight per
+ *                            (radial function, path, channel). */
+typedef enum { TPCONV_FULLY_CONNECTED = 0, TPCONV_CHANNELWISE = 1 } tpconv_connection;
+
 typedef enum {
   TPCONV_OP_FORWARD = 0,
   TPCONV_OP_BACKWARD = 1,
@@ -88,6 +96,7 @@ typedef struct {
   int32_t envelope_p;     /* polynomial envelope exponent p >= 2 (6 in the workloads) */
   int32_t x_dtype;        /* tpconv_dtype of x */
   int32_t w_dtype;        /* tpconv_dtype of W */
+  int32_t connection;     /* tpconv_connection; 0 (fully connected) when zero-initialised */
 } tpconv_desc;
 
 typedef struct {
@@ -105,7 +114,8 @@ typedef struct {
  * Key results: the CG product is the fully expressive coupling).  Host only;
  * touches no device.  *out receives an owning handle (free with
  * tpconv_plan_destroy).  Errors: INVALID_VALUE (null pointers, K not in {8,16},
- * cutoff <= 0, p < 2, bad dtype), IRREPS (bad strings), UNSUPPORTED (l > 3). */
+ * cutoff <= 0, p < 2, bad dtype or connection), IRREPS (bad strings, or
+ * C_in != C_out for the channel-wise connection), UNSUPPORTED (l > 3). */
 tpconv_status tpconv_plan_create(tpconv_plan* out, const tpconv_desc* desc);
 
 /* Release a plan (NULL is accepted). */
@@ -113,7 +123,7 @@ tpconv_status tpconv_plan_destroy(tpconv_plan plan);
 
 /* Sizes of a plan; any output pointer may be NULL.
  * rows_* = sum of (2l+1) over the irreps, ch_* = the multiplicity,
- * w_numel = K * P * C_in * C_out. */
+ * w_numel = K * P * C_in * C_out (fully connected) or K * P * C (channel-wise). */
 tpconv_status tpconv_plan_info(tpconv_plan plan, int32_t* num_paths, int64_t* w_numel,
                                int32_t* rows_in, int32_t* ch_in, int32_t* rows_out, int32_t* ch_out);
 
@@ -195,7 +205,10 @@ typedef enum {
   TPCONV_KERNEL_GW_REDUCE = 9,     /* ordered sum of the grad_W partials */
   TPCONV_KERNEL_FILL = 10,         /* zero fills */
   TPCONV_KERNEL_GRAPH = 11,        /* sender-sorted view construction */
-  TPCONV_KERNEL_COUNT = 12
+  TPCONV_KERNEL_CW_CONTRACT = 12,  /* channel-wise: out, grad_x, d_grad_out, d_x from S / T */
+  TPCONV_KERNEL_CW_GW = 13,        /* channel-wise: grad_W partials (also d_W) */
+  TPCONV_KERNEL_CW_REDUCE = 14,    /* channel-wise: ordered sum of the partials */
+  TPCONV_KERNEL_COUNT = 15
 } tpconv_kernel;
 
 /* Diagnostics for roofline measurements (not needed for computing).

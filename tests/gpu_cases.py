@@ -36,17 +36,20 @@ def rel_err(gpu, ref):
 class DeviceCase:
     """Seeded problem uploaded to cuda:0 plus the matching oracle Problem."""
 
-    def __init__(self, irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype="f32"):
+    def __init__(self, irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype="f32",
+                 channelwise=False):
         import torch
 
         self.dev = torch.device("cuda:0")
         xd = tp.TPCONV_BF16 if dtype == "bf16" else tp.TPCONV_F32
-        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, 6, xd, xd)
-        self.prob = otp.Problem(irreps_in, irreps_out, sh_lmax, K)
+        conn = tp.CHANNELWISE if channelwise else tp.FULLY_CONNECTED
+        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, 6, xd, xd, conn)
+        self.prob = otp.Problem(irreps_in, irreps_out, sh_lmax, K, channelwise=channelwise)
         assert self.plan.num_paths == self.prob.P
+        assert tuple(self.plan.w_shape) == tuple(self.prob.w_shape)
         N = len(rowptr) - 1
         t = inputs.make_tensors(rng, N, self.prob.D_in, self.prob.C_in, self.prob.D_out, self.prob.C_out, K,
-                                self.prob.P, dtype)
+                                self.prob.P, dtype, channelwise=channelwise)
         self.np = dict(pos=pos, rowptr=rowptr, senders=senders, **t)
         self.receivers = otp.csr_receivers(rowptr)
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
@@ -109,12 +112,13 @@ class DeviceCase:
         return otp.double_backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"])
 
 
-def small_case(irreps_in, irreps_out, sh_lmax, K, N, deg, seed, dtype="f32"):
+def small_case(irreps_in, irreps_out, sh_lmax, K, N, deg, seed, dtype="f32", channelwise=False):
     pos, rowptr, senders, rng = inputs.random_graph(N, deg, seed)
-    return DeviceCase(irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype)
+    return DeviceCase(irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype, channelwise)
 
 
 def workload_case(name):
     w = inputs.WORKLOADS[name]
     pos, rowptr, senders, _, rng = inputs.make_graph(w)
-    return DeviceCase(w.irreps, w.irreps, w.lmax, w.num_basis, pos, rowptr, senders, rng, w.dtype)
+    return DeviceCase(w.irreps, w.irreps, w.lmax, w.num_basis, pos, rowptr, senders, rng, w.dtype,
+                      w.channelwise)

@@ -18,7 +18,7 @@ from equivariant_gnn_tensor_receiver_amd import inputs
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 # workload -> receivers sampled (the oracle's per-edge work grows with C^2 * P)
-SAMPLE = {"molecular": 512, "edge_scaling": 512, "wide_l": 64, "force": 48}
+SAMPLE = {"molecular": 512, "edge_scaling": 512, "wide_l": 64, "force": 48, "molecular_uvu": 512}
 
 
 @pytest.fixture(scope="module", params=list(SAMPLE))

@@ -125,3 +125,27 @@ def test_argument_errors_before_any_launch():
     # graph prepare: short workspace
     assert lib.tpconv_graph_prepare(plan.handle, ctypes.byref(g), fake, fake, 1, fake, 8, None) == 4
     assert lib.tpconv_status_string(4) == b"workspace missing or too small"
+
+
+def test_channelwise_plan():
+    w = inputs.WORKLOADS["molecular_uvu"]
+    plan = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis, connection=tp.CHANNELWISE)
+    assert plan.w_shape == (8, 11, 32)
+    assert plan.w_numel == 8 * 11 * 32
+    # same paths and tables as the fully connected plan
+    full = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis)
+    for i in range(plan.num_paths):
+        assert plan.path(i) == full.path(i)
+        assert np.array_equal(plan.cg(i), full.cg(i))
+    # the state is shared; the backward needs no gS buffer
+    assert plan.workspace_size(tp.OP_FORWARD, 4096, 0) == full.workspace_size(tp.OP_FORWARD, 4096, 0)
+    assert plan.workspace_size(tp.OP_BACKWARD, 4096, 0) < full.workspace_size(tp.OP_BACKWARD, 4096, 0)
+    for op in (tp.OP_FORWARD, tp.OP_BACKWARD, tp.OP_DOUBLE_BACKWARD):
+        assert len({plan.workspace_size(op, 4096, E) for E in (0, 131072, 8_388_608)}) == 1
+    # channel-wise needs equal multiplicities; unknown connections are rejected
+    with pytest.raises(tp.TpconvError) as e:
+        tp.Plan("8x0e", "16x0e", 0, 8, connection=tp.CHANNELWISE)
+    assert e.value.status == 2
+    with pytest.raises(tp.TpconvError) as e:
+        tp.Plan("8x0e", "8x0e", 0, 8, connection=7)
+    assert e.value.status == 1
