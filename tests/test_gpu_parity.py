@@ -120,11 +120,12 @@ def edge_case_graph(kind):
     return pos, rowptr, senders, rng
 
 
+@pytest.mark.parametrize("channelwise", [False, True], ids=["uvw", "uvu"])
 @pytest.mark.parametrize("kind", ["empty", "self_loop_duplicates_isolated", "one_node", "long_segment"])
-def test_edge_cases(kind):
-    say(f"[case] edge case {kind}")
+def test_edge_cases(kind, channelwise):
+    say(f"[case] edge case {kind} {'channel-wise' if channelwise else 'fully connected'}")
     pos, rowptr, senders, rng = edge_case_graph(kind)
-    c = DeviceCase("8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8, pos, rowptr, senders, rng)
+    c = DeviceCase("8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8, pos, rowptr, senders, rng, channelwise=channelwise)
     out = c.forward()
     ref = c.o_forward()
     assert rel_err(out, ref) <= FWD_TOL
