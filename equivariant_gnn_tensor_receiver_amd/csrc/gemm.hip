@@ -39,20 +39,16 @@ constexpr int kMaxWaveSplit = 4;
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-__device__ __forceinline__ float load_w(const void* W, int64_t i, bool bf16) {
-  return bf16 ? load_feat(static_cast<const uint16_t*>(W), i) : static_cast<const float*>(W)[i];
+// Raw 32-bit pattern of one weight: the fp32 bits, or the bf16 bits
+// zero-extended (widened by a shift where the value is used).
+template <bool WBF16>
+__device__ __forceinline__ uint32_t raw_w(const void* W, int64_t i) {
+  if constexpr (WBF16)
+    return static_cast<const uint16_t*>(W)[i];
+  else
+    return __float_as_uint(static_cast<const float*>(W)[i]);
 }
 
-template <bool WBF16>
-__device__ __forceinline__ floatx4 load_w4(const void* W, int64_t i) {
-  if constexpr (WBF16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(W) + i);
-    return floatx4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                   __uint_as_float(u.y & 0xffff0000u)};
-  } else {
-    return *reinterpret_cast<const floatx4*>(static_cast<const float*>(W) + i);
-  }
-}
 
 // VH consecutive floats p[0..VH) (16-byte loads when VEC).  Loads are never
 // predicated and their values are not touched here: the caller clamps `p`
@@ -109,60 +105,80 @@ __device__ __forceinline__ void load_a(const GemmArgs& a, const GemmGroup& G, in
   }
 }
 
-// B operand: values t = 0..VH-1 of column n at reductions rs + t (< r_end).
+// B operand: values t = 0..VH-1 of column n at reductions rs + t, as raw bits
+// (see Bits); indices past the end of the reduction read inside the tensor.
+template <int KIND, int VH, bool WBF16, bool VEC>
+struct Bits {
+  // bf16 weights read 4 at a time (gS and g_x with 16-byte channel rows) stay
+  // packed two per word; other bf16 weights take one word each
+  static constexpr bool PACKED = WBF16 && VEC && (KIND == kGemmGs || KIND == kGemmGx);
+  static constexpr int N = PACKED ? VH / 2 : VH;
+  __device__ __forceinline__ static float get(const uint32_t (&v)[N], int t) {
+    if constexpr (!WBF16)
+      return __uint_as_float(v[t]);
+    else if constexpr (PACKED)
+      return __uint_as_float((t & 1) ? (v[t >> 1] & 0xffff0000u) : (v[t >> 1] << 16));
+    else
+      return __uint_as_float(v[t] << 16);
+  }
+};
+
 template <int KIND, int VH, bool WBF16, bool VEC>
 __device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, int n, int rs, int r_end, int pl,
-                                       float (&v)[VH]) {
+                                       uint32_t (&v)[Bits<KIND, VH, WBF16, VEC>::N]) {
   if constexpr (KIND == kGemmOut) {  // B(r = (k,q,ci), n = co) = W[k][p][ci][co]
     if constexpr (VEC) {  // the VH reductions share (k, q): C_in is a multiple of 16
       int ci;
       const int64_t kp = w_row(a, G, rs < r_end ? rs : 0, a.C_in, pl, ci);
       const int64_t base = (kp * a.C_in + ci) * a.C_out + n;
 #pragma unroll
-      for (int t = 0; t < VH; ++t) v[t] = load_w(a.W, base + (int64_t)t * a.C_out, WBF16);
+      for (int t = 0; t < VH; ++t) v[t] = raw_w<WBF16>(a.W, base + (int64_t)t * a.C_out);
     } else {
 #pragma unroll
       for (int t = 0; t < VH; ++t) {
         int ci;
         const int r = min(rs + t, G.Kr - 1);
         const int64_t kp = w_row(a, G, r, a.C_in, pl, ci);
-        v[t] = load_w(a.W, (kp * a.C_in + ci) * a.C_out + n, WBF16);
+        v[t] = raw_w<WBF16>(a.W, (kp * a.C_in + ci) * a.C_out + n);
       }
     }
-  } else if constexpr (KIND == kGemmGs) {  // B(r = co, n = (k,q,ci)) = W[k][p][ci][co]
-    int ci;
-    const int64_t kp = w_row(a, G, n, a.C_in, pl, ci);
-    const int64_t row = (kp * a.C_in + ci) * a.C_out;
-    if constexpr (VEC) {
-      const int64_t base = row + (rs < r_end ? rs : 0);
-#pragma unroll
-      for (int j = 0; j < VH / 4; ++j) {
-        const floatx4 x = load_w4<WBF16>(a.W, base + 4 * j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < VH; ++t) v[t] = load_w(a.W, row + min(rs + t, r_end - 1), WBF16);
-    }
-  } else if constexpr (KIND == kGemmGx) {  // B(r = (k,q,co), n = ci) = W[k][p][ci][co]
-    if constexpr (VEC) {  // the VH reductions share (k, q): C_out is a multiple of 16
+  } else if constexpr (KIND == kGemmGs || KIND == kGemmGx) {
+    // gS: B(r = co, n = (k,q,ci)) = W[k][p][ci][co];  g_x: B(r = (k,q,co), n = ci) = W[k][p][ci][co]
+    int64_t base;
+    if constexpr (KIND == kGemmGs) {
+      int ci;
+      const int64_t kp = w_row(a, G, n, a.C_in, pl, ci);
+      base = (kp * a.C_in + ci) * a.C_out + (VEC ? (rs < r_end ? rs : 0) : 0);
+    } else if constexpr (VEC) {  // the VH reductions share (k, q): C_out is a multiple of 16
       int co;
       const int64_t kp = w_row(a, G, rs < r_end ? rs : 0, a.C_out, pl, co);
-      const int64_t base = (kp * a.C_in + n) * a.C_out + co;
+      base = (kp * a.C_in + n) * a.C_out + co;
+    } else {
+      base = 0;
+    }
+    if constexpr (VEC) {
 #pragma unroll
       for (int j = 0; j < VH / 4; ++j) {
-        const floatx4 x = load_w4<WBF16>(a.W, base + 4 * j);
+        if constexpr (WBF16) {
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.W) + base + 4 * j);
+          v[2 * j] = u.x;
+          v[2 * j + 1] = u.y;
+        } else {
+          const floatx4 x = *reinterpret_cast<const floatx4*>(static_cast<const float*>(a.W) + base + 4 * j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * j + e] = x[e];
+          for (int e = 0; e < 4; ++e) v[4 * j + e] = __float_as_uint(x[e]);
+        }
       }
+    } else if constexpr (KIND == kGemmGs) {
+#pragma unroll
+      for (int t = 0; t < VH; ++t) v[t] = raw_w<WBF16>(a.W, base + min(rs + t, r_end - 1));
     } else {
 #pragma unroll
       for (int t = 0; t < VH; ++t) {
         int co;
         const int r = min(rs + t, G.Kr - 1);
         const int64_t kp = w_row(a, G, r, a.C_out, pl, co);
-        v[t] = load_w(a.W, (kp * a.C_in + n) * a.C_out + co, WBF16);
+        v[t] = raw_w<WBF16>(a.W, (kp * a.C_in + n) * a.C_out + co);
       }
     }
   } else {  // Gw: B(r = (v, m3), n = co) = g_out[v][row_off + m3][co]; rows stepped without division
@@ -171,7 +187,7 @@ __device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, in
     const float* base = a.feat + (int64_t)G.row_off * a.C_out + n;
 #pragma unroll
     for (int t = 0; t < VH; ++t) {
-      v[t] = base[((int64_t)node * a.D_feat + mm) * a.C_out];
+      v[t] = __float_as_uint(base[((int64_t)node * a.D_feat + mm) * a.C_out]);
       // next row; past the end of the reduction the last row is read again
       const bool adv = rs + t + 1 < G.Kr;
       const bool wrap = mm + 1 == G.n;
@@ -199,8 +215,9 @@ __device__ __forceinline__ void store_c(const GemmArgs& a, const GemmGroup& G, i
 
 template <int KIND, int NT, int VH, bool WBF16, bool VEC>
 struct Chunk {
+  using B = Bits<KIND, VH, WBF16, VEC>;
   float a[VH];
-  float b[NT][VH];
+  uint32_t b[NT][B::N];  // raw; widened in mul
   int valid;  // reductions of this lane half inside the range (<= 0: none)
   __device__ __forceinline__ void load(const GemmArgs& ar, const GemmGroup& G, int m, const int (&n)[NT], int rs,
                                        int r_end, int pl) {
@@ -214,7 +231,7 @@ struct Chunk {
     for (int t = 0; t < VH; ++t) {
       const float av = t < valid ? a[t] : 0.f;  // past the end of the reduction
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[j][t], acc[j], 0, 0, 0);
+      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, B::get(b[j], t), acc[j], 0, 0, 0);
     }
   }
 };
@@ -282,17 +299,34 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
     // has no valid reductions and reads clamped addresses) and only the
     // multiplies are guarded: guarded loads make the compiler copy the
     // accumulators around the branches.
+    // The main loop body is straight-line, so every entry to its header has
+    // the same loads in flight (chunks c and c+1, in that order) and the
+    // compiler's wait before chunk c's multiplies leaves the younger ones
+    // outstanding; a guarded multiply inside the loop makes it drain all
+    // loads instead.  The 0 to 2 chunks left over are multiplied after it.
+    // Scheduling barriers keep each load group ahead of the multiplies that
+    // precede its use (the scheduler would otherwise sink the loads next to
+    // their consumers, one chunk of prefetch at best).
     Chunk<KIND, NT, VH, WBF16, VEC> c0, c1, c2;
     c0.load(a, G, m, n, at(0), re, pl);
     c1.load(a, G, m, n, at(1), re, pl);
-    for (int c = 0; c < nch; c += 3) {
+    int c = 0;
+    for (; c + 3 <= nch; c += 3) {
       c2.load(a, G, m, n, at(c + 2), re, pl);
+      __builtin_amdgcn_sched_barrier(0);
       c0.mul(acc);
+      __builtin_amdgcn_sched_barrier(0);
       c0.load(a, G, m, n, at(c + 3), re, pl);
-      if (c + 1 < nch) c1.mul(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      c1.mul(acc);
+      __builtin_amdgcn_sched_barrier(0);
       c1.load(a, G, m, n, at(c + 4), re, pl);
-      if (c + 2 < nch) c2.mul(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      c2.mul(acc);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (c < nch) c0.mul(acc);
+    if (c + 1 < nch) c1.mul(acc);
   }
 
   if (nw > 1) {  // fixed-order sum of the waves' partial tiles
