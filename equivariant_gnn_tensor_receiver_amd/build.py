@@ -84,7 +84,10 @@ def compile_one(unit, incremental=False):
 def build(jobs: int = 8, verbose: bool = False, incremental: bool = False) -> str:
     """Compile every unit (incremental=True skips objects newer than all sources) and link."""
     os.makedirs(BUILD, exist_ok=True)
-    if not (incremental and os.path.exists(os.path.join(GEN, "cg_tables.inc"))):
+    tables = os.path.join(GEN, "cg_tables.inc")
+    gen_inputs = [os.path.join(CSRC, f) for f in ("cg_codegen.cpp", "plan.cpp", "plan.h")]
+    if not (incremental and os.path.exists(tables)
+            and os.path.getmtime(tables) > max(os.path.getmtime(f) for f in gen_inputs)):
         generate()
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda u: compile_one(u, incremental), UNITS))

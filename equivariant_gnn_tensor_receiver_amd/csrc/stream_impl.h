@@ -309,55 +309,38 @@ struct StreamCtx {
     float y[N2];
 #pragma unroll
     for (int i = 0; i < N2; ++i) y[i] = L.Y[j][P::l2][i];
-    float gU[4][NO], gD[4][NO];
+    // One output component o at a time, so that only its two 4-vectors are
+    // live; the quad's channels are summed before the coupling table is applied:
+    //   alpha += <U, gD>_o = sum c y[m2] p[m1],  p[m1] = sum_i x_i[m1] gD_i[o]
+    //   gy    += CG^T(x, gU)_o = sum c q[m1],     q[m1] = sum_i x_i[m1] gU_i[o]
+    // (entries of p and q that the table does not use are never formed).
 #pragma unroll
     for (int o = 0; o < NO; ++o) {
       floatx4 g = {0.f, 0.f, 0.f, 0.f}, gd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        g = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], r[k], g, 0, 0, 0);
-        gd = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], rd[k], gd, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], r[k], g, 0, 0, 0);    // sum_k R_k gS[k]
+        gd = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], rd[k], gd, 0, 0, 0);  // sum_k R'_k gS[k]
       }
+      float p[NIN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gU[i][o] = g[i];   // sum_k R_k gS[k]
-        gD[i][o] = gd[i];  // sum_k R'_k gS[k]
+      for (int m1 = 0; m1 < NIN; ++m1) {
+        float t = xv[m1][0] * gd[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], gd[i], t);
+        p[m1] = t;
       }
-    }
-    // The quad's channels are summed before the coupling table is applied:
-    //   alpha += <U, gD> = sum c y[m2] p[m1][m3],  p[m1][m3] = sum_i x_i[m1] gD_i[m3]
-    //   gy    += CG^T(x, gU)   via q[m1][m3] = sum_i x_i[m1] gU_i[m3] when that is cheaper
-    float pq[NIN * NO];
+      alpha = Tab::ydot_col(o, y, p, alpha);
+      if constexpr (P::l2 > 0) {  // Y_00 is constant
+        float q[NIN];
 #pragma unroll
-    for (int m1 = 0; m1 < NIN; ++m1)
+        for (int m1 = 0; m1 < NIN; ++m1) {
+          float t = xv[m1][0] * g[0];
 #pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        float t = xv[m1][0] * gD[0][o];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], gD[i][o], t);
-        pq[m1 * NO + o] = t;
-      }
-    alpha = Tab::ydot(y, pq, alpha);
-    if constexpr (P::l2 > 0) {  // Y_00 is constant
-      if constexpr (4 * NIN * NO + Tab::kNnz < 4 * Tab::kYbarOps) {
-#pragma unroll
-        for (int m1 = 0; m1 < NIN; ++m1)
-#pragma unroll
-          for (int o = 0; o < NO; ++o) {
-            float t = xv[m1][0] * gU[0][o];
-#pragma unroll
-            for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], gU[i][o], t);
-            pq[m1 * NO + o] = t;
-          }
-        Tab::qbar(pq, gy + P::l2 * P::l2);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float xi[NIN];
-#pragma unroll
-          for (int m1 = 0; m1 < NIN; ++m1) xi[m1] = xv[m1][i];
-          Tab::ybar(xi, gU[i], gy + P::l2 * P::l2);
+          for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], g[i], t);
+          q[m1] = t;
         }
+        Tab::qbar_col(o, q, gy + P::l2 * P::l2);
       }
     }
     if constexpr (sizeof...(Rest) > 0) pos_edge<OFF + NO, TOT, NIN, Rest...>(xv, j, r, rd, gs, alpha, gy);
@@ -483,13 +466,19 @@ struct StreamCtx {
         }
         edge<0, TOT, NIN, Ps...>(av, jj, r, rd, acc);
       };
+      // scheduling barriers keep each gather one step ahead of its use (the
+      // scheduler would otherwise move the loads next to their consumers)
       typename Raw::type bA[NIN], bB[NIN];
       gather(0, bA);
       for (int t = 0; t < nslots; t += 2) {  // an odd last slot is masked
         gather(t + 1, bB);
+        __builtin_amdgcn_sched_barrier(0);
         step(t, bA);
+        __builtin_amdgcn_sched_barrier(0);
         gather(t + 2, bA);
+        __builtin_amdgcn_sched_barrier(0);
         step(t + 1, bB);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     float v[K * TOT];
@@ -589,9 +578,13 @@ struct StreamCtx {
       gather(0, bA);
       for (int t = 0; t < nsteps; t += 2) {  // an odd last step is masked
         gather(t + 1, bB);
+        __builtin_amdgcn_sched_barrier(0);
         step(t, bA);
+        __builtin_amdgcn_sched_barrier(0);
         gather(t + 2, bA);
+        __builtin_amdgcn_sched_barrier(0);
         step(t + 1, bB);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     vs0 = channel_sum(vs0, 6);
@@ -615,7 +608,10 @@ struct StreamCtx {
 // the first argument, at offset 0).  Naming the by-value parameter instead
 // would let the compiler copy the whole 2.7 KB block to scratch memory when
 // the inlined code reads it in many places.
-template <int LMAX, int K, int MODE, typename FT>
+// BUNDLED selects the natural path bundles or single-path units; the two are
+// separate kernels so that each gets the register allocation of its own code
+// (the single-path dispatch covers every path up to LMAX).
+template <int LMAX, int K, int MODE, typename FT, bool BUNDLED>
 __global__ __launch_bounds__(64) void stream_kernel(const StreamArgs /*args*/, int64_t items) {
   const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ EdgeLds<K, LMAX, MODE> L;
@@ -626,7 +622,7 @@ __global__ __launch_bounds__(64) void stream_kernel(const StreamArgs /*args*/, i
   const int tile = (int)(t % a.ntiles);
   const int node = (int)(t / a.ntiles);
   StreamCtx<MODE, FT, LMAX, K> ctx{node, tile, unit, L};
-  if (a.bundled) {
+  if constexpr (BUNDLED) {
     Bundles<LMAX, K, ModeTraits<MODE>::bwdpos ? 2 : (ModeTraits<MODE>::recv ? 0 : 1)>::run(unit, ctx, a);
     return;
   }
@@ -648,10 +644,13 @@ template <int MODE, typename FT>
 hipError_t launch_stream_mode(int lmax, int K, const StreamArgs& a, int64_t items, hipStream_t s) {
   const int64_t grid = (items + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
-#define TPCONV_LAUNCH(LM, KK)                                                                      \
-  if (lmax == LM && K == KK) {                                                                     \
-    hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
-    return hipGetLastError();                                                                      \
+#define TPCONV_LAUNCH(LM, KK)                                                                           \
+  if (lmax == LM && K == KK) {                                                                          \
+    if (a.bundled)                                                                                      \
+      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
+    else                                                                                                \
+      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, false>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
+    return hipGetLastError();                                                                           \
   }
   TPCONV_LAUNCH(0, 8) TPCONV_LAUNCH(0, 16)
   TPCONV_LAUNCH(1, 8) TPCONV_LAUNCH(1, 16)
