@@ -470,7 +470,8 @@ struct StreamCtx {
       // scheduler would otherwise move the loads next to their consumers)
       typename Raw::type bA[NIN], bB[NIN];
       gather(0, bA);
-      for (int t = 0; t < nslots; t += 2) {  // an odd last slot is masked
+      int t = 0;
+      for (; t + 1 < nslots; t += 2) {
         gather(t + 1, bB);
         __builtin_amdgcn_sched_barrier(0);
         step(t, bA);
@@ -480,6 +481,7 @@ struct StreamCtx {
         step(t + 1, bB);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (t < nslots) step(t, bA);  // an odd last slot (its rows are in bA)
     }
     float v[K * TOT];
 #pragma unroll
@@ -576,7 +578,8 @@ struct StreamCtx {
       };
       Quads<FT, NIN> bA, bB;
       gather(0, bA);
-      for (int t = 0; t < nsteps; t += 2) {  // an odd last step is masked
+      int t = 0;
+      for (; t + 1 < nsteps; t += 2) {
         gather(t + 1, bB);
         __builtin_amdgcn_sched_barrier(0);
         step(t, bA);
@@ -586,6 +589,7 @@ struct StreamCtx {
         step(t + 1, bB);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (t < nsteps) step(t, bA);  // an odd last step (its rows are in bA)
     }
     vs0 = channel_sum(vs0, 6);
     vs1 = channel_sum(vs1, 6);
