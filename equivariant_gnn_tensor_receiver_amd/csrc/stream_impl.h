@@ -238,6 +238,10 @@ struct StreamCtx {
   static constexpr bool TAN = ModeTraits<MODE>::tangent;
 
   static constexpr int NSH = (LMAX + 1) * (LMAX + 1);
+  // Whether the LDS geometry of the next step is held in registers: not where
+  // those registers would take the kernel below two waves per SIMD.
+  static constexpr bool kAccGeoAhead = !(LMAX >= 3 && K == 16 && TAN);
+  static constexpr bool kPosGeoAhead = LMAX <= 2;
 
   // vec += J^T gy over the harmonic degrees L2.. that a member path uses.
   template <int L2, class... Ps>
@@ -255,17 +259,28 @@ struct StreamCtx {
     }
   }
 
+  // Geometry of one edge slot as the accumulating modes use it, read from LDS
+  // one step ahead of its use: the matrix-core operand R[4 kq + lane % 4] (and
+  // R_dot), the harmonics (entries that no member path reads are never
+  // loaded) and the mask of a slot past the last edge.
+  struct AccGeo {
+    float r[K / 4], rd[K / 4], mask;
+    float y[LMAX + 1][2 * LMAX + 1];
+    float yd[TAN ? LMAX + 1 : 1][2 * LMAX + 1];
+  };
+
   // One edge for the member paths OFF.. of the unit (compile-time recursion);
   // accumulating modes.
   template <int OFF, int TOT, int NIN, class P, class... Rest>
-  __device__ __forceinline__ void edge(const float (&av)[NIN], int j, const float (&r)[K / 4],
-                                       const float (&rd)[K / 4], floatx4 (&acc)[K / 4][TOT]) {
+  __device__ __forceinline__ void edge(const float (&av)[NIN], const AccGeo& g, floatx4 (&acc)[K / 4][TOT]) {
     constexpr int N2 = 2 * P::l2 + 1;
     constexpr int NO = out_dim<MODE, P>();
     using Tab = CG<P::l1, P::l2, P::l3>;
+    const float(&r)[K / 4] = g.r;
+    const float(&rd)[K / 4] = g.rd;
     float y[N2];
 #pragma unroll
-    for (int i = 0; i < N2; ++i) y[i] = L.Y[j][P::l2][i];
+    for (int i = 0; i < N2; ++i) y[i] = g.y[P::l2][i];
     float u[NO];
     if constexpr (RECV) Tab::fwd(av, y, u); else Tab::snd(av, y, u);
     if constexpr (!TAN) {
@@ -278,7 +293,7 @@ struct StreamCtx {
     } else {
       float yd[N2], ud[NO];
 #pragma unroll
-      for (int i = 0; i < N2; ++i) yd[i] = L.Yd[j][P::l2][i];
+      for (int i = 0; i < N2; ++i) yd[i] = g.yd[TAN ? P::l2 : 0][i];
       if constexpr (RECV) Tab::fwd(av, yd, ud); else Tab::snd(av, yd, ud);
 #pragma unroll
       for (int kq = 0; kq < K / 4; ++kq)
@@ -288,7 +303,7 @@ struct StreamCtx {
           acc[kq][OFF + o] = __builtin_amdgcn_mfma_f32_4x4x1f32(rd[kq], u[o], acc[kq][OFF + o], 0, 0, 0);
         }
     }
-    if constexpr (sizeof...(Rest) > 0) edge<OFF + NO, TOT, NIN, Rest...>(av, j, r, rd, acc);
+    if constexpr (sizeof...(Rest) > 0) edge<OFF + NO, TOT, NIN, Rest...>(av, g, acc);
   }
 
   // Position gradient, one edge per lane and four channels per lane (compile-
@@ -299,16 +314,27 @@ struct StreamCtx {
   // K 4x4x1 outer products then leaves in register i of lane 4b + j
   //   sum_k gS[k][o](channel c0 + i) * R_k(edge of lane 4b + j),
   // i.e. sum_k R_k gS[k] for the lane's own edge and its quad's channels.
+  // Geometry of the lane's edge for one position-gradient step, read from
+  // LDS one step ahead of its use (harmonic entries that no member path reads
+  // are never loaded).
+  struct PosGeo {
+    float r[K], rd[K];
+    float y[LMAX + 1][2 * LMAX + 1];
+    int jj, sender;
+    float mask;
+  };
+
   template <int OFF, int TOT, int NIN, class P, class... Rest>
-  __device__ __forceinline__ void pos_edge(const float (&xv)[NIN][4], int j, const float (&r)[K],
-                                           const float (&rd)[K], const float (&gs)[K][TOT], float& alpha,
-                                           float (&gy)[NSH]) {
+  __device__ __forceinline__ void pos_edge(const float (&xv)[NIN][4], const PosGeo& g, const float (&gs)[K][TOT],
+                                           float& alpha, float (&gy)[NSH]) {
     constexpr int N2 = 2 * P::l2 + 1;
     constexpr int NO = 2 * P::l3 + 1;
     using Tab = CG<P::l1, P::l2, P::l3>;
+    const float(&r)[K] = g.r;
+    const float(&rd)[K] = g.rd;
     float y[N2];
 #pragma unroll
-    for (int i = 0; i < N2; ++i) y[i] = L.Y[j][P::l2][i];
+    for (int i = 0; i < N2; ++i) y[i] = g.y[P::l2][i];
     // One output component o at a time, so that only its two 4-vectors are
     // live; the quad's channels are summed before the coupling table is applied:
     //   alpha += <U, gD>_o = sum c y[m2] p[m1],  p[m1] = sum_i x_i[m1] gD_i[o]
@@ -343,7 +369,7 @@ struct StreamCtx {
         Tab::qbar_col(o, q, gy + P::l2 * P::l2);
       }
     }
-    if constexpr (sizeof...(Rest) > 0) pos_edge<OFF + NO, TOT, NIN, Rest...>(xv, j, r, rd, gs, alpha, gy);
+    if constexpr (sizeof...(Rest) > 0) pos_edge<OFF + NO, TOT, NIN, Rest...>(xv, g, gs, alpha, gy);
   }
 
   // Load the receiver-state cotangent of the member paths (position gradient).
@@ -435,53 +461,79 @@ struct StreamCtx {
       __syncthreads();
       if (lane < nb) edge_prep<LMAX, K, MODE>(a, node, psx, psy, psz, b0 + lane, lane, L);
       __syncthreads();
-      // Branch-free edge loop: the gathers for the next edge slot are issued
-      // before the current slot is used (edge indices clamped into the batch,
-      // so every load is unconditional), and a slot past the last edge is
-      // masked by zeroing R.  The loop is unrolled by two over alternating
+      // Branch-free edge loop: the gathers and the LDS geometry for the next
+      // edge slot are issued before the current slot is used, and the
+      // neighbour index one slot further ahead (edge indices clamped into the
+      // batch, so every load is unconditional); a slot past the last edge is
+      // masked by zeroing x.  The loop is unrolled by two over alternating
       // buffers so that no register copy waits on a load in flight; divergent
       // branches or such copies would make the compiler wait for every
-      // outstanding gather.
+      // outstanding load.
       const int last = nb - 1;
       const int nslots = (nb + ES - 1) / ES;
       using Raw = FeatRaw<FT>;
-      auto gather = [&](int slot, typename Raw::type (&v)[NIN]) {
-        const int64_t f = (int64_t)L.nbr[min(slot * ES + es, last)] * a.feat_rows * C + fcol;
+      auto nbr_of = [&](int slot) { return L.nbr[min(slot * ES + es, last)]; };
+      auto gather = [&](int nbr, typename Raw::type (&v)[NIN]) {
+        const int64_t f = (int64_t)nbr * a.feat_rows * C + fcol;
 #pragma unroll
         for (int i = 0; i < NIN; ++i) v[i] = Raw::load(feat, f + (int64_t)i * C);
       };
-      auto step = [&](int slot, const typename Raw::type (&raw)[NIN]) {
-        float av[NIN];
-#pragma unroll
-        for (int i = 0; i < NIN; ++i) av[i] = Raw::f32(raw[i]);
+      auto geo = [&](int slot, AccGeo& g) {
         const int j = slot * ES + es;
         const int jj = min(j, last);
-        const float mask = j < nb ? 1.f : 0.f;  // multiply, not select: no branch around the reads
-        // the matrix-core operand of this lane: R[4 kq + lane % 4]
-        float r[K / 4], rd[K / 4];
+        g.mask = j < nb ? 1.f : 0.f;  // applied to x at use (multiply, not select: no branch around the reads)
 #pragma unroll
         for (int kq = 0; kq < K / 4; ++kq) {
-          r[kq] = L.R[jj][4 * kq + q4] * mask;
-          rd[kq] = TAN ? L.Rd[jj][4 * kq + q4] * mask : 0.f;
+          g.r[kq] = L.R[jj][4 * kq + q4];
+          g.rd[kq] = TAN ? L.Rd[jj][4 * kq + q4] : 0.f;
         }
-        edge<0, TOT, NIN, Ps...>(av, jj, r, rd, acc);
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int i = 0; i < 2 * LMAX + 1; ++i) {
+            g.y[l][i] = i <= 2 * l ? L.Y[jj][l][i] : 0.f;
+            if constexpr (TAN) g.yd[l][i] = i <= 2 * l ? L.Yd[jj][l][i] : 0.f;
+          }
       };
-      // scheduling barriers keep each gather one step ahead of its use (the
-      // scheduler would otherwise move the loads next to their consumers)
+      auto step = [&](const typename Raw::type (&raw)[NIN], const AccGeo& g) {
+        float av[NIN];
+#pragma unroll
+        for (int i = 0; i < NIN; ++i) av[i] = Raw::f32(raw[i]) * g.mask;  // every term is linear in x
+        edge<0, TOT, NIN, Ps...>(av, g, acc);
+      };
+      // scheduling barriers keep each load ahead of its use (the scheduler
+      // would otherwise move the loads next to their consumers); where the
+      // geometry registers would cost a wave of occupancy it is read at use
+      auto run_step = [&](int slot, const typename Raw::type (&raw)[NIN], const AccGeo& g) {
+        if constexpr (kAccGeoAhead) {
+          step(raw, g);
+        } else {
+          AccGeo gl;
+          geo(slot, gl);
+          step(raw, gl);
+        }
+      };
       typename Raw::type bA[NIN], bB[NIN];
-      gather(0, bA);
+      AccGeo gA, gB;
+      gather(nbr_of(0), bA);
+      if constexpr (kAccGeoAhead) geo(0, gA);
+      int nb1 = nbr_of(1), nb2;
       int t = 0;
       for (; t + 1 < nslots; t += 2) {
-        gather(t + 1, bB);
+        gather(nb1, bB);
+        nb2 = nbr_of(t + 2);
+        if constexpr (kAccGeoAhead) geo(t + 1, gB);
         __builtin_amdgcn_sched_barrier(0);
-        step(t, bA);
+        run_step(t, bA, gA);
         __builtin_amdgcn_sched_barrier(0);
-        gather(t + 2, bA);
+        gather(nb2, bA);
+        nb1 = nbr_of(t + 3);
+        if constexpr (kAccGeoAhead) geo(t + 2, gA);
         __builtin_amdgcn_sched_barrier(0);
-        step(t + 1, bB);
+        run_step(t + 1, bB, gB);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (t < nslots) step(t, bA);  // an odd last slot (its rows are in bA)
+      if (t < nslots) run_step(t, bA, gA);  // an odd last slot (its rows are in bA)
     }
     float v[K * TOT];
 #pragma unroll
@@ -534,40 +586,49 @@ struct StreamCtx {
       __syncthreads();
       const int last = nb - 1;
       const int nsteps = (nb + per_step - 1) / per_step;
-      // gathered block of the lane's edge for the quad's channels (clamped
-      // edge index: unconditional loads, as in the accumulating modes)
-      // (channels past C, only when C is not a multiple of 4, read as zero)
-      auto gather = [&](int t, Quads<FT, NIN>& v) {
-        const int jl = min(t * per_step + 4 * es + j4, last);
-        v.load(feat, (int64_t)L.nbr[jl] * a.feat_rows * C + frow + min(c0, C - 1), C, min(c0, C - 1), vec4);
+      // The gathered block of the lane's edge for the quad's channels and the
+      // edge's LDS geometry are loaded one step ahead of their use and the
+      // neighbour index one step further (clamped edge index: unconditional
+      // loads, as in the accumulating modes; channels past C, only when C is
+      // not a multiple of 4, read as zero).
+      auto nbr_of = [&](int t) { return L.nbr[min(t * per_step + 4 * es + j4, last)]; };
+      auto gather = [&](int nbr, Quads<FT, NIN>& v) {
+        v.load(feat, (int64_t)nbr * a.feat_rows * C + frow + min(c0, C - 1), C, min(c0, C - 1), vec4);
       };
-      auto step = [&](int t, const Quads<FT, NIN>& raw) {
-        float tmp[NIN][4];
-        const float(&xv)[NIN][4] = raw.get(tmp);
+      auto geo = [&](int t, int nbr, PosGeo& g) {
         const int jl = t * per_step + 4 * es + j4;
-        const int jj = min(jl, last);
-        float r[K], rd[K];
+        g.jj = min(jl, last);
+        g.sender = nbr;
+        g.mask = jl < nb ? 1.f : 0.f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-          r[k] = L.R[jj][k];
-          rd[k] = L.Rd[jj][k];
+          g.r[k] = L.R[g.jj][k];
+          g.rd[k] = L.Rd[g.jj][k];
         }
+#pragma unroll
+        for (int l = 0; l <= LMAX; ++l)
+#pragma unroll
+          for (int i = 0; i < 2 * LMAX + 1; ++i) g.y[l][i] = i <= 2 * l ? L.Y[g.jj][l][i] : 0.f;
+      };
+      auto step = [&](const Quads<FT, NIN>& raw, const PosGeo& g) {
+        float tmp[NIN][4];
+        const float(&xv)[NIN][4] = raw.get(tmp);
+        const int jj = g.jj;
         float alpha = 0.f;
         float gy[NSH];
 #pragma unroll
         for (int i = 0; i < NSH; ++i) gy[i] = 0.f;
-        pos_edge<0, TOT, NIN, Ps...>(xv, jj, r, rd, gs, alpha, gy);
+        pos_edge<0, TOT, NIN, Ps...>(xv, g, gs, alpha, gy);
         // this unit's share of g_r = alpha r_hat + J^T gy for the quad's channels
         float vec[3];
 #pragma unroll
         for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * L.rhat[jj][cc];
         apply_jacobian<1, Ps...>(gy, jj, vec);
-        const float mask = jl < nb ? 1.f : 0.f;
 #pragma unroll
-        for (int cc = 0; cc < 3; ++cc) vec[cc] *= mask;
+        for (int cc = 0; cc < 3; ++cc) vec[cc] *= g.mask;
         quad_sum3(vec, ctl);
-        if (jl < nb && quad == 0) {
-          const int64_t s3 = 3 * (int64_t)L.nbr[jj];
+        if (g.mask != 0.f && quad == 0) {
+          const int64_t s3 = 3 * (int64_t)g.sender;
           atomicAdd(&a.gpos[s3 + 0], vec[0]);
           atomicAdd(&a.gpos[s3 + 1], vec[1]);
           atomicAdd(&a.gpos[s3 + 2], vec[2]);
@@ -576,20 +637,41 @@ struct StreamCtx {
           vs2 -= vec[2];
         }
       };
+      // (where the geometry registers would cost a wave of occupancy it is
+      // read at use)
+      auto run_step = [&](int t, const Quads<FT, NIN>& raw, const PosGeo& g) {
+        if constexpr (kPosGeoAhead) {
+          step(raw, g);
+        } else {
+          PosGeo gl;
+          geo(t, nbr_of(t), gl);
+          step(raw, gl);
+        }
+      };
       Quads<FT, NIN> bA, bB;
-      gather(0, bA);
+      PosGeo gA, gB;
+      {
+        const int n0 = nbr_of(0);
+        gather(n0, bA);
+        if constexpr (kPosGeoAhead) geo(0, n0, gA);
+      }
+      int nb1 = nbr_of(1), nb2;
       int t = 0;
       for (; t + 1 < nsteps; t += 2) {
-        gather(t + 1, bB);
+        gather(nb1, bB);
+        nb2 = nbr_of(t + 2);
+        if constexpr (kPosGeoAhead) geo(t + 1, nb1, gB);
         __builtin_amdgcn_sched_barrier(0);
-        step(t, bA);
+        run_step(t, bA, gA);
         __builtin_amdgcn_sched_barrier(0);
-        gather(t + 2, bA);
+        gather(nb2, bA);
+        nb1 = nbr_of(t + 3);
+        if constexpr (kPosGeoAhead) geo(t + 2, nb2, gA);
         __builtin_amdgcn_sched_barrier(0);
-        step(t + 1, bB);
+        run_step(t + 1, bB, gB);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (t < nsteps) step(t, bA);  // an odd last step (its rows are in bA)
+      if (t < nsteps) run_step(t, bA, gA);  // an odd last step (its rows are in bA)
     }
     vs0 = channel_sum(vs0, 6);
     vs1 = channel_sum(vs1, 6);
@@ -612,11 +694,19 @@ struct StreamCtx {
 // the first argument, at offset 0).  Naming the by-value parameter instead
 // would let the compiler copy the whole 2.7 KB block to scratch memory when
 // the inlined code reads it in many places.
+// Waves per SIMD the register allocation must leave room for: the lmax <= 2,
+// K = 8 forward and sender streams fit three waves (168 registers) when asked
+// to, which hides more of the gather latency than the compiler's own choice.
+constexpr int stream_min_waves(int lmax, int K, int mode) {
+  return (lmax <= 2 && K == 8 && (mode == kFwd || mode == kSnd)) ? 3 : 1;
+}
+
 // BUNDLED selects the natural path bundles or single-path units; the two are
 // separate kernels so that each gets the register allocation of its own code
 // (the single-path dispatch covers every path up to LMAX).
 template <int LMAX, int K, int MODE, typename FT, bool BUNDLED>
-__global__ __launch_bounds__(64) void stream_kernel(const StreamArgs /*args*/, int64_t items) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(stream_min_waves(LMAX, K, MODE))))
+void stream_kernel(const StreamArgs /*args*/, int64_t items) {
   const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ EdgeLds<K, LMAX, MODE> L;
   const int64_t item = xcd_item(blockIdx.x, gridDim.x);
