@@ -20,7 +20,8 @@
 // along the reduction is then read as 16-byte vectors per lane; one that is
 // contiguous along its row or column index is read as 128-byte coalesced
 // rows.  The next chunk is loaded while the current one is multiplied.  Small
-// problems split the reduction over the 1, 2 or 4 waves of a block; the waves'
+// problems split the reduction over the 1, 2 or 4 waves of a block (interleaved
+// chunks, so that the waves read neighbouring segments of a row); the waves'
 // partial tiles are summed in a fixed order through LDS, so results do not
 // depend on timing.
 #include "device_common.h"
@@ -262,11 +263,10 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
     rb = min(G.Kr, (int)blockIdx.y * per);
     re = min(G.Kr, rb + per);
   }
-  {
-    const int per = ceil_div(ceil_div(re - rb, nw), KC) * KC;
-    rb = min(re, rb + w * per);
-    re = min(re, rb + per);
-  }
+  // The block's waves take interleaved chunks (wave w: chunks w, w + nw, ..),
+  // so that at any time they read neighbouring segments of the same rows
+  // rather than one row region each.
+  const int first = rb + w * KC, stride = nw * KC;
   const int m = min(m0 + i, G.M - 1);
   int n[NT];
 #pragma unroll
@@ -280,8 +280,8 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
 
   // the group's path list, one entry per lane, for the W row lookups
   const int pl = (KIND == kGemmGw || G.npg <= 0) ? 0 : a.path_list[G.plist + min(lane, G.npg - 1)];
-  const int nch = re > rb ? ceil_div(re - rb, KC) : 0;
-  auto at = [&](int c) { return rb + c * KC + VH * h; };
+  const int nch = re > first ? ceil_div(re - first, stride) : 0;
+  auto at = [&](int c) { return first + c * stride + VH * h; };
   if constexpr (KIND == kGemmGs) {
     // short reduction (C_out): one chunk ahead, loads guarded so that no
     // chunk past the end is fetched
