@@ -62,7 +62,7 @@ int gw_splits(const Plan& p, int64_t N) {
   for (const auto& g : p.out_groups) {
     if (g.paths.empty()) continue;
     const int64_t M = (int64_t)p.K * g.paths.size() * p.C_in;
-    tiles += gemm_wave_tiles((int)M, p.C_out, p.C_out);
+    tiles += gemm_wave_tiles(kGemmGw, (int)M, p.C_out, p.C_out);
     min_kr = std::min<int64_t>(min_kr, N * (2 * g.l + 1));
   }
   if (tiles == 0) return 1;

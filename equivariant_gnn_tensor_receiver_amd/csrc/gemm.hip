@@ -11,7 +11,7 @@
 //
 // These products are skinny (32..128 columns) and stream a node-sized
 // operand once, so the kernel is built for bytes in flight rather than for
-// LDS reuse.  Every wave owns a 32-row x (32*NT)-column tile and loads its
+// LDS reuse.  Every wave owns a (32*MT)-row x (32*NT)-column tile and loads its
 // operands straight into registers: for v_mfma_f32_32x32x2f32 lane (i, h)
 // (i = lane % 32, h = lane / 32) supplies A[i][kk = h] and B[kk = h][i], and
 // the reduction order inside a chunk of 2*VH indices is permuted so that lane
@@ -214,35 +214,50 @@ __device__ __forceinline__ void store_c(const GemmArgs& a, const GemmGroup& G, i
   }
 }
 
-template <int KIND, int NT, int VH, bool WBF16, bool VEC>
+template <int KIND, int MT, int NT, int VH, bool WBF16, bool VEC>
 struct Chunk {
   using B = Bits<KIND, VH, WBF16, VEC>;
-  float a[VH];
+  float a[MT][VH];
   uint32_t b[NT][B::N];  // raw; widened in mul
   int valid;  // reductions of this lane half inside the range (<= 0: none)
-  __device__ __forceinline__ void load(const GemmArgs& ar, const GemmGroup& G, int m, const int (&n)[NT], int rs,
-                                       int r_end, int pl) {
+  __device__ __forceinline__ void load(const GemmArgs& ar, const GemmGroup& G, const int (&m)[MT], const int (&n)[NT],
+                                       int rs, int r_end, int pl) {
     valid = r_end - rs;
-    load_a<KIND, VH, VEC>(ar, G, m, rs, r_end, a);
+#pragma unroll
+    for (int u = 0; u < MT; ++u) load_a<KIND, VH, VEC>(ar, G, m[u], rs, r_end, a[u]);
 #pragma unroll
     for (int j = 0; j < NT; ++j) load_b<KIND, VH, WBF16, VEC>(ar, G, n[j], rs, r_end, pl, b[j]);
   }
-  __device__ __forceinline__ void mul(floatx16 (&acc)[NT]) const {
+  __device__ __forceinline__ void mul(floatx16 (&acc)[MT][NT]) const {
 #pragma unroll
     for (int t = 0; t < VH; ++t) {
-      const float av = t < valid ? a[t] : 0.f;  // past the end of the reduction
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, B::get(b[j], t), acc[j], 0, 0, 0);
+      for (int j = 0; j < NT; ++j) {
+        const float bv = B::get(b[j], t);
+#pragma unroll
+        for (int u = 0; u < MT; ++u) {
+          const float av = t < valid ? a[u][t] : 0.f;  // past the end of the reduction
+          acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[u][j], 0, 0, 0);
+        }
+      }
     }
   }
 };
 
-template <int KIND, int NT, int VH, bool WBF16, bool VEC>
-__global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs /*args*/) {
+// Waves per SIMD the register allocation must leave room for (accumulators,
+// three chunk buffers and addressing fit; left to itself the compiler spreads
+// the accumulators over extra registers and halves the occupancy).
+constexpr int gemm_min_waves(int mt, int nt, int vh) {
+  return 16 * mt * nt + 3 * vh * (mt + nt) <= 112 ? 3 : 2;
+}
+
+template <int KIND, int MT, int NT, int VH, bool WBF16, bool VEC>
+__global__ __launch_bounds__(64 * kMaxWaveSplit) __attribute__((amdgpu_waves_per_eu(gemm_min_waves(MT, NT, VH))))
+void gemm_kernel(const GemmArgs /*args*/) {
   // Read the arguments in place: a by-value copy indexed by a runtime group
   // would be spilled to scratch.
   const GemmArgs& a = *(const GemmArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  extern __shared__ float red[];  // (waves - 1) x NT x 16 x 64 partial tiles
+  extern __shared__ float red[];  // (waves - 1) x MT x NT x 16 x 64 partial tiles
   const int b = blockIdx.x;
   int gi = 0;
   while (gi + 1 < a.ngroups && b >= a.g[gi + 1].tile_begin) ++gi;
@@ -250,7 +265,7 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
   const int tile = b - G.tile_begin;
   if (tile >= G.tiles) return;  // uniform over the block
   const int tm = tile / G.tiles_n, tn = tile - tm * G.tiles_n;
-  const int m0 = tm * 32, n0 = tn * 32 * NT;
+  const int m0 = tm * 32 * MT, n0 = tn * 32 * NT;
   // wave index and loop bounds in scalar registers: the chunk loop then needs
   // no exec masking and the accumulators stay in place across iterations
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
@@ -267,16 +282,20 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
   // so that at any time they read neighbouring segments of the same rows
   // rather than one row region each.
   const int first = rb + w * KC, stride = nw * KC;
-  const int m = min(m0 + i, G.M - 1);
+  int m[MT];
+#pragma unroll
+  for (int u = 0; u < MT; ++u) m[u] = min(m0 + 32 * u + i, G.M - 1);
   int n[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) n[j] = min(n0 + 32 * j + i, G.N - 1);
 
-  floatx16 acc[NT];
+  floatx16 acc[MT][NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+  for (int u = 0; u < MT; ++u)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][j][r] = 0.f;
 
   // the group's path list, one entry per lane, for the W row lookups
   const int pl = (KIND == kGemmGw || G.npg <= 0) ? 0 : a.path_list[G.plist + min(lane, G.npg - 1)];
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
   if constexpr (KIND == kGemmGs) {
     // short reduction (C_out): one chunk ahead, loads guarded so that no
     // chunk past the end is fetched
-    Chunk<KIND, NT, VH, WBF16, VEC> c0, c1;
+    Chunk<KIND, MT, NT, VH, WBF16, VEC> c0, c1;
     if (0 < nch) c0.load(a, G, m, n, at(0), re, pl);
     for (int c = 0; c < nch; c += 2) {
       if (c + 1 < nch) c1.load(a, G, m, n, at(c + 1), re, pl);
@@ -307,7 +326,7 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
     // Scheduling barriers keep each load group ahead of the multiplies that
     // precede its use (the scheduler would otherwise sink the loads next to
     // their consumers, one chunk of prefetch at best).
-    Chunk<KIND, NT, VH, WBF16, VEC> c0, c1, c2;
+    Chunk<KIND, MT, NT, VH, WBF16, VEC> c0, c1, c2;
     c0.load(a, G, m, n, at(0), re, pl);
     c1.load(a, G, m, n, at(1), re, pl);
     int c = 0;
@@ -332,27 +351,33 @@ __global__ __launch_bounds__(64 * kMaxWaveSplit) void gemm_kernel(const GemmArgs
   if (nw > 1) {  // fixed-order sum of the waves' partial tiles
     if (w > 0) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int u = 0; u < MT; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[(((w - 1) * NT + j) * 16 + r) * 64 + lane] = acc[j][r];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((((w - 1) * MT + u) * NT + j) * 16 + r) * 64 + lane] = acc[u][j][r];
     }
     __syncthreads();
     if (w > 0) return;
     for (int ww = 1; ww < nw; ++ww)
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+      for (int u = 0; u < MT; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j][r] += red[(((ww - 1) * NT + j) * 16 + r) * 64 + lane];
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[u][j][r] += red[((((ww - 1) * MT + u) * NT + j) * 16 + r) * 64 + lane];
   }
   // D layout of 32x32x2: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
-  for (int j = 0; j < NT; ++j)
+  for (int u = 0; u < MT; ++u)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int gm = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      const int gn = n0 + 32 * j + i;
-      if (gm < G.M && gn < G.N) store_c<KIND>(a, G, gm, gn, acc[j][r]);
-    }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = m0 + 32 * u + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int gn = n0 + 32 * j + i;
+        if (gm < G.M && gn < G.N) store_c<KIND>(a, G, gm, gn, acc[u][j][r]);
+      }
 }
 
 __global__ void gw_reduce_kernel(const ReduceArgs a, int64_t total) {
@@ -381,32 +406,54 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
   if (i < n) p[i] = v;
 }
 
-int nt_for(int max_cols) { return max_cols > 64 ? 4 : (max_cols > 32 ? 2 : 1); }
+// Tile of one wave: MT 32-row tiles x NT 32-column tiles.  A value loaded
+// for the B operand then serves MT matrix-core products and a row value NT;
+// since these products have few columns, the B operand (read from L2 by every
+// row tile) costs more than the node-sized A stream, so waves take two row
+// tiles when that still leaves enough waves to fill the chip (measured: a
+// gain for gW and for 64 or more columns, a loss for the 32-column out and
+// g_x products).  gS keeps one 32 x 32 tile (short reduction, store-bound).
+struct Shape {
+  int mt, nt, vh;
+};
+Shape gemm_shape(int kind, int max_cols, bool two_rows) {
+  if (kind == kGemmGs) return {1, 1, 16};
+  if (two_rows) return max_cols <= 32 ? Shape{2, 1, 8} : Shape{2, 2, 8};
+  return max_cols <= 32 ? Shape{1, 1, 16} : (max_cols <= 64 ? Shape{1, 2, 16} : Shape{1, 4, 8});
+}
+constexpr int64_t kFillWaves = 4096;
 
-template <int KIND, int NT, bool WBF16, bool VEC>
+template <int KIND, int MT, int NT, int VH, bool WBF16, bool VEC>
 hipError_t launch_inst(const GemmArgs& a, dim3 grid, int waves, hipStream_t s) {
-  constexpr int VH = NT == 4 ? 8 : 16;
-  const size_t lds = (size_t)(waves - 1) * NT * 16 * 64 * sizeof(float);
-  hipLaunchKernelGGL((gemm_kernel<KIND, NT, VH, WBF16, VEC>), grid, dim3(64 * waves), lds, s, a);
+  const size_t lds = (size_t)(waves - 1) * MT * NT * 16 * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemm_kernel<KIND, MT, NT, VH, WBF16, VEC>), grid, dim3(64 * waves), lds, s, a);
   return hipGetLastError();
 }
 
+template <int KIND, int MT, int NT, int VH, bool WBF16>
+hipError_t launch_vec(const GemmArgs& a, dim3 grid, int waves, hipStream_t s) {
+  return a.vec != 0 ? launch_inst<KIND, MT, NT, VH, WBF16, true>(a, grid, waves, s)
+                    : launch_inst<KIND, MT, NT, VH, WBF16, false>(a, grid, waves, s);
+}
+
 template <int KIND, bool WBF16>
-hipError_t launch_kind(const GemmArgs& a, int nt, dim3 grid, int waves, hipStream_t s) {
-  const bool vec = a.vec != 0;
-  switch (nt) {
-    case 4: return vec ? launch_inst<KIND, 4, WBF16, true>(a, grid, waves, s) : launch_inst<KIND, 4, WBF16, false>(a, grid, waves, s);
-    case 2: return vec ? launch_inst<KIND, 2, WBF16, true>(a, grid, waves, s) : launch_inst<KIND, 2, WBF16, false>(a, grid, waves, s);
-    default: return vec ? launch_inst<KIND, 1, WBF16, true>(a, grid, waves, s) : launch_inst<KIND, 1, WBF16, false>(a, grid, waves, s);
+hipError_t launch_kind(const GemmArgs& a, Shape sh, dim3 grid, int waves, hipStream_t s) {
+  if (sh.mt == 1 && sh.nt == 1 && sh.vh == 16) return launch_vec<KIND, 1, 1, 16, WBF16>(a, grid, waves, s);
+  if (sh.mt == 2 && sh.nt == 1 && sh.vh == 8) return launch_vec<KIND, 2, 1, 8, WBF16>(a, grid, waves, s);
+  if (sh.mt == 2 && sh.nt == 2 && sh.vh == 8) return launch_vec<KIND, 2, 2, 8, WBF16>(a, grid, waves, s);
+  if (KIND != kGemmGs) {
+    if (sh.mt == 1 && sh.nt == 2 && sh.vh == 16) return launch_vec<KIND, 1, 2, 16, WBF16>(a, grid, waves, s);
+    if (sh.mt == 1 && sh.nt == 4 && sh.vh == 8) return launch_vec<KIND, 1, 4, 8, WBF16>(a, grid, waves, s);
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int64_t gemm_wave_tiles(int M, int N, int max_cols) {
+int64_t gemm_wave_tiles(int kind, int M, int N, int max_cols) {
   if (M <= 0 || N <= 0) return 0;
-  const int cols = 32 * nt_for(max_cols);
-  return (int64_t)ceil_div(M, 32) * ceil_div(N, cols);
+  const Shape sh = gemm_shape(kind, max_cols, true);
+  return (int64_t)ceil_div(M, 32 * sh.mt) * ceil_div(N, 32 * sh.nt);
 }
 
 hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
@@ -415,22 +462,30 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   for (int g = 0; g < a.ngroups; ++g) max_cols = a.g[g].N > max_cols ? a.g[g].N : max_cols;
   // gS has a short reduction (C_out) and a wide output: one 32-column tile per
   // wave keeps registers low and many waves resident for the store stream.
-  const int nt = kind == kGemmGs ? 1 : nt_for(max_cols);
+  const int splits = kind == kGemmGw ? a.splits : 1;
+  Shape sh = gemm_shape(kind, max_cols, true);
+  {
+    int64_t t2 = 0;
+    for (int g = 0; g < a.ngroups; ++g)
+      if (a.g[g].M > 0 && a.g[g].N > 0)
+        t2 += (int64_t)ceil_div(a.g[g].M, 32 * sh.mt) * ceil_div(a.g[g].N, 32 * sh.nt);
+    if (!(kind == kGemmGw || max_cols > 32) || t2 * splits * kMaxWaveSplit < kFillWaves)
+      sh = gemm_shape(kind, max_cols, false);
+  }
   int64_t total = 0;
   for (int g = 0; g < a.ngroups; ++g) {
     GemmGroup& G = a.g[g];
-    G.tiles_n = G.N > 0 ? ceil_div(G.N, 32 * nt) : 0;
-    G.tiles = (G.M > 0 && G.N > 0) ? ceil_div(G.M, 32) * G.tiles_n : 0;
+    G.tiles_n = G.N > 0 ? ceil_div(G.N, 32 * sh.nt) : 0;
+    G.tiles = (G.M > 0 && G.N > 0) ? ceil_div(G.M, 32 * sh.mt) * G.tiles_n : 0;
     G.tile_begin = (int32_t)total;
     total += G.tiles;
     if (G.tiles > 0 && G.Kr < min_kr) min_kr = G.Kr;
   }
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) return hipErrorInvalidValue;
-  const int splits = kind == kGemmGw ? a.splits : 1;
   // Split the reduction over the waves of a block while the launch is small
   // and every wave keeps at least four chunks of the reduction.
-  const int kc = nt == 4 ? 16 : 32;
+  const int kc = 2 * sh.vh;
   int waves = 1;
   while (waves < kMaxWaveSplit && total * splits * waves < kTargetWaves &&
          (int64_t)min_kr >= (int64_t)splits * waves * 2 * 4 * kc)
@@ -439,10 +494,10 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   const bool wb = a.w_bf16 != 0;
   TimingScope ts(kcGemmOut + kind, s);
   switch (kind) {
-    case kGemmOut: return wb ? launch_kind<kGemmOut, true>(a, nt, grid, waves, s) : launch_kind<kGemmOut, false>(a, nt, grid, waves, s);
-    case kGemmGs: return wb ? launch_kind<kGemmGs, true>(a, nt, grid, waves, s) : launch_kind<kGemmGs, false>(a, nt, grid, waves, s);
-    case kGemmGx: return wb ? launch_kind<kGemmGx, true>(a, nt, grid, waves, s) : launch_kind<kGemmGx, false>(a, nt, grid, waves, s);
-    case kGemmGw: return launch_kind<kGemmGw, false>(a, nt, grid, waves, s);
+    case kGemmOut: return wb ? launch_kind<kGemmOut, true>(a, sh, grid, waves, s) : launch_kind<kGemmOut, false>(a, sh, grid, waves, s);
+    case kGemmGs: return wb ? launch_kind<kGemmGs, true>(a, sh, grid, waves, s) : launch_kind<kGemmGs, false>(a, sh, grid, waves, s);
+    case kGemmGx: return wb ? launch_kind<kGemmGx, true>(a, sh, grid, waves, s) : launch_kind<kGemmGx, false>(a, sh, grid, waves, s);
+    case kGemmGw: return launch_kind<kGemmGw, false>(a, sh, grid, waves, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -141,8 +141,8 @@ hipError_t launch_stream(int mode, int lmax, int K, bool feat_bf16, const Stream
                          hipStream_t s);
 // Fills the tiling fields of a.g[] (tiles, tiles_n, tile_begin) and launches.
 hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s);
-// Wave tiles of a C[M][N] product (32 rows x up to 128 columns per wave).
-int64_t gemm_wave_tiles(int M, int N, int max_cols);
+// Wave tiles of a C[M][N] product of the given kind (the tile shape launch_gemm uses).
+int64_t gemm_wave_tiles(int kind, int M, int N, int max_cols);
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 hipError_t launch_zero_rows(float* base, int64_t N, int rows, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
