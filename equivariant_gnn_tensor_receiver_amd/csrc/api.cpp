@@ -56,19 +56,20 @@ int ct_log2_of(int C) {
 }
 
 // Reduction splits of the gW product over blocks: enough waves to fill the
-// chip (with up to 4 waves per block) while each split keeps >= 512 reductions.
+// chip (with up to 4 waves per block) while each split of the largest group
+// keeps >= 512 reductions (smaller groups get shorter splits).
 int gw_splits(const Plan& p, int64_t N) {
-  int64_t tiles = 0, min_kr = INT64_MAX;
+  int64_t tiles = 0, max_kr = 0;
   for (const auto& g : p.out_groups) {
     if (g.paths.empty()) continue;
     const int64_t M = (int64_t)p.K * g.paths.size() * p.C_in;
     tiles += gemm_wave_tiles(kGemmGw, (int)M, p.C_out, p.C_out);
-    min_kr = std::min<int64_t>(min_kr, N * (2 * g.l + 1));
+    max_kr = std::max<int64_t>(max_kr, N * (2 * g.l + 1));
   }
   if (tiles == 0) return 1;
   int64_t s = (1024 + tiles - 1) / tiles;
   s = std::min<int64_t>(s, 64);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, min_kr / 512));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, max_kr / 512));
   return (int)std::max<int64_t>(1, s);
 }
 

@@ -393,8 +393,19 @@ __global__ void gw_reduce_kernel(const ReduceArgs a, int64_t total) {
   if (gi >= a.ngroups) return;
   const GemmGroup& G = a.g[gi];
   const int j = (int)(rem / G.N), co = (int)(rem - (int64_t)j * G.N);
+  // summed in split order; eight loads are issued before their adds
+  const float* src = a.part + G.part_off + (int64_t)j * G.N + co;
+  const int64_t step = (int64_t)G.M * G.N;
   float s = 0.f;
-  for (int sp = 0; sp < a.splits; ++sp) s += a.part[G.part_off + ((int64_t)sp * G.M + j) * G.N + co];
+  int sp = 0;
+  for (; sp + 8 <= a.splits; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(sp + u) * step];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; sp < a.splits; ++sp) s += src[sp * step];
   const int cpk = G.npg * a.C_in;
   const int k = j / cpk, r2 = j - k * cpk, q = r2 / a.C_in, ci = r2 - q * a.C_in;
   const int path = a.path_list[G.plist + q];
@@ -458,7 +469,7 @@ int64_t gemm_wave_tiles(int kind, int M, int N, int max_cols) {
 
 hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   if (a.ngroups <= 0) return hipSuccess;
-  int max_cols = 0, min_kr = INT32_MAX;
+  int max_cols = 0, max_kr = 0;
   for (int g = 0; g < a.ngroups; ++g) max_cols = a.g[g].N > max_cols ? a.g[g].N : max_cols;
   // gS has a short reduction (C_out) and a wide output: one 32-column tile per
   // wave keeps registers low and many waves resident for the store stream.
@@ -479,7 +490,7 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
     G.tiles = (G.M > 0 && G.N > 0) ? ceil_div(G.M, 32 * sh.mt) * G.tiles_n : 0;
     G.tile_begin = (int32_t)total;
     total += G.tiles;
-    if (G.tiles > 0 && G.Kr < min_kr) min_kr = G.Kr;
+    if (G.tiles > 0 && G.Kr > max_kr) max_kr = G.Kr;
   }
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) return hipErrorInvalidValue;
@@ -488,7 +499,7 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   const int kc = 2 * sh.vh;
   int waves = 1;
   while (waves < kMaxWaveSplit && total * splits * waves < kTargetWaves &&
-         (int64_t)min_kr >= (int64_t)splits * waves * 2 * 4 * kc)
+         (int64_t)max_kr >= (int64_t)splits * waves * 2 * 4 * kc)
     waves *= 2;
   const dim3 grid((unsigned)total, (unsigned)splits, 1);
   const bool wb = a.w_bf16 != 0;
