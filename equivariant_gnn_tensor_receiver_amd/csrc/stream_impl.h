@@ -242,20 +242,24 @@ struct StreamCtx {
   // those registers would take the kernel below two waves per SIMD.
   static constexpr bool kAccGeoAhead = !(LMAX >= 3 && K == 16 && TAN);
   static constexpr bool kPosGeoAhead = LMAX <= 2;
+  // Whether the position stream reads an edge's Jacobian rows at the start of
+  // its step (registers held through the step) rather than at their use.
+  static constexpr bool kPosJacobianFirst = LMAX <= 2 && K == 8;
 
-  // vec += J^T gy over the harmonic degrees L2.. that a member path uses.
+  // vec += J^T gy over the harmonic degrees L2.. that a member path uses
+  // (J: the edge's Jacobian rows, in registers).
   template <int L2, class... Ps>
-  __device__ __forceinline__ void apply_jacobian(const float (&gy)[NSH], int j, float (&vec)[3]) {
+  __device__ __forceinline__ void apply_jacobian(const float (&gy)[NSH], const float (&J)[NSH][3], float (&vec)[3]) {
     if constexpr (L2 <= LMAX) {
       if constexpr (((Ps::l2 == L2) || ...)) {
 #pragma unroll
         for (int i = 0; i < 2 * L2 + 1; ++i) {
           const int row = L2 * L2 + i;
 #pragma unroll
-          for (int cc = 0; cc < 3; ++cc) vec[cc] = __builtin_fmaf(gy[row], L.J[j][row][cc], vec[cc]);
+          for (int cc = 0; cc < 3; ++cc) vec[cc] = __builtin_fmaf(gy[row], J[row][cc], vec[cc]);
         }
       }
-      apply_jacobian<L2 + 1, Ps...>(gy, j, vec);
+      apply_jacobian<L2 + 1, Ps...>(gy, J, vec);
     }
   }
 
@@ -614,16 +618,33 @@ struct StreamCtx {
         float tmp[NIN][4];
         const float(&xv)[NIN][4] = raw.get(tmp);
         const int jj = g.jj;
+        // The Jacobian rows and r_hat are used last; where the registers allow
+        // they are read first, so that their LDS latency passes under the
+        // step's arithmetic (rows that no member path uses are never read).
+        float J[NSH][3], rh[3];
+        auto read_jacobian = [&] {
+#pragma unroll
+          for (int row = 0; row < NSH; ++row)
+#pragma unroll
+            for (int cc = 0; cc < 3; ++cc) J[row][cc] = L.J[jj][row][cc];
+#pragma unroll
+          for (int cc = 0; cc < 3; ++cc) rh[cc] = L.rhat[jj][cc];
+        };
+        if constexpr (kPosJacobianFirst) {
+          read_jacobian();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         float alpha = 0.f;
         float gy[NSH];
 #pragma unroll
         for (int i = 0; i < NSH; ++i) gy[i] = 0.f;
         pos_edge<0, TOT, NIN, Ps...>(xv, g, gs, alpha, gy);
+        if constexpr (!kPosJacobianFirst) read_jacobian();
         // this unit's share of g_r = alpha r_hat + J^T gy for the quad's channels
         float vec[3];
 #pragma unroll
-        for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * L.rhat[jj][cc];
-        apply_jacobian<1, Ps...>(gy, jj, vec);
+        for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * rh[cc];
+        apply_jacobian<1, Ps...>(gy, J, vec);
 #pragma unroll
         for (int cc = 0; cc < 3; ++cc) vec[cc] *= g.mask;
         quad_sum3(vec, ctl);
