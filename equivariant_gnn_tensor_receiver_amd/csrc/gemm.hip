@@ -73,14 +73,45 @@ __device__ __forceinline__ void load_run(const float* p, int valid, float (&v)[V
   }
 }
 
+// x / d for 0 <= x < 2^22 and 0 < d < 2^22: the quotient through the fp32
+// reciprocal is off by at most one, and the remainder test corrects it (the
+// divisors are uniform, so the reciprocal is one scalar-side instruction).
+__device__ __forceinline__ int div_small(int x, int d) {
+  int q = (int)((float)x * __builtin_amdgcn_rcpf((float)d));
+  const int r = x - q * d;
+  q += r >= d ? 1 : 0;
+  q -= r < 0 ? 1 : 0;
+  return q;
+}
+
+// (k, q, c) of a reduction/column index k * npg * C + q * C + c of a group.
+__device__ __forceinline__ int w_index(const GemmGroup& G, int kqc, int C, int& q, int& c) {
+  const int cpk = G.npg * C;
+  const int k = div_small(kqc, cpk), rem = kqc - k * cpk;
+  q = div_small(rem, C);
+  c = rem - q * C;
+  return k;
+}
+
 // Row k * P + path of W and channel c for a reduction/column index (k, q, c)
 // of a group.  `pl` holds, in lane i, the group's i-th path index (read once
 // per kernel), so the lookup is a lane shuffle, not a memory load.
 __device__ __forceinline__ int64_t w_row(const GemmArgs& a, const GemmGroup& G, int kqc, int C, int pl, int& c) {
-  const int cpk = G.npg * C;
-  const int k = kqc / cpk, rem = kqc - k * cpk, q = rem / C;
-  c = rem - q * C;
+  int q;
+  const int k = w_index(G, kqc, C, q, c);
   return (int64_t)k * a.P + __shfl(pl, q);
+}
+
+// The same for an index that is uniform over each lane half (h = lane / 32,
+// as the reduction indices of a chunk are): the path comes from two lane
+// reads instead of a shuffle through LDS.
+__device__ __forceinline__ int64_t w_row_halves(const GemmArgs& a, const GemmGroup& G, int kqc, int C, int pl,
+                                                int h, int& c) {
+  int q;
+  const int k = w_index(G, kqc, C, q, c);
+  const int q0 = __builtin_amdgcn_readfirstlane(q), q1 = __builtin_amdgcn_readlane(q, 32);
+  const int p0 = __builtin_amdgcn_readlane(pl, q0), p1 = __builtin_amdgcn_readlane(pl, q1);
+  return (int64_t)k * a.P + (h ? p1 : p0);
 }
 
 // A operand: values t = 0..VH-1 of row m at reductions rs + t; indices past
@@ -130,7 +161,7 @@ __device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, in
   if constexpr (KIND == kGemmOut) {  // B(r = (k,q,ci), n = co) = W[k][p][ci][co]
     if constexpr (VEC) {  // the VH reductions share (k, q): C_in is a multiple of 16
       int ci;
-      const int64_t kp = w_row(a, G, rs < r_end ? rs : 0, a.C_in, pl, ci);
+      const int64_t kp = w_row_halves(a, G, rs < r_end ? rs : 0, a.C_in, pl, (int)(threadIdx.x & 63) >> 5, ci);
       const int64_t base = (kp * a.C_in + ci) * a.C_out + n;
 #pragma unroll
       for (int t = 0; t < VH; ++t) v[t] = raw_w<WBF16>(a.W, base + (int64_t)t * a.C_out);
@@ -152,7 +183,7 @@ __device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, in
       base = (kp * a.C_in + ci) * a.C_out + (VEC ? (rs < r_end ? rs : 0) : 0);
     } else if constexpr (VEC) {  // the VH reductions share (k, q): C_out is a multiple of 16
       int co;
-      const int64_t kp = w_row(a, G, rs < r_end ? rs : 0, a.C_out, pl, co);
+      const int64_t kp = w_row_halves(a, G, rs < r_end ? rs : 0, a.C_out, pl, (int)(threadIdx.x & 63) >> 5, co);
       base = (kp * a.C_in + n) * a.C_out + co;
     } else {
       base = 0;
