@@ -454,12 +454,14 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
 // row tile) costs more than the node-sized A stream, so waves take two row
 // tiles when that still leaves enough waves to fill the chip (measured: a
 // gain for gW and for 64 or more columns, a loss for the 32-column out and
-// g_x products).  gS keeps one 32 x 32 tile (short reduction, store-bound).
+// g_x products).  gS (reduction C_out, store-bound) takes two column tiles
+// per wave when the reduction has at least 64 terms and one otherwise
+// (measured both ways).
 struct Shape {
   int mt, nt, vh;
 };
-Shape gemm_shape(int kind, int max_cols, bool two_rows) {
-  if (kind == kGemmGs) return {1, 1, 16};
+Shape gemm_shape(int kind, int max_cols, bool two_rows, int kr = 0) {
+  if (kind == kGemmGs) return kr >= 64 ? Shape{1, 2, 16} : Shape{1, 1, 16};
   if (two_rows) return max_cols <= 32 ? Shape{2, 1, 8} : Shape{2, 2, 8};
   return max_cols <= 32 ? Shape{1, 1, 16} : (max_cols <= 64 ? Shape{1, 2, 16} : Shape{1, 4, 8});
 }
@@ -483,10 +485,8 @@ hipError_t launch_kind(const GemmArgs& a, Shape sh, dim3 grid, int waves, hipStr
   if (sh.mt == 1 && sh.nt == 1 && sh.vh == 16) return launch_vec<KIND, 1, 1, 16, WBF16>(a, grid, waves, s);
   if (sh.mt == 2 && sh.nt == 1 && sh.vh == 8) return launch_vec<KIND, 2, 1, 8, WBF16>(a, grid, waves, s);
   if (sh.mt == 2 && sh.nt == 2 && sh.vh == 8) return launch_vec<KIND, 2, 2, 8, WBF16>(a, grid, waves, s);
-  if (KIND != kGemmGs) {
-    if (sh.mt == 1 && sh.nt == 2 && sh.vh == 16) return launch_vec<KIND, 1, 2, 16, WBF16>(a, grid, waves, s);
-    if (sh.mt == 1 && sh.nt == 4 && sh.vh == 8) return launch_vec<KIND, 1, 4, 8, WBF16>(a, grid, waves, s);
-  }
+  if (sh.mt == 1 && sh.nt == 2 && sh.vh == 16) return launch_vec<KIND, 1, 2, 16, WBF16>(a, grid, waves, s);
+  if (KIND != kGemmGs && sh.mt == 1 && sh.nt == 4 && sh.vh == 8) return launch_vec<KIND, 1, 4, 8, WBF16>(a, grid, waves, s);
   return hipErrorInvalidValue;
 }
 
@@ -502,17 +502,15 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   if (a.ngroups <= 0) return hipSuccess;
   int max_cols = 0, max_kr = 0;
   for (int g = 0; g < a.ngroups; ++g) max_cols = a.g[g].N > max_cols ? a.g[g].N : max_cols;
-  // gS has a short reduction (C_out) and a wide output: one 32-column tile per
-  // wave keeps registers low and many waves resident for the store stream.
   const int splits = kind == kGemmGw ? a.splits : 1;
-  Shape sh = gemm_shape(kind, max_cols, true);
+  Shape sh = gemm_shape(kind, max_cols, true, a.C_out);
   {
     int64_t t2 = 0;
     for (int g = 0; g < a.ngroups; ++g)
       if (a.g[g].M > 0 && a.g[g].N > 0)
         t2 += (int64_t)ceil_div(a.g[g].M, 32 * sh.mt) * ceil_div(a.g[g].N, 32 * sh.nt);
     if (!(kind == kGemmGw || max_cols > 32) || t2 * splits * kMaxWaveSplit < kFillWaves)
-      sh = gemm_shape(kind, max_cols, false);
+      sh = gemm_shape(kind, max_cols, false, a.C_out);
   }
   int64_t total = 0;
   for (int g = 0; g < a.ngroups; ++g) {
