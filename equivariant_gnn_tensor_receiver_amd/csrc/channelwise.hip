@@ -95,8 +95,18 @@ __global__ __launch_bounds__(256) void cw_gw_kernel(const CwArgs /*args*/) {
   const int64_t per = (rows + a.splits - 1) / a.splits;
   const int64_t r0 = min(rows, (int64_t)blockIdx.y * per), r1 = min(rows, r0 + per);
   const int64_t stride = (int64_t)a.K * cpk;
-  const float* sp = a.state + G.state_off + (int64_t)k * cpk + q * a.C + c;
+  const float* sp = a.state + G.state_off + (int64_t)k * cpk + q * a.C + c + r0 * stride;
   const float* gp = a.gout + (int64_t)G.row_off * a.C + c;
+  // row r = (node, mm) of the group, stepped without division
+  int64_t node = r0 / G.n;
+  int mm = (int)(r0 - node * G.n);
+  auto g_at = [&]() { return gp[(node * a.D_feat + mm) * a.C]; };
+  auto advance = [&]() {
+    const int m2 = mm + 1;
+    const bool wrap = m2 == G.n;
+    mm = wrap ? 0 : m2;
+    node += wrap ? 1 : 0;
+  };
   float acc = 0.f;
   constexpr int U = 8;
   int64_t r = r0;
@@ -104,17 +114,18 @@ __global__ __launch_bounds__(256) void cw_gw_kernel(const CwArgs /*args*/) {
     float sv[U], gv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t rr = r + u;
-      const int64_t node = rr / G.n;
-      sv[u] = sp[rr * stride];
-      gv[u] = gp[(node * a.D_feat + (rr - node * G.n)) * a.C];
+      sv[u] = sp[u * stride];
+      gv[u] = g_at();
+      advance();
     }
+    sp += U * stride;
 #pragma unroll
     for (int u = 0; u < U; ++u) acc = __builtin_fmaf(sv[u], gv[u], acc);
   }
   for (; r < r1; ++r) {
-    const int64_t node = r / G.n;
-    acc = __builtin_fmaf(sp[r * stride], gp[(node * a.D_feat + (r - node * G.n)) * a.C], acc);
+    acc = __builtin_fmaf(*sp, g_at(), acc);
+    sp += stride;
+    advance();
   }
   a.dst[(int64_t)blockIdx.y * a.elems + e] = acc;
 }
