@@ -474,7 +474,7 @@ struct StreamCtx {
       // branches or such copies would make the compiler wait for every
       // outstanding load.
       const int last = nb - 1;
-      const int nslots = (nb + ES - 1) / ES;
+      const int nslots = (nb + ES - 1) >> (6 - ctl);  // ES = 2^(6 - ctl)
       using Raw = FeatRaw<FT>;
       auto nbr_of = [&](int slot) { return L.nbr[min(slot * ES + es, last)]; };
       auto gather = [&](int nbr, typename Raw::type (&v)[NIN]) {
@@ -589,7 +589,7 @@ struct StreamCtx {
       if (lane < nb) edge_prep<LMAX, K, MODE>(a, node, psx, psy, psz, b0 + lane, lane, L);
       __syncthreads();
       const int last = nb - 1;
-      const int nsteps = (nb + per_step - 1) / per_step;
+      const int nsteps = (nb + per_step - 1) >> (8 - ctl);  // per_step = 2^(8 - ctl)
       // The gathered block of the lane's edge for the quad's channels and the
       // edge's LDS geometry are loaded one step ahead of their use and the
       // neighbour index one step further (clamped edge index: unconditional
@@ -730,12 +730,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(stream_min_w
 void stream_kernel(const StreamArgs /*args*/, int64_t items) {
   const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ EdgeLds<K, LMAX, MODE> L;
-  const int64_t item = xcd_item(blockIdx.x, gridDim.x);
-  if (item >= items) return;
-  const int unit = (int)(item % a.nunits);
-  const int64_t t = item / a.nunits;
-  const int tile = (int)(t % a.ntiles);
-  const int node = (int)(t / a.ntiles);
+  // 32-bit index arithmetic (the launch keeps items below 2^31): a 64-bit
+  // division here costs hundreds of instructions per wave.
+  const uint32_t item = (uint32_t)xcd_item(blockIdx.x, gridDim.x);
+  if (item >= (uint32_t)items) return;
+  const uint32_t nu = (uint32_t)a.nunits, nt = (uint32_t)a.ntiles;
+  const int unit = (int)(item % nu);
+  const uint32_t t = item / nu;
+  const int tile = (int)(t % nt);
+  const int node = (int)(t / nt);
   StreamCtx<MODE, FT, LMAX, K> ctx{node, tile, unit, L};
   if constexpr (BUNDLED) {
     Bundles<LMAX, K, ModeTraits<MODE>::bwdpos ? 2 : (ModeTraits<MODE>::recv ? 0 : 1)>::run(unit, ctx, a);
@@ -759,6 +762,7 @@ template <int MODE, typename FT>
 hipError_t launch_stream_mode(int lmax, int K, const StreamArgs& a, int64_t items, hipStream_t s) {
   const int64_t grid = (items + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
 #define TPCONV_LAUNCH(LM, KK)                                                                           \
   if (lmax == LM && K == KK) {                                                                          \
     if (a.bundled)                                                                                      \
