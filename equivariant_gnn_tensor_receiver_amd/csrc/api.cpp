@@ -631,6 +631,11 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
     set_units(p, a, p.pos_units);
     a.gstate = gS;
     a.gpos = grad_pos;
+    // Low mean degree (nearly every node one 64-edge batch): the units of a
+    // node share one block and its batch geometry.  With more batches per
+    // node the block waits for its slowest unit at every batch boundary, which
+    // measured slower than recomputing the geometry per unit.
+    a.share_geometry = g->num_edges <= 48 * g->num_nodes;
     if (cw) {
       a.cw = 1;
       a.W = W;

@@ -39,6 +39,7 @@ struct StreamArgs {
   int32_t npaths;
   int32_t nunits;       // work units per (node, tile)
   int32_t bundled;      // units are the compile-time bundles of the natural path list
+  int32_t share_geometry;  // kBwdPos: the units of a (node, tile) share one block and its batch geometry
   int32_t ct_log2;      // channel tile = 1 << ct_log2 (<= 64); edge slots per wave = 64 / tile
   int32_t ntiles;       // channels / tile
   int32_t feat_rows;    // rows per node of the gathered feature tensor

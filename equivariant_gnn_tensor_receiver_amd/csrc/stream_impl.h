@@ -37,11 +37,12 @@ struct ModeTraits {
   static constexpr int batch = (MODE == kFwd || MODE == kSnd) ? 64 : 32;
 };
 
-// Wave-private geometry of one batch of edges.  Harmonic blocks are padded to
-// 8 floats per degree and Jacobian rows to 4 so that reads are 16-byte aligned.
-template <int K, int LMAX, int MODE>
+// Geometry of one batch of BATCH edges (wave-private, or shared by the waves
+// of a block).  Harmonic blocks are padded to 8 floats per degree and Jacobian
+// rows to 4 so that reads are 16-byte aligned.
+template <int K, int LMAX, int MODE, int BATCH = ModeTraits<MODE>::batch>
 struct __attribute__((aligned(16))) EdgeLds {
-  static constexpr int B = ModeTraits<MODE>::batch;
+  static constexpr int B = BATCH;
   static constexpr int NSH = sh_count(LMAX);
   static constexpr int BT = ModeTraits<MODE>::tangent ? B : 1;
   static constexpr int BP = ModeTraits<MODE>::bwdpos ? B : 1;
@@ -55,9 +56,9 @@ struct __attribute__((aligned(16))) EdgeLds {
 };
 
 // Geometry of one edge into LDS slot j.
-template <int LMAX, int K, int MODE>
+template <int LMAX, int K, int MODE, int BATCH>
 __device__ __forceinline__ void edge_prep(const StreamArgs& a, int self, float psx, float psy, float psz, int e,
-                                          int j, EdgeLds<K, LMAX, MODE>& L) {
+                                          int j, EdgeLds<K, LMAX, MODE, BATCH>& L) {
   constexpr int NSH = sh_count(LMAX);
   constexpr bool RECV = ModeTraits<MODE>::recv;
   constexpr bool DER = ModeTraits<MODE>::tangent || ModeTraits<MODE>::bwdpos;
@@ -228,10 +229,10 @@ constexpr int out_dim() {
 // The kernel arguments travel as an explicit reference parameter through the
 // (inlined) call chain; storing a reference to them in this object would make
 // the compiler copy the whole argument block to scratch memory.
-template <int MODE, typename FT, int LMAX, int K>
+template <int MODE, typename FT, int LMAX, int K, int BATCH = ModeTraits<MODE>::batch>
 struct StreamCtx {
   int node, tile, unit;
-  EdgeLds<K, LMAX, MODE>& L;
+  EdgeLds<K, LMAX, MODE, BATCH>& L;
 
   static constexpr bool RECV = ModeTraits<MODE>::recv;
   static constexpr bool BPOS = ModeTraits<MODE>::bwdpos;
@@ -434,8 +435,8 @@ struct StreamCtx {
     using P0 = typename First<Ps...>::type;
     constexpr int NIN = RECV ? 2 * P0::l1 + 1 : 2 * P0::l3 + 1;
     constexpr int TOT = (out_dim<MODE, Ps>() + ...);
-    constexpr int B = ModeTraits<MODE>::batch;
-    const int lane = threadIdx.x;
+    constexpr int B = BATCH;
+    const int lane = threadIdx.x & 63;
     const int ctl = a.ct_log2;
     const int CT = 1 << ctl;
     const int ES = 64 >> ctl;
@@ -463,7 +464,8 @@ struct StreamCtx {
     for (int b0 = e0; b0 < e1; b0 += B) {
       const int nb = min(B, e1 - b0);
       __syncthreads();
-      if (lane < nb) edge_prep<LMAX, K, MODE>(a, node, psx, psy, psz, b0 + lane, lane, L);
+      // thread j of the block (its first wave when the block shares the batch)
+      if ((int)threadIdx.x < nb) edge_prep(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, L);
       __syncthreads();
       // Branch-free edge loop: the gathers and the LDS geometry for the next
       // edge slot are issued before the current slot is used, and the
@@ -559,8 +561,8 @@ struct StreamCtx {
     using P0 = typename First<Ps...>::type;
     constexpr int NIN = 2 * P0::l1 + 1;
     constexpr int TOT = (out_dim<MODE, Ps>() + ...);
-    constexpr int B = ModeTraits<MODE>::batch;
-    const int lane = threadIdx.x;
+    constexpr int B = BATCH;
+    const int lane = threadIdx.x & 63;
     const int ctl = a.ct_log2;
     const int CT = 1 << ctl;
     const int ES = 64 >> ctl;
@@ -586,7 +588,8 @@ struct StreamCtx {
     for (int b0 = e0; b0 < e1; b0 += B) {
       const int nb = min(B, e1 - b0);
       __syncthreads();
-      if (lane < nb) edge_prep<LMAX, K, MODE>(a, node, psx, psy, psz, b0 + lane, lane, L);
+      // thread j of the block (its first wave when the block shares the batch)
+      if ((int)threadIdx.x < nb) edge_prep(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, L);
       __syncthreads();
       const int last = nb - 1;
       const int nsteps = (nb + per_step - 1) >> (8 - ctl);  // per_step = 2^(8 - ctl)
@@ -715,6 +718,8 @@ struct StreamCtx {
 // the first argument, at offset 0).  Naming the by-value parameter instead
 // would let the compiler copy the whole 2.7 KB block to scratch memory when
 // the inlined code reads it in many places.
+constexpr int kMaxSharedUnits = 8;  // waves of a block that shares the batch geometry
+
 // Waves per SIMD the register allocation must leave room for: the lmax <= 2,
 // K = 8 forward and sender streams fit three waves (168 registers) when asked
 // to, which hides more of the gather latency than the compiler's own choice.
@@ -725,21 +730,27 @@ constexpr int stream_min_waves(int lmax, int K, int mode) {
 // BUNDLED selects the natural path bundles or single-path units; the two are
 // separate kernels so that each gets the register allocation of its own code
 // (the single-path dispatch covers every path up to LMAX).
-template <int LMAX, int K, int MODE, typename FT, bool BUNDLED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(stream_min_waves(LMAX, K, MODE))))
+// SHARED (position gradient of bundled plans with low mean degree): one
+// block per (node, tile) whose waves are the units; the first wave computes
+// the geometry of a 64-edge batch into LDS for all of them, instead of every
+// unit's wave computing it again.  `items` counts blocks then, waves otherwise.
+template <int LMAX, int K, int MODE, typename FT, bool BUNDLED, bool SHARED>
+__global__ __launch_bounds__(SHARED ? 64 * kMaxSharedUnits : 64)
+__attribute__((amdgpu_waves_per_eu(stream_min_waves(LMAX, K, MODE))))
 void stream_kernel(const StreamArgs /*args*/, int64_t items) {
   const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  __shared__ EdgeLds<K, LMAX, MODE> L;
+  constexpr int BATCH = SHARED ? 64 : ModeTraits<MODE>::batch;
+  __shared__ EdgeLds<K, LMAX, MODE, BATCH> L;
   // 32-bit index arithmetic (the launch keeps items below 2^31): a 64-bit
   // division here costs hundreds of instructions per wave.
   const uint32_t item = (uint32_t)xcd_item(blockIdx.x, gridDim.x);
-  if (item >= (uint32_t)items) return;
+  if (item >= (uint32_t)items) return;  // uniform over the block
   const uint32_t nu = (uint32_t)a.nunits, nt = (uint32_t)a.ntiles;
-  const int unit = (int)(item % nu);
-  const uint32_t t = item / nu;
+  const int unit = SHARED ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : (int)(item % nu);
+  const uint32_t t = SHARED ? item : item / nu;
   const int tile = (int)(t % nt);
   const int node = (int)(t / nt);
-  StreamCtx<MODE, FT, LMAX, K> ctx{node, tile, unit, L};
+  StreamCtx<MODE, FT, LMAX, K, BATCH> ctx{node, tile, unit, L};
   if constexpr (BUNDLED) {
     Bundles<LMAX, K, ModeTraits<MODE>::bwdpos ? 2 : (ModeTraits<MODE>::recv ? 0 : 1)>::run(unit, ctx, a);
     return;
@@ -763,12 +774,22 @@ hipError_t launch_stream_mode(int lmax, int K, const StreamArgs& a, int64_t item
   const int64_t grid = (items + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
+  const bool shared = MODE == kBwdPos && a.bundled && a.share_geometry && a.nunits >= 1 &&
+                      a.nunits <= kMaxSharedUnits && items % a.nunits == 0;
+  const int64_t blocks = shared ? items / a.nunits : 0, sgrid = (blocks + 7) / 8 * 8;
 #define TPCONV_LAUNCH(LM, KK)                                                                           \
   if (lmax == LM && K == KK) {                                                                          \
+    if constexpr (MODE == kBwdPos) {                                                                    \
+      if (shared) {                                                                                     \
+        hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true, true>), dim3((unsigned)sgrid),        \
+                           dim3(64 * a.nunits), 0, s, a, blocks);                                       \
+        return hipGetLastError();                                                                       \
+      }                                                                                                 \
+    }                                                                                                   \
     if (a.bundled)                                                                                      \
-      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
+      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true, false>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
     else                                                                                                \
-      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, false>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
+      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, false, false>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
     return hipGetLastError();                                                                           \
   }
   TPCONV_LAUNCH(0, 8) TPCONV_LAUNCH(0, 16)
