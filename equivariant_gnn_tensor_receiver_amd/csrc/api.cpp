@@ -224,9 +224,16 @@ void set_units(const Plan& p, StreamArgs& a, const std::vector<std::vector<int>>
 
 // Receiver-side stream over the CSR: gathered features x [N][D_in][C_in],
 // state S (or S_dot) in the output-group layout.
+// Low mean degree (nearly every node one 64-edge batch): the units of a node
+// may share one block and its batch geometry (the launcher decides per mode).
+// With more batches per node the block waits for its slowest unit at every
+// batch boundary, which measured slower than recomputing the geometry per unit.
+bool share_geometry(const tpconv_graph* g) { return g->num_edges <= 48 * g->num_nodes; }
+
 void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const void* x) {
   const int64_t N = g->num_nodes;
   fill_common(p, a, N, pos);
+  a.share_geometry = share_geometry(g);
   a.ptr = g->rowptr;
   a.nbr = g->senders;
   a.feat = x;
@@ -248,6 +255,7 @@ void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
 void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const float* gout) {
   const int64_t N = g->num_nodes;
   fill_common(p, a, N, pos);
+  a.share_geometry = share_geometry(g);
   a.ptr = g->csc_colptr;
   a.nbr = g->csc_receivers;
   a.feat = gout;
@@ -631,11 +639,6 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
     set_units(p, a, p.pos_units);
     a.gstate = gS;
     a.gpos = grad_pos;
-    // Low mean degree (nearly every node one 64-edge batch): the units of a
-    // node share one block and its batch geometry.  With more batches per
-    // node the block waits for its slowest unit at every batch boundary, which
-    // measured slower than recomputing the geometry per unit.
-    a.share_geometry = g->num_edges <= 48 * g->num_nodes;
     if (cw) {
       a.cw = 1;
       a.W = W;

@@ -774,12 +774,15 @@ hipError_t launch_stream_mode(int lmax, int K, const StreamArgs& a, int64_t item
   const int64_t grid = (items + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  const bool shared = MODE == kBwdPos && a.bundled && a.share_geometry && a.nunits >= 1 &&
+  // (measured: a gain for the position gradient, whose per-edge geometry is the
+  // most expensive; a loss for the forward and sender streams)
+  constexpr bool kCanShare = MODE == kBwdPos;
+  const bool shared = kCanShare && a.bundled && a.share_geometry && a.nunits >= 1 &&
                       a.nunits <= kMaxSharedUnits && items % a.nunits == 0;
   const int64_t blocks = shared ? items / a.nunits : 0, sgrid = (blocks + 7) / 8 * 8;
 #define TPCONV_LAUNCH(LM, KK)                                                                           \
   if (lmax == LM && K == KK) {                                                                          \
-    if constexpr (MODE == kBwdPos) {                                                                    \
+    if constexpr (kCanShare) {                                                                          \
       if (shared) {                                                                                     \
         hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true, true>), dim3((unsigned)sgrid),        \
                            dim3(64 * a.nunits), 0, s, a, blocks);                                       \
