@@ -144,7 +144,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single "
-              "MI355X; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "MI355X; sharding over several GPUs is not built)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -287,7 +287,7 @@ def main():
         "setup_s": {"inputs": round(t_gen, 2), "graph_prepare": round(t_prep, 4)},
     }
     if not args.no_cpu_baseline:
-        # about 10-30 s of oracle work on the machine's host cores
+        # about 10-30 s of oracle work on the host cores
         sample = args.cpu_sample_edges or {"tiny": 512, "molecular": 80000, "wide_l": 4000,
                                            "edge_scaling": 80000, "force": 2000,
                                            "molecular_uvu": 120000}[w.name]

@@ -66,7 +66,7 @@ typedef enum {
   TPCONV_ERROR_IRREPS = 2,        /* unparsable irreps, non-uniform multiplicity, l > 3 */
   TPCONV_ERROR_GRAPH = 3,         /* CSR fails validation (tpconv_graph_prepare, validate=1) */
   TPCONV_ERROR_WORKSPACE = 4,     /* workspace pointer null or smaller than required */
-  TPCONV_ERROR_UNSUPPORTED = 5,   /* valid request this build does not implement */
+  TPCONV_ERROR_UNSUPPORTED = 5,   /* valid request the library does not implement */
   TPCONV_ERROR_DEVICE = 6         /* HIP runtime or launch failure */
 } tpconv_status;
 

@@ -22,5 +22,6 @@ Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 library routines (sympy CG, scipy spherical harmonics, scipy quadrature),
 invariants (rotation, inversion, translation, permutation) and finite
 differences.  Conventions that nothing on the pages fixes (the sign of odd-sum
-paths, the Bessel prefactor) are "parity unpinned" and listed in the design doc.
+paths, the Bessel prefactor) are "parity unpinned": they hold by choice and are
+checked only against the library's exported tables.
 """

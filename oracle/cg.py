@@ -9,8 +9,7 @@ the CG product is the fully expressive equivariant bilinear map, governed by
 nonzero selection rules, and it can form the antisymmetric 1e cross-product
 term).
 
-Conventions (the pages fix none of them; these are the readings this project
-takes, listed in DESIGN.md):
+Conventions (the pages fix none of them; these are the readings taken here):
 
 * complex CG <l1 m1 l2 m2 | l3 m3> from the Racah closed form, evaluated in
   exact rational arithmetic and rounded once to fp64;

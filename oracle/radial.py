@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 The Sobek abstract reassociates a "radial projection" with the harmonic
 coupling and the aggregation; the workload description fixes K Bessel
-functions with a p = 6 polynomial cutoff.  Reading taken (DESIGN.md):
+functions with a p = 6 polynomial cutoff.  Reading taken:
 
     R_k(d) = sqrt(2/c) * sin(k pi d / c) / d * u(d / c),   k = 1..K,
     u(x)   = 1 - (p+1)(p+2)/2 x^p + p(p+2) x^(p+1) - p(p+1)/2 x^(p+2)   (x < 1)
