@@ -3,19 +3,24 @@
 
 A step is one pass of the workload's hot path over its synthetic radius graph:
 forward (receiver stream + contraction) and backward w.r.t. x, W and
-positions; the "force" workload adds the double backward of the force loss.
-Inputs are resident in HBM before the timed region.  Prints ONE JSON line with
-edges/s (whole job), per-pass throughput, peak workspace bytes, the dominant
-kernel's roofline (algorithmic FLOPs or bytes per launch over its HIP-event
-duration) and the CPU oracle's throughput on a bounded sample.
+positions; the "force" workload runs forward, the position gradient (forces)
+and the double backward of the force loss.  Inputs are resident in HBM before
+the timed region.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload molecular]
+Prints ONE JSON line.  `value` is edges/s of the headline workload's step
+(Edge-scaling by default, the largest configuration).  The line also carries,
+for that workload, per-pass throughput, peak workspace bytes, the dominant
+kernel's roofline (algorithmic FLOPs or bytes per launch over its HIP-event
+duration) and the CPU oracle's throughput on a bounded sample; and under
+`per_config`, every configuration's forward and fwd+bwd (Force: each stage of
+its chain) edges/s with the whole-pass lower bound T_lb and T_lb / T_measured.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload edge_scaling]
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -24,7 +29,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "edges/sec fwd and fwd+bwd per config; % of HBM/MFMA roofline; peak bytes"
-PEAK = {"hbm": (8000.0, "GB/s"), "mfma": (157.3, "TFLOP/s"), "alu": (157.3, "TFLOP/s")}
+HBM_GBS = 8000.0          # MI355X HBM3E
+FP32_TFLOPS = 157.3       # fp32 MFMA, and packed fp32 VALU (256 CUs x 4 SIMDs x 64 FLOP/clk x 2.4 GHz)
+BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK = {"hbm": (HBM_GBS, "GB/s"), "mfma": (FP32_TFLOPS, "TFLOP/s"), "alu": (FP32_TFLOPS, "TFLOP/s")}
+CONFIG_ORDER = ("tiny", "molecular", "wide_l", "edge_scaling", "force", "molecular_uvu")
 
 
 def plan_counts(plan):
@@ -38,32 +47,76 @@ def plan_counts(plan):
     return out
 
 
-def algorithmic(plan, paths, N, E, xbytes):
-    """Algorithmic FLOPs and compulsory HBM bytes per launch of each kernel class."""
+def sizes(plan, N, E, xbytes, wbytes):
+    """Bytes of every tensor a pass must read or write once."""
+    fin, fout, wf = 4 * N * plan.rows_in * plan.ch_in, 4 * N * plan.rows_out * plan.ch_out, 4 * plan.w_numel
+    return {"x": N * plan.rows_in * plan.ch_in * xbytes, "W": plan.w_numel * wbytes, "pos": 12 * N,
+            "csr": 4 * (N + 1) + 4 * E, "csc": 4 * (N + 1) + 4 * E, "out": fout, "g_out": fout, "g_x": fin,
+            "gW": wf, "g_pos": 12 * N, "gg_pos": 12 * N, "d_W": wf, "d_x": fin}
+
+
+def algorithmic(plan, paths, N, E, xbytes, wbytes):
+    """Algorithmic FLOPs and compulsory HBM bytes per launch of each kernel class.
+
+    Edge streams count the coupling (2 C nnz per edge and direction) and the
+    radial products (2 K C M per edge and direction); the per-edge weights and
+    messages of the conventional schedule are not counted.  A stream writes
+    (or reads) its node-sized state once."""
     K, Ci, Co = plan.num_basis, plan.ch_in, plan.ch_out
     M3 = sum(2 * l3 + 1 for _, _, l3, _ in paths)
     M1 = sum(2 * l1 + 1 for l1, _, _, _ in paths)
     nnz = sum(n for *_, n in paths)
     S = 4 * N * K * Ci * M3
     T = 4 * N * K * Co * M1
-    Wb = plan.w_numel * xbytes
-    x = N * plan.rows_in * Ci * xbytes
-    go = 4 * N * plan.rows_out * Co
-    graph = 4 * (N + 1) + 4 * E + 12 * N
+    z = sizes(plan, N, E, xbytes, wbytes)
+    x, Wb, go, graph = z["x"], z["W"], z["g_out"], z["csr"] + z["pos"]
     return {
         "stream_fwd": (E * Ci * (2 * nnz + 2 * K * M3), x + graph + S),
         "stream_jvp": (E * Ci * (4 * nnz + 4 * K * M3), x + graph + 12 * N + S),
         "stream_snd": (E * Co * (2 * nnz + 2 * K * M1), go + graph + T),
         "stream_sndt": (E * Co * (4 * nnz + 4 * K * M1), go + graph + 12 * N + T),
-        "stream_bwdpos": (E * Ci * (4 * nnz + 4 * K * M3), x + graph + S + 24 * N),
+        "stream_bwdpos": (E * Ci * (4 * nnz + 4 * K * M3), x + graph + S + 12 * N),
         "gemm_out": (2 * N * K * Ci * Co * M3, S + Wb + go),
         "gemm_gs": (2 * N * K * Ci * Co * M3, go + Wb + S),
-        "gemm_gx": (2 * N * K * Ci * Co * M1, T + Wb + x // xbytes * 4),
+        "gemm_gx": (2 * N * K * Ci * Co * M1, T + Wb + z["g_x"]),
         "gemm_gw": (2 * N * K * Ci * Co * M3, S + go + 4 * plan.w_numel),
         # channel-wise contractions (out side shown; the input side is the same size for these path sets)
         "cw_contract": (2 * N * K * Ci * M3, S + Wb + go),
         "cw_gw": (2 * N * K * Ci * M3, S + go),
     }
+
+
+# Kernel classes of each pass and the tensors it must read or write once.
+PASS_KERNELS = {
+    "fwd": (("stream_fwd", "gemm_out"), {"x", "W", "pos", "csr", "out"}),
+    # backward w.r.t. x, W and positions
+    "bwd": (("stream_snd", "gemm_gx", "gemm_gw", "gemm_gs", "stream_bwdpos"),
+            {"x", "W", "pos", "csr", "csc", "g_out", "g_x", "gW", "g_pos"}),
+    # Force chain: the position gradient only, then the double backward w.r.t. W and x
+    "forces": (("gemm_gs", "stream_bwdpos"), {"x", "W", "pos", "csr", "g_out", "g_pos"}),
+    "dbwd": (("stream_jvp", "gemm_gw", "stream_sndt", "gemm_gx"),
+             {"x", "W", "pos", "csr", "csc", "g_out", "gg_pos", "d_W", "d_x"}),
+}
+CW_KERNEL = {"gemm_out": "cw_contract", "gemm_gx": "cw_contract", "gemm_gw": "cw_gw", "gemm_gs": None}
+
+
+def pass_bound(names, alg, channelwise, mfma_peak_tflops, nbytes):
+    """T_lb = max(bytes / HBM, VALU FLOPs / VALU peak, MFMA FLOPs / MFMA peak), perfect overlap assumed."""
+    valu = mfma = 0
+    for n in names:
+        if channelwise and n in CW_KERNEL:
+            n = CW_KERNEL[n]
+            if n is None:
+                continue
+            valu += alg[n][0]  # channel-diagonal contractions run on the vector ALUs
+        elif n.startswith("gemm"):
+            mfma += alg[n][0]
+        else:
+            valu += alg[n][0]
+    terms = {"hbm": nbytes / (HBM_GBS * 1e9), "alu": valu / (FP32_TFLOPS * 1e12),
+             "mfma": mfma / (mfma_peak_tflops * 1e12)}
+    bind = max(terms, key=terms.get)
+    return terms[bind], bind, valu, mfma
 
 
 def roofline_for(name, flops, nbytes, ms):
@@ -97,17 +150,37 @@ def load_traffic(workload, kernel):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(name, w, data, plan, sample_edges):
+def host_info():
+    """Cores this process may run on, the CPU model and numpy's BLAS."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", 1
+    try:
+        from threadpoolctl import threadpool_info
+
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')}"
+                threads = max(threads, int(i.get("num_threads", 1)))
+    except Exception:  # pragma: no cover
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model, "blas": blas,
+            "blas_threads": threads}
+
+
+def cpu_baseline(w, data, sample_edges):
     """The fp64 oracle (materialising schedule) on the in-edges of the first receivers."""
     import numpy as np
     from oracle import tpconv as otp
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    host = host_info()
     prob = otp.Problem(w.irreps, w.irreps, w.lmax, w.num_basis, channelwise=w.channelwise)
     rowptr = data["rowptr"]
     nrecv = int(np.searchsorted(rowptr, sample_edges, side="right") - 1)
@@ -128,37 +201,27 @@ def cpu_baseline(name, w, data, plan, sample_edges):
         reps += 1
     passes = "+".join(p for p in w.passes)
     rep = f" x {reps} repetitions" if reps > 1 else ""
-    return {"value": round(reps * e1 / dt, 2), "unit": "edges/s", "cores": int(cores), "kind": "oracle",
+    # numpy's einsum contractions run on BLAS; its thread count is what the oracle used
+    return {"value": round(reps * e1 / dt, 2), "unit": "edges/s", "cores": host["blas_threads"], "kind": "oracle",
             "sample": f"in-edges of receivers 0..{nrecv - 1} ({e1} of {len(data['senders'])} edges){rep}, "
-                      f"{passes}, fp64 numpy, {dt:.1f} s"}
+                      f"{passes}, fp64 numpy, {dt:.1f} s",
+            "host": host}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="molecular")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-edges", type=int, default=0, help="oracle sample size (edges); 0 = default")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single "
-              "MI355X; sharding over several GPUs is not built)", file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(name, steps, warmup, detail):
+    """Time one workload; returns its report (and the oracle inputs when `detail`)."""
     import numpy as np
     import torch
 
     from equivariant_gnn_tensor_receiver_amd import inputs
     from equivariant_gnn_tensor_receiver_amd import tpconv as tp
 
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.WORKLOADS[name]
     dt_code = tp.TPCONV_BF16 if w.dtype == "bf16" else tp.TPCONV_F32
     plan = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis, inputs.CUTOFF, 6, dt_code, dt_code,
                    tp.CHANNELWISE if w.channelwise else tp.FULLY_CONNECTED)
     t0 = time.perf_counter()
-    data = inputs.make_workload(args.workload, plan.num_paths)
+    data = inputs.make_workload(name, plan.num_paths)
     t_gen = time.perf_counter() - t0
     N, E = w.num_nodes, len(data["senders"])
     dev = torch.device("cuda:0")
@@ -189,12 +252,13 @@ def main():
     ws_d = torch.empty(plan.workspace_size(tp.OP_DOUBLE_BACKWARD, N, E), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     io_alloc = torch.cuda.memory_allocated()
+    force = name == "force"
 
     def fwd():
         tp.tpconv_forward(plan, graph, pos, x, W, out=out, saved_state=S)
 
     def bwd():
-        if args.workload == "force":
+        if force:  # forces: the position gradient only
             tp.tpconv_backward(plan, graph, pos, x, W, g_out, saved_state=S, want=("pos",), workspace=ws_b,
                                grad_pos=gp)
         else:
@@ -219,61 +283,70 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t) / k * 1e3
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
-    ms_step = timed(step, args.steps)
+    ms_step = timed(step, steps)
     peak_alloc = torch.cuda.max_memory_allocated()
-    value = E / (ms_step * 1e-3)
+
+    xbytes = wbytes = 2 if w.dtype == "bf16" else 4
+    alg = algorithmic(plan, plan_counts(plan), N, E, xbytes, wbytes)
+    z = sizes(plan, N, E, xbytes, wbytes)
+    mfma_peak = BF16_TFLOPS if w.dtype == "bf16" else FP32_TFLOPS
+
+    def bound(pass_names, measured_ms):
+        ks, ts = [], set()
+        for pn in pass_names:
+            ks += PASS_KERNELS[pn][0]
+            ts |= PASS_KERNELS[pn][1]  # a tensor several passes of one step touch counts once
+        nbytes = sum(z[t] for t in ts)
+        t_lb, bind, valu, mfma = pass_bound(ks, alg, w.channelwise, mfma_peak, nbytes)
+        return {"ms": round(measured_ms, 4), "edges_per_s": round(E / (measured_ms * 1e-3), 1),
+                "t_lb_us": round(t_lb * 1e6, 2), "binding": bind, "frac_of_bound": round(t_lb / (measured_ms * 1e-3), 4),
+                "valu_gflop": round(valu / 1e9, 3), "mfma_gflop": round(mfma / 1e9, 3),
+                "compulsory_mb": round(nbytes / 1e6, 2)}
 
     passes = {}
-    ms_f = timed(fwd, args.steps)
-    passes["fwd"] = {"ms": round(ms_f, 4), "edges_per_s": round(E / (ms_f * 1e-3), 1)}
+    ms_f = timed(fwd, steps)
+    passes["fwd"] = bound(["fwd"], ms_f)
     if "bwd" in w.passes:
-        ms_b = timed(bwd, args.steps)
-        passes["bwd"] = {"ms": round(ms_b, 4)}
-        passes["fwd+bwd"] = {"ms": round(ms_f + ms_b, 4), "edges_per_s": round(E / ((ms_f + ms_b) * 1e-3), 1)}
+        ms_b = timed(bwd, steps)
+        key = "forces" if force else "bwd"
+        passes[key] = bound([key], ms_b)
+        passes["fwd+" + key] = bound(["fwd", key], ms_f + ms_b)
     if "dbwd" in w.passes:
-        ms_d = timed(dbwd, args.steps)
-        passes["dbwd"] = {"ms": round(ms_d, 4), "edges_per_s": round(E / (ms_d * 1e-3), 1)}
+        ms_d = timed(dbwd, steps)
+        passes["dbwd"] = bound(["dbwd"], ms_d)
+        passes["fwd+forces+dbwd"] = bound(["fwd", "forces", "dbwd"], ms_f + ms_b + ms_d)
+
+    rep = {"workload": w.name, "num_nodes": N, "num_edges": E, "step": "+".join(w.passes),
+           "ms_per_step": round(ms_step, 4), "edges_per_s": round(E / (ms_step * 1e-3), 1), "passes": passes}
+    if not detail:
+        return rep, None
 
     # per-kernel HIP-event durations over a second timed region
     tp.tpconv_kernel_timing(True)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     ktimes = tp.tpconv_kernel_timing_read()
     tp.tpconv_kernel_timing(False)
-    xbytes = 2 if w.dtype == "bf16" else 4
-    alg = algorithmic(plan, plan_counts(plan), N, E, xbytes)
     kernels = {}
-    for name, (n, ms) in ktimes.items():
-        kernels[name] = {"launches_per_step": n / args.steps, "avg_us": round(ms / n * 1e3, 2),
-                         "share": round(ms / sum(v[1] for v in ktimes.values()), 4)}
+    for kname, (n, ms) in ktimes.items():
+        kernels[kname] = {"launches_per_step": n / steps, "avg_us": round(ms / n * 1e3, 2),
+                          "share": round(ms / sum(v[1] for v in ktimes.values()), 4)}
     dom = max((k for k in ktimes if k in alg), key=lambda k: ktimes[k][1])
     n_dom, ms_dom = ktimes[dom]
     roof = roofline_for(dom, alg[dom][0], alg[dom][1], ms_dom / n_dom)
-    roof["traffic"] = load_traffic(args.workload, dom)
-
-    res = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "edges/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+    roof["traffic"] = load_traffic(w.name, dom)
+    rep.update({
+        "value": E / (ms_step * 1e-3),
         "dtype": "f32" if w.dtype == "f32" else "bf16-in/f32",
-        "data": "synthetic",
         "config": {"workload": w.name, "num_nodes": N, "num_edges": E, "mean_degree": round(E / N, 2),
                    "irreps": w.irreps, "sh_lmax": w.lmax, "num_basis": w.num_basis, "paths": plan.num_paths,
                    "step": "+".join(w.passes), "cutoff": inputs.CUTOFF, "box": round(data["box"], 4),
                    "connection": "channelwise" if w.channelwise else "fully_connected"},
-        "passes": passes,
         "peak_bytes": {"workspace_fwd": plan.workspace_size(tp.OP_FORWARD, N, E),
                        "workspace_bwd": plan.workspace_size(tp.OP_BACKWARD, N, E),
                        "workspace_dbwd": plan.workspace_size(tp.OP_DOUBLE_BACKWARD, N, E),
@@ -282,16 +355,70 @@ def main():
                        "allocated_over_inputs_outputs_ws": int(peak_alloc - io_alloc),
                        "csc_index": 4 * (N + 1 + E),
                        "conventional_edge_weights": 4 * E * plan.w_numel // plan.num_basis},
-        "roofline": roof,
-        "kernels": kernels,
+        "roofline": roof, "kernels": kernels,
         "setup_s": {"inputs": round(t_gen, 2), "graph_prepare": round(t_prep, 4)},
+    })
+    return rep, (w, data)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="edge_scaling")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-all-configs", action="store_true", help="time the headline workload only")
+    ap.add_argument("--cpu-sample-edges", type=int, default=0, help="oracle sample size (edges); 0 = default")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single "
+              "MI355X; sharding over several GPUs is not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    head, oracle_inputs = run_workload(args.workload, args.steps, args.warmup, detail=True)
+    per_config = {}
+    if not args.no_all_configs:
+        for name in CONFIG_ORDER:
+            if name == args.workload:
+                per_config[name] = {k: head[k] for k in ("num_edges", "step", "ms_per_step", "edges_per_s",
+                                                         "passes")}
+                continue
+            torch.cuda.empty_cache()
+            rep, _ = run_workload(name, max(5, args.steps // 2), 2, detail=False)
+            per_config[name] = {k: rep[k] for k in ("num_edges", "step", "ms_per_step", "edges_per_s", "passes")}
+            print(f"[bench] {name}: {rep['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+
+    res = {
+        "metric": METRIC,
+        "value": round(head["value"], 1),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        "passes": head["passes"],
+        "peak_bytes": head["peak_bytes"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "setup_s": head["setup_s"],
+        "per_config": per_config,
     }
     if not args.no_cpu_baseline:
+        w, data = oracle_inputs
         # about 10-30 s of oracle work on the host cores
         sample = args.cpu_sample_edges or {"tiny": 512, "molecular": 80000, "wide_l": 4000,
                                            "edge_scaling": 80000, "force": 2000,
                                            "molecular_uvu": 120000}[w.name]
-        res["cpu_baseline"] = cpu_baseline(w.name, w, data, plan, sample)
+        res["cpu_baseline"] = cpu_baseline(w, data, sample)
     print(json.dumps(res), flush=True)
 
 

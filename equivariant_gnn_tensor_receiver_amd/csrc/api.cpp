@@ -291,7 +291,9 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
   int64_t part = 0;
   for (const auto& g : groups) {
     const int npg = (int)g.paths.size();
-    if (npg == 0 && (kind == kGemmGs || kind == kGemmGw)) continue;
+    // A group that no path reaches has an empty reduction (out, g_x: its rows
+    // are zero-filled by run_gemm) or no columns (gS, gW): never launched.
+    if (npg == 0) continue;
     GemmGroup G{};
     const int n = 2 * g.l + 1;
     G.n = n;
@@ -324,6 +326,15 @@ void set_vec(const Plan& p, GemmArgs& a) {
 
 tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, const float* feat,
                        const void* W, float* out, int splits, hipStream_t s) {
+  if (kind == kGemmOut || kind == kGemmGx) {  // rows of irreps that no path reaches are zero
+    const bool in_side = kind == kGemmGx;
+    for (const auto& g : in_side ? p.in_groups : p.out_groups) {
+      if (!g.paths.empty()) continue;
+      const hipError_t e = launch_zero_rows(out, N, in_side ? p.D_in : p.D_out, in_side ? p.C_in : p.C_out,
+                                            g.row_off, 2 * g.l + 1, s);
+      if (e != hipSuccess) return dev(e);
+    }
+  }
   GemmArgs a;
   gemm_setup(p, kind, N, a, splits);
   a.state = state;

@@ -448,6 +448,15 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
   if (i < n) p[i] = v;
 }
 
+// The nrows * C floats of rows row_off.. of a node are contiguous.
+__global__ void zero_rows_kernel(float* base, int64_t N, int D, int C, int row_off, int nrows) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)nrows * C;
+  if (i >= N * per) return;
+  const int64_t node = i / per, r = i - node * per;
+  base[(node * D + row_off) * C + r] = 0.f;
+}
+
 // Tile of one wave: MT 32-row tiles x NT 32-column tiles.  A value loaded
 // for the B operand then serves MT matrix-core products and a row value NT;
 // since these products have few columns, the B operand (read from L2 by every
@@ -507,7 +516,7 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   {
     int64_t t2 = 0;
     for (int g = 0; g < a.ngroups; ++g)
-      if (a.g[g].M > 0 && a.g[g].N > 0)
+      if (a.g[g].M > 0 && a.g[g].N > 0 && a.g[g].Kr > 0)
         t2 += (int64_t)ceil_div(a.g[g].M, 32 * sh.mt) * ceil_div(a.g[g].N, 32 * sh.nt);
     if (!(kind == kGemmGw || max_cols > 32) || t2 * splits * kMaxWaveSplit < kFillWaves)
       sh = gemm_shape(kind, max_cols, false, a.C_out);
@@ -516,7 +525,7 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   for (int g = 0; g < a.ngroups; ++g) {
     GemmGroup& G = a.g[g];
     G.tiles_n = G.N > 0 ? ceil_div(G.N, 32 * sh.nt) : 0;
-    G.tiles = (G.M > 0 && G.N > 0) ? ceil_div(G.M, 32 * sh.mt) * G.tiles_n : 0;
+    G.tiles = (G.M > 0 && G.N > 0 && G.Kr > 0) ? ceil_div(G.M, 32 * sh.mt) * G.tiles_n : 0;
     G.tile_begin = (int32_t)total;
     total += G.tiles;
     if (G.tiles > 0 && G.Kr > max_kr) max_kr = G.Kr;
@@ -546,6 +555,16 @@ hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s) {
   if (total <= 0) return hipSuccess;
   TimingScope ts(kcGwReduce, s);
   hipLaunchKernelGGL(gw_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s) {
+  const int64_t n = N * nrows * (int64_t)C;
+  if (n <= 0) return hipSuccess;
+  if (row_off < 0 || nrows < 0 || row_off + nrows > D) return hipErrorInvalidValue;
+  TimingScope ts(kcFill, s);
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, base, N, D, C, row_off,
+                     nrows);
   return hipGetLastError();
 }
 

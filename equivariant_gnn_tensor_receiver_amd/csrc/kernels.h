@@ -145,7 +145,8 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s);
 // Wave tiles of a C[M][N] product of the given kind (the tile shape launch_gemm uses).
 int64_t gemm_wave_tiles(int kind, int M, int N, int max_cols);
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
-hipError_t launch_zero_rows(float* base, int64_t N, int rows, int C, int row_off, int nrows, hipStream_t s);
+// Zeroes rows [row_off, row_off + nrows) of every node of a [N][D][C] tensor.
+hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_cw_contract(const CwArgs& a, hipStream_t s);
 hipError_t launch_cw_gw(const CwArgs& a, hipStream_t s);

@@ -160,8 +160,10 @@ def make_graph(w: Workload):
 
 
 def make_tensors(rng, num_nodes, rows_in, c_in, rows_out, c_out, num_basis, num_paths, dtype="f32",
-                 channelwise=False):
-    """x [N,rows_in,c_in], W [K,P,c_in,c_out] (or [K,P,c_in] channel-wise), g_out [N,rows_out,c_out], gg_pos [N,3]."""
+                 channelwise=False, w_dtype=None):
+    """x [N,rows_in,c_in], W [K,P,c_in,c_out] (or [K,P,c_in] channel-wise), g_out [N,rows_out,c_out], gg_pos [N,3].
+
+    `dtype` is the storage type of x and, unless `w_dtype` is given, of W."""
     x = rng.standard_normal((num_nodes, rows_in, c_in), dtype=np.float32)
     if channelwise:
         W = (rng.standard_normal((num_basis, num_paths, c_in), dtype=np.float32)
@@ -173,6 +175,7 @@ def make_tensors(rng, num_nodes, rows_in, c_in, rows_out, c_out, num_basis, num_
     gg_pos = rng.standard_normal((num_nodes, 3), dtype=np.float32)
     if dtype == "bf16":
         x = bf16_round(x)
+    if (dtype if w_dtype is None else w_dtype) == "bf16":
         W = bf16_round(W)
     return dict(x=x, W=W.astype(np.float32), g_out=g_out, gg_pos=gg_pos)
 

@@ -173,13 +173,71 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _require(t, name, dtype, numel, device, min_bytes=None):
+    """Reject a tensor the kernels would misread: wrong dtype, not contiguous,
+    too few elements or on another device (None is passed through)."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, at least {min_bytes} needed")
+
+
+def _feature_dtype(code):
+    import torch
+
+    return torch.bfloat16 if code == TPCONV_BF16 else torch.float32
+
+
+def _check_inputs(plan, graph, pos, x, W, **more):
+    """Checks shared by the passes: graph index tensors, pos, x, W, and the
+    named fp32 node tensors in `more` (name -> (tensor, rows, channels))."""
+    import torch
+
+    dev = pos.device
+    N = graph.num_nodes
+    _require(graph.rowptr, "rowptr", torch.int32, N + 1, dev)
+    _require(graph.senders, "senders", torch.int32, None, dev)
+    if graph.senders.numel() < graph.num_edges:
+        raise ValueError("senders: fewer entries than num_edges")
+    _require(pos, "pos", torch.float32, 3 * N, dev)
+    _require(x, "x", _feature_dtype(plan.x_dtype), N * plan.rows_in * plan.ch_in, dev)
+    _require(W, "W", _feature_dtype(plan.w_dtype), plan.w_numel, dev)
+    for name, (t, rows, ch) in more.items():
+        _require(t, name, torch.float32, N * rows * ch, dev)
+
+
+def _keep_for_stream(stream, *tensors):
+    """Tensors allocated here but used on a stream other than the current one
+    must not be reused by the caching allocator before that stream is done."""
+    import torch
+
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def tpconv_graph_prepare(plan: Plan, graph: Graph, validate: bool = True, stream=None) -> Graph:
     import torch
 
     dev = graph.rowptr.device
+    _require(graph.rowptr, "rowptr", torch.int32, graph.num_nodes + 1, dev)
+    _require(graph.senders, "senders", torch.int32, None, dev)
+    if graph.senders.numel() < graph.num_edges:
+        raise ValueError("senders: fewer entries than num_edges")
     colptr = torch.empty(graph.num_nodes + 1, dtype=torch.int32, device=dev)
     recv = torch.empty(max(graph.num_edges, 1), dtype=torch.int32, device=dev)
     ws = _workspace(plan.workspace_size(OP_GRAPH_PREPARE, graph.num_nodes, graph.num_edges), dev)
+    _keep_for_stream(stream, colptr, recv, ws)
     g = graph.c()
     _check(_lib().tpconv_graph_prepare(plan.handle, ctypes.byref(g), _ptr(colptr), _ptr(recv), int(validate),
                                        _ptr(ws), ws.numel(), _stream(stream)), "tpconv_graph_prepare")
@@ -190,12 +248,18 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
     import torch
 
     dev = pos.device
+    N = graph.num_nodes
     if out is None:
-        out = torch.empty((graph.num_nodes, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev)
+        out = torch.empty((N, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev)
+        _keep_for_stream(stream, out)
+    _check_inputs(plan, graph, pos, x, W, out=(out, plan.rows_out, plan.ch_out))
+    _require(saved_state, "saved_state", torch.float32, plan.state_size(N) // 4, dev)
     if workspace is None and saved_state is None:
-        workspace = _workspace(plan.workspace_size(OP_FORWARD, graph.num_nodes, graph.num_edges), dev)
+        workspace = _workspace(plan.workspace_size(OP_FORWARD, N, graph.num_edges), dev)
+        _keep_for_stream(stream, workspace)
+    _require(workspace, "workspace", None, None, dev)
     g = graph.c()
-    nbytes = 0 if workspace is None else workspace.numel()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().tpconv_forward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(out),
                                  _ptr(saved_state), _ptr(workspace), nbytes, _stream(stream)), "tpconv_forward")
     return out
@@ -213,12 +277,19 @@ def tpconv_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, saved_state=N
         grad_W = torch.empty(plan.w_shape, dtype=torch.float32, device=dev)
     if grad_pos is None and "pos" in want:
         grad_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
+    _keep_for_stream(stream, grad_x, grad_W, grad_pos)
+    _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.rows_out, plan.ch_out),
+                  grad_x=(grad_x, plan.rows_in, plan.ch_in), grad_pos=(grad_pos, 1, 3))
+    _require(grad_W, "grad_W", torch.float32, plan.w_numel, dev)
+    _require(saved_state, "saved_state", torch.float32, plan.state_size(N) // 4, dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_BACKWARD, N, graph.num_edges), dev)
+        _keep_for_stream(stream, workspace)
+    _require(workspace, "workspace", None, None, dev)
     g = graph.c()
     _check(_lib().tpconv_backward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(grad_out),
                                   _ptr(saved_state), _ptr(grad_x), _ptr(grad_W), _ptr(grad_pos), _ptr(workspace),
-                                  workspace.numel(), _stream(stream)), "tpconv_backward")
+                                  workspace.numel() * workspace.element_size(), _stream(stream)), "tpconv_backward")
     return grad_x, grad_W, grad_pos
 
 
@@ -234,12 +305,19 @@ def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos
         d_x = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev)
     if d_grad_out is None and "grad_out" in want:
         d_grad_out = torch.empty((N, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev)
+    _keep_for_stream(stream, d_W, d_x, d_grad_out)
+    _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.rows_out, plan.ch_out), gg_pos=(gg_pos, 1, 3),
+                  d_x=(d_x, plan.rows_in, plan.ch_in), d_grad_out=(d_grad_out, plan.rows_out, plan.ch_out))
+    _require(d_W, "d_W", torch.float32, plan.w_numel, dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_DOUBLE_BACKWARD, N, graph.num_edges), dev)
+        _keep_for_stream(stream, workspace)
+    _require(workspace, "workspace", None, None, dev)
     g = graph.c()
     _check(_lib().tpconv_double_backward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W),
                                          _ptr(grad_out), _ptr(gg_pos), _ptr(d_W), _ptr(d_x), _ptr(d_grad_out),
-                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)),
            "tpconv_double_backward")
     return d_W, d_x, d_grad_out
 

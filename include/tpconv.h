@@ -137,10 +137,15 @@ tpconv_status tpconv_plan_path(tpconv_plan plan, int32_t path, int32_t* l123, in
 tpconv_status tpconv_plan_cg(tpconv_plan plan, int32_t path, double* out);
 
 /* Bytes of caller-provided device workspace an operation needs for N nodes and
- * E edges.  For FORWARD, BACKWARD and DOUBLE_BACKWARD the size does not depend
- * on E (bounded receiver state, O(N)); GRAPH_PREPARE needs O(E) int32 scratch
- * for the sender sort.  FORWARD's figure assumes saved_state == NULL (0 is
- * returned for the in-place-state case via tpconv_state_size). */
+ * E edges ("Sobek" page, abstract: edge-local products go straight into a
+ * receiver-side state of bounded size, so the tensor-product workspace does
+ * not grow with the edge count).  For FORWARD, BACKWARD and DOUBLE_BACKWARD the
+ * size does not depend on E: it holds node-sized states (S, its cotangent, the
+ * sender state T) and the fixed-count partial sums of the weight gradient.
+ * GRAPH_PREPARE needs O(E) int32 scratch for the sender sort (index
+ * metadata, not tensor-product workspace).  FORWARD's figure assumes
+ * saved_state == NULL; with a saved state the forward needs none.
+ * Errors: INVALID_VALUE (null plan or bytes, negative sizes, unknown op). */
 tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t num_nodes,
                                     int64_t num_edges, size_t* bytes);
 
@@ -149,7 +154,13 @@ tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t num_no
 tpconv_status tpconv_state_size(tpconv_plan plan, int64_t num_nodes, size_t* bytes);
 
 /* Build the sender-sorted view of the receiver-sorted graph (stable: for each
- * sender, receivers in increasing edge order).  g->rowptr, g->senders are read;
+ * sender, receivers in increasing edge order).  The pages say nothing about how
+ * the backward reaches the senders; the reading taken here is that the
+ * sender-side passes (grad_x, and d_x of the double backward) stream the same
+ * edges grouped by sender, the mirror of the receiver-side schedule ("Sobek"
+ * page, abstract: the streaming form extends through the backward and double
+ * backward), so they too accumulate into node-sized state without atomics.
+ * g->rowptr, g->senders are read;
  * csc_colptr [N+1] and csc_receivers [E] are written (device).  With
  * validate != 0 the CSR is first checked on the device (rowptr[0] = 0,
  * non-decreasing, rowptr[N] = E, 0 <= sender < N); this synchronises the
@@ -167,7 +178,10 @@ tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const floa
                              const void* x, const void* W, float* out, float* saved_state,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of <grad_out, out>: grad_x [N][rows_in][C_in], grad_W [K][P][C_in][C_out],
+/* Backward ("Sobek" page, abstract: the streaming formulation covers the
+ * backward pass; the same receiver-side schedule, with no per-edge adjoint
+ * stored).  Gradients of <grad_out, out>: grad_x [N][rows_in][C_in],
+ * grad_W [K][P][C_in][C_out],
  * grad_pos [N][3]; each may be NULL to skip it (at least one must be given).
  * saved_state: S from tpconv_forward with the same inputs, or NULL to recompute it.
  * Needs g->csc_colptr / csc_receivers when grad_x is requested.  grad_pos sums
@@ -179,7 +193,9 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
                               float* grad_pos, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Double backward of the scalar force loss L = sum_n <gg_pos[n], grad_pos[n]>,
+/* Double backward ("Sobek" page, abstract: the streaming formulation covers the
+ * double backward; tangent states are node-sized like S and T) of the scalar
+ * force loss L = sum_n <gg_pos[n], grad_pos[n]>,
  * where grad_pos is the backward above for the given grad_out:
  *   d_W = dL/dW, d_x = dL/dx, d_grad_out = dL/dgrad_out (each may be NULL).
  * With phi_e = gg_pos[s] - gg_pos[v], L is the derivative of the edge

@@ -37,19 +37,21 @@ class DeviceCase:
     """Seeded problem uploaded to cuda:0 plus the matching oracle Problem."""
 
     def __init__(self, irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype="f32",
-                 channelwise=False):
+                 channelwise=False, w_dtype=None, env_p=6):
         import torch
 
         self.dev = torch.device("cuda:0")
+        w_dtype = dtype if w_dtype is None else w_dtype
         xd = tp.TPCONV_BF16 if dtype == "bf16" else tp.TPCONV_F32
+        wd = tp.TPCONV_BF16 if w_dtype == "bf16" else tp.TPCONV_F32
         conn = tp.CHANNELWISE if channelwise else tp.FULLY_CONNECTED
-        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, 6, xd, xd, conn)
-        self.prob = otp.Problem(irreps_in, irreps_out, sh_lmax, K, channelwise=channelwise)
+        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, env_p, xd, wd, conn)
+        self.prob = otp.Problem(irreps_in, irreps_out, sh_lmax, K, envelope_p=env_p, channelwise=channelwise)
         assert self.plan.num_paths == self.prob.P
         assert tuple(self.plan.w_shape) == tuple(self.prob.w_shape)
         N = len(rowptr) - 1
         t = inputs.make_tensors(rng, N, self.prob.D_in, self.prob.C_in, self.prob.D_out, self.prob.C_out, K,
-                                self.prob.P, dtype, channelwise=channelwise)
+                                self.prob.P, dtype, channelwise=channelwise, w_dtype=w_dtype)
         self.np = dict(pos=pos, rowptr=rowptr, senders=senders, **t)
         self.receivers = otp.csr_receivers(rowptr)
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
@@ -57,12 +59,8 @@ class DeviceCase:
         self.rowptr = to(rowptr.astype(np.int32))
         self.senders = to(senders.astype(np.int32)) if len(senders) else torch.zeros(1, dtype=torch.int32,
                                                                                       device=self.dev)
-        if dtype == "bf16":
-            self.x = tp.to_device_bf16(t["x"], self.dev)
-            self.W = tp.to_device_bf16(t["W"], self.dev)
-        else:
-            self.x = to(t["x"])
-            self.W = to(t["W"])
+        self.x = tp.to_device_bf16(t["x"], self.dev) if dtype == "bf16" else to(t["x"])
+        self.W = tp.to_device_bf16(t["W"], self.dev) if w_dtype == "bf16" else to(t["W"])
         self.g_out = to(t["g_out"])
         self.gg = to(t["gg_pos"])
         g = tp.Graph(self.rowptr, self.senders)
@@ -112,9 +110,11 @@ class DeviceCase:
         return otp.double_backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"])
 
 
-def small_case(irreps_in, irreps_out, sh_lmax, K, N, deg, seed, dtype="f32", channelwise=False):
+def small_case(irreps_in, irreps_out, sh_lmax, K, N, deg, seed, dtype="f32", channelwise=False, w_dtype=None,
+               env_p=6):
     pos, rowptr, senders, rng = inputs.random_graph(N, deg, seed)
-    return DeviceCase(irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype, channelwise)
+    return DeviceCase(irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype, channelwise, w_dtype,
+                      env_p)
 
 
 def workload_case(name):

@@ -23,6 +23,9 @@ CASES = [
     ("cw_l3_c16_bf16", "16x0e+16x1o+16x2e+16x3o", "16x0e+16x1o+16x2e+16x3o", 3, 8, 60, 14, "bf16"),
     ("cw_mixed", "8x0e+8x1o+8x1e+8x2e", "8x0e+8x0o+8x1o+8x1e+8x2e+8x3o", 2, 8, 50, 12, "f32"),
     ("cw_c3_k16", "3x0e+3x1o+3x2e", "3x0e+3x1o+3x2e", 2, 16, 40, 90, "f32"),
+    ("cw_l3_k16", "16x0e+16x1o+16x2e+16x3o", "16x0e+16x1o+16x2e+16x3o", 3, 16, 30, 40, "f32"),
+    # an output irrep (2o) that no path reaches and an input irrep (3o) that reaches nothing
+    ("cw_no_path_groups", "8x0e+8x1o+8x3o", "8x0e+8x1o+8x2o", 1, 8, 50, 12, "f32"),
 ]
 
 

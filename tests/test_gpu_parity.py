@@ -14,24 +14,41 @@ from equivariant_gnn_tensor_receiver_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
+L3 = "16x0e+16x1o+16x2e+16x3o"
 SMALL = [
-    # name, irreps_in, irreps_out, sh_lmax, K, N, deg, dtype
+    # name, irreps_in, irreps_out, sh_lmax, K, N, deg, x dtype[, options]
     ("l1_c8", "8x0e+8x1o", "8x0e+8x1o", 1, 8, 60, 12, "f32"),
     ("l2_c32", "32x0e+32x1o+32x2e", "32x0e+32x1o+32x2e", 2, 8, 150, 20, "f32"),
     ("l2_c128_k16", "128x0e+128x1o+128x2e", "128x0e+128x1o+128x2e", 2, 16, 40, 14, "f32"),
-    ("l3_c16_bf16", "16x0e+16x1o+16x2e+16x3o", "16x0e+16x1o+16x2e+16x3o", 3, 8, 60, 14, "bf16"),
+    ("l3_c16_bf16", L3, L3, 3, 8, 60, 14, "bf16"),
     ("l3_c64_bf16", "64x0e+64x1o+64x2e+64x3o", "64x0e+64x1o+64x2e+64x3o", 3, 8, 30, 10, "bf16"),
     ("mixed_cin_ne_cout", "16x0e+16x1o+16x1e+16x2e", "8x0e+8x0o+8x1o+8x1e+8x2e+8x3o", 2, 8, 50, 12, "f32"),
     ("c3_odd_channels", "3x0e+3x1o+3x2e", "5x0e+5x1o", 2, 16, 40, 90, "f32"),
     ("scalar_only", "24x0e", "40x0e", 0, 8, 70, 10, "f32"),
+    # every (lmax, K) instantiation the plan accepts
+    ("l0_k16", "16x0e", "16x0e", 0, 16, 60, 12, "f32"),
+    ("l1_k16", "16x0e+16x1o", "16x0e+16x1o", 1, 16, 60, 14, "f32"),
+    ("l3_k16", L3, L3, 3, 16, 40, 40, "f32"),
+    ("l3_k16_bf16", L3, L3, 3, 16, 30, 70, "bf16"),
+    # x and W of different storage types
+    ("l2_x_bf16_w_f32", "32x0e+32x1o+32x2e", "32x0e+32x1o+32x2e", 2, 8, 60, 16, "bf16", dict(w_dtype="f32")),
+    ("l2_x_f32_w_bf16", "32x0e+32x1o+32x2e", "32x0e+32x1o+32x2e", 2, 8, 60, 16, "f32", dict(w_dtype="bf16")),
+    # envelope exponents other than 6
+    ("l2_env_p3", "8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8, 60, 14, "f32", dict(env_p=3)),
+    ("l1_env_p11_k16", "16x0e+16x1o", "16x0e+16x1o", 1, 16, 60, 14, "f32", dict(env_p=11)),
+    # an output irrep (2o) that no path reaches and an input irrep (3o) that reaches nothing
+    ("no_path_groups_c8", "8x0e+8x1o+8x3o", "8x0e+8x1o+8x2o", 1, 8, 50, 12, "f32"),
+    ("no_path_groups_c16", "16x0e+16x1o+16x3o", "16x2o+16x0e+16x1o", 1, 8, 50, 12, "f32"),
 ]
 
 
 @pytest.fixture(scope="module", params=SMALL, ids=[c[0] for c in SMALL])
 def case(request):
-    name, ii, io, lsh, K, N, deg, dt = request.param
-    say(f"[case] {name}: N={N} deg~{deg} irreps_in={ii} irreps_out={io} lsh={lsh} K={K} {dt}")
-    return DeviceCase(ii, io, lsh, K, *inputs.random_graph(N, deg, seed=zlib.crc32(name.encode()) % 1000), dtype=dt)
+    name, ii, io, lsh, K, N, deg, dt, *opt = request.param
+    opt = opt[0] if opt else {}
+    say(f"[case] {name}: N={N} deg~{deg} irreps_in={ii} irreps_out={io} lsh={lsh} K={K} {dt} {opt}")
+    return DeviceCase(ii, io, lsh, K, *inputs.random_graph(N, deg, seed=zlib.crc32(name.encode()) % 1000), dtype=dt,
+                      **opt)
 
 
 def test_forward(case):

@@ -70,14 +70,52 @@ def test_sh_zero_vector():
     assert np.all(sh.sh_jacobian(3, np.zeros((2, 3))) == 0)
 
 
+def _envelope_from_conditions(x, p):
+    """u(x) = 1 + a x^p + b x^(p+1) + c x^(p+2) with u(1) = u'(1) = u''(1) = 0,
+    the coefficients solved here from those three conditions (not read from
+    the oracle), so this is an independent statement of the cutoff polynomial."""
+    A = np.array([[1.0, 1.0, 1.0],
+                  [p, p + 1.0, p + 2.0],
+                  [p * (p - 1.0), (p + 1.0) * p, (p + 2.0) * (p + 1.0)]])
+    a, b, c = np.linalg.solve(A, np.array([-1.0, 0.0, 0.0]))
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x < 1.0, 1.0 + a * x ** p + b * x ** (p + 1) + c * x ** (p + 2), 0.0)
+
+
+@pytest.mark.parametrize("p", [2, 3, 6, 9])
+def test_envelope_matches_boundary_conditions(p):
+    xs = np.linspace(0.0, 1.2, 61)
+    assert np.abs(radial.envelope(xs, p) - _envelope_from_conditions(xs, p)).max() < 1e-12
+
+
+@pytest.mark.parametrize("p", [3, 6, 8])
+def test_bessel_radial_interior_values(p):
+    # R_k(d) = sqrt(2/c) sin(k pi d / c) / d * u(d / c), with sin(t)/t = j0(t):
+    # sin(k pi d / c) / d = (k pi / c) j0(k pi d / c).  A radial basis whose
+    # envelope were taken at d instead of d / c, or with the wrong prefactor or
+    # frequency, fails this.
+    c, K = 5.0, 16
+    rng = np.random.default_rng(4)
+    d = np.concatenate([rng.uniform(0.01, c, 50), [0.3, 2.5, 4.99]])
+    k = np.arange(1, K + 1)
+    w = k * math.pi / c
+    want = (math.sqrt(2.0 / c) * w[None, :] * special.spherical_jn(0, w[None, :] * d[:, None])
+            * _envelope_from_conditions(d / c, p)[:, None])
+    got = radial.bessel_radial(d, K, c, p)
+    assert np.abs(got - want).max() < 1e-12
+
+
 def test_bessel_orthonormal():
-    c = 5.0
-    for n in range(1, 6):
-        for m in range(1, 6):
-            f = lambda d: (math.sqrt(2 / c) * math.sin(n * math.pi * d / c) / d
-                           * math.sqrt(2 / c) * math.sin(m * math.pi * d / c) / d * d * d)
-            val, _ = integrate.quad(f, 1e-12, c, limit=200)
-            assert val == pytest.approx(float(n == m), abs=1e-10)
+    # the oracle's own basis with its envelope divided out is orthonormal under
+    # the d^2 dd measure on [0, c]
+    c, K = 5.0, 6
+    for n in range(1, K + 1):
+        for m in range(n, K + 1):
+            def f(d):
+                R = radial.bessel_radial(np.array([d]), K, c)[0] / radial.envelope(np.array(d / c))
+                return R[n - 1] * R[m - 1] * d * d
+            val, _ = integrate.quad(f, 1e-9, c * (1 - 1e-12), limit=200)
+            assert val == pytest.approx(float(n == m), abs=1e-9)
 
 
 def test_envelope_boundary_and_derivative():
