@@ -464,6 +464,7 @@ const char* tpconv_status_string(tpconv_status st) {
     case TPCONV_ERROR_WORKSPACE: return "workspace missing or too small";
     case TPCONV_ERROR_UNSUPPORTED: return "unsupported configuration";
     case TPCONV_ERROR_DEVICE: return "device error";
+    case TPCONV_ERROR_SCRATCH: return "problem needs more than the library's static scratch (64 MiB)";
   }
   return "unknown status";
 }

@@ -21,12 +21,13 @@ TPCONV_F32, TPCONV_BF16 = 0, 1
 FULLY_CONNECTED, CHANNELWISE = 0, 1  # tpconv_connection
 OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_GRAPH_PREPARE = 0, 1, 2, 3
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "IRREPS", 3: "GRAPH", 4: "WORKSPACE", 5: "UNSUPPORTED",
-          6: "DEVICE"}
+          6: "DEVICE", 7: "SCRATCH"}
+STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("tpconv_plan_create", "tpconv_plan_destroy", "tpconv_plan_info", "tpconv_plan_path",
            "tpconv_plan_cg", "tpconv_workspace_size", "tpconv_state_size", "tpconv_graph_prepare",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string",
-           "tpconv_kernel_timing", "tpconv_kernel_timing_read")
+           "tpconv_kernel_timing", "tpconv_kernel_timing_read", "tpconv_forward_static")
 KERNELS = ("stream_fwd", "stream_jvp", "stream_snd", "stream_sndt", "stream_bwdpos", "gemm_out", "gemm_gs",
            "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce")
 
@@ -68,6 +69,7 @@ def _lib():
         L.tpconv_state_size.argtypes = [P, c_int64, POINTER(c_size_t)]
         L.tpconv_graph_prepare.argtypes = [P, POINTER(TpconvGraph), P, P, c_int32, P, c_size_t, P]
         L.tpconv_forward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, c_size_t, P]
+        L.tpconv_forward_static.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P]
         L.tpconv_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
         L.tpconv_double_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
         L.tpconv_kernel_timing.argtypes = [c_int32]
@@ -262,6 +264,16 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().tpconv_forward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(out),
                                  _ptr(saved_state), _ptr(workspace), nbytes, _stream(stream)), "tpconv_forward")
+    return out
+
+
+def tpconv_forward_static(plan: Plan, graph: Graph, pos, x, W, out, stream=None):
+    """tpconv_forward with the receiver state in the library's static device
+    scratch: no workspace, nothing allocated (`out` must be given)."""
+    _check_inputs(plan, graph, pos, x, W, out=(out, plan.rows_out, plan.ch_out))
+    g = graph.c()
+    _check(_lib().tpconv_forward_static(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(out),
+                                        _stream(stream)), "tpconv_forward_static")
     return out
 
 

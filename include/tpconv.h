@@ -67,8 +67,12 @@ typedef enum {
   TPCONV_ERROR_GRAPH = 3,         /* CSR fails validation (tpconv_graph_prepare, validate=1) */
   TPCONV_ERROR_WORKSPACE = 4,     /* workspace pointer null or smaller than required */
   TPCONV_ERROR_UNSUPPORTED = 5,   /* valid request the library does not implement */
-  TPCONV_ERROR_DEVICE = 6         /* HIP runtime or launch failure */
+  TPCONV_ERROR_DEVICE = 6,        /* HIP runtime or launch failure */
+  TPCONV_ERROR_SCRATCH = 7        /* tpconv_forward_static: the problem needs more than the static scratch */
 } tpconv_status;
+
+/* Size of the per-device static scratch array behind tpconv_forward_static. */
+#define TPCONV_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum { TPCONV_F32 = 0, TPCONV_BF16 = 1 } tpconv_dtype;
 
@@ -206,6 +210,22 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
                                      const float* gg_pos, float* d_W, float* d_x,
                                      float* d_grad_out, void* workspace, size_t workspace_bytes,
                                      void* stream);
+
+/* tpconv_forward without workspace and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP stream capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The receiver state S is
+ * kept in a file-scope device array of TPCONV_STATIC_SCRATCH_BYTES (64 MiB)
+ * that every GPU the library runs on holds until the process ends; it fits
+ * problems whose tpconv_workspace_size(FORWARD) is at most that size (for
+ * example N <= 1872 nodes at 32 channels of 0e+1o+2e with K = 8, 35 KiB of
+ * state per node, or N <= 32768 at 8 channels of 0e+1o, 2 KiB).  Larger
+ * problems return TPCONV_ERROR_SCRATCH before any launch.  The array is looked
+ * up on the first call on each device (the call then needs that device
+ * current).  Same arguments, results and errors as tpconv_forward otherwise.
+ * All calls on one GPU share the array: calls that overlap in time on one GPU
+ * (several streams or threads) race and must be serialised by the caller. */
+tpconv_status tpconv_forward_static(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                                    const void* W, float* out, void* stream);
 
 /* Kernel classes for tpconv_kernel_timing_read. */
 typedef enum {
