@@ -34,15 +34,17 @@ HIP_FLAGS = [
 STREAM_VARIANTS = [
     ("fwd_f32", "kFwd", "float"), ("fwd_bf16", "kFwd", "uint16_t"),
     ("jvp_f32", "kJvp", "float"), ("jvp_bf16", "kJvp", "uint16_t"),
-    ("bpos_f32", "kBwdPos", "float"), ("bpos_bf16", "kBwdPos", "uint16_t"),
     ("snd_f32", "kSnd", "float"), ("sndt_f32", "kSndT", "float"),
 ]
+POS_VARIANTS = [("bpos_f32", "float"), ("bpos_bf16", "uint16_t")]
 # The edge streams keep their 4x4 outer-product accumulators in ordinary VGPRs
 # (the accumulation registers would otherwise be copied back and forth).
 STREAM_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 UNITS = ([(f"stream_{n}", "stream_inst.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f"-DTP_FT={t}",
                                                             f"-DTP_LAUNCHER=launch_stream_{n}"])
           for n, m, t in STREAM_VARIANTS]
+         + [(f"stream_{n}", "stream_pos.hip", STREAM_FLAGS + [f"-DTP_FT={t}", f"-DTP_LAUNCHER=launch_stream_{n}"])
+            for n, t in POS_VARIANTS]
          + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("channelwise", ".hip"), ("graph", ".hip"),
                                              ("scratch", ".hip"), ("api", ".cpp"),
                                              ("stream_dispatch", ".cpp"), ("plan", ".cpp"),

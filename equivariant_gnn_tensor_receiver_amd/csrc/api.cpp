@@ -101,10 +101,15 @@ size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
   return have_saved ? 0 : align_up(state_in_elems(p, N) * 4);
 }
 
+// bf16 hi and lo planes of fp32 input features (the position-gradient stream's gathers)
+size_t split_elems(const Plan& p, int64_t N) {
+  return p.x_dtype == TPCONV_F32 ? (size_t)N * p.D_in * p.C_in : 0;
+}
+
 size_t ws_backward(const Plan& p, int64_t N) {
-  // S (recomputed when not saved), gS (fully connected only), T, gW partials
+  // S (recomputed when not saved), gS (fully connected only), T, gW partials, split x
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4);
+         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
@@ -618,6 +623,9 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
   float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
   float* T = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
+  const size_t nsplit = split_elems(p, N);
+  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
+  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
 
   const float* S = saved_state;
   if (grad_W && !S) {  // recompute the receiver state for the weight gradient
@@ -649,6 +657,13 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
     StreamArgs a;
     recv_args(p, a, g, pos, x);
     set_units(p, a, p.pos_units);
+    a.nslices = (p.C_in + 31) / 32;
+    if (nsplit > 0) {  // fp32 features reach the matrix cores as bf16 hi + lo
+      if ((st = dev(launch_split_bf16(static_cast<const float*>(x), xhi, xlo, (int64_t)nsplit, s))) != TPCONV_SUCCESS)
+        return st;
+      a.feat = xhi;
+      a.feat_lo = xlo;
+    }
     a.gstate = gS;
     a.gpos = grad_pos;
     if (cw) {

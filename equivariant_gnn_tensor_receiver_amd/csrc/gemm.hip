@@ -448,6 +448,21 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
   if (i < n) p[i] = v;
 }
 
+// fp32 -> bf16 hi + lo, four values per thread (n4 groups of four, then a tail).
+__global__ void split_bf16_kernel(const float* x, uint16_t* hi, uint16_t* lo, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (i + t >= n) break;
+    const float v = x[i + t];
+    const __bf16 h = (__bf16)v;
+    const __bf16 l = (__bf16)(v - (float)h);
+    hi[i + t] = __builtin_bit_cast(uint16_t, h);
+    lo[i + t] = __builtin_bit_cast(uint16_t, l);
+  }
+}
+
 // The nrows * C floats of rows row_off.. of a node are contiguous.
 __global__ void zero_rows_kernel(float* base, int64_t N, int D, int C, int row_off, int nrows) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -565,6 +580,15 @@ hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, i
   TimingScope ts(kcFill, s);
   hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, base, N, D, C, row_off,
                      nrows);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_bf16(const float* x, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  if ((threads + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;
+  TimingScope ts(kcFill, s);
+  hipLaunchKernelGGL(split_bf16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, hi, lo, n);
   return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ struct StreamArgs {
   int32_t share_geometry;  // kBwdPos: the units of a (node, tile) share one block and its batch geometry
   int32_t ct_log2;      // channel tile = 1 << ct_log2 (<= 64); edge slots per wave = 64 / tile
   int32_t ntiles;       // channels / tile
+  int32_t nslices;      // kBwdPos: 32-channel slices of the reduction
   int32_t feat_rows;    // rows per node of the gathered feature tensor
   int32_t C;            // channels of the gathered features and of the state
   int32_t env_p;
@@ -51,7 +52,8 @@ struct StreamArgs {
   const int32_t* nbr;   // [E] neighbour of each edge
   const float* pos;     // [N][3]
   const float* ggpos;   // [N][3] tangent (kJvp, kSndT)
-  const void* feat;     // [N][feat_rows][C], fp32 or bf16
+  const void* feat;     // [N][feat_rows][C], fp32 or bf16 (kBwdPos: bf16, or the hi plane of split fp32)
+  const void* feat_lo;  // kBwdPos: lo bf16 plane of fp32 features split into hi + lo (NULL: bf16 features)
   float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
   const float* gstate;  // receiver-state cotangent gS (kBwdPos, fully connected)
   float* gpos;          // position gradient, accumulated (kBwdPos)
@@ -148,6 +150,8 @@ hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 // Zeroes rows [row_off, row_off + nrows) of every node of a [N][D][C] tensor.
 hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+// hi[i] = bf16(x[i]), lo[i] = bf16(x[i] - hi[i]) (round to nearest even), as raw bf16 bits.
+hipError_t launch_split_bf16(const float* x, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s);
 hipError_t launch_cw_contract(const CwArgs& a, hipStream_t s);
 hipError_t launch_cw_gw(const CwArgs& a, hipStream_t s);
 hipError_t launch_cw_reduce(const CwArgs& a, hipStream_t s);
