@@ -39,7 +39,6 @@ struct StreamArgs {
   int32_t npaths;
   int32_t nunits;       // work units per (node, tile)
   int32_t bundled;      // units are the compile-time bundles of the natural path list
-  int32_t share_geometry;  // kBwdPos: the units of a (node, tile) share one block and its batch geometry
   int32_t ct_log2;      // channel tile = 1 << ct_log2 (<= 64); edge slots per wave = 64 / tile
   int32_t ntiles;       // channels / tile
   int32_t nslices;      // kBwdPos: 32-channel slices of the reduction

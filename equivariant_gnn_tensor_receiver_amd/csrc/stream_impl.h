@@ -182,26 +182,6 @@ __device__ __forceinline__ void channel_sum3(float (&v)[3], int ct_log2) {
   if (ct_log2 >= 6) { v[0] = half32_add(v[0]); v[1] = half32_add(v[1]); v[2] = half32_add(v[2]); }
 }
 
-// Sum over the channel quads of one edge slot (lanes with the same lane % 4
-// within the slot's CT lanes), every such lane receiving the sum.
-__device__ __forceinline__ void quad_sum3(float (&v)[3], int ct_log2) {
-  if (ct_log2 == 3) {  // two quads: partner lane ^ 4 (shift right into banks 1, 3; left into banks 0, 2)
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int x = __float_as_int(v[i]);
-      int p = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xA, false);  // row_shr:4
-      p = __builtin_amdgcn_update_dpp(p, x, 0x104, 0xF, 0x5, false);      // row_shl:4
-      v[i] += __int_as_float(p);
-    }
-  }
-  if (ct_log2 >= 4) {
-    v[0] = dpp_add<0x124>(v[0]); v[1] = dpp_add<0x124>(v[1]); v[2] = dpp_add<0x124>(v[2]);  // row_ror:4
-    v[0] = dpp_add<0x128>(v[0]); v[1] = dpp_add<0x128>(v[1]); v[2] = dpp_add<0x128>(v[2]);  // row_ror:8
-  }
-  if (ct_log2 >= 5) { v[0] = row16_add(v[0]); v[1] = row16_add(v[1]); v[2] = row16_add(v[2]); }
-  if (ct_log2 >= 6) { v[0] = half32_add(v[0]); v[1] = half32_add(v[1]); v[2] = half32_add(v[2]); }
-}
-
 // Sum over the channel lanes of one edge slot (lanes c = 0..CT-1 of a group),
 // every lane of the group receiving the sum.  After the two quad steps each
 // quad is uniform, so the half-row and row mirrors pair it with the right
@@ -235,34 +215,12 @@ struct StreamCtx {
   EdgeLds<K, LMAX, MODE, BATCH>& L;
 
   static constexpr bool RECV = ModeTraits<MODE>::recv;
-  static constexpr bool BPOS = ModeTraits<MODE>::bwdpos;
   static constexpr bool TAN = ModeTraits<MODE>::tangent;
 
   static constexpr int NSH = (LMAX + 1) * (LMAX + 1);
   // Whether the LDS geometry of the next step is held in registers: not where
   // those registers would take the kernel below two waves per SIMD.
   static constexpr bool kAccGeoAhead = !(LMAX >= 3 && K == 16 && TAN);
-  static constexpr bool kPosGeoAhead = LMAX <= 2;
-  // Whether the position stream reads an edge's Jacobian rows at the start of
-  // its step (registers held through the step) rather than at their use.
-  static constexpr bool kPosJacobianFirst = LMAX <= 2 && K == 8;
-
-  // vec += J^T gy over the harmonic degrees L2.. that a member path uses
-  // (J: the edge's Jacobian rows, in registers).
-  template <int L2, class... Ps>
-  __device__ __forceinline__ void apply_jacobian(const float (&gy)[NSH], const float (&J)[NSH][3], float (&vec)[3]) {
-    if constexpr (L2 <= LMAX) {
-      if constexpr (((Ps::l2 == L2) || ...)) {
-#pragma unroll
-        for (int i = 0; i < 2 * L2 + 1; ++i) {
-          const int row = L2 * L2 + i;
-#pragma unroll
-          for (int cc = 0; cc < 3; ++cc) vec[cc] = __builtin_fmaf(gy[row], J[row][cc], vec[cc]);
-        }
-      }
-      apply_jacobian<L2 + 1, Ps...>(gy, J, vec);
-    }
-  }
 
   // Geometry of one edge slot as the accumulating modes use it, read from LDS
   // one step ahead of its use: the matrix-core operand R[4 kq + lane % 4] (and
@@ -311,98 +269,6 @@ struct StreamCtx {
     if constexpr (sizeof...(Rest) > 0) edge<OFF + NO, TOT, NIN, Rest...>(av, g, acc);
   }
 
-  // Position gradient, one edge per lane and four channels per lane (compile-
-  // time recursion over the member paths).  xv[m][i] holds row m of the gathered
-  // block for channel c0 + i, where c0 is the first channel of the lane's quad; gs is
-  // the lane's own channel's state cotangent, the A operand of the matrix
-  // cores, and r / rd this lane's edge's R and R', the B operand.  A chain of
-  // K 4x4x1 outer products then leaves in register i of lane 4b + j
-  //   sum_k gS[k][o](channel c0 + i) * R_k(edge of lane 4b + j),
-  // i.e. sum_k R_k gS[k] for the lane's own edge and its quad's channels.
-  // Geometry of the lane's edge for one position-gradient step, read from
-  // LDS one step ahead of its use (harmonic entries that no member path reads
-  // are never loaded).
-  struct PosGeo {
-    float r[K], rd[K];
-    float y[LMAX + 1][2 * LMAX + 1];
-    int jj, sender;
-    float mask;
-  };
-
-  template <int OFF, int TOT, int NIN, class P, class... Rest>
-  __device__ __forceinline__ void pos_edge(const float (&xv)[NIN][4], const PosGeo& g, const float (&gs)[K][TOT],
-                                           float& alpha, float (&gy)[NSH]) {
-    constexpr int N2 = 2 * P::l2 + 1;
-    constexpr int NO = 2 * P::l3 + 1;
-    using Tab = CG<P::l1, P::l2, P::l3>;
-    const float(&r)[K] = g.r;
-    const float(&rd)[K] = g.rd;
-    float y[N2];
-#pragma unroll
-    for (int i = 0; i < N2; ++i) y[i] = g.y[P::l2][i];
-    // One output component o at a time, so that only its two 4-vectors are
-    // live; the quad's channels are summed before the coupling table is applied:
-    //   alpha += <U, gD>_o = sum c y[m2] p[m1],  p[m1] = sum_i x_i[m1] gD_i[o]
-    //   gy    += CG^T(x, gU)_o = sum c q[m1],     q[m1] = sum_i x_i[m1] gU_i[o]
-    // (entries of p and q that the table does not use are never formed).
-#pragma unroll
-    for (int o = 0; o < NO; ++o) {
-      floatx4 g = {0.f, 0.f, 0.f, 0.f}, gd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        g = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], r[k], g, 0, 0, 0);    // sum_k R_k gS[k]
-        gd = __builtin_amdgcn_mfma_f32_4x4x1f32(gs[k][OFF + o], rd[k], gd, 0, 0, 0);  // sum_k R'_k gS[k]
-      }
-      float p[NIN];
-#pragma unroll
-      for (int m1 = 0; m1 < NIN; ++m1) {
-        float t = xv[m1][0] * gd[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], gd[i], t);
-        p[m1] = t;
-      }
-      alpha = Tab::ydot_col(o, y, p, alpha);
-      if constexpr (P::l2 > 0) {  // Y_00 is constant
-        float q[NIN];
-#pragma unroll
-        for (int m1 = 0; m1 < NIN; ++m1) {
-          float t = xv[m1][0] * g[0];
-#pragma unroll
-          for (int i = 1; i < 4; ++i) t = __builtin_fmaf(xv[m1][i], g[i], t);
-          q[m1] = t;
-        }
-        Tab::qbar_col(o, q, gy + P::l2 * P::l2);
-      }
-    }
-    if constexpr (sizeof...(Rest) > 0) pos_edge<OFF + NO, TOT, NIN, Rest...>(xv, g, gs, alpha, gy);
-  }
-
-  // Load the receiver-state cotangent of the member paths (position gradient).
-  template <int I, int OFF, int TOT, class P, class... Rest>
-  __device__ __forceinline__ void load_gs(const StreamArgs& a, float (&gs)[K][TOT], int c) {
-    constexpr int NO = out_dim<MODE, P>();
-    const StreamPath& Q = a.paths[a.unit_paths[unit][I]];
-    if (a.cw) {  // channel-wise: gS[k][o] = W[k, path, c] grad_out[node][out_row + o][c]
-      float go[NO];
-#pragma unroll
-      for (int o = 0; o < NO; ++o) go[o] = a.gout[((int64_t)node * a.gout_rows + Q.out_row + o) * a.C + c];
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int64_t wi = ((int64_t)k * a.npaths + Q.path) * a.C + c;
-        const float w = a.w_bf16 ? load_feat(static_cast<const uint16_t*>(a.W), wi) : static_cast<const float*>(a.W)[wi];
-#pragma unroll
-        for (int o = 0; o < NO; ++o) gs[k][OFF + o] = w * go[o];
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int o = 0; o < NO; ++o)
-          gs[k][OFF + o] = a.gstate[Q.state_base + ((int64_t)(node * NO + o) * K + k) * Q.cols_per_k + Q.q * a.C + c];
-    }
-    if constexpr (sizeof...(Rest) > 0) load_gs<I + 1, OFF + NO, TOT, Rest...>(a, gs, c);
-  }
-
   // Write the member paths' slot-summed state (each entry once).
   template <int I, int OFF, int TOT, class P, class... Rest>
   __device__ __forceinline__ void store(const StreamArgs& a, const float (&v)[K * TOT], int c, bool owner) {
@@ -421,11 +287,7 @@ struct StreamCtx {
 
   template <class... Ps>
   __device__ __forceinline__ void run(const StreamArgs& a) {
-    if constexpr (BPOS) {
-      run_pos<Ps...>(a);
-    } else {
-      run_acc<Ps...>(a);
-    }
+    run_acc<Ps...>(a);
   }
 
   // Accumulating modes: lanes are (channel, edge slot); each lane gathers its
@@ -464,7 +326,6 @@ struct StreamCtx {
     for (int b0 = e0; b0 < e1; b0 += B) {
       const int nb = min(B, e1 - b0);
       __syncthreads();
-      // thread j of the block (its first wave when the block shares the batch)
       if ((int)threadIdx.x < nb) edge_prep(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, L);
       __syncthreads();
       // Branch-free edge loop: the gathers and the LDS geometry for the next
@@ -550,162 +411,6 @@ struct StreamCtx {
     store<0, 0, TOT, Ps...>(a, v, c, es == 0 && c_ok);
   }
 
-  // Position gradient: lanes are (channel quad, edge slot, edge j4 = lane % 4).
-  // Each lane takes one edge and the four channels of its quad per step (four
-  // edges per slot per step), so the K-contractions with the state cotangent
-  // become 4x4x1 outer-product chains on the matrix cores, and the per-edge
-  // vector g_r is summed over the quads of the tile.  Sender shares go out as
-  // atomic adds; the receiver's share is reduced over the wave.
-  template <class... Ps>
-  __device__ __forceinline__ void run_pos(const StreamArgs& a) {
-    using P0 = typename First<Ps...>::type;
-    constexpr int NIN = 2 * P0::l1 + 1;
-    constexpr int TOT = (out_dim<MODE, Ps>() + ...);
-    constexpr int B = BATCH;
-    const int lane = threadIdx.x & 63;
-    const int ctl = a.ct_log2;
-    const int CT = 1 << ctl;
-    const int ES = 64 >> ctl;
-    const int cl = lane & (CT - 1);
-    const int es = lane >> ctl;
-    const int j4 = lane & 3;
-    const int quad = cl >> 2;
-    const int C = a.C;
-    const int c_own = min(tile * CT + cl, C - 1);  // this lane's channel of the cotangent
-    const int c0 = tile * CT + 4 * quad;           // the quad's first channel
-    const bool vec4 = (C & 3) == 0;                 // whole quads, 16-byte aligned rows
-    const FT* feat = static_cast<const FT*>(a.feat);
-    const int64_t frow = (int64_t)a.paths[a.unit_paths[unit][0]].feat_row * C;
-
-    float gs[K][TOT];
-    load_gs<0, 0, TOT, Ps...>(a, gs, c_own);
-    float vs0 = 0.f, vs1 = 0.f, vs2 = 0.f;  // receiver share of the position gradient
-
-    const float psx = a.pos[3 * (int64_t)node], psy = a.pos[3 * (int64_t)node + 1],
-                psz = a.pos[3 * (int64_t)node + 2];
-    const int e0 = a.ptr[node], e1 = a.ptr[node + 1];
-    const int per_step = 4 * ES;
-    for (int b0 = e0; b0 < e1; b0 += B) {
-      const int nb = min(B, e1 - b0);
-      __syncthreads();
-      // thread j of the block (its first wave when the block shares the batch)
-      if ((int)threadIdx.x < nb) edge_prep(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, L);
-      __syncthreads();
-      const int last = nb - 1;
-      const int nsteps = (nb + per_step - 1) >> (8 - ctl);  // per_step = 2^(8 - ctl)
-      // The gathered block of the lane's edge for the quad's channels and the
-      // edge's LDS geometry are loaded one step ahead of their use and the
-      // neighbour index one step further (clamped edge index: unconditional
-      // loads, as in the accumulating modes; channels past C, only when C is
-      // not a multiple of 4, read as zero).
-      auto nbr_of = [&](int t) { return L.nbr[min(t * per_step + 4 * es + j4, last)]; };
-      auto gather = [&](int nbr, Quads<FT, NIN>& v) {
-        v.load(feat, (int64_t)nbr * a.feat_rows * C + frow + min(c0, C - 1), C, min(c0, C - 1), vec4);
-      };
-      auto geo = [&](int t, int nbr, PosGeo& g) {
-        const int jl = t * per_step + 4 * es + j4;
-        g.jj = min(jl, last);
-        g.sender = nbr;
-        g.mask = jl < nb ? 1.f : 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          g.r[k] = L.R[g.jj][k];
-          g.rd[k] = L.Rd[g.jj][k];
-        }
-#pragma unroll
-        for (int l = 0; l <= LMAX; ++l)
-#pragma unroll
-          for (int i = 0; i < 2 * LMAX + 1; ++i) g.y[l][i] = i <= 2 * l ? L.Y[g.jj][l][i] : 0.f;
-      };
-      auto step = [&](const Quads<FT, NIN>& raw, const PosGeo& g) {
-        float tmp[NIN][4];
-        const float(&xv)[NIN][4] = raw.get(tmp);
-        const int jj = g.jj;
-        // The Jacobian rows and r_hat are used last; where the registers allow
-        // they are read first, so that their LDS latency passes under the
-        // step's arithmetic (rows that no member path uses are never read).
-        float J[NSH][3], rh[3];
-        auto read_jacobian = [&] {
-#pragma unroll
-          for (int row = 0; row < NSH; ++row)
-#pragma unroll
-            for (int cc = 0; cc < 3; ++cc) J[row][cc] = L.J[jj][row][cc];
-#pragma unroll
-          for (int cc = 0; cc < 3; ++cc) rh[cc] = L.rhat[jj][cc];
-        };
-        if constexpr (kPosJacobianFirst) {
-          read_jacobian();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        float alpha = 0.f;
-        float gy[NSH];
-#pragma unroll
-        for (int i = 0; i < NSH; ++i) gy[i] = 0.f;
-        pos_edge<0, TOT, NIN, Ps...>(xv, g, gs, alpha, gy);
-        if constexpr (!kPosJacobianFirst) read_jacobian();
-        // this unit's share of g_r = alpha r_hat + J^T gy for the quad's channels
-        float vec[3];
-#pragma unroll
-        for (int cc = 0; cc < 3; ++cc) vec[cc] = alpha * rh[cc];
-        apply_jacobian<1, Ps...>(gy, J, vec);
-#pragma unroll
-        for (int cc = 0; cc < 3; ++cc) vec[cc] *= g.mask;
-        quad_sum3(vec, ctl);
-        if (g.mask != 0.f && quad == 0) {
-          const int64_t s3 = 3 * (int64_t)g.sender;
-          atomicAdd(&a.gpos[s3 + 0], vec[0]);
-          atomicAdd(&a.gpos[s3 + 1], vec[1]);
-          atomicAdd(&a.gpos[s3 + 2], vec[2]);
-          vs0 -= vec[0];
-          vs1 -= vec[1];
-          vs2 -= vec[2];
-        }
-      };
-      // (where the geometry registers would cost a wave of occupancy it is
-      // read at use)
-      auto run_step = [&](int t, const Quads<FT, NIN>& raw, const PosGeo& g) {
-        if constexpr (kPosGeoAhead) {
-          step(raw, g);
-        } else {
-          PosGeo gl;
-          geo(t, nbr_of(t), gl);
-          step(raw, gl);
-        }
-      };
-      Quads<FT, NIN> bA, bB;
-      PosGeo gA, gB;
-      {
-        const int n0 = nbr_of(0);
-        gather(n0, bA);
-        if constexpr (kPosGeoAhead) geo(0, n0, gA);
-      }
-      int nb1 = nbr_of(1), nb2;
-      int t = 0;
-      for (; t + 1 < nsteps; t += 2) {
-        gather(nb1, bB);
-        nb2 = nbr_of(t + 2);
-        if constexpr (kPosGeoAhead) geo(t + 1, nb1, gB);
-        __builtin_amdgcn_sched_barrier(0);
-        run_step(t, bA, gA);
-        __builtin_amdgcn_sched_barrier(0);
-        gather(nb2, bA);
-        nb1 = nbr_of(t + 3);
-        if constexpr (kPosGeoAhead) geo(t + 2, nb2, gA);
-        __builtin_amdgcn_sched_barrier(0);
-        run_step(t + 1, bB, gB);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (t < nsteps) run_step(t, bA, gA);  // an odd last step (its rows are in bA)
-    }
-    vs0 = channel_sum(vs0, 6);
-    vs1 = channel_sum(vs1, 6);
-    vs2 = channel_sum(vs2, 6);
-    if (lane == 0 && e1 > e0) {
-      atomicAdd(&a.gpos[3 * (int64_t)node + 0], vs0);
-      atomicAdd(&a.gpos[3 * (int64_t)node + 1], vs1);
-      atomicAdd(&a.gpos[3 * (int64_t)node + 2], vs2);
-    }
-  }
 };
 
 #define TPCONV_PATH_CASES(X)                                                                                  \
@@ -718,7 +423,6 @@ struct StreamCtx {
 // the first argument, at offset 0).  Naming the by-value parameter instead
 // would let the compiler copy the whole 2.7 KB block to scratch memory when
 // the inlined code reads it in many places.
-constexpr int kMaxSharedUnits = 8;  // waves of a block that shares the batch geometry
 
 // Waves per SIMD the register allocation must leave room for: the lmax <= 2,
 // K = 8 forward and sender streams fit three waves (168 registers) when asked
@@ -730,29 +434,25 @@ constexpr int stream_min_waves(int lmax, int K, int mode) {
 // BUNDLED selects the natural path bundles or single-path units; the two are
 // separate kernels so that each gets the register allocation of its own code
 // (the single-path dispatch covers every path up to LMAX).
-// SHARED (position gradient of bundled plans with low mean degree): one
-// block per (node, tile) whose waves are the units; the first wave computes
-// the geometry of a 64-edge batch into LDS for all of them, instead of every
-// unit's wave computing it again.  `items` counts blocks then, waves otherwise.
-template <int LMAX, int K, int MODE, typename FT, bool BUNDLED, bool SHARED>
-__global__ __launch_bounds__(SHARED ? 64 * kMaxSharedUnits : 64)
+template <int LMAX, int K, int MODE, typename FT, bool BUNDLED>
+__global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(stream_min_waves(LMAX, K, MODE))))
 void stream_kernel(const StreamArgs /*args*/, int64_t items) {
   const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int BATCH = SHARED ? 64 : ModeTraits<MODE>::batch;
+  constexpr int BATCH = ModeTraits<MODE>::batch;
   __shared__ EdgeLds<K, LMAX, MODE, BATCH> L;
   // 32-bit index arithmetic (the launch keeps items below 2^31): a 64-bit
   // division here costs hundreds of instructions per wave.
   const uint32_t item = (uint32_t)xcd_item(blockIdx.x, gridDim.x);
   if (item >= (uint32_t)items) return;  // uniform over the block
   const uint32_t nu = (uint32_t)a.nunits, nt = (uint32_t)a.ntiles;
-  const int unit = SHARED ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : (int)(item % nu);
-  const uint32_t t = SHARED ? item : item / nu;
+  const int unit = (int)(item % nu);
+  const uint32_t t = item / nu;
   const int tile = (int)(t % nt);
   const int node = (int)(t / nt);
   StreamCtx<MODE, FT, LMAX, K, BATCH> ctx{node, tile, unit, L};
   if constexpr (BUNDLED) {
-    Bundles<LMAX, K, ModeTraits<MODE>::bwdpos ? 2 : (ModeTraits<MODE>::recv ? 0 : 1)>::run(unit, ctx, a);
+    Bundles<LMAX, K, ModeTraits<MODE>::recv ? 0 : 1>::run(unit, ctx, a);
     return;
   }
   const StreamPath& P = a.paths[a.unit_paths[unit][0]];
@@ -774,25 +474,12 @@ hipError_t launch_stream_mode(int lmax, int K, const StreamArgs& a, int64_t item
   const int64_t grid = (items + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  // (measured: a gain for the position gradient, whose per-edge geometry is the
-  // most expensive; a loss for the forward and sender streams)
-  constexpr bool kCanShare = MODE == kBwdPos;
-  const bool shared = kCanShare && a.bundled && a.share_geometry && a.nunits >= 1 &&
-                      a.nunits <= kMaxSharedUnits && items % a.nunits == 0;
-  const int64_t blocks = shared ? items / a.nunits : 0, sgrid = (blocks + 7) / 8 * 8;
 #define TPCONV_LAUNCH(LM, KK)                                                                           \
   if (lmax == LM && K == KK) {                                                                          \
-    if constexpr (kCanShare) {                                                                          \
-      if (shared) {                                                                                     \
-        hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true, true>), dim3((unsigned)sgrid),        \
-                           dim3(64 * a.nunits), 0, s, a, blocks);                                       \
-        return hipGetLastError();                                                                       \
-      }                                                                                                 \
-    }                                                                                                   \
     if (a.bundled)                                                                                      \
-      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true, false>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
+      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, true>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
     else                                                                                                \
-      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, false, false>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
+      hipLaunchKernelGGL((stream_kernel<LM, KK, MODE, FT, false>), dim3((unsigned)grid), dim3(64), 0, s, a, items); \
     return hipGetLastError();                                                                           \
   }
   TPCONV_LAUNCH(0, 8) TPCONV_LAUNCH(0, 16)
