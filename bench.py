@@ -237,6 +237,7 @@ def run_workload(name, steps, warmup, detail):
 
     t0 = time.perf_counter()
     graph = tp.tpconv_graph_prepare(plan, tp.Graph(rowptr, senders), validate=True)
+    graph = tp.tpconv_graph_order(plan, graph, pos)  # Morton visiting order of the nodes
     torch.cuda.synchronize()
     t_prep = time.perf_counter() - t0
 

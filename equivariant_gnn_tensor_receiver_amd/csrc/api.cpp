@@ -204,8 +204,10 @@ tpconv_status check_graph(const tpconv_graph* g, bool need_csc) {
   return TPCONV_SUCCESS;
 }
 
-void fill_common(const Plan& p, StreamArgs& a, int64_t N, const float* pos) {
+void fill_common(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos) {
+  const int64_t N = g->num_nodes;
   std::memset(&a, 0, sizeof(a));
+  a.order = g->node_order;
   a.num_nodes = (int32_t)N;
   a.npaths = p.P;
   a.env_p = p.env_p;
@@ -231,7 +233,7 @@ void set_units(const Plan& p, StreamArgs& a, const std::vector<std::vector<int>>
 // state S (or S_dot) in the output-group layout.
 void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const void* x) {
   const int64_t N = g->num_nodes;
-  fill_common(p, a, N, pos);
+  fill_common(p, a, g, pos);
   a.ptr = g->rowptr;
   a.nbr = g->senders;
   a.feat = x;
@@ -252,7 +254,7 @@ void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
 // state T (or T_dot) in the input-group layout.
 void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const float* gout) {
   const int64_t N = g->num_nodes;
-  fill_common(p, a, N, pos);
+  fill_common(p, a, g, pos);
   a.ptr = g->csc_colptr;
   a.nbr = g->csc_receivers;
   a.feat = gout;
@@ -539,6 +541,7 @@ tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t N, int
     case TPCONV_OP_BACKWARD: *bytes = ws_backward(p, N); break;
     case TPCONV_OP_DOUBLE_BACKWARD: *bytes = ws_double_backward(p, N); break;
     case TPCONV_OP_GRAPH_PREPARE: *bytes = graph_csc_workspace(N, E) + kAlign; break;
+    case TPCONV_OP_GRAPH_ORDER: *bytes = graph_order_workspace(N); break;
     default: return TPCONV_ERROR_INVALID_VALUE;
   }
   return TPCONV_SUCCESS;
@@ -566,6 +569,18 @@ tpconv_status tpconv_graph_prepare(tpconv_plan plan, const tpconv_graph* g, int3
   }
   if (N == 0) return TPCONV_SUCCESS;
   return dev(graph_csc(g->rowptr, g->senders, N, E, csc_colptr, csc_receivers, ws, ws_bytes, s));
+}
+
+tpconv_status tpconv_graph_order(tpconv_plan plan, const tpconv_graph* g, const float* pos, int32_t* node_order,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  tpconv_status st = check_graph(g, false);
+  if (st != TPCONV_SUCCESS) return st;
+  const int64_t N = g->num_nodes;
+  if (N == 0) return TPCONV_SUCCESS;
+  if (!pos || !node_order) return TPCONV_ERROR_INVALID_VALUE;
+  if (!ws || ws_bytes < graph_order_workspace(N)) return TPCONV_ERROR_WORKSPACE;
+  return dev(graph_order(pos, N, node_order, ws, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,

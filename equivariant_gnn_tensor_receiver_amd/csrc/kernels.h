@@ -47,6 +47,7 @@ struct StreamArgs {
   int32_t env_p;
   float cutoff, inv_cutoff, pref;          // pref = sqrt(2 / cutoff)
   float env_a, env_b, env_c, env_d;        // u = 1 - a x^p + b x^(p+1) - c x^(p+2); u' = -d x^(p-1) (1-x)^2
+  const int32_t* order; // [N] visiting order of the self nodes (NULL: 0..N-1)
   const int32_t* ptr;   // [N+1] segment offsets of self
   const int32_t* nbr;   // [E] neighbour of each edge
   const float* pos;     // [N][3]
@@ -159,5 +160,8 @@ hipError_t launch_graph_validate(const int32_t* rowptr, const int32_t* senders, 
 hipError_t graph_csc(const int32_t* rowptr, const int32_t* senders, int64_t N, int64_t E, int32_t* colptr,
                      int32_t* receivers_out, void* ws, size_t ws_bytes, hipStream_t s);
 size_t graph_csc_workspace(int64_t N, int64_t E);
+// Morton order of the node positions (a permutation of 0..N-1, deterministic).
+hipError_t graph_order(const float* pos, int64_t N, int32_t* order, void* ws, size_t ws_bytes, hipStream_t s);
+size_t graph_order_workspace(int64_t N);
 
 }  // namespace tpconv

@@ -449,7 +449,7 @@ void stream_kernel(const StreamArgs /*args*/, int64_t items) {
   const int unit = (int)(item % nu);
   const uint32_t t = item / nu;
   const int tile = (int)(t % nt);
-  const int node = (int)(t / nt);
+  const int node = a.order ? a.order[t / nt] : (int)(t / nt);
   StreamCtx<MODE, FT, LMAX, K, BATCH> ctx{node, tile, unit, L};
   if constexpr (BUNDLED) {
     Bundles<LMAX, K, ModeTraits<MODE>::recv ? 0 : 1>::run(unit, ctx, a);

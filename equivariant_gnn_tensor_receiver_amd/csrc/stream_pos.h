@@ -366,7 +366,7 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
   __shared__ PosLds<K, LMAX> S;
   const uint32_t item = (uint32_t)xcd_item(blockIdx.x, gridDim.x);
   if (item >= (uint32_t)nodes) return;  // uniform over the block
-  const int node = (int)item;
+  const int node = a.order ? a.order[item] : (int)item;
   const int nw = (int)(blockDim.x >> 6);
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;

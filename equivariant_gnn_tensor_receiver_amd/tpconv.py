@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.s
 
 TPCONV_F32, TPCONV_BF16 = 0, 1
 FULLY_CONNECTED, CHANNELWISE = 0, 1  # tpconv_connection
-OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_GRAPH_PREPARE = 0, 1, 2, 3
+OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_GRAPH_PREPARE, OP_GRAPH_ORDER = 0, 1, 2, 3, 4
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "IRREPS", 3: "GRAPH", 4: "WORKSPACE", 5: "UNSUPPORTED",
           6: "DEVICE", 7: "SCRATCH"}
 STATIC_SCRATCH_BYTES = 64 << 20
@@ -27,7 +27,7 @@ STATIC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("tpconv_plan_create", "tpconv_plan_destroy", "tpconv_plan_info", "tpconv_plan_path",
            "tpconv_plan_cg", "tpconv_workspace_size", "tpconv_state_size", "tpconv_graph_prepare",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string",
-           "tpconv_kernel_timing", "tpconv_kernel_timing_read", "tpconv_forward_static")
+           "tpconv_kernel_timing", "tpconv_kernel_timing_read", "tpconv_forward_static", "tpconv_graph_order")
 KERNELS = ("stream_fwd", "stream_jvp", "stream_snd", "stream_sndt", "stream_bwdpos", "gemm_out", "gemm_gs",
            "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce")
 
@@ -46,7 +46,7 @@ class TpconvDesc(ctypes.Structure):
 
 class TpconvGraph(ctypes.Structure):
     _fields_ = [("num_nodes", c_int64), ("num_edges", c_int64), ("rowptr", c_void_p), ("senders", c_void_p),
-                ("csc_colptr", c_void_p), ("csc_receivers", c_void_p)]
+                ("csc_colptr", c_void_p), ("csc_receivers", c_void_p), ("node_order", c_void_p)]
 
 
 _LIB = None
@@ -68,6 +68,7 @@ def _lib():
         L.tpconv_workspace_size.argtypes = [P, c_int32, c_int64, c_int64, POINTER(c_size_t)]
         L.tpconv_state_size.argtypes = [P, c_int64, POINTER(c_size_t)]
         L.tpconv_graph_prepare.argtypes = [P, POINTER(TpconvGraph), P, P, c_int32, P, c_size_t, P]
+        L.tpconv_graph_order.argtypes = [P, POINTER(TpconvGraph), P, P, P, c_size_t, P]
         L.tpconv_forward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, c_size_t, P]
         L.tpconv_forward_static.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P]
         L.tpconv_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
@@ -156,17 +157,26 @@ class Plan:
 
 
 class Graph:
-    """Receiver-sorted CSR (device int32 tensors) plus the sender-sorted view."""
+    """Receiver-sorted CSR (device int32 tensors), the sender-sorted view and
+    an optional visiting order of the nodes."""
 
-    def __init__(self, rowptr, senders, csc_colptr=None, csc_receivers=None):
+    def __init__(self, rowptr, senders, csc_colptr=None, csc_receivers=None, node_order=None):
         self.rowptr, self.senders = rowptr, senders
         self.csc_colptr, self.csc_receivers = csc_colptr, csc_receivers
+        self.node_order = node_order
         self.num_nodes = rowptr.numel() - 1
         self.num_edges = senders.numel()
 
     def c(self) -> TpconvGraph:
         return TpconvGraph(self.num_nodes, self.num_edges, _ptr(self.rowptr), _ptr(self.senders),
-                           _ptr(self.csc_colptr), _ptr(self.csc_receivers))
+                           _ptr(self.csc_colptr), _ptr(self.csc_receivers), _ptr(self.node_order))
+
+    def _with(self, **kw):
+        g = Graph(self.rowptr, self.senders, self.csc_colptr, self.csc_receivers, self.node_order)
+        g.num_edges = self.num_edges
+        for k, v in kw.items():
+            setattr(g, k, v)
+        return g
 
 
 def _workspace(nbytes, device):
@@ -243,7 +253,22 @@ def tpconv_graph_prepare(plan: Plan, graph: Graph, validate: bool = True, stream
     g = graph.c()
     _check(_lib().tpconv_graph_prepare(plan.handle, ctypes.byref(g), _ptr(colptr), _ptr(recv), int(validate),
                                        _ptr(ws), ws.numel(), _stream(stream)), "tpconv_graph_prepare")
-    return Graph(graph.rowptr, graph.senders, colptr, recv)
+    return graph._with(csc_colptr=colptr, csc_receivers=recv)
+
+
+def tpconv_graph_order(plan: Plan, graph: Graph, pos, stream=None) -> Graph:
+    """The graph with node_order set to the Morton order of `pos`."""
+    import torch
+
+    dev = pos.device
+    _require(pos, "pos", torch.float32, 3 * graph.num_nodes, dev)
+    order = torch.empty(max(graph.num_nodes, 1), dtype=torch.int32, device=dev)
+    ws = _workspace(plan.workspace_size(OP_GRAPH_ORDER, graph.num_nodes, graph.num_edges), dev)
+    _keep_for_stream(stream, order, ws)
+    g = graph.c()
+    _check(_lib().tpconv_graph_order(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(order), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "tpconv_graph_order")
+    return graph._with(node_order=order)
 
 
 def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=None, workspace=None, stream=None):

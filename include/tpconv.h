@@ -88,7 +88,8 @@ typedef enum {
   TPCONV_OP_FORWARD = 0,
   TPCONV_OP_BACKWARD = 1,
   TPCONV_OP_DOUBLE_BACKWARD = 2,
-  TPCONV_OP_GRAPH_PREPARE = 3
+  TPCONV_OP_GRAPH_PREPARE = 3,
+  TPCONV_OP_GRAPH_ORDER = 4
 } tpconv_op;
 
 typedef struct {
@@ -110,6 +111,8 @@ typedef struct {
   const int32_t* senders;       /* device [E] */
   const int32_t* csc_colptr;    /* device [N+1] or NULL (needed by backward passes) */
   const int32_t* csc_receivers; /* device [E] or NULL (needed by backward passes) */
+  const int32_t* node_order;    /* device [N] permutation of 0..N-1, or NULL (identity): the order
+                                   in which the edge streams visit nodes (tpconv_graph_order) */
 } tpconv_graph;
 
 /* Build a plan from the descriptor: parses the irreps, enumerates the
@@ -146,8 +149,9 @@ tpconv_status tpconv_plan_cg(tpconv_plan plan, int32_t path, double* out);
  * not grow with the edge count).  For FORWARD, BACKWARD and DOUBLE_BACKWARD the
  * size does not depend on E: it holds node-sized states (S, its cotangent, the
  * sender state T) and the fixed-count partial sums of the weight gradient.
- * GRAPH_PREPARE needs O(E) int32 scratch for the sender sort (index
- * metadata, not tensor-product workspace).  FORWARD's figure assumes
+ * GRAPH_PREPARE needs O(N) int32 scratch for the sender sort (index
+ * metadata, not tensor-product workspace), GRAPH_ORDER O(N) for the sort of
+ * the nodes.  FORWARD's figure assumes
  * saved_state == NULL; with a saved state the forward needs none.
  * Errors: INVALID_VALUE (null plan or bytes, negative sizes, unknown op). */
 tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t num_nodes,
@@ -173,6 +177,20 @@ tpconv_status tpconv_state_size(tpconv_plan plan, int64_t num_nodes, size_t* byt
 tpconv_status tpconv_graph_prepare(tpconv_plan plan, const tpconv_graph* g, int32_t* csc_colptr,
                                    int32_t* csc_receivers, int32_t validate, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* A spatial visiting order of the nodes for g->node_order: the nodes sorted
+ * by the Morton code of their positions (30 bits over the bounding cube; ties,
+ * which only coincident quantised positions produce, by node id), so the
+ * deterministic permutation does not depend on the graph's node numbering.  The
+ * pages say nothing about the order in which receivers are processed; every
+ * receiver's result is independent of it (grad_pos only up to the rounding
+ * of its atomic additions).  Streams that visit spatially close receivers one
+ * after another gather mostly the same sender rows, so those gathers hit the
+ * L2 cache of the XCD that runs them.  pos: device [N][3]; node_order: device
+ * [N] (written).  Workspace: tpconv_workspace_size(GRAPH_ORDER), O(N).
+ * Errors: INVALID_VALUE (null pointers), WORKSPACE, DEVICE. */
+tpconv_status tpconv_graph_order(tpconv_plan plan, const tpconv_graph* g, const float* pos, int32_t* node_order,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Forward: out = conv(pos, x, W) as defined at the top of this header.
  * saved_state: NULL, or device memory of tpconv_state_size bytes that receives

@@ -37,7 +37,7 @@ class DeviceCase:
     """Seeded problem uploaded to cuda:0 plus the matching oracle Problem."""
 
     def __init__(self, irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype="f32",
-                 channelwise=False, w_dtype=None, env_p=6):
+                 channelwise=False, w_dtype=None, env_p=6, ordered=True):
         import torch
 
         self.dev = torch.device("cuda:0")
@@ -66,6 +66,8 @@ class DeviceCase:
         g = tp.Graph(self.rowptr, self.senders)
         g.num_edges = len(senders)
         self.graph = tp.tpconv_graph_prepare(self.plan, g, validate=True)
+        if ordered:  # the streams visit nodes in Morton order, as in bench.py
+            self.graph = tp.tpconv_graph_order(self.plan, self.graph, self.pos)
 
     def forward(self, **kw):
         import torch

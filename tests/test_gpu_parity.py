@@ -180,3 +180,41 @@ def test_graph_prepare_matches_stable_sort_and_validation():
     with pytest.raises(tp.TpconvError) as e:
         tp.tpconv_graph_prepare(c.plan, tp.Graph(c.rowptr, bad_snd), validate=True)
     assert e.value.status == 3
+
+
+def morton_order_numpy(pos):
+    """The node order tpconv_graph_order defines, restated in numpy fp32."""
+    p = np.asarray(pos, dtype=np.float32)
+    lo, hi = p.min(0), p.max(0)
+    ext = np.float32(max(float((hi - lo).max()), 1e-30))
+    scale = np.float32(1024.0) / ext
+    q = np.clip((p - lo) * scale, np.float32(0), np.float32(1023)).astype(np.uint32)
+
+    def spread(v):
+        v = v & 0x3FF
+        v = (v | (v << 16)) & 0x030000FF
+        v = (v | (v << 8)) & 0x0300F00F
+        v = (v | (v << 4)) & 0x030C30C3
+        v = (v | (v << 2)) & 0x09249249
+        return v
+
+    code = spread(q[:, 0]) | (spread(q[:, 1]) << 1) | (spread(q[:, 2]) << 2)
+    return np.lexsort((np.arange(len(p)), code))
+
+
+def test_node_order_is_morton_and_changes_nothing():
+    say("[case] Morton visiting order: results with and without it")
+    pos, rowptr, senders, rng = inputs.random_graph(700, 20, seed=11)
+    args = ("16x0e+16x1o+16x2e", "16x0e+16x1o+16x2e", 2, 8, pos, rowptr, senders)
+    a = DeviceCase(*args, np.random.default_rng(3), ordered=True)
+    b = DeviceCase(*args, np.random.default_rng(3), ordered=False)
+    order = a.graph.node_order.cpu().numpy()
+    assert np.array_equal(np.sort(order), np.arange(700))
+    assert np.array_equal(order, morton_order_numpy(pos))
+    assert np.array_equal(a.forward(), b.forward())
+    ga, gb = a.backward(), b.backward()
+    assert np.array_equal(ga[0], gb[0]) and np.array_equal(ga[1], gb[1])
+    assert rel_err(ga[2], gb[2]) <= 1e-6
+    da, db = a.double_backward(), b.double_backward()
+    for u, v in zip(da, db):
+        assert np.array_equal(u, v)

@@ -29,7 +29,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(tp.LIB_PATH)
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert sorted(names) == sorted(tp.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -106,11 +106,11 @@ def test_workspace_is_independent_of_edges():
 def test_argument_errors_before_any_launch():
     lib = tp._lib()
     plan = tp.Plan("8x0e+8x1o", "8x0e+8x1o", 1, 8)
-    g = tp.TpconvGraph(4, 3, ctypes.c_void_p(16), ctypes.c_void_p(32), None, None)
+    g = tp.TpconvGraph(4, 3, ctypes.c_void_p(16), ctypes.c_void_p(32), None, None, None)
     fake = ctypes.c_void_p(64)
     # null plan, negative sizes, missing output, missing/short workspace
     assert lib.tpconv_forward(None, ctypes.byref(g), fake, fake, fake, fake, None, fake, 1 << 30, None) == 1
-    bad = tp.TpconvGraph(-1, 3, ctypes.c_void_p(16), ctypes.c_void_p(32), None, None)
+    bad = tp.TpconvGraph(-1, 3, ctypes.c_void_p(16), ctypes.c_void_p(32), None, None, None)
     assert lib.tpconv_forward(plan.handle, ctypes.byref(bad), fake, fake, fake, fake, None, fake, 1 << 30, None) == 1
     assert lib.tpconv_forward(plan.handle, ctypes.byref(g), fake, fake, fake, None, None, fake, 1 << 30, None) == 1
     assert lib.tpconv_forward(plan.handle, ctypes.byref(g), fake, fake, fake, fake, None, fake, 16, None) == 4
@@ -122,8 +122,10 @@ def test_argument_errors_before_any_launch():
                                fake, 1 << 30, None) == 1
     assert lib.tpconv_double_backward(plan.handle, ctypes.byref(g), fake, fake, fake, fake, None, fake, None,
                                       None, fake, 1 << 30, None) == 1
-    # graph prepare: short workspace
+    # graph prepare / order: short workspace, missing positions
     assert lib.tpconv_graph_prepare(plan.handle, ctypes.byref(g), fake, fake, 1, fake, 8, None) == 4
+    assert lib.tpconv_graph_order(plan.handle, ctypes.byref(g), fake, fake, fake, 8, None) == 4
+    assert lib.tpconv_graph_order(plan.handle, ctypes.byref(g), None, fake, fake, 1 << 30, None) == 1
     assert lib.tpconv_status_string(4) == b"workspace missing or too small"
 
 
