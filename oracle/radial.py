@@ -13,7 +13,9 @@ functions with a p = 6 polynomial cutoff.  Reading taken:
 so u(0) = 1 and u, u', u'' vanish at x = 1.  The frequencies are fixed (no
 trainable radial network), so R feeds the weights W directly, which is what the
 reassociation needs.  At d = 0, R_k takes its limit sqrt(2/c) k pi / c and the
-derivative is 0 (the function is even in d).
+derivative is 0 (the function is even in d); the second derivative, which only
+the position Hessian of the force loss uses, is taken as 0 there as well (the
+reading for a coincident edge: it contributes no position derivatives).
 """
 from __future__ import annotations
 
@@ -65,3 +67,31 @@ def bessel_radial_deriv(d: np.ndarray, K: int, cutoff: float, p: int = 6) -> np.
     du = envelope_deriv(d / cutoff, p)[..., None] / cutoff
     dR = pref * ((w * c / safe - s / safe ** 2) * u + s / safe * du)
     return np.where((d > 0)[..., None], dR, 0.0)
+
+
+def envelope_deriv2(x: np.ndarray, p: int = 6) -> np.ndarray:
+    """u''(x) = -p(p+1)(p+2)/2 * [(p-1) x^(p-2) (1-x)^2 - 2 x^(p-1) (1-x)] for x < 1, else 0."""
+    x = np.asarray(x, dtype=np.float64)
+    k = p * (p + 1) * (p + 2) / 2.0
+    d2 = -k * ((p - 1) * x ** (p - 2) * (1.0 - x) ** 2 - 2.0 * x ** (p - 1) * (1.0 - x))
+    return np.where(x < 1.0, d2, 0.0)
+
+
+def bessel_radial_deriv2(d: np.ndarray, K: int, cutoff: float, p: int = 6) -> np.ndarray:
+    """d^2 R_k / dd^2 (product rule on pref * f(d) * u(d/c), f = sin(w d) / d); 0 at d = 0 and d >= cutoff."""
+    d = np.asarray(d, dtype=np.float64)
+    k = np.arange(1, K + 1, dtype=np.float64)
+    pref = math.sqrt(2.0 / cutoff)
+    w = k * math.pi / cutoff
+    safe = np.where(d > 0, d, 1.0)[..., None]
+    dd = d[..., None]
+    s = np.sin(w * dd)
+    c = np.cos(w * dd)
+    f = s / safe
+    f1 = w * c / safe - s / safe ** 2
+    f2 = -w * w * s / safe - 2.0 * w * c / safe ** 2 + 2.0 * s / safe ** 3
+    u = envelope(d / cutoff, p)[..., None]
+    u1 = envelope_deriv(d / cutoff, p)[..., None] / cutoff
+    u2 = envelope_deriv2(d / cutoff, p)[..., None] / cutoff ** 2
+    d2R = pref * (f2 * u + 2.0 * f1 * u1 + f * u2)
+    return np.where((d > 0)[..., None], d2R, 0.0)

@@ -12,7 +12,7 @@ harmonic polynomial of degree l, written out below for l <= 3.  The tests pin
 these polynomials against scipy's complex harmonics mapped through U.
 
 At r = 0 the direction is undefined; the reading taken is r_hat := 0, so
-Y_00 = 1, Y_{l>=1} = 0 and the Jacobian is 0.
+Y_00 = 1, Y_{l>=1} = 0 and the Jacobian (and Hessian) is 0.
 """
 from __future__ import annotations
 
@@ -127,3 +127,67 @@ def sh_jacobian_single_l(l: int, r: np.ndarray) -> np.ndarray:
 def sh_jacobian(lmax: int, r: np.ndarray) -> np.ndarray:
     """(..., (lmax+1)^2, 3)."""
     return np.concatenate([sh_jacobian_single_l(l, r) for l in range(lmax + 1)], -2)
+
+
+def _poly_hess(l, x, y, z):
+    """Hessians of P_lm: shape (..., 2l+1, 3, 3) (constant for l = 2, linear for l = 3)."""
+    zero = np.zeros_like(x)
+
+    def sym(xx, xy, xz, yy, yz, zz):
+        return np.stack([np.stack([xx, xy, xz], -1), np.stack([xy, yy, yz], -1), np.stack([xz, yz, zz], -1)], -2)
+
+    if l <= 1:
+        return np.zeros(x.shape + (2 * l + 1, 3, 3))
+    one = np.ones_like(x)
+    if l == 2:
+        return np.stack([
+            sym(zero, _S15 * one, zero, zero, zero, zero),
+            sym(zero, zero, zero, zero, _S15 * one, zero),
+            sym(-_S5 * one, zero, zero, -_S5 * one, zero, 2 * _S5 * one),
+            sym(zero, zero, _S15 * one, zero, zero, zero),
+            sym(_S15 * one, zero, zero, -_S15 * one, zero, zero),
+        ], -3)
+    if l == 3:
+        a = 0.25 * _S70
+        b = 0.25 * _S42
+        c = 0.5 * _S7
+        e = 0.5 * _S105
+        return np.stack([
+            sym(6 * a * y, 6 * a * x, zero, -6 * a * y, zero, zero),
+            sym(zero, _S105 * z, _S105 * y, zero, _S105 * x, zero),
+            sym(-2 * b * y, -2 * b * x, zero, -6 * b * y, 8 * b * z, 8 * b * y),
+            sym(-6 * c * z, zero, -6 * c * x, -6 * c * z, -6 * c * y, 12 * c * z),
+            sym(-6 * b * x, -2 * b * y, 8 * b * z, -2 * b * x, zero, 8 * b * x),
+            sym(2 * e * z, zero, 2 * e * x, -2 * e * z, -2 * e * y, zero),
+            sym(6 * a * x, -6 * a * y, zero, -6 * a * x, zero, zero),
+        ], -3)
+    raise ValueError(f"l={l} > {LMAX} not supported")
+
+
+def sh_hessian_single_l(l: int, r: np.ndarray) -> np.ndarray:
+    """d^2 Y_lm / dr dr (..., 2l+1, 3, 3) for Y = P q, q = |r|^-l; zero at r = 0.
+
+    Product rule: H = H_P q + grad P (x) grad q + grad q (x) grad P + P H_q, with
+    grad q = -l r |r|^-(l+2) and H_q = -l |r|^-(l+2) I + l (l+2) |r|^-(l+4) r r^T.
+    """
+    r = np.asarray(r, dtype=np.float64)
+    d = np.linalg.norm(r, axis=-1)
+    ok = d > 0
+    safe = np.where(ok, d, 1.0)[..., None, None]
+    x, y, z = r[..., 0], r[..., 1], r[..., 2]
+    P = _poly(l, x, y, z)[..., None, None]                     # (..., m, 1, 1)
+    G = _poly_grad(l, x, y, z)                                 # (..., m, 3)
+    HP = _poly_hess(l, x, y, z)                                # (..., m, 3, 3)
+    rr = r[..., None, :, None] * r[..., None, None, :]         # (..., 1, 3, 3)
+    eye = np.eye(3)
+    q = safe[..., None] ** (-l)                                # (..., 1, 1, 1)
+    gq = -l * r[..., None, :] / safe ** (l + 2)                # (..., 1, 3)
+    Hq = (-l * eye / safe[..., None] ** (l + 2) + l * (l + 2) * rr / safe[..., None] ** (l + 4))
+    H = (HP * q + G[..., :, :, None] * gq[..., :, None, :] + gq[..., :, :, None] * G[..., :, None, :]
+         + P * Hq)
+    return np.where(ok[..., None, None, None], H, 0.0)
+
+
+def sh_hessian(lmax: int, r: np.ndarray) -> np.ndarray:
+    """(..., (lmax+1)^2, 3, 3)."""
+    return np.concatenate([sh_hessian_single_l(l, r) for l in range(lmax + 1)], -3)

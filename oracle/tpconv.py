@@ -259,3 +259,58 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
                    + np.einsum(ops["msg"], w_e[:, pi], U_dot, optimize=True))
             np.add.at(d_gout[:, _out_rows(prob, p), :], v, dgo)
     return d_W, d_x, d_gout
+
+
+def double_backward_pos(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos):
+    """dL_F/dpos for L_F = sum_n <gg_pos[n], g_pos[n]> (the Hessian term).
+
+    For an edge e, the energy <g_m_e, m_e> is eps(r) = sum_k R_k(|r|) b_k . Y(r)
+    with b_k[l2, m2] = sum_{p -> l2} sum W[k,p,ci,co] g_m[l3,co,m3] C^p[m1,m2,m3]
+    x_s[l1,ci,m1], and g_r_e is its gradient.  With phi_e fixed,
+    dL_F/dr_e = H_e phi_e for the Hessian H_e of eps:
+      H_e = sum_k [ R''_k B_k rr^T + R'_k B_k (I - rr^T)/d + R'_k (r (J^T b_k)^T + (J^T b_k) r^T)
+                    + R_k sum_m2 b_k[m2] Hess Y_m2 ]      (r = r_hat, B_k = b_k . Y)
+    and dL_F/dpos[s] += H_e phi_e, dL_F/dpos[v] -= H_e phi_e.  An edge with
+    d = 0 or d >= c contributes nothing.
+    """
+    pos, x, W = _as64(pos), _as64(x), _as64(W)
+    g_out, gg_pos = _as64(g_out), _as64(gg_pos)
+    senders = np.asarray(senders, dtype=np.int64)
+    receivers = np.asarray(receivers, dtype=np.int64)
+    K = prob.num_basis
+    nsh = (prob.sh_lmax + 1) ** 2
+    d_pos = np.zeros_like(pos)
+    eye = np.eye(3)
+    for a, b in _chunks(prob, len(senders)):
+        s, v = senders[a:b], receivers[a:b]
+        r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
+        dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
+        d2R = _radial.bessel_radial_deriv2(d, K, prob.cutoff, prob.envelope_p)
+        JY = _sh.sh_jacobian(prob.sh_lmax, r)                       # [e, m, 3]
+        HY = _sh.sh_hessian(prob.sh_lmax, r)                        # [e, m, 3, 3]
+        phi = gg_pos[s] - gg_pos[v]
+        g_m = g_out[v]
+        bk = np.zeros((len(s), K, nsh))
+        for pi, p in enumerate(prob.paths):
+            gm = g_m[:, _out_rows(prob, p), :]                       # [e, m3, co]
+            if prob.channelwise:
+                G = np.einsum("ki,eci->ekic", W[:, pi], gm, optimize=True)
+            else:
+                G = np.einsum("kio,eco->ekic", W[:, pi], gm, optimize=True)
+            l2 = p["l2"]
+            bk[:, :, l2 * l2:(l2 + 1) * (l2 + 1)] += np.einsum(
+                "abc,eai,ekic->ekb", p["C"], _x_block(prob, x, s, p), G, optimize=True)
+        B = np.einsum("ekm,em->ek", bk, Y)
+        Jb = np.einsum("ekm,emj->ekj", bk, JY)
+        Hb = np.einsum("ekm,emij->eij", np.einsum("ek,ekm->ekm", R, bk), HY)
+        rr = rhat[:, :, None] * rhat[:, None, :]
+        safe = np.where(d > 0, d, 1.0)
+        H = (np.einsum("ek,ek->e", d2R, B)[:, None, None] * rr
+             + (np.einsum("ek,ek->e", dR, B) / safe)[:, None, None] * (eye[None] - rr)
+             + np.einsum("ek,eki,ej->eij", dR, Jb, rhat) + np.einsum("ek,ei,ekj->eij", dR, rhat, Jb)
+             + Hb)
+        Hphi = np.einsum("eij,ej->ei", H, phi)
+        Hphi = np.where((d > 0)[:, None], Hphi, 0.0)
+        np.add.at(d_pos, s, Hphi)
+        np.add.at(d_pos, v, -Hphi)
+    return d_pos

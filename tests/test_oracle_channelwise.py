@@ -67,6 +67,13 @@ def test_double_backward_equals_diagonal_fully_connected():
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * np.abs(b).max())
 
 
+def test_double_backward_pos_equals_diagonal_fully_connected():
+    cw, full, pos, s, v, x, W, Wf, g, gg = _case()
+    a = otp.double_backward_pos(cw, pos, s, v, x, W, g, gg)
+    b = otp.double_backward_pos(full, pos, s, v, x, Wf, g, gg)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * np.abs(b).max())
+
+
 def test_weight_gradient_finite_difference():
     cw, _, pos, s, v, x, W, _, g, _ = _case(seed=5)
     _, gW, _ = otp.backward(cw, pos, s, v, x, W, g)

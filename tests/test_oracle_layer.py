@@ -9,7 +9,8 @@ Each check is independent of the oracle's own formulas:
   * single-edge closed forms: dot product, vector scaling and cross product;
   * backward against central differences in random directions; sum of position
     gradients is zero;
-  * double backward against central differences of <gg_pos, g_pos>.
+  * double backward against central differences of <gg_pos, g_pos>, including
+    its position derivative (the Hessian term).
 """
 import math
 
@@ -18,7 +19,7 @@ import pytest
 
 from equivariant_gnn_tensor_receiver_amd import inputs
 from oracle import cg, radial, sh
-from oracle.tpconv import Problem, backward, csr_receivers, double_backward, forward
+from oracle.tpconv import Problem, backward, csr_receivers, double_backward, double_backward_pos, forward
 
 from test_oracle_cg import random_rotation, wigner_from_sh
 
@@ -232,6 +233,46 @@ def test_double_backward_finite_differences(spec):
         assert fd_x == pytest.approx((d_x * dx).sum(), rel=1e-7)
         assert fd_W == pytest.approx((d_W * dW).sum(), rel=1e-7)
         assert fd_g == pytest.approx((d_gout * dg).sum(), rel=1e-7)
+
+
+L3 = ("2x0e+2x1o+2x2e+2x3o", "2x0e+2x1o+2x2e+2x3o", 3, 4)
+
+
+@pytest.mark.parametrize("spec", [NAT2, MIXED, L3])
+def test_double_backward_pos_finite_differences(spec):
+    # dL_F/dpos against central differences of L_F(pos) = <gg_pos, g_pos(pos)>,
+    # whose g_pos is the backward oracle pinned above: an independent route
+    prob, pos, snd, rcv, x, W, g_out, gg = case(*spec, N=10, deg=5)
+    d_pos = double_backward_pos(prob, pos, snd, rcv, x, W, g_out, gg)
+    assert np.abs(d_pos.sum(0)).max() < 1e-12 * np.abs(d_pos).max()
+
+    def LF(ppos):
+        return float((backward(prob, ppos, snd, rcv, x, W, g_out)[2] * gg).sum())
+
+    rng = np.random.default_rng(7)
+    h = 1e-5
+    for _ in range(3):
+        dp = rng.standard_normal(pos.shape)
+        fd = (LF(pos + h * dp) - LF(pos - h * dp)) / (2 * h)
+        assert fd == pytest.approx((d_pos * dp).sum(), rel=1e-7)
+    for n, j in [(0, 0), (4, 2), (9, 1)]:
+        e = np.zeros_like(pos)
+        e[n, j] = h
+        fd = (LF(pos + e) - LF(pos - e)) / (2 * h)
+        assert fd == pytest.approx(d_pos[n, j], rel=1e-6, abs=1e-8)
+
+
+def test_double_backward_pos_degenerate_edges():
+    # a coincident edge and an edge at or past the cutoff contribute nothing
+    prob = Problem("2x0e+2x1o", "2x0e+2x1o", 1, 4)
+    rng = np.random.default_rng(2)
+    pos = np.array([[0.0, 0.0, 0.0], [0.0, 0.0, 0.0], [5.0, 0.0, 0.0], [7.0, 1.0, 0.0]])
+    x = rng.standard_normal((4, prob.D_in, prob.C_in))
+    W = rng.standard_normal(prob.w_shape)
+    g = rng.standard_normal((4, prob.D_out, prob.C_out))
+    gg = rng.standard_normal((4, 3))
+    snd, rcv = np.array([1, 2, 3]), np.array([0, 0, 0])
+    assert np.all(double_backward_pos(prob, pos, snd, rcv, x, W, g, gg) == 0)
 
 
 def test_sampled_receivers_are_exact():

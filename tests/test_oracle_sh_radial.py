@@ -150,3 +150,31 @@ def test_radial_derivative_limit_and_cutoff():
     assert np.allclose(r0[0], math.sqrt(2 / c) * np.arange(1, K + 1) * math.pi / c)
     assert np.all(radial.bessel_radial(np.array([5.0, 6.0]), K, c) == 0)
     assert np.all(radial.bessel_radial_deriv(np.array([0.0, 5.0, 6.0]), K, c) == 0)
+
+
+def test_sh_hessian_against_jacobian_differences():
+    rng = np.random.default_rng(5)
+    pts = rng.normal(size=(15, 3)) * 2.0
+    H = sh.sh_hessian(sh.LMAX, pts)
+    assert np.abs(H - np.swapaxes(H, -1, -2)).max() < 1e-12
+    h = 1e-6
+    for j in range(3):
+        e = np.zeros(3)
+        e[j] = h
+        fd = (sh.sh_jacobian(sh.LMAX, pts + e) - sh.sh_jacobian(sh.LMAX, pts - e)) / (2 * h)
+        assert np.abs(fd - H[..., j]).max() < 1e-7
+    assert np.all(sh.sh_hessian(3, np.zeros((2, 3))) == 0)
+
+
+@pytest.mark.parametrize("p", [3, 6])
+def test_radial_second_derivative(p):
+    c, K = 5.0, 16
+    d = np.linspace(0.2, 4.9, 40)
+    h = 1e-6
+    fd = (radial.bessel_radial_deriv(d + h, K, c, p) - radial.bessel_radial_deriv(d - h, K, c, p)) / (2 * h)
+    assert np.abs(fd - radial.bessel_radial_deriv2(d, K, c, p)).max() < 1e-5
+    xs = np.linspace(0.05, 0.95, 19)
+    fd = (radial.envelope_deriv(xs + h, p) - radial.envelope_deriv(xs - h, p)) / (2 * h)
+    assert np.abs(fd - radial.envelope_deriv2(xs, p)).max() < 1e-6
+    assert abs(radial.envelope_deriv2(np.array(1.0 - 1e-12), p)) < 1e-9
+    assert np.all(radial.bessel_radial_deriv2(np.array([0.0, 5.0, 6.0]), K, c, p) == 0)
