@@ -36,15 +36,17 @@ STREAM_VARIANTS = [
     ("jvp_f32", "kJvp", "float"), ("jvp_bf16", "kJvp", "uint16_t"),
     ("snd_f32", "kSnd", "float"), ("sndt_f32", "kSndT", "float"),
 ]
-POS_VARIANTS = [("bpos_f32", "float"), ("bpos_bf16", "uint16_t")]
+POS_VARIANTS = [("bpos_f32", "float", 0), ("bpos_bf16", "uint16_t", 0), ("hess_f32", "float", 1),
+                ("hess_bf16", "uint16_t", 1)]
 # The edge streams keep their 4x4 outer-product accumulators in ordinary VGPRs
 # (the accumulation registers would otherwise be copied back and forth).
 STREAM_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 UNITS = ([(f"stream_{n}", "stream_inst.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f"-DTP_FT={t}",
                                                             f"-DTP_LAUNCHER=launch_stream_{n}"])
           for n, m, t in STREAM_VARIANTS]
-         + [(f"stream_{n}", "stream_pos.hip", STREAM_FLAGS + [f"-DTP_FT={t}", f"-DTP_LAUNCHER=launch_stream_{n}"])
-            for n, t in POS_VARIANTS]
+         + [(f"stream_{n}", "stream_pos.hip", STREAM_FLAGS + [f"-DTP_FT={t}", f"-DTP_HESS={h}",
+                                                             f"-DTP_LAUNCHER=launch_stream_{n}"])
+            for n, t, h in POS_VARIANTS]
          + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("channelwise", ".hip"), ("graph", ".hip"),
                                              ("scratch", ".hip"), ("api", ".cpp"),
                                              ("stream_dispatch", ".cpp"), ("plan", ".cpp"),

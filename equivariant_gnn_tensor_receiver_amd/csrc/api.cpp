@@ -113,8 +113,9 @@ size_t ws_backward(const Plan& p, int64_t N) {
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
-  return align_up(state_in_elems(p, N) * 4) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4);
+  // S_dot, T_dot, weight partials; for d_pos also gS (fully connected) and split x
+  return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
+         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2);
 }
 
 tpconv_status dev(hipError_t e) { return e == hipSuccess ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE; }
@@ -447,6 +448,42 @@ tpconv_status run_cw_gw(const Plan& p, int64_t N, const float* state, const floa
   return dev(launch_cw_reduce(a, s));
 }
 
+// The receiver-side position streams (kBwdPos: grad_pos; kBwdHess: the
+// position derivative of the force loss along gg_pos) into out [N][3]:
+// gS = g_out W^T first (formed in registers when channel-wise), fp32 features
+// split into bf16 hi + lo planes for the matrix cores.
+tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, const float* pos, const void* x,
+                             const void* W, const float* grad_out, const float* gg_pos, float* gS, uint16_t* xhi,
+                             uint16_t* xlo, float* out, hipStream_t s) {
+  const int64_t N = g->num_nodes;
+  const bool cw = channelwise(p);
+  tpconv_status st;
+  if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, grad_out, W, gS, 1, s)) != TPCONV_SUCCESS) return st;
+  if ((st = dev(launch_fill(out, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
+  StreamArgs a;
+  recv_args(p, a, g, pos, x);
+  set_units(p, a, p.pos_units);
+  a.nslices = (p.C_in + 31) / 32;
+  const size_t nsplit = split_elems(p, N);
+  if (nsplit > 0) {
+    if ((st = dev(launch_split_bf16(static_cast<const float*>(x), xhi, xlo, (int64_t)nsplit, s))) != TPCONV_SUCCESS)
+      return st;
+    a.feat = xhi;
+    a.feat_lo = xlo;
+  }
+  a.gstate = gS;
+  a.gpos = out;
+  a.ggpos = gg_pos;
+  if (cw) {
+    a.cw = 1;
+    a.W = W;
+    a.w_bf16 = p.w_dtype == TPCONV_BF16;
+    a.gout = grad_out;
+    a.gout_rows = p.D_out;
+  }
+  return dev(launch_stream(mode, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s));
+}
+
 }  // namespace
 }  // namespace tpconv
 
@@ -658,42 +695,21 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
     st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, grad_out, part, grad_W, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
-  if (grad_pos) {  // caller's stream: gS = g_out W^T (formed in registers when channel-wise), then the stream
-    if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, grad_out, W, gS, 1, s)) != TPCONV_SUCCESS) return st;
-    if ((st = dev(launch_fill(grad_pos, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
-    StreamArgs a;
-    recv_args(p, a, g, pos, x);
-    set_units(p, a, p.pos_units);
-    a.nslices = (p.C_in + 31) / 32;
-    if (nsplit > 0) {  // fp32 features reach the matrix cores as bf16 hi + lo
-      if ((st = dev(launch_split_bf16(static_cast<const float*>(x), xhi, xlo, (int64_t)nsplit, s))) != TPCONV_SUCCESS)
-        return st;
-      a.feat = xhi;
-      a.feat_lo = xlo;
-    }
-    a.gstate = gS;
-    a.gpos = grad_pos;
-    if (cw) {
-      a.cw = 1;
-      a.W = W;
-      a.w_bf16 = p.w_dtype == TPCONV_BF16;
-      a.gout = grad_out;
-      a.gout_rows = p.D_out;
-    }
-    if ((st = dev(launch_stream(kBwdPos, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
-        TPCONV_SUCCESS)
-      return st;
+  if (grad_pos) {  // caller's stream
+    st = run_pos_stream(p, kBwdPos, g, pos, x, W, grad_out, nullptr, gS, xhi, xlo, grad_pos, s);
+    if (st != TPCONV_SUCCESS) return st;
   }
   return fork.join();
 }
 
 tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
                                      const void* W, const float* grad_out, const float* gg_pos, float* d_W,
-                                     float* d_x, float* d_grad_out, void* ws, size_t ws_bytes, void* stream) {
+                                     float* d_x, float* d_grad_out, float* d_pos, void* ws, size_t ws_bytes,
+                                     void* stream) {
   if (!plan) return TPCONV_ERROR_INVALID_VALUE;
   tpconv_status st = check_graph(g, d_x != nullptr);
   if (st != TPCONV_SUCCESS) return st;
-  if (!d_W && !d_x && !d_grad_out) return TPCONV_ERROR_INVALID_VALUE;
+  if (!d_W && !d_x && !d_grad_out && !d_pos) return TPCONV_ERROR_INVALID_VALUE;
   const Plan& p = plan->plan;
   const int64_t N = g->num_nodes;
   if (N > 0 && (!pos || !x || !W || !grad_out || !gg_pos)) return TPCONV_ERROR_INVALID_VALUE;
@@ -709,6 +725,10 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
   float* Sd = c.take(state_in_elems(p, N));
   float* Td = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
+  float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
+  const size_t nsplit = split_elems(p, N);
+  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
+  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
@@ -737,6 +757,10 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
               : run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s);
       if (st != TPCONV_SUCCESS) return st;
     }
+  }
+  if (d_pos) {  // caller's stream: the Hessian term
+    st = run_pos_stream(p, kBwdHess, g, pos, x, W, grad_out, gg_pos, gS, xhi, xlo, d_pos, s);
+    if (st != TPCONV_SUCCESS) return st;
   }
   return fork.join();
 }

@@ -163,6 +163,53 @@ __device__ __forceinline__ void radial(float d, float cutoff, float inv_cutoff, 
   }
 }
 
+// R, R' and R'' of the Bessel basis (the position derivative of the force
+// loss): with f = sin(k w d) / d and u = u(d / c),
+//   R = pref f u,  R' = pref (f' u + f u_d),  R'' = pref (f'' u + 2 f' u_d + f u_dd),
+//   f' = k w cos / d - sin / d^2,  f'' = -(k w)^2 sin / d - 2 k w cos / d^2 + 2 sin / d^3,
+//   u_d = u'(x) / c,  u_dd = u''(x) / c^2,  u''(x) = -ed [(p-1) x^(p-2) (1-x)^2 - 2 x^(p-1) (1-x)].
+// At d = 0 (limit R, R' = R'' = 0) and d >= c (all 0) as in radial().
+template <int K>
+__device__ __forceinline__ void radial2(float d, float inv_cutoff, float pref, int p, float ea, float eb, float ec,
+                                        float ed, float* R, float* dR, float* d2R) {
+  const float w = 3.14159265358979f * inv_cutoff;
+  const float x = d * inv_cutoff;
+  if (d <= 0.f || x >= 1.f) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      R[k] = d <= 0.f ? pref * w * (float)(k + 1) : 0.f;
+      dR[k] = 0.f;
+      d2R[k] = 0.f;
+    }
+    return;
+  }
+  float xp2 = 1.f;  // x^(p-2)
+  for (int i = 0; i < p - 2; ++i) xp2 *= x;
+  const float xp1 = xp2 * x, xp = xp1 * x;
+  const float u = 1.f - ea * xp + eb * xp * x - ec * xp * x * x;
+  const float omx = 1.f - x;
+  const float ud = -ed * xp1 * omx * omx * inv_cutoff;
+  const float udd = -ed * ((float)(p - 1) * xp2 * omx * omx - 2.f * xp1 * omx) * inv_cutoff * inv_cutoff;
+  float s1, c1;
+  __sincosf(w * d, &s1, &c1);
+  const float inv_d = 1.f / d;
+  float sk = s1, ck = c1;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float kw = (float)(k + 1) * w;
+    const float f = sk * inv_d;
+    const float f1 = (kw * ck - f) * inv_d;
+    const float f2 = (-kw * kw * sk - 2.f * f1) * inv_d;
+    R[k] = pref * f * u;
+    dR[k] = pref * (f1 * u + f * ud);
+    d2R[k] = pref * (f2 * u + 2.f * f1 * ud + f * udd);
+    const float sn = sk * c1 + ck * s1;
+    const float cn = ck * c1 - sk * s1;
+    sk = sn;
+    ck = cn;
+  }
+}
+
 // Real harmonics of a unit vector (x, y, z), component normalised, rows l^2 + l + m.
 template <int L>
 __device__ __forceinline__ void sh_eval(float x, float y, float z, float* Y) {
@@ -228,6 +275,38 @@ __device__ __forceinline__ void sh_poly_grad(float x, float y, float z, float (*
     G[13][2] = 8.f * b * x * z;
     G[14][0] = 2.f * h105 * x * z;  G[14][1] = -2.f * h105 * y * z;  G[14][2] = h105 * (x * x - y * y);
     G[15][0] = a * 3.f * (x * x - y * y);  G[15][1] = -a * 6.f * x * y;  G[15][2] = 0.f;
+  }
+}
+
+// H_P(u) phi for the Hessians H_P of the homogeneous polynomials P_lm at the
+// unit vector u = (x, y, z) (constant for l = 2, linear for l = 3): out[row][3].
+template <int L>
+__device__ __forceinline__ void sh_poly_hess_dir(float x, float y, float z, float fx, float fy, float fz,
+                                                 float (*out)[3]) {
+  auto sym = [&](float (&o)[3], float xx, float xy, float xz, float yy, float yz, float zz) {
+    o[0] = xx * fx + xy * fy + xz * fz;
+    o[1] = xy * fx + yy * fy + yz * fz;
+    o[2] = xz * fx + yz * fy + zz * fz;
+  };
+  for (int r = 0; r < (L < 1 ? 1 : 4); ++r) out[r][0] = out[r][1] = out[r][2] = 0.f;
+  if (L >= 2) {
+    const float s15 = 3.872983346207417f, s5 = 2.23606797749979f;
+    sym(out[4], 0.f, s15, 0.f, 0.f, 0.f, 0.f);
+    sym(out[5], 0.f, 0.f, 0.f, 0.f, s15, 0.f);
+    sym(out[6], -s5, 0.f, 0.f, -s5, 0.f, 2.f * s5);
+    sym(out[7], 0.f, 0.f, s15, 0.f, 0.f, 0.f);
+    sym(out[8], s15, 0.f, 0.f, -s15, 0.f, 0.f);
+  }
+  if (L >= 3) {
+    const float a = 0.25f * 8.366600265340756f, b = 0.25f * 6.48074069840786f, s105 = 10.246950765959598f,
+                c = 0.5f * 2.6457513110645907f, e = 0.5f * 10.246950765959598f;
+    sym(out[9], 6.f * a * y, 6.f * a * x, 0.f, -6.f * a * y, 0.f, 0.f);
+    sym(out[10], 0.f, s105 * z, s105 * y, 0.f, s105 * x, 0.f);
+    sym(out[11], -2.f * b * y, -2.f * b * x, 0.f, -6.f * b * y, 8.f * b * z, 8.f * b * y);
+    sym(out[12], -6.f * c * z, 0.f, -6.f * c * x, -6.f * c * z, -6.f * c * y, 12.f * c * z);
+    sym(out[13], -6.f * b * x, -2.f * b * y, 8.f * b * z, -2.f * b * x, 0.f, 8.f * b * x);
+    sym(out[14], 2.f * e * z, 0.f, 2.f * e * x, -2.f * e * z, -2.f * e * y, 0.f);
+    sym(out[15], 6.f * a * x, -6.f * a * y, 0.f, -6.f * a * x, 0.f, 0.f);
   }
 }
 

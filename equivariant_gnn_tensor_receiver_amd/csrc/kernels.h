@@ -20,6 +20,7 @@ enum StreamMode : int {
   kSnd = 2,      // T_s   += R (x) CG'(g_v, Y)                      (sender)
   kSndT = 3,     // Td_s  += R (x) CG'(g_v, Yd) + Rd (x) CG'(g_v, Y) (sender)
   kBwdPos = 4,   // grad_pos from gS_v and the edge geometry        (receiver)
+  kBwdHess = 5,  // d(force loss)/dpos: H_e phi_e from gS_v          (receiver)
 };
 
 struct StreamPath {
@@ -56,7 +57,7 @@ struct StreamArgs {
   const void* feat_lo;  // kBwdPos: lo bf16 plane of fp32 features split into hi + lo (NULL: bf16 features)
   float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
   const float* gstate;  // receiver-state cotangent gS (kBwdPos, fully connected)
-  float* gpos;          // position gradient, accumulated (kBwdPos)
+  float* gpos;          // position gradient (kBwdPos) or force-loss position derivative (kBwdHess), accumulated
   // kBwdPos with channel-wise weights: the cotangent gS[k, p, c, m3] =
   // W[k, p, c] grad_out[v][out_row + m3][c] is formed in registers
   int32_t cw;           // 1: channel-wise cotangent from W and grad_out

@@ -98,11 +98,88 @@ constexpr int kPosNcl = kPosSlice / 4;  // channels per lane group (8 bf16 of on
 constexpr int kPosMaxWaves = 8;     // waves per block
 constexpr int kPosBatch = 64;       // edges whose geometry is in LDS at a time
 
+// Batch geometry of the position derivative of the force loss (HESS): what
+// the position gradient uses plus R'', the tangent phi = gg_pos[s] - gg_pos[v]
+// (with 1/d in its fourth entry) and the directional Hessians (d^2 Y / dr^2) phi.
 template <int K, int LMAX>
-struct PosLds {
-  EdgeLds<K, LMAX, kBwdPos, kPosBatch> geo;
-  float gr[kPosMaxWaves][kPosBatch][3];  // per wave: its share of g_r per edge of the batch
+struct __attribute__((aligned(16))) HessLds {
+  static constexpr int B = kPosBatch;
+  static constexpr int NSH = sh_count(LMAX);
+  int nbr[B];
+  float R[B][K];
+  float Rd[B][K];
+  float Rdd[B][K];
+  float Y[B][LMAX + 1][8];
+  float J[B][NSH][4];
+  float HYp[B][NSH][4];
+  float rhat[B][4];
+  float phi[B][4];
 };
+
+template <int K, int LMAX, bool HESS>
+struct PosLds {
+  typename std::conditional<HESS, HessLds<K, LMAX>, EdgeLds<K, LMAX, kBwdPos, kPosBatch>>::type geo;
+  float gr[kPosMaxWaves][kPosBatch][3];  // per wave: its share of the per-edge vector
+};
+
+// Geometry of edge e into slot j for the position derivative of the force loss.
+//   HY phi = d^-2 [H_P(u) phi - l grad P(u) (u.phi) - l u (grad P(u).phi) - l P(u) (phi - (l+2) (u.phi) u)]
+// (Y = P(r) / |r|^l, with P homogeneous of degree l evaluated at u = r / d).
+template <int LMAX, int K>
+__device__ __forceinline__ void edge_prep_hess(const StreamArgs& a, int self, float psx, float psy, float psz, int e,
+                                               int j, HessLds<K, LMAX>& L) {
+  constexpr int NSH = sh_count(LMAX);
+  const int nb = a.nbr[e];
+  const float rx = a.pos[3 * (int64_t)nb] - psx, ry = a.pos[3 * (int64_t)nb + 1] - psy,
+              rz = a.pos[3 * (int64_t)nb + 2] - psz;
+  const float d = sqrtf(rx * rx + ry * ry + rz * rz);
+  float ux = 0.f, uy = 0.f, uz = 0.f, inv_d = 0.f;
+  if (d > 0.f) {
+    inv_d = 1.f / d;
+    ux = rx * inv_d;
+    uy = ry * inv_d;
+    uz = rz * inv_d;
+  }
+  float R[K], dR[K], d2R[K];
+  radial2<K>(d, a.inv_cutoff, a.pref, a.env_p, a.env_a, a.env_b, a.env_c, a.env_d, R, dR, d2R);
+  float Y[NSH], G[NSH][3], HP[NSH][3];
+  sh_eval<LMAX>(ux, uy, uz, Y);
+  sh_poly_grad<LMAX>(ux, uy, uz, G);
+  const float fx = a.ggpos[3 * (int64_t)nb] - a.ggpos[3 * (int64_t)self];
+  const float fy = a.ggpos[3 * (int64_t)nb + 1] - a.ggpos[3 * (int64_t)self + 1];
+  const float fz = a.ggpos[3 * (int64_t)nb + 2] - a.ggpos[3 * (int64_t)self + 2];
+  sh_poly_hess_dir<LMAX>(ux, uy, uz, fx, fy, fz, HP);
+  const float uphi = ux * fx + uy * fy + uz * fz;
+  const float uu[3] = {ux, uy, uz}, ff[3] = {fx, fy, fz};
+  L.nbr[j] = nb;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    L.R[j][k] = R[k];
+    L.Rd[j][k] = dR[k];
+    L.Rdd[j][k] = d2R[k];
+  }
+  const float inv_d2 = inv_d * inv_d;
+#pragma unroll
+  for (int i = 0; i < NSH; ++i) {
+    const int li = sh_degree_of_row(i);
+    const float l = (float)li;
+    L.Y[j][li][i - li * li] = Y[i];
+    const float gphi = G[i][0] * fx + G[i][1] * fy + G[i][2] * fz;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      L.J[j][i][c] = (G[i][c] - l * Y[i] * uu[c]) * inv_d;
+      L.HYp[j][i][c] = (HP[i][c] - l * G[i][c] * uphi - l * uu[c] * gphi -
+                        l * Y[i] * (ff[c] - (l + 2.f) * uphi * uu[c])) * inv_d2;
+    }
+  }
+  L.rhat[j][0] = ux;
+  L.rhat[j][1] = uy;
+  L.rhat[j][2] = uz;
+  L.phi[j][0] = fx;
+  L.phi[j][1] = fy;
+  L.phi[j][2] = fz;
+  L.phi[j][3] = inv_d;
+}
 
 // Eight consecutive bf16 values p[c0 .. c0+8) as one MFMA operand (a 16-byte
 // load when `vec`; otherwise each value on its own, clamped into the row: a
@@ -135,8 +212,10 @@ __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
 
 // LO: the gathered features have a lo plane (fp32 features, pre-split);
 // without it they are bf16 values used as stored.  VEC: C is a multiple of
-// the slice, so every operand is one aligned 16-byte (or two) load.
-template <int LMAX, int K, bool LO, bool VEC>
+// the slice, so every operand is one aligned 16-byte (or two) load.  HESS:
+// the per-edge vector is H_e phi_e (the position derivative of the force
+// loss) instead of g_r.
+template <int LMAX, int K, bool LO, bool VEC, bool HESS>
 struct PosWave {
   static constexpr int NSH = (LMAX + 1) * (LMAX + 1);
 
@@ -212,6 +291,27 @@ struct PosWave {
     split_bf16x8(A, hi, lo);
   }
 
+  // HESS: one component J with the tile's fixed m1 adds its shares of
+  // A_i[m2] = sum_k R^(i)_k b_k[m2] (i = 0, 1, 2: R, R', R'') with
+  // b_k[m2] = sum C^p[m1,m2,m3] Z[(p,m3,k),(m1,e)].
+  template <class PK, int J, int M1>
+  __device__ __forceinline__ static void couple3(float q0, float q1, float q2, float (&A0)[NSH], float (&A1)[NSH],
+                                                 float (&A2)[NSH]) {
+    if constexpr (J < PK::TOT) {
+      constexpr int I = PK::member_of(J), M3 = PK::m3_of(J);
+      constexpr int L1 = PK::L1, L2 = PK::l2s[I], L3 = PK::l3s[I];
+      static_for<2 * L2 + 1>([&](auto M2) {
+        constexpr float c = cg_coef(L1, L2, L3, M1, decltype(M2)::value, M3);
+        constexpr int row = L2 * L2 + decltype(M2)::value;
+        if constexpr (c != 0.f) {
+          A0[row] = __builtin_fmaf(c, q0, A0[row]);
+          A1[row] = __builtin_fmaf(c, q1, A1[row]);
+          A2[row] = __builtin_fmaf(c, q2, A2[row]);
+        }
+      });
+    }
+  }
+
   // One component J = (member path, m3) with the tile's fixed m1: the share
   // q (of Q) and pd (of P) of this lane enter alpha and gY.
   template <class PK, int J, int M1, int NY>
@@ -236,7 +336,7 @@ struct PosWave {
   // share of g_r for every edge of the batch to gr[w][e].
   template <class... Ps>
   __device__ __forceinline__ static void run(const StreamArgs& a, int unit, int node, int slice, int nb,
-                                             PosLds<K, LMAX>& S, float (&gr)[kPosBatch][3]) {
+                                             PosLds<K, LMAX, HESS>& S, float (&gr)[kPosBatch][3]) {
     using PK = PosPack<Ps...>;
     constexpr int NIN = PK::NIN;
     constexpr int TILES = (K * PK::TOT + 15) / 16;
@@ -268,20 +368,25 @@ struct PosWave {
     for (int t = 0; t < ntiles; ++t) {
       const int e = t * 16 + i;
       const int ee = min(e, nb - 1);
-      float r4[4], rd4[4];
+      float r4[4], rd4[4], rdd4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         r4[r] = S.geo.R[ee][kb + r];
         rd4[r] = S.geo.Rd[ee][kb + r];
+        if constexpr (HESS) rdd4[r] = S.geo.Rdd[ee][kb + r];
       }
       float y[LMAX + 1][2 * LMAX + 1];
 #pragma unroll
       for (int l = 0; l <= LMAX; ++l)
 #pragma unroll
         for (int m = 0; m < 2 * LMAX + 1; ++m) y[l][m] = (m <= 2 * l && PK::uses_l2(l)) ? S.geo.Y[ee][l][m] : 0.f;
-      float alpha = 0.f, gy[NSH];
+      float alpha = 0.f, gy[NSH], A1[HESS ? NSH : 1], A2[HESS ? NSH : 1];
 #pragma unroll
       for (int r = 0; r < NSH; ++r) gy[r] = 0.f;
+      if constexpr (HESS) {
+#pragma unroll
+        for (int r = 0; r < NSH; ++r) A1[r] = A2[r] = 0.f;
+      }
       const int tn = min(t + 1, ntiles - 1);
       static_for<NIN>([&](auto M1c) {
         constexpr int M1 = decltype(M1c)::value;
@@ -305,7 +410,17 @@ struct PosWave {
             q = __builtin_fmaf(r4[r], acc[T][r], q);
             pd = __builtin_fmaf(rd4[r], acc[T][r], pd);
           }
-          if constexpr (K == 16) {
+          if constexpr (HESS) {  // gy holds A0 = sum_k R_k b_k
+            float q2 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) q2 = __builtin_fmaf(rdd4[r], acc[T][r], q2);
+            if constexpr (K == 16) {
+              couple3<PK, T, M1>(q, pd, q2, gy, A1, A2);
+            } else {
+              couple3<PK, 2 * T, M1>(upper ? 0.f : q, upper ? 0.f : pd, upper ? 0.f : q2, gy, A1, A2);
+              couple3<PK, 2 * T + 1, M1>(upper ? q : 0.f, upper ? pd : 0.f, upper ? q2 : 0.f, gy, A1, A2);
+            }
+          } else if constexpr (K == 16) {
             couple<PK, T, M1>(q, pd, y, alpha, gy);
           } else {
             couple<PK, 2 * T, M1>(upper ? 0.f : q, upper ? 0.f : pd, y, alpha, gy);
@@ -318,19 +433,53 @@ struct PosWave {
         asm volatile("" : "+v"(alpha));
 #pragma unroll
         for (int r = 0; r < NSH; ++r) asm volatile("" : "+v"(gy[r]));
+        if constexpr (HESS) {
+#pragma unroll
+          for (int r = 0; r < NSH; ++r) asm volatile("" : "+v"(A1[r]), "+v"(A2[r]));
+        }
       });
-      // this lane's share of g_r = alpha r_hat + J^T gY (harmonic degrees the bundle uses)
       float vec3[3];
+      if constexpr (HESS) {
+        // this lane's share of H_e phi = a2 (r.phi) r + a1 (phi - (r.phi) r) / d + r (J^T A1 . phi)
+        //   + (r.phi) J^T A1 + sum A0[m] (HY_m phi),  a_i = A_i . Y
+        float a1 = 0.f, a2 = 0.f, jb[3] = {0.f, 0.f, 0.f}, hy[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cc = 0; cc < 3; ++cc) vec3[cc] = alpha * S.geo.rhat[ee][cc];
+        for (int l = 0; l <= LMAX; ++l) {
+          if (!PK::uses_l2(l)) continue;
 #pragma unroll
-      for (int l = 1; l <= LMAX; ++l) {
-        if (!PK::uses_l2(l)) continue;
+          for (int m = 0; m < 2 * l + 1; ++m) {
+            const int row = l * l + m;
+            const float yv = S.geo.Y[ee][l][m];
+            a1 = __builtin_fmaf(A1[row], yv, a1);
+            a2 = __builtin_fmaf(A2[row], yv, a2);
 #pragma unroll
-        for (int m = 0; m < 2 * l + 1; ++m)
+            for (int cc = 0; cc < 3; ++cc) {
+              jb[cc] = __builtin_fmaf(A1[row], S.geo.J[ee][row][cc], jb[cc]);
+              hy[cc] = __builtin_fmaf(gy[row], S.geo.HYp[ee][row][cc], hy[cc]);
+            }
+          }
+        }
+        const float ph[3] = {S.geo.phi[ee][0], S.geo.phi[ee][1], S.geo.phi[ee][2]};
+        const float inv_d = S.geo.phi[ee][3];
+        const float rh[3] = {S.geo.rhat[ee][0], S.geo.rhat[ee][1], S.geo.rhat[ee][2]};
+        const float rphi = rh[0] * ph[0] + rh[1] * ph[1] + rh[2] * ph[2];
+        const float jphi = jb[0] * ph[0] + jb[1] * ph[1] + jb[2] * ph[2];
 #pragma unroll
-          for (int cc = 0; cc < 3; ++cc)
-            vec3[cc] = __builtin_fmaf(gy[l * l + m], S.geo.J[ee][l * l + m][cc], vec3[cc]);
+        for (int cc = 0; cc < 3; ++cc)
+          vec3[cc] = a2 * rphi * rh[cc] + a1 * inv_d * (ph[cc] - rphi * rh[cc]) + rh[cc] * jphi + rphi * jb[cc] + hy[cc];
+      } else {
+        // this lane's share of g_r = alpha r_hat + J^T gY (harmonic degrees the bundle uses)
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc) vec3[cc] = alpha * S.geo.rhat[ee][cc];
+#pragma unroll
+        for (int l = 1; l <= LMAX; ++l) {
+          if (!PK::uses_l2(l)) continue;
+#pragma unroll
+          for (int m = 0; m < 2 * l + 1; ++m)
+#pragma unroll
+            for (int cc = 0; cc < 3; ++cc)
+              vec3[cc] = __builtin_fmaf(gy[l * l + m], S.geo.J[ee][l * l + m][cc], vec3[cc]);
+        }
       }
 #pragma unroll
       for (int cc = 0; cc < 3; ++cc) vec3[cc] = half32_add(row16_add(vec3[cc]));
@@ -343,27 +492,29 @@ struct PosWave {
 };
 
 // A bundle (BUNDLED) or single-path unit for the position gradient.
-template <int LMAX, int K, bool LO, bool VEC, bool BUNDLED>
+template <int LMAX, int K, bool LO, bool VEC, bool HESS>
 struct PosUnitRunner {
   const StreamArgs& a;
   int unit, node, slice, nb;
-  PosLds<K, LMAX>& S;
+  PosLds<K, LMAX, HESS>& S;
   float (&gr)[kPosBatch][3];
   template <class... Ps>
   __device__ __forceinline__ void run(const StreamArgs&) {
-    PosWave<LMAX, K, LO, VEC>::template run<Ps...>(a, unit, node, slice, nb, S, gr);
+    PosWave<LMAX, K, LO, VEC, HESS>::template run<Ps...>(a, unit, node, slice, nb, S, gr);
   }
 };
 
 // Waves per SIMD the register allocation must leave room for (lmax 3 with
-// K = 8 needs about 220 registers, the others fit 168).
-constexpr int pos_min_waves(int lmax, int K) { return lmax <= 1 ? 4 : (lmax == 3 && K == 8 ? 2 : 3); }
+// K = 8, and lmax 3 for the Hessian, need more than the 168 registers of three).
+constexpr int pos_min_waves(int lmax, int K, bool hess) {
+  return lmax <= 1 ? 4 : (lmax == 3 && (K == 8 || hess) ? 2 : 3);
+}
 
-template <int LMAX, int K, bool LO, bool VEC, bool BUNDLED>
-__global__ __launch_bounds__(64 * kPosMaxWaves) __attribute__((amdgpu_waves_per_eu(pos_min_waves(LMAX, K))))
+template <int LMAX, int K, bool LO, bool VEC, bool BUNDLED, bool HESS>
+__global__ __launch_bounds__(64 * kPosMaxWaves) __attribute__((amdgpu_waves_per_eu(pos_min_waves(LMAX, K, HESS))))
 void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
   const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  __shared__ PosLds<K, LMAX> S;
+  __shared__ PosLds<K, LMAX, HESS> S;
   const uint32_t item = (uint32_t)xcd_item(blockIdx.x, gridDim.x);
   if (item >= (uint32_t)nodes) return;  // uniform over the block
   const int node = a.order ? a.order[item] : (int)item;
@@ -377,13 +528,18 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
   for (int b0 = e0; b0 < e1; b0 += kPosBatch) {
     const int nb = min(kPosBatch, e1 - b0);
     __syncthreads();
-    if ((int)threadIdx.x < nb) edge_prep(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, S.geo);
+    if ((int)threadIdx.x < nb) {
+      if constexpr (HESS)
+        edge_prep_hess(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, S.geo);
+      else
+        edge_prep(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, S.geo);
+    }
 #pragma unroll
     for (int cc = 0; cc < 3; ++cc) S.gr[w][lane][cc] = 0.f;
     __syncthreads();
     for (int pr = w; pr < npairs; pr += nw) {
       const int unit = pr % a.nunits, slice = pr / a.nunits;
-      PosUnitRunner<LMAX, K, LO, VEC, BUNDLED> run{a, unit, node, slice, nb, S, S.gr[w]};
+      PosUnitRunner<LMAX, K, LO, VEC, HESS> run{a, unit, node, slice, nb, S, S.gr[w]};
       if constexpr (BUNDLED) {
         Bundles<LMAX, K, 2>::run(unit, run, a);
       } else {
@@ -402,7 +558,7 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
       }
     }
     __syncthreads();
-    if (w == 0 && lane < nb) {  // fixed-order sum over the waves, then the sender's share
+    if (w == 0 && lane < nb) {  // fixed-order sum over the waves, then the sender's share (+) and the receiver's (-)
       float v0 = 0.f, v1 = 0.f, v2 = 0.f;
       for (int ww = 0; ww < nw; ++ww) {
         v0 += S.gr[ww][lane][0];
@@ -439,7 +595,7 @@ inline int pos_block_waves(int npairs) {
 
 // LO: the features are fp32, pre-split into the bf16 planes a.feat (hi) and
 // a.feat_lo (lo); otherwise a.feat holds them in bf16.
-template <bool LO>
+template <bool LO, bool HESS>
 hipError_t launch_pos(int lmax, int K, const StreamArgs& a, hipStream_t s) {
   if (LO != (a.feat_lo != nullptr)) return hipErrorInvalidValue;
   const int64_t nodes = a.num_nodes;
@@ -454,13 +610,13 @@ hipError_t launch_pos(int lmax, int K, const StreamArgs& a, hipStream_t s) {
 #define TPCONV_LAUNCH(LM, KK)                                                                                      \
   if (lmax == LM && K == KK) {                                                                                     \
     if (vec && a.bundled)                                                                                          \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, true>), dim3((unsigned)grid), block, 0, s, a, nodes);      \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, true, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);      \
     else if (vec)                                                                                                  \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, false>), dim3((unsigned)grid), block, 0, s, a, nodes);     \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, false, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);     \
     else if (a.bundled)                                                                                            \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, true>), dim3((unsigned)grid), block, 0, s, a, nodes);     \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, true, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);     \
     else                                                                                                           \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, false>), dim3((unsigned)grid), block, 0, s, a, nodes);    \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, false, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);    \
     return hipGetLastError();                                                                                      \
   }
   TPCONV_LAUNCH(0, 8) TPCONV_LAUNCH(0, 16)

@@ -29,7 +29,7 @@ EXPORTS = ("tpconv_plan_create", "tpconv_plan_destroy", "tpconv_plan_info", "tpc
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string",
            "tpconv_kernel_timing", "tpconv_kernel_timing_read", "tpconv_forward_static", "tpconv_graph_order")
 KERNELS = ("stream_fwd", "stream_jvp", "stream_snd", "stream_sndt", "stream_bwdpos", "gemm_out", "gemm_gs",
-           "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce")
+           "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce", "stream_hess")
 
 
 class TpconvError(RuntimeError):
@@ -72,7 +72,7 @@ def _lib():
         L.tpconv_forward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, c_size_t, P]
         L.tpconv_forward_static.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P]
         L.tpconv_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
-        L.tpconv_double_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
+        L.tpconv_double_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, P, c_size_t, P]
         L.tpconv_kernel_timing.argtypes = [c_int32]
         L.tpconv_kernel_timing_read.argtypes = [c_int32, POINTER(c_int64), POINTER(c_double)]
         L.tpconv_status_string.argtypes = [c_int32]
@@ -330,8 +330,10 @@ def tpconv_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, saved_state=N
     return grad_x, grad_W, grad_pos
 
 
-def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos, want=("W", "x", "grad_out"),
-                           workspace=None, stream=None, d_W=None, d_x=None, d_grad_out=None):
+def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos, want=("W", "x", "grad_out", "pos"),
+                           workspace=None, stream=None, d_W=None, d_x=None, d_grad_out=None, d_pos=None):
+    """Gradients of sum_n <gg_pos[n], grad_pos[n]>: (d_W, d_x, d_grad_out, d_pos) for the names in
+    `want` ("W", "x", "grad_out", "pos"); the others are None."""
     import torch
 
     dev = pos.device
@@ -342,9 +344,12 @@ def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos
         d_x = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev)
     if d_grad_out is None and "grad_out" in want:
         d_grad_out = torch.empty((N, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev)
-    _keep_for_stream(stream, d_W, d_x, d_grad_out)
+    if d_pos is None and "pos" in want:
+        d_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
+    _keep_for_stream(stream, d_W, d_x, d_grad_out, d_pos)
     _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.rows_out, plan.ch_out), gg_pos=(gg_pos, 1, 3),
-                  d_x=(d_x, plan.rows_in, plan.ch_in), d_grad_out=(d_grad_out, plan.rows_out, plan.ch_out))
+                  d_x=(d_x, plan.rows_in, plan.ch_in), d_grad_out=(d_grad_out, plan.rows_out, plan.ch_out),
+                  d_pos=(d_pos, 1, 3))
     _require(d_W, "d_W", torch.float32, plan.w_numel, dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_DOUBLE_BACKWARD, N, graph.num_edges), dev)
@@ -353,10 +358,10 @@ def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos
     g = graph.c()
     _check(_lib().tpconv_double_backward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W),
                                          _ptr(grad_out), _ptr(gg_pos), _ptr(d_W), _ptr(d_x), _ptr(d_grad_out),
-                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _ptr(d_pos), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                          _stream(stream)),
            "tpconv_double_backward")
-    return d_W, d_x, d_grad_out
+    return d_W, d_x, d_grad_out, d_pos
 
 
 def tpconv_kernel_timing(enable: bool):

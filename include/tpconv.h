@@ -217,17 +217,22 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
 
 /* Double backward ("Sobek" page, abstract: the streaming formulation covers the
  * double backward; tangent states are node-sized like S and T) of the scalar
- * force loss L = sum_n <gg_pos[n], grad_pos[n]>,
- * where grad_pos is the backward above for the given grad_out:
- *   d_W = dL/dW, d_x = dL/dx, d_grad_out = dL/dgrad_out (each may be NULL).
- * With phi_e = gg_pos[s] - gg_pos[v], L is the derivative of the edge
- * energies along phi, so it is linear in W, x and grad_out; dL/dpos (the
- * Hessian term) is not computed.  Needs the CSC view when d_x is requested. */
+ * force loss L = sum_n <gg_pos[n], grad_pos[n]>, where grad_pos is the
+ * backward above for the given grad_out:
+ *   d_W = dL/dW, d_x = dL/dx, d_grad_out = dL/dgrad_out, d_pos = dL/dpos
+ *   (each may be NULL; at least one must be given).
+ * With phi_e = gg_pos[s] - gg_pos[v], L = sum_e <phi_e, grad_r eps_e> for the
+ * edge energies eps_e = <grad_out[v], message_e>; L is linear in W, x and
+ * grad_out, and its position derivative is the Hessian term
+ * dL/dpos[s] += H_e phi_e, dL/dpos[v] -= H_e phi_e (H_e the Hessian of eps_e
+ * w.r.t. r_e, from R'' and the second derivatives of the harmonics), summed
+ * with fp32 atomics like grad_pos.  Needs the CSC view when d_x is requested.
+ * Errors as tpconv_backward. */
 tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos,
                                      const void* x, const void* W, const float* grad_out,
                                      const float* gg_pos, float* d_W, float* d_x,
-                                     float* d_grad_out, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     float* d_grad_out, float* d_pos, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* tpconv_forward without workspace and without any allocation, for callers
  * that cannot allocate device memory (code under HIP stream capture, tight
@@ -262,7 +267,8 @@ typedef enum {
   TPCONV_KERNEL_CW_CONTRACT = 12,  /* channel-wise: out, grad_x, d_grad_out, d_x from S / T */
   TPCONV_KERNEL_CW_GW = 13,        /* channel-wise: grad_W partials (also d_W) */
   TPCONV_KERNEL_CW_REDUCE = 14,    /* channel-wise: ordered sum of the partials */
-  TPCONV_KERNEL_COUNT = 15
+  TPCONV_KERNEL_STREAM_HESS = 15,  /* receiver stream: position derivative of the force loss */
+  TPCONV_KERNEL_COUNT = 16
 } tpconv_kernel;
 
 /* Diagnostics for roofline measurements (not needed for computing).

@@ -106,10 +106,12 @@ class DeviceCase:
         return otp.backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out)
 
     def o_double_backward(self, g_out, snd=None, rcv=None):
+        """Oracle (d_W, d_x, d_grad_out, d_pos)."""
         n = self.np
         snd = n["senders"] if snd is None else snd
         rcv = self.receivers if rcv is None else rcv
-        return otp.double_backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"])
+        return otp.double_backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"]) + (
+            otp.double_backward_pos(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"]),)
 
 
 def small_case(irreps_in, irreps_out, sh_lmax, K, N, deg, seed, dtype="f32", channelwise=False, w_dtype=None,

@@ -62,8 +62,8 @@ def test_cw_backward(case):
 
 def test_cw_double_backward(case):
     say("[step] double backward")
-    dW, dx, dgo = case.double_backward()
-    rW, rx, rgo = case.o_double_backward(case.np["g_out"])
-    eW, ex, eg = rel_err(dW, rW), rel_err(dx, rx), rel_err(dgo, rgo)
-    say(f"  d_W {eW:.2e}  d_x {ex:.2e}  d_g_out {eg:.2e}")
-    assert eW <= GRAD_TOL and ex <= GRAD_TOL and eg <= GRAD_TOL
+    dW, dx, dgo, dp = case.double_backward()
+    rW, rx, rgo, rp = case.o_double_backward(case.np["g_out"])
+    eW, ex, eg, ep = rel_err(dW, rW), rel_err(dx, rx), rel_err(dgo, rgo), rel_err(dp, rp)
+    say(f"  d_W {eW:.2e}  d_x {ex:.2e}  d_g_out {eg:.2e}  d_pos {ep:.2e}")
+    assert eW <= GRAD_TOL and ex <= GRAD_TOL and eg <= GRAD_TOL and ep <= GRAD_TOL

@@ -43,7 +43,7 @@ def run_passes(deg):
     out = torch.empty((N, plan.rows_out, plan.ch_out), **f32)
     gx, dx = (torch.empty((N, plan.rows_in, plan.ch_in), **f32) for _ in range(2))
     gW, dW = (torch.empty(plan.w_shape, **f32) for _ in range(2))
-    gp = torch.empty((N, 3), **f32)
+    gp, dp = torch.empty((N, 3), **f32), torch.empty((N, 3), **f32)
     dg = torch.empty((N, plan.rows_out, plan.ch_out), **f32)
     ws = {op: plan.workspace_size(op, N, E) for op in (tp.OP_FORWARD, tp.OP_BACKWARD, tp.OP_DOUBLE_BACKWARD)}
     buf = {op: torch.empty(max(b, 1), dtype=torch.uint8, device=dev) for op, b in ws.items()}
@@ -53,7 +53,7 @@ def run_passes(deg):
         tp.tpconv_backward(plan, graph, P, X, W, G, workspace=buf[tp.OP_BACKWARD], grad_x=gx, grad_W=gW,
                            grad_pos=gp)
         tp.tpconv_double_backward(plan, graph, P, X, W, G, GG, workspace=buf[tp.OP_DOUBLE_BACKWARD], d_W=dW,
-                                  d_x=dx, d_grad_out=dg)
+                                  d_x=dx, d_grad_out=dg, d_pos=dp)
 
     passes()  # first use: code objects and the side stream are set up
     torch.cuda.synchronize()
@@ -64,7 +64,7 @@ def run_passes(deg):
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated() - base
     free1, _ = torch.cuda.mem_get_info()
-    for a in (out, gx, gW, gp, dW, dx, dg):
+    for a in (out, gx, gW, gp, dW, dx, dg, dp):
         assert torch.isfinite(a).all()
     return E, ws, peak, free0 - free1
 

@@ -5,8 +5,8 @@ exactly from a seeded sample V* of receivers:
   forward      out[V*] needs only the in-edges of V*;
   backward     with g_out zero outside V*, g_x (every sender), gW and g_pos
                (every node) are exact sums over the in-edges of V*;
-  double bwd   the same masked g_out makes dL/dW and dL/dx exact over the
-               in-edges of V*, and dL/dg_out[V*] needs only those edges.
+  double bwd   the same masked g_out makes dL/dW, dL/dx and dL/dpos exact
+               over the in-edges of V*, and dL/dg_out[V*] needs only those edges.
 The GPU always runs the whole graph.
 """
 import numpy as np
@@ -77,8 +77,8 @@ def test_workload_double_backward(wl):
         pytest.skip("no double backward in this workload")
     say(f"[step] {name} double backward with g_out masked to the sample")
     go = torch.from_numpy(g_masked).to(case.dev)
-    dW, dx, dgo = case.double_backward(g_out=go)
-    rW, rx, rgo = case.o_double_backward(g_masked, snd, rcv)
-    eW, ex, eg = rel_err(dW, rW), rel_err(dx, rx), rel_err(dgo[vs], rgo[vs])
-    say(f"  d_W {eW:.2e}  d_x {ex:.2e}  d_g_out {eg:.2e}")
-    assert eW <= GRAD_TOL and ex <= GRAD_TOL and eg <= GRAD_TOL
+    dW, dx, dgo, dp = case.double_backward(g_out=go)
+    rW, rx, rgo, rp = case.o_double_backward(g_masked, snd, rcv)
+    eW, ex, eg, ep = rel_err(dW, rW), rel_err(dx, rx), rel_err(dgo[vs], rgo[vs]), rel_err(dp, rp)
+    say(f"  d_W {eW:.2e}  d_x {ex:.2e}  d_g_out {eg:.2e}  d_pos {ep:.2e}")
+    assert eW <= GRAD_TOL and ex <= GRAD_TOL and eg <= GRAD_TOL and ep <= GRAD_TOL

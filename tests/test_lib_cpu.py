@@ -121,7 +121,9 @@ def test_argument_errors_before_any_launch():
     assert lib.tpconv_backward(plan.handle, ctypes.byref(g), fake, fake, fake, fake, None, fake, None, None,
                                fake, 1 << 30, None) == 1
     assert lib.tpconv_double_backward(plan.handle, ctypes.byref(g), fake, fake, fake, fake, None, fake, None,
-                                      None, fake, 1 << 30, None) == 1
+                                      None, None, fake, 1 << 30, None) == 1
+    assert lib.tpconv_double_backward(plan.handle, ctypes.byref(g), fake, fake, fake, fake, fake, None, None,
+                                      None, None, fake, 1 << 30, None) == 1
     # graph prepare / order: short workspace, missing positions
     assert lib.tpconv_graph_prepare(plan.handle, ctypes.byref(g), fake, fake, 1, fake, 8, None) == 4
     assert lib.tpconv_graph_order(plan.handle, ctypes.byref(g), fake, fake, fake, 8, None) == 4
