@@ -28,8 +28,10 @@ U_e[p, c, m3] (the Sobek page's abstract names two operator families; this
 reading takes the channel-wise product as the second).
 
 Layouts (shared with the library's public header only as a data contract):
-  x   [N][D_in][C_in],  out [N][D_out][C_out]   rows ordered by irreps, l^2+l+m
-  W   [K][P][C_in][C_out] (uvw) or [K][P][C] (uvu), P paths in oracle.cg order
+  x   [N][F_in], out [N][F_out]: per irrep a [2l+1][mul] block, irreps in order
+      (with one multiplicity per side: [N][D][C], rows l^2+l+m)
+  W   per k, per path a [mul(l1 irrep)][mul(l3 irrep)] block (uvw) or a
+      [mul] block (uvu), P paths in oracle.cg order (uniform: [K][P][Ci][Co] / [K][P][C])
   pos [N][3]
 """
 from __future__ import annotations
@@ -45,6 +47,18 @@ from . import sh as _sh
 
 @dataclass
 class Problem:
+    """Irreps, paths and layouts of one operator.
+
+    Multiplicities may differ between irreps ("varied feature structures"):
+    irrep i of a side has mul_i channels.  Node tensors are stored flat,
+    [N][F] with F = sum_i (2l_i+1) mul_i, irrep i's block [2l_i+1][mul_i] at
+    offset foff[i]; with one multiplicity C per side this is the [N][D][C]
+    array.  Fully connected weights are [K][sum_p mul(i1_p) mul(i3_p)], path
+    p's block [mul(i1_p)][mul(i3_p)] at woff[p] within each k; with uniform
+    multiplicities this is [K][P][C_in][C_out].  Channel-wise weights need
+    mul(i1_p) = mul(i3_p) and are [K][sum_p mul_p] (uniform: [K][P][C]).
+    """
+
     irreps_in: str
     irreps_out: str
     sh_lmax: int
@@ -61,36 +75,45 @@ class Problem:
         self.ir_out = _cg.parse_irreps(self.irreps_out)
         muls_in = {m for m, _, _ in self.ir_in}
         muls_out = {m for m, _, _ in self.ir_out}
-        if len(muls_in) != 1 or len(muls_out) != 1:
-            raise ValueError("uniform multiplicity per irreps string is required")
-        self.C_in = muls_in.pop()
-        self.C_out = muls_out.pop()
-        if self.channelwise and self.C_in != self.C_out:
-            raise ValueError("the channel-wise product needs equal multiplicities")
+        self.uniform = len(muls_in) == 1 and len(muls_out) == 1
+        self.C_in = next(iter(muls_in)) if len(muls_in) == 1 else None
+        self.C_out = next(iter(muls_out)) if len(muls_out) == 1 else None
         self.D_in = _cg.irreps_dim(self.ir_in)
         self.D_out = _cg.irreps_dim(self.ir_out)
         self.off_in = _cg.irreps_offsets(self.ir_in)
         self.off_out = _cg.irreps_offsets(self.ir_out)
+        self.F_in = sum((2 * l + 1) * m for m, l, _ in self.ir_in)
+        self.F_out = sum((2 * l + 1) * m for m, l, _ in self.ir_out)
+        self.foff_in = list(np.cumsum([0] + [(2 * l + 1) * m for m, l, _ in self.ir_in])[:-1])
+        self.foff_out = list(np.cumsum([0] + [(2 * l + 1) * m for m, l, _ in self.ir_out])[:-1])
         self.paths = _cg.enumerate_paths(self.ir_in, self.sh_lmax, self.ir_out)
         self.P = len(self.paths)
+        woff = 0
         for p in self.paths:
             p["C"] = _cg.real_cg(p["l1"], p["l2"], p["l3"])
+            p["C1"] = self.ir_in[p["i1"]][0]
+            p["C3"] = self.ir_out[p["i3"]][0]
+            if self.channelwise and p["C1"] != p["C3"]:
+                raise ValueError("the channel-wise product needs equal multiplicities on each path")
+            p["woff"] = woff
+            woff += p["C1"] if self.channelwise else p["C1"] * p["C3"]
+        self.W_per_k = woff
+        if self.channelwise and self.uniform and self.C_in != self.C_out:
+            raise ValueError("the channel-wise product needs equal multiplicities")
 
     @property
     def w_shape(self):
-        if self.channelwise:
-            return (self.num_basis, self.P, self.C_in)
-        return (self.num_basis, self.P, self.C_in, self.C_out)
+        if self.uniform:
+            if self.channelwise:
+                return (self.num_basis, self.P, self.C_in)
+            return (self.num_basis, self.P, self.C_in, self.C_out)
+        return (self.num_basis, self.W_per_k)
 
-    # einsum forms of the weight contractions.  Index letters: e edge, k basis,
-    # p path, i input channel, o output channel, c (in U) the m3 component.
-    @property
-    def ops(self):
-        if self.channelwise:  # w_e[e, p, i]; messages and adjoints keep the channel i
-            return dict(w="ek,kpi->epi", msg="ei,eic->eci", g_w="eic,eci->ei", g_U="ei,eci->eic",
-                        g_W="ek,epi->kpi", g_R="kpi,epi->ek", dW_a="ek,ei->ki", dW_b="ek,eic,eci->ki")
-        return dict(w="ek,kpio->epio", msg="eio,eic->eco", g_w="eic,eco->eio", g_U="eio,eco->eic",
-                    g_W="ek,epio->kpio", g_R="kpio,epio->ek", dW_a="ek,eio->kio", dW_b="ek,eic,eco->kio")
+    def in_shape(self, N):
+        return (N, self.D_in, self.C_in) if self.uniform else (N, self.F_in)
+
+    def out_shape(self, N):
+        return (N, self.D_out, self.C_out) if self.uniform else (N, self.F_out)
 
 
 def csr_receivers(rowptr: np.ndarray) -> np.ndarray:
@@ -107,7 +130,7 @@ def _geometry(pos, s, v):
 
 
 def _chunks(prob: Problem, E: int):
-    per_edge = 8 * max(1, prob.P * prob.C_in * prob.C_out)
+    per_edge = 8 * max(1, prob.W_per_k)
     step = int(max(1, min(E, 48_000_000 // per_edge)))
     for a in range(0, E, step):
         yield a, min(E, a + step)
@@ -120,9 +143,29 @@ def _edge_terms(prob, pos, s, v):
     return r, d, rhat, R, Y
 
 
+# Views of the flat node tensors and weights for one path.
+def _in_slice(prob, p):
+    o = prob.foff_in[p["i1"]]
+    return slice(o, o + (2 * p["l1"] + 1) * p["C1"])
+
+
+def _out_slice(prob, p):
+    o = prob.foff_out[p["i3"]]
+    return slice(o, o + (2 * p["l3"] + 1) * p["C3"])
+
+
 def _x_block(prob, x, s, p):
-    o = prob.off_in[p["i1"]]
-    return x[s, o:o + 2 * p["l1"] + 1, :]               # [e, m1, ci]
+    return x[s, _in_slice(prob, p)].reshape(len(s), 2 * p["l1"] + 1, p["C1"])      # [e, m1, ci]
+
+
+def _go_block(prob, g, v, p):
+    return g[v, _out_slice(prob, p)].reshape(len(v), 2 * p["l3"] + 1, p["C3"])     # [e, m3, co]
+
+
+def _w_block(prob, W, p):
+    if prob.channelwise:
+        return W[:, p["woff"]:p["woff"] + p["C1"]]                                   # [k, i]
+    return W[:, p["woff"]:p["woff"] + p["C1"] * p["C3"]].reshape(-1, p["C1"], p["C3"])  # [k, i, o]
 
 
 def _y_block(Y, p):
@@ -130,19 +173,29 @@ def _y_block(Y, p):
     return Y[:, l2 * l2:(l2 + 1) * (l2 + 1)]            # [e, m2]
 
 
-def _out_rows(prob, p):
-    o = prob.off_out[p["i3"]]
-    return slice(o, o + 2 * p["l3"] + 1)
+def _flat(prob, a, side):
+    a = np.asarray(a, dtype=np.float64)
+    return a.reshape(a.shape[0], prob.F_in if side == "in" else prob.F_out)
 
 
-def _in_rows(prob, p):
-    o = prob.off_in[p["i1"]]
-    return slice(o, o + 2 * p["l1"] + 1)
+def _flat_w(prob, W):
+    W = np.asarray(W, dtype=np.float64)
+    return W.reshape(W.shape[0], prob.W_per_k)
 
 
 def _coupling(C, xs, y):
     """U[e, ci, m3] = sum_{m1,m2} C[m1,m2,m3] xs[e,m1,ci] y[e,m2]."""
     return np.einsum("abc,eai,eb->eic", C, xs, y, optimize=True)
+
+
+# einsum forms of the per-path weight contractions (e edge, k basis, i input
+# channel, o output channel, c the m3 component).
+def _ops(prob):
+    if prob.channelwise:  # w_e[e, i]; messages and adjoints keep the channel i
+        return dict(w="ek,ki->ei", msg="ei,eic->eci", g_w="eic,eci->ei", g_U="ei,eci->eic",
+                    g_W="ek,ei->ki", g_R="ki,ei->ek", dW_b="ek,eic,eci->ki", G="ki,eci->ekic")
+    return dict(w="ek,kio->eio", msg="eio,eic->eco", g_w="eic,eco->eio", g_U="eio,eco->eic",
+                g_W="ek,eio->kio", g_R="kio,eio->ek", dW_b="ek,eic,eco->kio", G="kio,eco->ekic")
 
 
 def _as64(a):
@@ -151,63 +204,65 @@ def _as64(a):
 
 def forward(prob: Problem, pos, senders, receivers, x, W, num_nodes=None):
     """out[v] = sum over edges into v of the materialised message m_e."""
-    pos, x, W = _as64(pos), _as64(x), _as64(W)
+    pos = _as64(pos)
+    xf, Wf = _flat(prob, x, "in"), _flat_w(prob, W)
     senders = np.asarray(senders, dtype=np.int64)
     receivers = np.asarray(receivers, dtype=np.int64)
-    N = x.shape[0] if num_nodes is None else num_nodes
-    out = np.zeros((N, prob.D_out, prob.C_out))
+    N = xf.shape[0] if num_nodes is None else num_nodes
+    out = np.zeros((N, prob.F_out))
+    ops = _ops(prob)
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
         _, _, _, R, Y = _edge_terms(prob, pos, s, v)
-        ops = prob.ops
-        w_e = np.einsum(ops["w"], R, W, optimize=True)              # per-edge weights
-        for pi, p in enumerate(prob.paths):
-            U = _coupling(p["C"], _x_block(prob, x, s, p), _y_block(Y, p))
-            msg = np.einsum(ops["msg"], w_e[:, pi], U, optimize=True)      # message
-            np.add.at(out[:, _out_rows(prob, p), :], v, msg)
-    return out
+        for p in prob.paths:
+            w_e = np.einsum(ops["w"], R, _w_block(prob, Wf, p), optimize=True)       # per-edge weights
+            U = _coupling(p["C"], _x_block(prob, xf, s, p), _y_block(Y, p))
+            msg = np.einsum(ops["msg"], w_e, U, optimize=True)                        # message [e, m3, co]
+            np.add.at(out[:, _out_slice(prob, p)], v, msg.reshape(len(s), -1))
+    return out.reshape(prob.out_shape(N))
 
 
 def backward(prob: Problem, pos, senders, receivers, x, W, g_out):
     """Materialised adjoints; returns (g_x, g_W, g_pos) for the loss <g_out, out>."""
-    pos, x, W, g_out = _as64(pos), _as64(x), _as64(W), _as64(g_out)
+    pos = _as64(pos)
+    xf, Wf, gf = _flat(prob, x, "in"), _flat_w(prob, W), _flat(prob, g_out, "out")
     senders = np.asarray(senders, dtype=np.int64)
     receivers = np.asarray(receivers, dtype=np.int64)
-    N = x.shape[0]
+    N = xf.shape[0]
     K = prob.num_basis
-    g_x = np.zeros_like(x)
-    g_W = np.zeros_like(W)
+    g_x = np.zeros_like(xf)
+    g_W = np.zeros_like(Wf)
     g_pos = np.zeros_like(pos)
+    ops = _ops(prob)
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
         r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
         dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
         JY = _sh.sh_jacobian(prob.sh_lmax, r)                     # [e, Dsh, 3]
-        ops = prob.ops
-        w_e = np.einsum(ops["w"], R, W, optimize=True)
-        g_m = g_out[v]                                           # message adjoint
-        g_w = np.zeros_like(w_e)
         g_Y = np.zeros_like(Y)
-        for pi, p in enumerate(prob.paths):
+        g_R = np.zeros_like(R)
+        for p in prob.paths:
             C = p["C"]
-            xs = _x_block(prob, x, s, p)
+            Wp = _w_block(prob, Wf, p)
+            w_e = np.einsum(ops["w"], R, Wp, optimize=True)
+            xs = _x_block(prob, xf, s, p)
             y = _y_block(Y, p)
             U = _coupling(C, xs, y)
-            gm = g_m[:, _out_rows(prob, p), :]                     # [e, m3, co]
-            g_w[:, pi] = np.einsum(ops["g_w"], U, gm, optimize=True)
-            g_U = np.einsum(ops["g_U"], w_e[:, pi], gm, optimize=True)
+            gm = _go_block(prob, gf, v, p)                            # message adjoint [e, m3, co]
+            g_w = np.einsum(ops["g_w"], U, gm, optimize=True)
+            g_U = np.einsum(ops["g_U"], w_e, gm, optimize=True)
             gx_e = np.einsum("abc,eb,eic->eai", C, y, g_U, optimize=True)
-            np.add.at(g_x[:, _in_rows(prob, p), :], s, gx_e)
+            np.add.at(g_x[:, _in_slice(prob, p)], s, gx_e.reshape(len(s), -1))
             l2 = p["l2"]
-            g_Y[:, l2 * l2:(l2 + 1) * (l2 + 1)] += np.einsum(
-                "abc,eai,eic->eb", C, xs, g_U, optimize=True)
-        g_W += np.einsum(ops["g_W"], R, g_w, optimize=True)
-        g_R = np.einsum(ops["g_R"], W, g_w, optimize=True)
+            g_Y[:, l2 * l2:(l2 + 1) * (l2 + 1)] += np.einsum("abc,eai,eic->eb", C, xs, g_U, optimize=True)
+            blk = np.einsum(ops["g_W"], R, g_w, optimize=True)
+            g_W[:, p["woff"]:p["woff"] + blk[0].size] += blk.reshape(K, -1)
+            g_R += np.einsum(ops["g_R"], Wp, g_w, optimize=True)
         g_r = (np.einsum("ek,ek->e", g_R, dR)[:, None] * rhat
                + np.einsum("em,emj->ej", g_Y, JY))
         np.add.at(g_pos, s, g_r)
         np.add.at(g_pos, v, -g_r)
-    return g_x, g_W, g_pos
+    return g_x.reshape(prob.in_shape(N)), g_W.reshape(np.shape(W)), g_pos
 
 
 def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos):
@@ -217,16 +272,18 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
     derivative of the edge energy <g_m_e, m_e> along phi_e.  The tangents are
     R_dot = R'(d) (r_hat . phi), Y_dot = J_Y phi, U_dot = CG(x_s, Y_dot) and
     w_dot = sum_k R_dot[k] W[k]; L_F is linear in W, x and g_out, so no second
-    derivatives of R or Y appear.  d/dpos (the Hessian term) is not computed.
+    derivatives of R or Y appear (those enter only d/dpos, double_backward_pos).
     """
-    pos, x, W = _as64(pos), _as64(x), _as64(W)
-    g_out, gg_pos = _as64(g_out), _as64(gg_pos)
+    pos, gg_pos = _as64(pos), _as64(gg_pos)
+    xf, Wf, gf = _flat(prob, x, "in"), _flat_w(prob, W), _flat(prob, g_out, "out")
     senders = np.asarray(senders, dtype=np.int64)
     receivers = np.asarray(receivers, dtype=np.int64)
+    N = xf.shape[0]
     K = prob.num_basis
-    d_W = np.zeros_like(W)
-    d_x = np.zeros_like(x)
-    d_gout = np.zeros_like(g_out)
+    d_W = np.zeros_like(Wf)
+    d_x = np.zeros_like(xf)
+    d_gout = np.zeros_like(gf)
+    ops = _ops(prob)
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
         r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
@@ -235,30 +292,30 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
         phi = gg_pos[s] - gg_pos[v]
         R_dot = dR * np.einsum("ej,ej->e", rhat, phi)[:, None]
         Y_dot = np.einsum("emj,ej->em", JY, phi)
-        ops = prob.ops
-        w_e = np.einsum(ops["w"], R, W, optimize=True)
-        w_dot = np.einsum(ops["w"], R_dot, W, optimize=True)
-        g_m = g_out[v]
-        for pi, p in enumerate(prob.paths):
+        for p in prob.paths:
             C = p["C"]
-            xs = _x_block(prob, x, s, p)
+            Wp = _w_block(prob, Wf, p)
+            w_e = np.einsum(ops["w"], R, Wp, optimize=True)
+            w_dot = np.einsum(ops["w"], R_dot, Wp, optimize=True)
+            xs = _x_block(prob, xf, s, p)
             y = _y_block(Y, p)
             y_dot = _y_block(Y_dot, p)
             U = _coupling(C, xs, y)
             U_dot = _coupling(C, xs, y_dot)
-            gm = g_m[:, _out_rows(prob, p), :]
+            gm = _go_block(prob, gf, v, p)
             g_w = np.einsum(ops["g_w"], U, gm, optimize=True)
-            g_U = np.einsum(ops["g_U"], w_e[:, pi], gm, optimize=True)
-            gUdot_w = np.einsum(ops["g_U"], w_dot[:, pi], gm, optimize=True)
-            d_W[:, pi] += (np.einsum(ops["dW_a"], R_dot, g_w, optimize=True)
-                           + np.einsum(ops["dW_b"], R, U_dot, gm, optimize=True))
+            g_U = np.einsum(ops["g_U"], w_e, gm, optimize=True)
+            gUdot_w = np.einsum(ops["g_U"], w_dot, gm, optimize=True)
+            blk = (np.einsum(ops["g_W"], R_dot, g_w, optimize=True)
+                   + np.einsum(ops["dW_b"], R, U_dot, gm, optimize=True))
+            d_W[:, p["woff"]:p["woff"] + blk[0].size] += blk.reshape(K, -1)
             dx_e = (np.einsum("abc,eb,eic->eai", C, y_dot, g_U, optimize=True)
                     + np.einsum("abc,eb,eic->eai", C, y, gUdot_w, optimize=True))
-            np.add.at(d_x[:, _in_rows(prob, p), :], s, dx_e)
-            dgo = (np.einsum(ops["msg"], w_dot[:, pi], U, optimize=True)
-                   + np.einsum(ops["msg"], w_e[:, pi], U_dot, optimize=True))
-            np.add.at(d_gout[:, _out_rows(prob, p), :], v, dgo)
-    return d_W, d_x, d_gout
+            np.add.at(d_x[:, _in_slice(prob, p)], s, dx_e.reshape(len(s), -1))
+            dgo = (np.einsum(ops["msg"], w_dot, U, optimize=True)
+                   + np.einsum(ops["msg"], w_e, U_dot, optimize=True))
+            np.add.at(d_gout[:, _out_slice(prob, p)], v, dgo.reshape(len(s), -1))
+    return d_W.reshape(np.shape(W)), d_x.reshape(prob.in_shape(N)), d_gout.reshape(prob.out_shape(N))
 
 
 def double_backward_pos(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos):
@@ -273,8 +330,9 @@ def double_backward_pos(prob: Problem, pos, senders, receivers, x, W, g_out, gg_
     and dL_F/dpos[s] += H_e phi_e, dL_F/dpos[v] -= H_e phi_e.  An edge with
     d = 0 or d >= c contributes nothing.
     """
-    pos, x, W = _as64(pos), _as64(x), _as64(W)
-    g_out, gg_pos = _as64(g_out), _as64(gg_pos)
+    pos, gg_pos = _as64(pos), _as64(gg_pos)
+    xf, Wf, gf = _flat(prob, x, "in"), _flat_w(prob, W), _flat(prob, g_out, "out")
+    ops = _ops(prob)
     senders = np.asarray(senders, dtype=np.int64)
     receivers = np.asarray(receivers, dtype=np.int64)
     K = prob.num_basis
@@ -289,17 +347,13 @@ def double_backward_pos(prob: Problem, pos, senders, receivers, x, W, g_out, gg_
         JY = _sh.sh_jacobian(prob.sh_lmax, r)                       # [e, m, 3]
         HY = _sh.sh_hessian(prob.sh_lmax, r)                        # [e, m, 3, 3]
         phi = gg_pos[s] - gg_pos[v]
-        g_m = g_out[v]
         bk = np.zeros((len(s), K, nsh))
-        for pi, p in enumerate(prob.paths):
-            gm = g_m[:, _out_rows(prob, p), :]                       # [e, m3, co]
-            if prob.channelwise:
-                G = np.einsum("ki,eci->ekic", W[:, pi], gm, optimize=True)
-            else:
-                G = np.einsum("kio,eco->ekic", W[:, pi], gm, optimize=True)
+        for p in prob.paths:
+            gm = _go_block(prob, gf, v, p)                            # [e, m3, co]
+            G = np.einsum(ops["G"], _w_block(prob, Wf, p), gm, optimize=True)
             l2 = p["l2"]
             bk[:, :, l2 * l2:(l2 + 1) * (l2 + 1)] += np.einsum(
-                "abc,eai,ekic->ekb", p["C"], _x_block(prob, x, s, p), G, optimize=True)
+                "abc,eai,ekic->ekb", p["C"], _x_block(prob, xf, s, p), G, optimize=True)
         B = np.einsum("ekm,em->ek", bk, Y)
         Jb = np.einsum("ekm,emj->ekj", bk, JY)
         Hb = np.einsum("ekm,emij->eij", np.einsum("ek,ekm->ekm", R, bk), HY)
