@@ -48,7 +48,7 @@ UNITS = ([(f"stream_{n}", "stream_inst.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f
                                                              f"-DTP_LAUNCHER=launch_stream_{n}"])
             for n, t, h in POS_VARIANTS]
          + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("channelwise", ".hip"), ("graph", ".hip"),
-                                             ("scratch", ".hip"), ("api", ".cpp"),
+                                             ("scratch", ".hip"), ("ragged", ".hip"), ("api", ".cpp"),
                                              ("stream_dispatch", ".cpp"), ("plan", ".cpp"),
                                              ("timing", ".cpp"))])
 

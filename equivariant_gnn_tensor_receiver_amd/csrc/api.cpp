@@ -97,8 +97,24 @@ size_t part_elems(const Plan& p, int64_t N) {
   return (size_t)(channelwise(p) ? cw_splits(p, N) : gw_splits(p, N)) * w_elems(p);
 }
 
+// Weights in the caller's layout (ragged plans: the per-path blocks).
+size_t w_elems_caller(const Plan& p) { return p.ragged ? (size_t)(p.K * p.rag.W_per_k) : w_elems(p); }
+
+// Padded copies of a ragged plan's inputs and outputs (placed in front of the
+// uniform passes' workspace): x, W and for each pass its node / weight outputs.
+size_t pad_bytes(const Plan& p, int64_t N, int op) {
+  if (!p.ragged) return 0;
+  const size_t xin = (size_t)N * p.D_in * p.C_in, xout = (size_t)N * p.D_out * p.C_out;
+  const size_t xb = p.x_dtype == TPCONV_BF16 ? 2 : 4, wb = p.w_dtype == TPCONV_BF16 ? 2 : 4;
+  size_t b = align_up(xin * xb) + align_up(w_elems(p) * wb);
+  if (op == TPCONV_OP_FORWARD) return b + align_up(xout * 4);  // out
+  b += align_up(xout * 4) + align_up(xin * 4) + align_up(w_elems(p) * 4);  // grad_out, grad_x / d_x, grad_W / d_W
+  if (op == TPCONV_OP_DOUBLE_BACKWARD) b += align_up(xout * 4);              // d_grad_out
+  return b;
+}
+
 size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
-  return have_saved ? 0 : align_up(state_in_elems(p, N) * 4);
+  return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + pad_bytes(p, N, TPCONV_OP_FORWARD);
 }
 
 // bf16 hi and lo planes of fp32 input features (the position-gradient stream's gathers)
@@ -109,13 +125,14 @@ size_t split_elems(const Plan& p, int64_t N) {
 size_t ws_backward(const Plan& p, int64_t N) {
   // S (recomputed when not saved), gS (fully connected only), T, gW partials, split x
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2);
+         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2) + pad_bytes(p, N, TPCONV_OP_BACKWARD);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
   // S_dot, T_dot, weight partials; for d_pos also gS (fully connected) and split x
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2);
+         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2) +
+         pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD);
 }
 
 tpconv_status dev(hipError_t e) { return e == hipSuccess ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE; }
@@ -484,6 +501,192 @@ tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, con
   return dev(launch_stream(mode, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s));
 }
 
+RaggedNodeMap node_map(const Plan& p, bool in_side) {
+  RaggedNodeMap m;
+  std::memset(&m, 0, sizeof(m));
+  const auto& irs = in_side ? p.in : p.out;
+  const auto& mul = in_side ? p.rag.mul_in : p.rag.mul_out;
+  const auto& foff = in_side ? p.rag.foff_in : p.rag.foff_out;
+  m.D = in_side ? p.D_in : p.D_out;
+  m.C = in_side ? p.C_in : p.C_out;
+  m.F = in_side ? p.rag.F_in : p.rag.F_out;
+  int r = 0;
+  for (size_t i = 0; i < irs.size(); ++i)
+    for (int k = 0; k < 2 * irs[i].l + 1; ++k, ++r) {
+      m.off[r] = (int32_t)(foff[i] + (int64_t)k * mul[i]);
+      m.mul[r] = mul[i];
+    }
+  return m;
+}
+
+RaggedWeightMap weight_map(const Plan& p) {
+  RaggedWeightMap m;
+  std::memset(&m, 0, sizeof(m));
+  m.K = p.K;
+  m.P = p.P;
+  m.Ci = p.C_in;
+  m.Co = p.C_out;
+  m.cw = channelwise(p) ? 1 : 0;
+  m.W_per_k = p.rag.W_per_k;
+  for (int i = 0; i < p.P; ++i) {
+    m.woff[i] = p.rag.woff[i];
+    m.c1[i] = p.rag.mul_in[p.paths[i].i1];
+    m.c3[i] = p.rag.mul_out[p.paths[i].i3];
+  }
+  return m;
+}
+
+// The passes on uniform (for ragged plans: padded) tensors.
+tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x, const void* W,
+                           float* out, float* saved_state, void* ws, hipStream_t s) {
+  const int64_t N = g->num_nodes;
+  float* S = saved_state ? saved_state : static_cast<float*>(ws);
+  StreamArgs a;
+  recv_args(p, a, g, pos, x);
+  a.state = S;
+  tpconv_status st;
+  if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+      TPCONV_SUCCESS)
+    return st;
+  if (channelwise(p)) return run_cw_contract(p, true, N, S, W, out, s);
+  return run_gemm(p, kGemmOut, N, S, nullptr, W, out, 1, s);
+}
+
+tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x, const void* W,
+                            const float* grad_out, const float* saved_state, float* grad_x, float* grad_W,
+                            float* grad_pos, void* ws, hipStream_t s) {
+  const int64_t N = g->num_nodes;
+  const bool cw = channelwise(p);
+  tpconv_status st;
+  Carver c(ws);
+  float* S_ws = c.take(state_in_elems(p, N));
+  float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
+  float* T = c.take(state_out_elems(p, N));
+  float* part = c.take(part_elems(p, N));
+  const size_t nsplit = split_elems(p, N);
+  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
+  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
+
+  const float* S = saved_state;
+  if (grad_W && !S) {  // recompute the receiver state for the weight gradient
+    StreamArgs a;
+    recv_args(p, a, g, pos, x);
+    a.state = S_ws;
+    if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+        TPCONV_SUCCESS)
+      return st;
+    S = S_ws;
+  }
+  Fork fork(s);
+  const hipStream_t s2 = fork.side();
+  if (grad_x) {  // side stream: sender stream, then g_x = T W^T
+    StreamArgs a;
+    send_args(p, a, g, pos, grad_out);
+    a.state = T;
+    if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
+    st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2) : run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s2);
+    if (st != TPCONV_SUCCESS) return st;
+  }
+  if (grad_W) {  // side stream: gW = S^T g_out
+    st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, grad_out, part, grad_W, s2);
+    if (st != TPCONV_SUCCESS) return st;
+  }
+  if (grad_pos) {  // caller's stream
+    st = run_pos_stream(p, kBwdPos, g, pos, x, W, grad_out, nullptr, gS, xhi, xlo, grad_pos, s);
+    if (st != TPCONV_SUCCESS) return st;
+  }
+  return fork.join();
+}
+
+tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x,
+                                   const void* W, const float* grad_out, const float* gg_pos, float* d_W, float* d_x,
+                                   float* d_grad_out, float* d_pos, void* ws, hipStream_t s) {
+  const int64_t N = g->num_nodes;
+  const bool cw = channelwise(p);
+  tpconv_status st;
+  Carver c(ws);
+  float* Sd = c.take(state_in_elems(p, N));
+  float* Td = c.take(state_out_elems(p, N));
+  float* part = c.take(part_elems(p, N));
+  float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
+  const size_t nsplit = split_elems(p, N);
+  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
+  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
+  Fork fork(s);
+  const hipStream_t s2 = fork.side();
+  if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
+    StreamArgs a;
+    send_args(p, a, g, pos, grad_out);
+    a.ggpos = gg_pos;
+    a.state = Td;
+    if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
+    st = cw ? run_cw_contract(p, false, N, Td, W, d_x, s2) : run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s2);
+    if (st != TPCONV_SUCCESS) return st;
+  }
+  if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
+    StreamArgs a;
+    recv_args(p, a, g, pos, x);
+    a.ggpos = gg_pos;
+    a.state = Sd;
+    if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+        TPCONV_SUCCESS)
+      return st;
+    if (d_W) {
+      st = cw ? run_cw_gw(p, N, Sd, grad_out, part, d_W, s) : run_gw(p, N, Sd, grad_out, part, d_W, s);
+      if (st != TPCONV_SUCCESS) return st;
+    }
+    if (d_grad_out) {
+      st = cw ? run_cw_contract(p, true, N, Sd, W, d_grad_out, s)
+              : run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s);
+      if (st != TPCONV_SUCCESS) return st;
+    }
+  }
+  if (d_pos) {  // caller's stream: the Hessian term
+    st = run_pos_stream(p, kBwdHess, g, pos, x, W, grad_out, gg_pos, gS, xhi, xlo, d_pos, s);
+    if (st != TPCONV_SUCCESS) return st;
+  }
+  return fork.join();
+}
+
+// A ragged plan's inputs in the padded layout, carved from the front of the
+// workspace; `rest` is where the uniform passes' workspace begins.
+struct Padded {
+  const Plan& p;
+  Carver c;
+  hipStream_t s;
+  RaggedNodeMap in_map, out_map;
+  tpconv_status st = TPCONV_SUCCESS;
+  Padded(const Plan& plan, void* ws, hipStream_t stream)
+      : p(plan), c(ws), s(stream), in_map(node_map(plan, true)), out_map(node_map(plan, false)) {}
+  void* take_bytes(size_t b) { return c.take((b + 3) / 4); }
+  const void* pack_nodes(const void* src, bool in_side, int elem, int64_t N) {
+    const RaggedNodeMap& m = in_side ? in_map : out_map;
+    void* dst = take_bytes((size_t)N * m.D * m.C * elem);
+    if (st == TPCONV_SUCCESS) st = dev(launch_ragged_nodes(m, src, dst, N, elem, true, s));
+    return dst;
+  }
+  const void* pack_w(const void* src, int elem) {
+    void* dst = take_bytes(w_elems(p) * elem);
+    if (st == TPCONV_SUCCESS) st = dev(launch_ragged_weights(weight_map(p), src, dst, elem, true, s));
+    return dst;
+  }
+  float* out_nodes(bool in_side, int64_t N) {
+    const RaggedNodeMap& m = in_side ? in_map : out_map;
+    return static_cast<float*>(take_bytes((size_t)N * m.D * m.C * 4));
+  }
+  float* out_w() { return static_cast<float*>(take_bytes(w_elems(p) * 4)); }
+  void unpack_nodes(const float* src, float* dst, bool in_side, int64_t N) {
+    if (dst && st == TPCONV_SUCCESS) st = dev(launch_ragged_nodes(in_side ? in_map : out_map, src, dst, N, 4, false, s));
+  }
+  void unpack_w(const float* src, float* dst) {
+    if (dst && st == TPCONV_SUCCESS) st = dev(launch_ragged_weights(weight_map(p), src, dst, 4, false, s));
+  }
+  void* rest() { return c.base + c.used; }
+};
+
+int xbytes(const Plan& p) { return p.x_dtype == TPCONV_BF16 ? 2 : 4; }
+int wbytes(const Plan& p) { return p.w_dtype == TPCONV_BF16 ? 2 : 4; }
+
 }  // namespace
 }  // namespace tpconv
 
@@ -534,11 +737,11 @@ tpconv_status tpconv_plan_info(tpconv_plan plan, int32_t* num_paths, int64_t* w_
   if (!plan) return TPCONV_ERROR_INVALID_VALUE;
   const Plan& p = plan->plan;
   if (num_paths) *num_paths = p.P;
-  if (w_numel) *w_numel = (int64_t)w_elems(p);
+  if (w_numel) *w_numel = (int64_t)w_elems_caller(p);
   if (rows_in) *rows_in = p.D_in;
-  if (ch_in) *ch_in = p.C_in;
+  if (ch_in) *ch_in = p.ragged ? 0 : p.C_in;
   if (rows_out) *rows_out = p.D_out;
-  if (ch_out) *ch_out = p.C_out;
+  if (ch_out) *ch_out = p.ragged ? 0 : p.C_out;
   return TPCONV_SUCCESS;
 }
 
@@ -633,15 +836,15 @@ tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const floa
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   if (N == 0) return TPCONV_SUCCESS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* S = saved_state ? saved_state : static_cast<float*>(ws);
-  StreamArgs a;
-  recv_args(p, a, g, pos, x);
-  a.state = S;
-  if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
-      TPCONV_SUCCESS)
-    return st;
-  if (channelwise(p)) return run_cw_contract(p, true, N, S, W, out, s);
-  return run_gemm(p, kGemmOut, N, S, nullptr, W, out, 1, s);
+  if (!p.ragged) return forward_core(p, g, pos, x, W, out, saved_state, ws, s);
+  Padded pd(p, ws, s);
+  const void* xp = pd.pack_nodes(x, true, xbytes(p), N);
+  const void* Wp = pd.pack_w(W, wbytes(p));
+  float* outp = pd.out_nodes(false, N);
+  if (pd.st != TPCONV_SUCCESS) return pd.st;
+  if ((st = forward_core(p, g, pos, xp, Wp, outp, saved_state, pd.rest(), s)) != TPCONV_SUCCESS) return st;
+  pd.unpack_nodes(outp, out, false, N);
+  return pd.st;
 }
 
 tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
@@ -658,48 +861,23 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
-    if (grad_W) return dev(launch_fill(grad_W, (int64_t)w_elems(p), 0.f, s));
+    if (grad_W) return dev(launch_fill(grad_W, (int64_t)w_elems_caller(p), 0.f, s));
     return TPCONV_SUCCESS;
   }
-  const bool cw = channelwise(p);
-  Carver c(ws);
-  float* S_ws = c.take(state_in_elems(p, N));
-  float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
-  float* T = c.take(state_out_elems(p, N));
-  float* part = c.take(part_elems(p, N));
-  const size_t nsplit = split_elems(p, N);
-  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
-  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
-
-  const float* S = saved_state;
-  if (grad_W && !S) {  // recompute the receiver state for the weight gradient
-    StreamArgs a;
-    recv_args(p, a, g, pos, x);
-    a.state = S_ws;
-    if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
-        TPCONV_SUCCESS)
-      return st;
-    S = S_ws;
-  }
-  Fork fork(s);
-  const hipStream_t s2 = fork.side();
-  if (grad_x) {  // side stream: sender stream, then g_x = T W^T
-    StreamArgs a;
-    send_args(p, a, g, pos, grad_out);
-    a.state = T;
-    if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2) : run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s2);
-    if (st != TPCONV_SUCCESS) return st;
-  }
-  if (grad_W) {  // side stream: gW = S^T g_out
-    st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, grad_out, part, grad_W, s2);
-    if (st != TPCONV_SUCCESS) return st;
-  }
-  if (grad_pos) {  // caller's stream
-    st = run_pos_stream(p, kBwdPos, g, pos, x, W, grad_out, nullptr, gS, xhi, xlo, grad_pos, s);
-    if (st != TPCONV_SUCCESS) return st;
-  }
-  return fork.join();
+  if (!p.ragged) return backward_core(p, g, pos, x, W, grad_out, saved_state, grad_x, grad_W, grad_pos, ws, s);
+  Padded pd(p, ws, s);
+  const void* xp = pd.pack_nodes(x, true, xbytes(p), N);
+  const void* Wp = pd.pack_w(W, wbytes(p));
+  const float* gop = static_cast<const float*>(pd.pack_nodes(grad_out, false, 4, N));
+  float* gxp = pd.out_nodes(true, N);
+  float* gWp = pd.out_w();
+  if (pd.st != TPCONV_SUCCESS) return pd.st;
+  if ((st = backward_core(p, g, pos, xp, Wp, gop, saved_state, grad_x ? gxp : nullptr, grad_W ? gWp : nullptr,
+                          grad_pos, pd.rest(), s)) != TPCONV_SUCCESS)
+    return st;
+  pd.unpack_nodes(gxp, grad_x, true, N);
+  pd.unpack_w(gWp, grad_W);
+  return pd.st;
 }
 
 tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
@@ -717,52 +895,34 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
-    if (d_W) return dev(launch_fill(d_W, (int64_t)w_elems(p), 0.f, s));
+    if (d_W) return dev(launch_fill(d_W, (int64_t)w_elems_caller(p), 0.f, s));
     return TPCONV_SUCCESS;
   }
-  const bool cw = channelwise(p);
-  Carver c(ws);
-  float* Sd = c.take(state_in_elems(p, N));
-  float* Td = c.take(state_out_elems(p, N));
-  float* part = c.take(part_elems(p, N));
-  float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
-  const size_t nsplit = split_elems(p, N);
-  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
-  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
-  Fork fork(s);
-  const hipStream_t s2 = fork.side();
-  if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
-    StreamArgs a;
-    send_args(p, a, g, pos, grad_out);
-    a.ggpos = gg_pos;
-    a.state = Td;
-    if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    st = cw ? run_cw_contract(p, false, N, Td, W, d_x, s2) : run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s2);
-    if (st != TPCONV_SUCCESS) return st;
-  }
-  if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
-    StreamArgs a;
-    recv_args(p, a, g, pos, x);
-    a.ggpos = gg_pos;
-    a.state = Sd;
-    if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
-        TPCONV_SUCCESS)
-      return st;
-    if (d_W) {
-      st = cw ? run_cw_gw(p, N, Sd, grad_out, part, d_W, s) : run_gw(p, N, Sd, grad_out, part, d_W, s);
-      if (st != TPCONV_SUCCESS) return st;
-    }
-    if (d_grad_out) {
-      st = cw ? run_cw_contract(p, true, N, Sd, W, d_grad_out, s)
-              : run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s);
-      if (st != TPCONV_SUCCESS) return st;
-    }
-  }
-  if (d_pos) {  // caller's stream: the Hessian term
-    st = run_pos_stream(p, kBwdHess, g, pos, x, W, grad_out, gg_pos, gS, xhi, xlo, d_pos, s);
-    if (st != TPCONV_SUCCESS) return st;
-  }
-  return fork.join();
+  if (!p.ragged)
+    return double_backward_core(p, g, pos, x, W, grad_out, gg_pos, d_W, d_x, d_grad_out, d_pos, ws, s);
+  Padded pd(p, ws, s);
+  const void* xp = pd.pack_nodes(x, true, xbytes(p), N);
+  const void* Wp = pd.pack_w(W, wbytes(p));
+  const float* gop = static_cast<const float*>(pd.pack_nodes(grad_out, false, 4, N));
+  float* dxp = pd.out_nodes(true, N);
+  float* dWp = pd.out_w();
+  float* dgp = pd.out_nodes(false, N);
+  if (pd.st != TPCONV_SUCCESS) return pd.st;
+  if ((st = double_backward_core(p, g, pos, xp, Wp, gop, gg_pos, d_W ? dWp : nullptr, d_x ? dxp : nullptr,
+                                 d_grad_out ? dgp : nullptr, d_pos, pd.rest(), s)) != TPCONV_SUCCESS)
+    return st;
+  pd.unpack_w(dWp, d_W);
+  pd.unpack_nodes(dxp, d_x, true, N);
+  pd.unpack_nodes(dgp, d_grad_out, false, N);
+  return pd.st;
+}
+
+tpconv_status tpconv_plan_features(tpconv_plan plan, int64_t* feat_in, int64_t* feat_out) {
+  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  const Plan& p = plan->plan;
+  if (feat_in) *feat_in = p.ragged ? p.rag.F_in : (int64_t)p.D_in * p.C_in;
+  if (feat_out) *feat_out = p.ragged ? p.rag.F_out : (int64_t)p.D_out * p.C_out;
+  return TPCONV_SUCCESS;
 }
 
 tpconv_status tpconv_kernel_timing(int32_t enable) {

@@ -140,7 +140,26 @@ struct ReduceArgs {
   GemmGroup g[kMaxGroups];
 };
 
+// Ragged multiplicities: maps between the caller's layout and the padded one.
+constexpr int kMaxRows = kMaxGroups * (2 * kMaxL + 1);
+struct RaggedNodeMap {
+  int32_t D, C;             // padded rows per node, padded channels
+  int64_t F;                // caller's features per node
+  int32_t off[kMaxRows];    // caller's feature offset of padded row r within a node
+  int32_t mul[kMaxRows];    // channels of row r in the caller's layout
+};
+struct RaggedWeightMap {
+  int32_t K, P, Ci, Co, cw;  // padded shape [K][P][Ci][Co] (channel-wise [K][P][Ci])
+  int64_t W_per_k;           // caller's weights per k
+  int64_t woff[kMaxPaths];   // caller's offset of path p's block within one k
+  int32_t c1[kMaxPaths], c3[kMaxPaths];
+};
+
 // Host launchers (return a hipError_t).
+hipError_t launch_ragged_nodes(const RaggedNodeMap& m, const void* src, void* dst, int64_t N, int elem_bytes,
+                               bool pack, hipStream_t s);
+hipError_t launch_ragged_weights(const RaggedWeightMap& m, const void* src, void* dst, int elem_bytes, bool pack,
+                                 hipStream_t s);
 hipError_t launch_stream(int mode, int lmax, int K, bool feat_bf16, const StreamArgs& a, int64_t items,
                          hipStream_t s);
 // Fills the tiling fields of a.g[] (tiles, tiles_n, tile_begin) and launches.

@@ -186,9 +186,34 @@ int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K
   if (sh_lmax < 0) return TPCONV_ERROR_INVALID_VALUE;
   Plan p;
   if (!parse_irreps(irreps_in, p.in) || !parse_irreps(irreps_out, p.out)) return TPCONV_ERROR_IRREPS;
+  // Ragged multiplicities: keep the caller's layout, pad every irrep of a side
+  // to its largest multiplicity (the channel-wise product pads both sides to
+  // one count, since it pairs input and output channels).
+  for (const auto& ir : p.in) p.rag.mul_in.push_back(ir.mul);
+  for (const auto& ir : p.out) p.rag.mul_out.push_back(ir.mul);
   for (const auto& v : {&p.in, &p.out})
     for (const auto& ir : *v)
-      if (ir.mul != (*v)[0].mul) return TPCONV_ERROR_IRREPS;
+      if (ir.mul != (*v)[0].mul) p.ragged = true;
+  if (p.ragged) {
+    int cin = 0, cout = 0;
+    for (const auto& ir : p.in) cin = std::max(cin, ir.mul);
+    for (const auto& ir : p.out) cout = std::max(cout, ir.mul);
+    if (connection == TPCONV_CHANNELWISE) cin = cout = std::max(cin, cout);
+    for (auto& ir : p.in) ir.mul = cin;
+    for (auto& ir : p.out) ir.mul = cout;
+    int64_t o = 0;
+    for (size_t i = 0; i < p.in.size(); ++i) {
+      p.rag.foff_in.push_back(o);
+      o += (int64_t)(2 * p.in[i].l + 1) * p.rag.mul_in[i];
+    }
+    p.rag.F_in = o;
+    o = 0;
+    for (size_t i = 0; i < p.out.size(); ++i) {
+      p.rag.foff_out.push_back(o);
+      o += (int64_t)(2 * p.out[i].l + 1) * p.rag.mul_out[i];
+    }
+    p.rag.F_out = o;
+  }
   int lmax = sh_lmax;
   for (const auto& ir : p.in) lmax = std::max(lmax, ir.l);
   for (const auto& ir : p.out) lmax = std::max(lmax, ir.l);
@@ -238,6 +263,16 @@ int build_plan(const char* irreps_in, const char* irreps_out, int sh_lmax, int K
   }
   p.P = (int)p.paths.size();
   if (p.P > kMaxPaths) return TPCONV_ERROR_UNSUPPORTED;
+  if (p.ragged) {
+    int64_t o = 0;
+    for (const auto& q : p.paths) {
+      const int c1 = p.rag.mul_in[q.i1], c3 = p.rag.mul_out[q.i3];
+      if (connection == TPCONV_CHANNELWISE && c1 != c3) return TPCONV_ERROR_IRREPS;
+      p.rag.woff.push_back(o);
+      o += connection == TPCONV_CHANNELWISE ? c1 : (int64_t)c1 * c3;
+    }
+    p.rag.W_per_k = o;
+  }
   p.cg.resize(p.P);
   for (int i = 0; i < p.P; ++i) real_cg(p.paths[i].l1, p.paths[i].l2, p.paths[i].l3, p.cg[i]);
   int64_t off = 0;

@@ -44,8 +44,23 @@ struct Group {
   int64_t base_per_node;    // element offset of this group's state = N * base_per_node
 };
 
+// Ragged multiplicities run on the uniform kernels with every irrep padded by
+// zero channels to the largest multiplicity of its side (C_in / C_out below);
+// the caller's tensors use the ragged layout: per node, irrep i's block
+// [2l_i+1][mul_i] at feature offset foff[i]; per k, path p's weight block
+// [mul(i1_p)][mul(i3_p)] (channel-wise: [mul_p]) at woff[p].
+struct RaggedLayout {
+  std::vector<int> mul_in, mul_out;     // caller's multiplicity per irrep
+  std::vector<int64_t> foff_in, foff_out;
+  int64_t F_in = 0, F_out = 0;          // caller's features per node
+  std::vector<int64_t> woff;            // per path, within one k
+  int64_t W_per_k = 0;
+};
+
 struct Plan {
   std::vector<Irrep> in, out;
+  bool ragged = false;  // the caller's multiplicities differ between irreps (layout in `rag`)
+  RaggedLayout rag;
   int sh_lmax = 0, K = 0, env_p = 6;
   float cutoff = 5.f;
   int x_dtype = 0, w_dtype = 0;

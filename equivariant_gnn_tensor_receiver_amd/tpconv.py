@@ -27,7 +27,8 @@ STATIC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("tpconv_plan_create", "tpconv_plan_destroy", "tpconv_plan_info", "tpconv_plan_path",
            "tpconv_plan_cg", "tpconv_workspace_size", "tpconv_state_size", "tpconv_graph_prepare",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string",
-           "tpconv_kernel_timing", "tpconv_kernel_timing_read", "tpconv_forward_static", "tpconv_graph_order")
+           "tpconv_kernel_timing", "tpconv_kernel_timing_read", "tpconv_forward_static", "tpconv_graph_order",
+           "tpconv_plan_features")
 KERNELS = ("stream_fwd", "stream_jvp", "stream_snd", "stream_sndt", "stream_bwdpos", "gemm_out", "gemm_gs",
            "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce", "stream_hess")
 
@@ -64,6 +65,7 @@ def _lib():
         L.tpconv_plan_info.argtypes = [P, POINTER(c_int32), POINTER(c_int64), POINTER(c_int32), POINTER(c_int32),
                                        POINTER(c_int32), POINTER(c_int32)]
         L.tpconv_plan_path.argtypes = [P, c_int32, POINTER(c_int32), POINTER(c_int32)]
+        L.tpconv_plan_features.argtypes = [P, POINTER(c_int64), POINTER(c_int64)]
         L.tpconv_plan_cg.argtypes = [P, c_int32, POINTER(c_double)]
         L.tpconv_workspace_size.argtypes = [P, c_int32, c_int64, c_int64, POINTER(c_size_t)]
         L.tpconv_state_size.argtypes = [P, c_int64, POINTER(c_size_t)]
@@ -119,6 +121,17 @@ class Plan:
         self.num_paths, self.w_numel = P.value, wn.value
         self.rows_in, self.ch_in, self.rows_out, self.ch_out = ri.value, ci.value, ro.value, co.value
         self.num_basis = num_basis
+        fi, fo = c_int64(), c_int64()
+        _check(_lib().tpconv_plan_features(h, ctypes.byref(fi), ctypes.byref(fo)), "tpconv_plan_features")
+        self.feat_in, self.feat_out = fi.value, fo.value
+        self.ragged = self.ch_in == 0 or self.ch_out == 0
+
+    def in_shape(self, N):
+        """Shape of x, grad_x, d_x: [N][rows][C], or [N][F] for ragged multiplicities."""
+        return (N, self.feat_in) if self.ragged else (N, self.rows_in, self.ch_in)
+
+    def out_shape(self, N):
+        return (N, self.feat_out) if self.ragged else (N, self.rows_out, self.ch_out)
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -151,6 +164,8 @@ class Plan:
 
     @property
     def w_shape(self):
+        if self.ragged:
+            return (self.num_basis, self.w_numel // self.num_basis)
         if self.connection == CHANNELWISE:
             return (self.num_basis, self.num_paths, self.ch_in)
         return (self.num_basis, self.num_paths, self.ch_in, self.ch_out)
@@ -210,7 +225,7 @@ def _feature_dtype(code):
 
 def _check_inputs(plan, graph, pos, x, W, **more):
     """Checks shared by the passes: graph index tensors, pos, x, W, and the
-    named fp32 node tensors in `more` (name -> (tensor, rows, channels))."""
+    named fp32 node tensors in `more` (name -> (tensor, values per node))."""
     import torch
 
     dev = pos.device
@@ -220,10 +235,10 @@ def _check_inputs(plan, graph, pos, x, W, **more):
     if graph.senders.numel() < graph.num_edges:
         raise ValueError("senders: fewer entries than num_edges")
     _require(pos, "pos", torch.float32, 3 * N, dev)
-    _require(x, "x", _feature_dtype(plan.x_dtype), N * plan.rows_in * plan.ch_in, dev)
+    _require(x, "x", _feature_dtype(plan.x_dtype), N * plan.feat_in, dev)
     _require(W, "W", _feature_dtype(plan.w_dtype), plan.w_numel, dev)
-    for name, (t, rows, ch) in more.items():
-        _require(t, name, torch.float32, N * rows * ch, dev)
+    for name, (t, per_node) in more.items():
+        _require(t, name, torch.float32, N * per_node, dev)
 
 
 def _keep_for_stream(stream, *tensors):
@@ -277,11 +292,11 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
     dev = pos.device
     N = graph.num_nodes
     if out is None:
-        out = torch.empty((N, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev)
+        out = torch.empty(plan.out_shape(N), dtype=torch.float32, device=dev)
         _keep_for_stream(stream, out)
-    _check_inputs(plan, graph, pos, x, W, out=(out, plan.rows_out, plan.ch_out))
+    _check_inputs(plan, graph, pos, x, W, out=(out, plan.feat_out))
     _require(saved_state, "saved_state", torch.float32, plan.state_size(N) // 4, dev)
-    if workspace is None and saved_state is None:
+    if workspace is None and (saved_state is None or plan.ragged):  # ragged plans pad inside the workspace
         workspace = _workspace(plan.workspace_size(OP_FORWARD, N, graph.num_edges), dev)
         _keep_for_stream(stream, workspace)
     _require(workspace, "workspace", None, None, dev)
@@ -295,7 +310,7 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
 def tpconv_forward_static(plan: Plan, graph: Graph, pos, x, W, out, stream=None):
     """tpconv_forward with the receiver state in the library's static device
     scratch: no workspace, nothing allocated (`out` must be given)."""
-    _check_inputs(plan, graph, pos, x, W, out=(out, plan.rows_out, plan.ch_out))
+    _check_inputs(plan, graph, pos, x, W, out=(out, plan.feat_out))
     g = graph.c()
     _check(_lib().tpconv_forward_static(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(out),
                                         _stream(stream)), "tpconv_forward_static")
@@ -309,14 +324,14 @@ def tpconv_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, saved_state=N
     dev = pos.device
     N = graph.num_nodes
     if grad_x is None and "x" in want:
-        grad_x = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev)
+        grad_x = torch.empty(plan.in_shape(N), dtype=torch.float32, device=dev)
     if grad_W is None and "W" in want:
         grad_W = torch.empty(plan.w_shape, dtype=torch.float32, device=dev)
     if grad_pos is None and "pos" in want:
         grad_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
     _keep_for_stream(stream, grad_x, grad_W, grad_pos)
-    _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.rows_out, plan.ch_out),
-                  grad_x=(grad_x, plan.rows_in, plan.ch_in), grad_pos=(grad_pos, 1, 3))
+    _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.feat_out), grad_x=(grad_x, plan.feat_in),
+                  grad_pos=(grad_pos, 3))
     _require(grad_W, "grad_W", torch.float32, plan.w_numel, dev)
     _require(saved_state, "saved_state", torch.float32, plan.state_size(N) // 4, dev)
     if workspace is None:
@@ -341,15 +356,14 @@ def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos
     if d_W is None and "W" in want:
         d_W = torch.empty(plan.w_shape, dtype=torch.float32, device=dev)
     if d_x is None and "x" in want:
-        d_x = torch.empty((N, plan.rows_in, plan.ch_in), dtype=torch.float32, device=dev)
+        d_x = torch.empty(plan.in_shape(N), dtype=torch.float32, device=dev)
     if d_grad_out is None and "grad_out" in want:
-        d_grad_out = torch.empty((N, plan.rows_out, plan.ch_out), dtype=torch.float32, device=dev)
+        d_grad_out = torch.empty(plan.out_shape(N), dtype=torch.float32, device=dev)
     if d_pos is None and "pos" in want:
         d_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
     _keep_for_stream(stream, d_W, d_x, d_grad_out, d_pos)
-    _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.rows_out, plan.ch_out), gg_pos=(gg_pos, 1, 3),
-                  d_x=(d_x, plan.rows_in, plan.ch_in), d_grad_out=(d_grad_out, plan.rows_out, plan.ch_out),
-                  d_pos=(d_pos, 1, 3))
+    _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.feat_out), gg_pos=(gg_pos, 3),
+                  d_x=(d_x, plan.feat_in), d_grad_out=(d_grad_out, plan.feat_out), d_pos=(d_pos, 3))
     _require(d_W, "d_W", torch.float32, plan.w_numel, dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_DOUBLE_BACKWARD, N, graph.num_edges), dev)

@@ -31,6 +31,15 @@
  *   x, out, grad_out, grad_x, d_x, d_grad_out : [N][rows][C]   rows ordered by the
  *       irreps string, row of (irrep i, m) = offset(i) + l_i + m; channels innermost
  *   W, grad_W, d_W : [K][P][C_in][C_out], paths in tpconv_plan_path order
+ *   Ragged multiplicities (irreps of one side with different channel counts,
+ *   the abstract's varied feature structures): node tensors are [N][F], irrep
+ *   i's block [2l_i+1][mul_i] following the blocks of irreps 0..i-1 (F from
+ *   tpconv_plan_features); weights are [K][sum_p mul(l1 irrep of p) *
+ *   mul(l3 irrep of p)], path p's block [mul_in][mul_out] following those of
+ *   paths 0..p-1 (channel-wise: [K][sum_p mul_p]).  With one multiplicity per
+ *   side these are exactly the layouts above.  Ragged plans pad every irrep of
+ *   a side to the side's largest multiplicity inside the workspace (zero
+ *   channels add nothing), so they cost what the padded uniform problem costs.
  *   pos, grad_pos, gg_pos : [N][3] fp32
  *   graph: rowptr[N+1], senders[E] int32, edges sorted by receiver;
  *          csc_colptr[N+1], csc_receivers[E] int32: the same edges sorted by
@@ -63,7 +72,7 @@ typedef struct tpconv_plan_s* tpconv_plan;
 typedef enum {
   TPCONV_SUCCESS = 0,
   TPCONV_ERROR_INVALID_VALUE = 1, /* null pointer, negative size, bad enum */
-  TPCONV_ERROR_IRREPS = 2,        /* unparsable irreps, non-uniform multiplicity, l > 3 */
+  TPCONV_ERROR_IRREPS = 2,        /* unparsable irreps, channel-wise path with unequal multiplicities */
   TPCONV_ERROR_GRAPH = 3,         /* CSR fails validation (tpconv_graph_prepare, validate=1) */
   TPCONV_ERROR_WORKSPACE = 4,     /* workspace pointer null or smaller than required */
   TPCONV_ERROR_UNSUPPORTED = 5,   /* valid request the library does not implement */
@@ -93,7 +102,7 @@ typedef enum {
 } tpconv_op;
 
 typedef struct {
-  const char* irreps_in;  /* e.g. "32x0e+32x1o+32x2e"; one multiplicity, l <= 3 */
+  const char* irreps_in;  /* e.g. "32x0e+32x1o+32x2e" or "64x0e+32x1o+16x2e"; l <= 3 */
   const char* irreps_out; /* same rules; may differ from irreps_in */
   int32_t sh_lmax;        /* degree of the edge harmonics, 0..3 */
   int32_t num_basis;      /* K radial functions: 8 or 16 */
@@ -121,18 +130,24 @@ typedef struct {
  * Key results: the CG product is the fully expressive coupling).  Host only;
  * touches no device.  *out receives an owning handle (free with
  * tpconv_plan_destroy).  Errors: INVALID_VALUE (null pointers, K not in {8,16},
- * cutoff <= 0, p < 2, bad dtype or connection), IRREPS (bad strings, or
- * C_in != C_out for the channel-wise connection), UNSUPPORTED (l > 3). */
+ * cutoff <= 0, p < 2, bad dtype or connection), IRREPS (bad strings, or for
+ * the channel-wise connection a path whose input and output multiplicities
+ * differ), UNSUPPORTED (l > 3). */
 tpconv_status tpconv_plan_create(tpconv_plan* out, const tpconv_desc* desc);
 
 /* Release a plan (NULL is accepted). */
 tpconv_status tpconv_plan_destroy(tpconv_plan plan);
 
 /* Sizes of a plan; any output pointer may be NULL.
- * rows_* = sum of (2l+1) over the irreps, ch_* = the multiplicity,
- * w_numel = K * P * C_in * C_out (fully connected) or K * P * C (channel-wise). */
+ * rows_* = sum of (2l+1) over the irreps, ch_* = the multiplicity (0 when the
+ * multiplicities of that side differ), w_numel = K * P * C_in * C_out (fully
+ * connected) or K * P * C (channel-wise), or the ragged layout's count. */
 tpconv_status tpconv_plan_info(tpconv_plan plan, int32_t* num_paths, int64_t* w_numel,
                                int32_t* rows_in, int32_t* ch_in, int32_t* rows_out, int32_t* ch_out);
+
+/* Features per node of the input and output tensors in the caller's layout
+ * (rows * C, or the ragged block sizes summed).  Either pointer may be NULL. */
+tpconv_status tpconv_plan_features(tpconv_plan plan, int64_t* feat_in, int64_t* feat_out);
 
 /* Path `path` (0 <= path < P): l123[3] = (l1, l2, l3), irrep_idx[2] = (input
  * irrep index, output irrep index).  Either pointer may be NULL. */
@@ -152,7 +167,8 @@ tpconv_status tpconv_plan_cg(tpconv_plan plan, int32_t path, double* out);
  * GRAPH_PREPARE needs O(N) int32 scratch for the sender sort (index
  * metadata, not tensor-product workspace), GRAPH_ORDER O(N) for the sort of
  * the nodes.  FORWARD's figure assumes
- * saved_state == NULL; with a saved state the forward needs none.
+ * saved_state == NULL; with a saved state a uniform plan's forward needs none
+ * and a ragged plan's at most that figure.
  * Errors: INVALID_VALUE (null plan or bytes, negative sizes, unknown op). */
 tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t num_nodes,
                                     int64_t num_edges, size_t* bytes);
@@ -194,8 +210,9 @@ tpconv_status tpconv_graph_order(tpconv_plan plan, const tpconv_graph* g, const 
 
 /* Forward: out = conv(pos, x, W) as defined at the top of this header.
  * saved_state: NULL, or device memory of tpconv_state_size bytes that receives
- * the receiver state S for a later tpconv_backward (then the workspace may be
- * NULL/0).  Device pointers: pos, x, W, out (and saved_state). */
+ * the receiver state S for a later tpconv_backward (then a uniform plan's
+ * workspace may be NULL/0; a ragged plan still needs room for its padded
+ * copies).  Device pointers: pos, x, W, out (and saved_state). */
 tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const float* pos,
                              const void* x, const void* W, float* out, float* saved_state,
                              void* workspace, size_t workspace_bytes, void* stream);

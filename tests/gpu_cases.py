@@ -50,8 +50,20 @@ class DeviceCase:
         assert self.plan.num_paths == self.prob.P
         assert tuple(self.plan.w_shape) == tuple(self.prob.w_shape)
         N = len(rowptr) - 1
-        t = inputs.make_tensors(rng, N, self.prob.D_in, self.prob.C_in, self.prob.D_out, self.prob.C_out, K,
-                                self.prob.P, dtype, channelwise=channelwise, w_dtype=w_dtype)
+        if self.prob.uniform:
+            t = inputs.make_tensors(rng, N, self.prob.D_in, self.prob.C_in, self.prob.D_out, self.prob.C_out, K,
+                                    self.prob.P, dtype, channelwise=channelwise, w_dtype=w_dtype)
+        else:  # ragged multiplicities: the flat per-irrep layout
+            cmax = max(m for m, _, _ in self.prob.ir_in)
+            t = dict(x=rng.standard_normal((N, self.prob.F_in), dtype=np.float32),
+                     W=(rng.standard_normal(self.prob.w_shape, dtype=np.float32)
+                        * np.float32((1.0 / (K * (1 if channelwise else cmax))) ** 0.5)),
+                     g_out=rng.standard_normal((N, self.prob.F_out), dtype=np.float32),
+                     gg_pos=rng.standard_normal((N, 3), dtype=np.float32))
+            if dtype == "bf16":
+                t["x"] = inputs.bf16_round(t["x"])
+            if w_dtype == "bf16":
+                t["W"] = inputs.bf16_round(t["W"])
         self.np = dict(pos=pos, rowptr=rowptr, senders=senders, **t)
         self.receivers = otp.csr_receivers(rowptr)
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)

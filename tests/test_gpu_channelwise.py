@@ -26,6 +26,8 @@ CASES = [
     ("cw_l3_k16", "16x0e+16x1o+16x2e+16x3o", "16x0e+16x1o+16x2e+16x3o", 3, 16, 30, 40, "f32"),
     # an output irrep (2o) that no path reaches and an input irrep (3o) that reaches nothing
     ("cw_no_path_groups", "8x0e+8x1o+8x3o", "8x0e+8x1o+8x2o", 1, 8, 50, 12, "f32"),
+    # ragged multiplicities: each path joins irreps of equal channel counts
+    ("cw_ragged", "16x0e+8x1e+12x2e", "16x0e+8x1e+12x2e", 1, 8, 50, 12, "f32"),
 ]
 
 

@@ -39,6 +39,10 @@ SMALL = [
     # an output irrep (2o) that no path reaches and an input irrep (3o) that reaches nothing
     ("no_path_groups_c8", "8x0e+8x1o+8x3o", "8x0e+8x1o+8x2o", 1, 8, 50, 12, "f32"),
     ("no_path_groups_c16", "16x0e+16x1o+16x3o", "16x2o+16x0e+16x1o", 1, 8, 50, 12, "f32"),
+    # ragged multiplicities (a channel count per irrep), natural and mixed parities
+    ("ragged_l2", "64x0e+32x1o+16x2e", "32x0e+48x1o+16x2e", 2, 8, 60, 14, "f32"),
+    ("ragged_mixed_k16", "12x0e+8x1o+6x1e+4x2e", "6x0e+4x0o+8x1o+4x1e+6x2e+4x3o", 2, 16, 50, 12, "f32"),
+    ("ragged_l3_bf16", "32x0e+16x1o+16x2e+8x3o", "32x0e+16x1o+16x2e+8x3o", 3, 8, 40, 12, "bf16"),
 ]
 
 

@@ -29,7 +29,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(tp.LIB_PATH)
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(names) == sorted(tp.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -77,7 +77,7 @@ def test_all_tables_up_to_l3():
 
 @pytest.mark.parametrize("desc,status", [
     (("8x0e+8x1q", "8x0e", 1, 8), 2),
-    (("8x0e+4x1o", "8x0e", 1, 8), 2),
+    (("8x0e+4x1o", "8x0e+4x1o", 1, 8, 5.0, 6, 0, 0, 1), 2),   # channel-wise path 0e x Y1 -> 1o: 8 vs 4 channels
     (("8x0e", "8x0e", 1, 7), 1),
     (("8x4e", "8x0e", 1, 8), 5),
     (("8x0e", "8x0e", 4, 8), 5),
@@ -90,6 +90,24 @@ def test_plan_errors(desc, status):
     with pytest.raises(tp.TpconvError) as e:
         tp.Plan("8x0e", "8x0e", 1, 8, cutoff=-1.0)
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("ir_in,ir_out,lsh", [("6x0e+3x1o+2x2e", "4x0e+5x1o+3x2e", 2),
+                                             ("5x0e+2x1o+3x1e+4x2e", "3x0e+2x0o+4x1o+2x1e+3x2e+2x3o", 2),
+                                             ("8x0e+4x1o", "4x0e+4x1o", 1)])
+def test_ragged_plan_matches_oracle_layout(ir_in, ir_out, lsh):
+    plan = tp.Plan(ir_in, ir_out, lsh, 8)
+    prob = Problem(ir_in, ir_out, lsh, 8)
+    assert plan.ragged and not prob.uniform
+    assert (plan.feat_in, plan.feat_out) == (prob.F_in, prob.F_out)
+    assert plan.w_numel == 8 * prob.W_per_k and plan.w_shape == prob.w_shape
+    assert plan.num_paths == prob.P
+    for i, p in enumerate(prob.paths):
+        (l1, l2, l3), (i1, i3) = plan.path(i)
+        assert (l1, l2, l3, i1, i3) == (p["l1"], p["l2"], p["l3"], p["i1"], p["i3"])
+        assert np.abs(plan.cg(i) - p["C"]).max() < 1e-15
+    for op in (tp.OP_FORWARD, tp.OP_BACKWARD, tp.OP_DOUBLE_BACKWARD):
+        assert len({plan.workspace_size(op, 300, E) for E in (0, 5000, 90000)}) == 1
 
 
 def test_workspace_is_independent_of_edges():
