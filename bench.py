@@ -52,7 +52,8 @@ def sizes(plan, N, E, xbytes, wbytes):
     fin, fout, wf = 4 * N * plan.rows_in * plan.ch_in, 4 * N * plan.rows_out * plan.ch_out, 4 * plan.w_numel
     return {"x": N * plan.rows_in * plan.ch_in * xbytes, "W": plan.w_numel * wbytes, "pos": 12 * N,
             "csr": 4 * (N + 1) + 4 * E, "csc": 4 * (N + 1) + 4 * E, "out": fout, "g_out": fout, "g_x": fin,
-            "gW": wf, "g_pos": 12 * N, "gg_pos": 12 * N, "d_W": wf, "d_x": fin}
+            "gW": wf, "g_pos": 12 * N, "gg_pos": 12 * N, "d_W": wf, "d_x": fin, "d_g_out": fout,
+            "d_pos": 12 * N}
 
 
 def algorithmic(plan, paths, N, E, xbytes, wbytes):
@@ -76,6 +77,8 @@ def algorithmic(plan, paths, N, E, xbytes, wbytes):
         "stream_snd": (E * Co * (2 * nnz + 2 * K * M1), go + graph + T),
         "stream_sndt": (E * Co * (4 * nnz + 4 * K * M1), go + graph + 12 * N + T),
         "stream_bwdpos": (E * Ci * (4 * nnz + 4 * K * M3), x + graph + S + 12 * N),
+        # Hessian term of dL/dpos: K-sums with R, R', R'' and three couplings
+        "stream_hess": (E * Ci * (6 * nnz + 6 * K * M3), x + graph + S + 24 * N),
         "gemm_out": (2 * N * K * Ci * Co * M3, S + Wb + go),
         "gemm_gs": (2 * N * K * Ci * Co * M3, go + Wb + S),
         "gemm_gx": (2 * N * K * Ci * Co * M1, T + Wb + z["g_x"]),
@@ -96,6 +99,9 @@ PASS_KERNELS = {
     "forces": (("gemm_gs", "stream_bwdpos"), {"x", "W", "pos", "csr", "g_out", "g_pos"}),
     "dbwd": (("stream_jvp", "gemm_gw", "stream_sndt", "gemm_gx"),
              {"x", "W", "pos", "csr", "csc", "g_out", "gg_pos", "d_W", "d_x"}),
+    # the whole double backward: also d_grad_out (S-dot W) and dL/dpos (gS, then the Hessian stream)
+    "dbwd_all": (("stream_jvp", "gemm_gw", "stream_sndt", "gemm_gx", "gemm_out", "gemm_gs", "stream_hess"),
+                 {"x", "W", "pos", "csr", "csc", "g_out", "gg_pos", "d_W", "d_x", "d_g_out", "d_pos"}),
 }
 CW_KERNEL = {"gemm_out": "cw_contract", "gemm_gx": "cw_contract", "gemm_gw": "cw_gw", "gemm_gs": None}
 
@@ -249,6 +255,8 @@ def run_workload(name, steps, warmup, detail):
     gp = torch.empty((N, 3), **f32)
     dW = torch.empty(plan.w_shape, **f32)
     dx = torch.empty((N, plan.rows_in, plan.ch_in), **f32)
+    dg = torch.empty((N, plan.rows_out, plan.ch_out), **f32) if "dbwd" in w.passes else None
+    dpos = torch.empty((N, 3), **f32)
     ws_b = torch.empty(plan.workspace_size(tp.OP_BACKWARD, N, E), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(plan.workspace_size(tp.OP_DOUBLE_BACKWARD, N, E), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -269,6 +277,10 @@ def run_workload(name, steps, warmup, detail):
     def dbwd():
         tp.tpconv_double_backward(plan, graph, pos, x, W, g_out, gg, want=("W", "x"), workspace=ws_d, d_W=dW,
                                   d_x=dx)
+
+    def dbwd_all():
+        tp.tpconv_double_backward(plan, graph, pos, x, W, g_out, gg, want=("W", "x", "grad_out", "pos"),
+                                  workspace=ws_d, d_W=dW, d_x=dx, d_grad_out=dg, d_pos=dpos)
 
     step_parts = [fwd] + ([bwd] if "bwd" in w.passes else []) + ([dbwd] if "dbwd" in w.passes else [])
 
@@ -320,6 +332,7 @@ def run_workload(name, steps, warmup, detail):
         ms_d = timed(dbwd, steps)
         passes["dbwd"] = bound(["dbwd"], ms_d)
         passes["fwd+forces+dbwd"] = bound(["fwd", "forces", "dbwd"], ms_f + ms_b + ms_d)
+        passes["dbwd_all"] = bound(["dbwd_all"], timed(dbwd_all, steps))
 
     rep = {"workload": w.name, "num_nodes": N, "num_edges": E, "step": "+".join(w.passes),
            "ms_per_step": round(ms_step, 4), "edges_per_s": round(E / (ms_step * 1e-3), 1), "passes": passes}

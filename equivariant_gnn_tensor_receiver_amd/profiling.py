@@ -12,6 +12,11 @@ are counter * (bytes the copy moves / what the counter reads for the copy).
   rocprofv3 --pmc WRITE_SIZE ... -d OUT/wl_write -- (same)
   python3 -m equivariant_gnn_tensor_receiver_amd.profiling summarize OUT W KERNEL_SUBSTRING NAME > traffic.json
 
+A kernel trace (``rocprofv3 --kernel-trace --stats --output-format csv -d DIR``)
+is turned into a short Markdown table with
+
+  python3 -m equivariant_gnn_tensor_receiver_amd.profiling stats DIR TITLE "COMMAND" > kernels.md
+
 The summary records the hash of the kernel sources it was taken with; bench.py
 ignores it once the sources change.
 """
@@ -28,7 +33,8 @@ from collections import defaultdict
 COPY_BYTES = 1 << 30  # 1 GiB read and 1 GiB written per copy
 COPY_REPS = 4
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("stream_impl.h", "stream_inst.hip", "device_common.h", "gemm.hip", "kernels.h", "cg_codegen.cpp")
+KERNEL_SOURCES = ("stream_impl.h", "stream_inst.hip", "stream_pos.h", "stream_pos.hip", "device_common.h", "gemm.hip",
+                  "channelwise.hip", "kernels.h", "cg_codegen.cpp")
 
 
 def kernel_source_hash() -> str:
@@ -86,11 +92,33 @@ def summarize(out_dir: str, workload: str, kernel_substr: str, name: str) -> dic
     return res
 
 
+def stats_table(run_dir: str, title: str, command: str) -> str:
+    """Markdown table of a rocprofv3 --stats kernel summary (durations in microseconds)."""
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {run_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# rocprofv3 kernel trace: {title}", "", "Command (from the repository root):", "", "```", command, "```",
+           "", "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    out += ["", "Kernel template arguments: stream_kernel<LMAX, K, MODE, feature type, bundled units> with MODE",
+            "0 = receiver state (forward), 1 = tangent state, 2 = sender state, 3 = sender tangent state;",
+            "pos_kernel<LMAX, K, fp32 features split hi+lo, 16-byte loads, bundled units, Hessian term>;",
+            "gemm_kernel<KIND, row tiles, column tiles, indices per lane half, bf16 W, vector loads> with KIND",
+            "0 = out, 1 = gS, 2 = g_x, 3 = gW."]
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if len(argv) >= 1 and argv[0] == "copy":
         copy_probe()
     elif len(argv) == 5 and argv[0] == "summarize":
         print(json.dumps(summarize(*argv[1:]), indent=1))
+    elif len(argv) == 4 and argv[0] == "stats":
+        sys.stdout.write(stats_table(*argv[1:]))
     else:
         print(__doc__)
         return 2
