@@ -32,18 +32,18 @@ HIP_FLAGS = [
 ]
 # (object name, source, extra defines)
 STREAM_VARIANTS = [
-    ("fwd_f32", "kFwd", "float"), ("fwd_bf16", "kFwd", "uint16_t"),
-    ("jvp_f32", "kJvp", "float"), ("jvp_bf16", "kJvp", "uint16_t"),
-    ("snd_f32", "kSnd", "float"), ("sndt_f32", "kSndT", "float"),
+    ("fwd_f32", "kFwd", 1), ("fwd_bf16", "kFwd", 0),
+    ("jvp_f32", "kJvp", 1), ("jvp_bf16", "kJvp", 0),
+    ("snd_f32", "kSnd", 1), ("sndt_f32", "kSndT", 1),
 ]
 POS_VARIANTS = [("bpos_f32", "float", 0), ("bpos_bf16", "uint16_t", 0), ("hess_f32", "float", 1),
                 ("hess_bf16", "uint16_t", 1)]
-# The edge streams keep their 4x4 outer-product accumulators in ordinary VGPRs
+# The edge streams keep their matrix-core accumulators in ordinary VGPRs
 # (the accumulation registers would otherwise be copied back and forth).
 STREAM_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-UNITS = ([(f"stream_{n}", "stream_inst.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f"-DTP_FT={t}",
-                                                            f"-DTP_LAUNCHER=launch_stream_{n}"])
-          for n, m, t in STREAM_VARIANTS]
+UNITS = ([(f"stream_{n}", "stream_gf.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f"-DTP_LO={lo}",
+                                                          f"-DTP_LAUNCHER=launch_stream_{n}"])
+          for n, m, lo in STREAM_VARIANTS]
          + [(f"stream_{n}", "stream_pos.hip", STREAM_FLAGS + [f"-DTP_FT={t}", f"-DTP_HESS={h}",
                                                              f"-DTP_LAUNCHER=launch_stream_{n}"])
             for n, t, h in POS_VARIANTS]

@@ -113,29 +113,65 @@ size_t pad_bytes(const Plan& p, int64_t N, int op) {
   return b;
 }
 
-size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
-  return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + pad_bytes(p, N, TPCONV_OP_FORWARD);
+tpconv_status dev(hipError_t e) { return e == hipSuccess ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE; }
+
+// bf16 planes of the features the edge streams gather, rows padded to a
+// multiple of 32 channels: fp32 features split into hi and lo, bf16 features
+// used in place when C is a multiple of 32 and copied otherwise.
+int plane_cs(int C) { return (C + 31) / 32 * 32; }
+size_t plane_bytes(int64_t N, int rows, int C, bool bf16) {
+  if (bf16 && C % 32 == 0) return 0;
+  const size_t one = align_up((size_t)N * rows * plane_cs(C) * 2);
+  return bf16 ? one : 2 * one;
+}
+size_t x_planes(const Plan& p, int64_t N) { return plane_bytes(N, p.D_in, p.C_in, p.x_dtype == TPCONV_BF16); }
+size_t g_planes(const Plan& p, int64_t N) { return plane_bytes(N, p.D_out, p.C_out, false); }
+// The streams address the planes with 32-bit byte offsets.
+bool planes_addressable(const Plan& p, int64_t N) {
+  return (uint64_t)N * p.D_in * plane_cs(p.C_in) * 2 < (uint64_t(1) << 32) &&
+         (uint64_t)N * p.D_out * plane_cs(p.C_out) * 2 < (uint64_t(1) << 32);
 }
 
-// bf16 hi and lo planes of fp32 input features (the position-gradient stream's gathers)
-size_t split_elems(const Plan& p, int64_t N) {
-  return p.x_dtype == TPCONV_F32 ? (size_t)N * p.D_in * p.C_in : 0;
+struct Planes {
+  const void* hi = nullptr;
+  const void* lo = nullptr;
+  int cs = 0;
+};
+
+// The planes of rows x C features, carved from the workspace (none for bf16
+// features already padded).
+tpconv_status make_planes(const void* x, bool bf16, int64_t N, int rows, int C, Carver& c, Planes& out,
+                          hipStream_t s) {
+  out.cs = plane_cs(C);
+  if (bf16 && C % 32 == 0) {
+    out.hi = x;
+    out.lo = nullptr;
+    return TPCONV_SUCCESS;
+  }
+  const size_t n = (size_t)N * rows * out.cs;
+  uint16_t* hi = reinterpret_cast<uint16_t*>(c.take((n + 1) / 2));
+  uint16_t* lo = bf16 ? nullptr : reinterpret_cast<uint16_t*>(c.take((n + 1) / 2));
+  out.hi = hi;
+  out.lo = lo;
+  return dev(launch_planes(x, bf16, N * rows, C, out.cs, hi, lo, s));
+}
+
+size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
+  return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + x_planes(p, N) + pad_bytes(p, N, TPCONV_OP_FORWARD);
 }
 
 size_t ws_backward(const Plan& p, int64_t N) {
-  // S (recomputed when not saved), gS (fully connected only), T, gW partials, split x
+  // S (recomputed when not saved), gS (fully connected only), T, gW partials, planes of x and g_out
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2) + pad_bytes(p, N, TPCONV_OP_BACKWARD);
+         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) + pad_bytes(p, N, TPCONV_OP_BACKWARD);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
-  // S_dot, T_dot, weight partials; for d_pos also gS (fully connected) and split x
+  // S_dot, T_dot, weight partials, gS (fully connected), planes of x and g_out
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + 2 * align_up(split_elems(p, N) * 2) +
+         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) +
          pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD);
 }
-
-tpconv_status dev(hipError_t e) { return e == hipSuccess ? TPCONV_SUCCESS : TPCONV_ERROR_DEVICE; }
 
 // Independent chains of one call (the position gradient, the input gradient
 // and the weight gradient) run concurrently: a second stream per device,
@@ -289,8 +325,17 @@ void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
   set_units(p, a, p.send_units);
 }
 
-// Work items of a stream launch: one wave per (node, channel tile, unit).
-int64_t stream_items(const StreamArgs& a) { return (int64_t)a.num_nodes * a.ntiles * a.nunits; }
+// The gathered features of a stream as bf16 planes; the streams take their
+// 32-channel slices.
+void use_planes(StreamArgs& a, const Planes& pl) {
+  a.feat = pl.hi;
+  a.feat_lo = pl.lo;
+  a.feat_cs = pl.cs;
+  a.nslices = pl.cs / 32;
+}
+
+// Work items of a stream launch: one wave (or block) per (node, unit, slice).
+int64_t stream_items(const StreamArgs& a) { return (int64_t)a.num_nodes * a.nunits * a.nslices; }
 
 // Groups of a GEMM over the output irreps (Out, Gs, Gw) or input irreps (Gx).
 int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
@@ -467,11 +512,11 @@ tpconv_status run_cw_gw(const Plan& p, int64_t N, const float* state, const floa
 
 // The receiver-side position streams (kBwdPos: grad_pos; kBwdHess: the
 // position derivative of the force loss along gg_pos) into out [N][3]:
-// gS = g_out W^T first (formed in registers when channel-wise), fp32 features
-// split into bf16 hi + lo planes for the matrix cores.
+// gS = g_out W^T first (formed in registers when channel-wise); xp: the
+// bf16 planes of x.
 tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, const float* pos, const void* x,
-                             const void* W, const float* grad_out, const float* gg_pos, float* gS, uint16_t* xhi,
-                             uint16_t* xlo, float* out, hipStream_t s) {
+                             const Planes& xp, const void* W, const float* grad_out, const float* gg_pos, float* gS,
+                             float* out, hipStream_t s) {
   const int64_t N = g->num_nodes;
   const bool cw = channelwise(p);
   tpconv_status st;
@@ -480,14 +525,7 @@ tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, con
   StreamArgs a;
   recv_args(p, a, g, pos, x);
   set_units(p, a, p.pos_units);
-  a.nslices = (p.C_in + 31) / 32;
-  const size_t nsplit = split_elems(p, N);
-  if (nsplit > 0) {
-    if ((st = dev(launch_split_bf16(static_cast<const float*>(x), xhi, xlo, (int64_t)nsplit, s))) != TPCONV_SUCCESS)
-      return st;
-    a.feat = xhi;
-    a.feat_lo = xlo;
-  }
+  use_planes(a, xp);
   a.gstate = gS;
   a.gpos = out;
   a.ggpos = gg_pos;
@@ -540,11 +578,15 @@ RaggedWeightMap weight_map(const Plan& p) {
 tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x, const void* W,
                            float* out, float* saved_state, void* ws, hipStream_t s) {
   const int64_t N = g->num_nodes;
-  float* S = saved_state ? saved_state : static_cast<float*>(ws);
+  Carver c(ws);
+  float* S = saved_state ? saved_state : c.take(state_in_elems(p, N));
+  tpconv_status st;
+  Planes xp;
+  if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
   StreamArgs a;
   recv_args(p, a, g, pos, x);
+  use_planes(a, xp);
   a.state = S;
-  tpconv_status st;
   if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
       TPCONV_SUCCESS)
     return st;
@@ -563,14 +605,16 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
   float* T = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
-  const size_t nsplit = split_elems(p, N);
-  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
-  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
 
   const float* S = saved_state;
+  Planes xp;
+  if ((grad_W && !S) || grad_pos) {
+    if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
+  }
   if (grad_W && !S) {  // recompute the receiver state for the weight gradient
     StreamArgs a;
     recv_args(p, a, g, pos, x);
+    use_planes(a, xp);
     a.state = S_ws;
     if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
         TPCONV_SUCCESS)
@@ -580,8 +624,11 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (grad_x) {  // side stream: sender stream, then g_x = T W^T
+    Planes gp;
+    if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s2)) != TPCONV_SUCCESS) return st;
     StreamArgs a;
     send_args(p, a, g, pos, grad_out);
+    use_planes(a, gp);
     a.state = T;
     if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
     st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2) : run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s2);
@@ -592,7 +639,7 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
     if (st != TPCONV_SUCCESS) return st;
   }
   if (grad_pos) {  // caller's stream
-    st = run_pos_stream(p, kBwdPos, g, pos, x, W, grad_out, nullptr, gS, xhi, xlo, grad_pos, s);
+    st = run_pos_stream(p, kBwdPos, g, pos, x, xp, W, grad_out, nullptr, gS, grad_pos, s);
     if (st != TPCONV_SUCCESS) return st;
   }
   return fork.join();
@@ -609,14 +656,18 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   float* Td = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
   float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
-  const size_t nsplit = split_elems(p, N);
-  uint16_t* xhi = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
-  uint16_t* xlo = reinterpret_cast<uint16_t*>(c.take((nsplit + 1) / 2));
+  Planes xp;
+  if (d_W || d_grad_out || d_pos) {
+    if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
+  }
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
+    Planes gp;
+    if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s2)) != TPCONV_SUCCESS) return st;
     StreamArgs a;
     send_args(p, a, g, pos, grad_out);
+    use_planes(a, gp);
     a.ggpos = gg_pos;
     a.state = Td;
     if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
@@ -626,6 +677,7 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
     StreamArgs a;
     recv_args(p, a, g, pos, x);
+    use_planes(a, xp);
     a.ggpos = gg_pos;
     a.state = Sd;
     if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
@@ -642,7 +694,7 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
     }
   }
   if (d_pos) {  // caller's stream: the Hessian term
-    st = run_pos_stream(p, kBwdHess, g, pos, x, W, grad_out, gg_pos, gS, xhi, xlo, d_pos, s);
+    st = run_pos_stream(p, kBwdHess, g, pos, x, xp, W, grad_out, gg_pos, gS, d_pos, s);
     if (st != TPCONV_SUCCESS) return st;
   }
   return fork.join();
@@ -778,6 +830,7 @@ tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t N, int
   const Plan& p = plan->plan;
   switch (op) {
     case TPCONV_OP_FORWARD: *bytes = ws_forward(p, N, false); break;
+    case TPCONV_OP_FORWARD_SAVED: *bytes = ws_forward(p, N, true); break;
     case TPCONV_OP_BACKWARD: *bytes = ws_backward(p, N); break;
     case TPCONV_OP_DOUBLE_BACKWARD: *bytes = ws_double_backward(p, N); break;
     case TPCONV_OP_GRAPH_PREPARE: *bytes = graph_csc_workspace(N, E) + kAlign; break;
@@ -832,6 +885,7 @@ tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const floa
   const Plan& p = plan->plan;
   const int64_t N = g->num_nodes;
   if (N > 0 && (!pos || !x || !W || !out)) return TPCONV_ERROR_INVALID_VALUE;
+  if (!planes_addressable(p, N)) return TPCONV_ERROR_INVALID_VALUE;
   const size_t need = ws_forward(p, N, saved_state != nullptr);
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   if (N == 0) return TPCONV_SUCCESS;
@@ -857,6 +911,7 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
   const Plan& p = plan->plan;
   const int64_t N = g->num_nodes;
   if (N > 0 && (!pos || !x || !W || !grad_out)) return TPCONV_ERROR_INVALID_VALUE;
+  if (!planes_addressable(p, N)) return TPCONV_ERROR_INVALID_VALUE;
   const size_t need = ws_backward(p, N);
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -891,6 +946,7 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
   const Plan& p = plan->plan;
   const int64_t N = g->num_nodes;
   if (N > 0 && (!pos || !x || !W || !grad_out || !gg_pos)) return TPCONV_ERROR_INVALID_VALUE;
+  if (!planes_addressable(p, N)) return TPCONV_ERROR_INVALID_VALUE;
   const size_t need = ws_double_backward(p, N);
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

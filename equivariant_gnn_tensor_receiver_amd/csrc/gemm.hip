@@ -448,19 +448,23 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
   if (i < n) p[i] = v;
 }
 
-// fp32 -> bf16 hi + lo, four values per thread (n4 groups of four, then a tail).
-__global__ void split_bf16_kernel(const float* x, uint16_t* hi, uint16_t* lo, int64_t n) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+// Rows of C features -> bf16 planes of CS >= C values per row, zero past C.
+// fp32 input: hi = v rounded to bf16, lo = (v - hi) rounded again; bf16 input
+// (lo == NULL): a padded copy.  One thread per plane element (n < 2^31).
+__global__ void planes_kernel(const void* x, int x_bf16, uint16_t* hi, uint16_t* lo, uint32_t n, uint32_t C,
+                              uint32_t CS) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (i + t >= n) break;
-    const float v = x[i + t];
-    const __bf16 h = (__bf16)v;
-    const __bf16 l = (__bf16)(v - (float)h);
-    hi[i + t] = __builtin_bit_cast(uint16_t, h);
-    lo[i + t] = __builtin_bit_cast(uint16_t, l);
+  const uint32_t r = i / CS, c = i - r * CS;
+  if (x_bf16) {
+    hi[i] = c < C ? static_cast<const uint16_t*>(x)[(size_t)r * C + c] : (uint16_t)0;
+    return;
   }
+  const float v = c < C ? static_cast<const float*>(x)[(size_t)r * C + c] : 0.f;
+  const __bf16 h = (__bf16)v;
+  const __bf16 l = (__bf16)(v - (float)h);
+  hi[i] = __builtin_bit_cast(uint16_t, h);
+  lo[i] = __builtin_bit_cast(uint16_t, l);
 }
 
 // The nrows * C floats of rows row_off.. of a node are contiguous.
@@ -583,12 +587,14 @@ hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, i
   return hipGetLastError();
 }
 
-hipError_t launch_split_bf16(const float* x, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s) {
+hipError_t launch_planes(const void* x, bool x_bf16, int64_t rows, int C, int CS, uint16_t* hi, uint16_t* lo,
+                         hipStream_t s) {
+  const int64_t n = rows * CS;
   if (n <= 0) return hipSuccess;
-  const int64_t threads = (n + 3) / 4;
-  if ((threads + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;
+  if (n >= INT32_MAX || CS < C || (!x_bf16 && !lo)) return hipErrorInvalidValue;
   TimingScope ts(kcFill, s);
-  hipLaunchKernelGGL(split_bf16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, hi, lo, n);
+  hipLaunchKernelGGL(planes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, x_bf16 ? 1 : 0, hi, lo,
+                     (uint32_t)n, (uint32_t)C, (uint32_t)CS);
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ struct StreamArgs {
   int32_t nslices;      // kBwdPos: 32-channel slices of the reduction
   int32_t feat_rows;    // rows per node of the gathered feature tensor
   int32_t C;            // channels of the gathered features and of the state
+  int32_t feat_cs;      // channel stride of the gathered planes (>= C; a multiple of 32 except bf16 used in place)
   int32_t env_p;
   float cutoff, inv_cutoff, pref;          // pref = sqrt(2 / cutoff)
   float env_a, env_b, env_c, env_d;        // u = 1 - a x^p + b x^(p+1) - c x^(p+2); u' = -d x^(p-1) (1-x)^2
@@ -53,8 +54,8 @@ struct StreamArgs {
   const int32_t* nbr;   // [E] neighbour of each edge
   const float* pos;     // [N][3]
   const float* ggpos;   // [N][3] tangent (kJvp, kSndT)
-  const void* feat;     // [N][feat_rows][C], fp32 or bf16 (kBwdPos: bf16, or the hi plane of split fp32)
-  const void* feat_lo;  // kBwdPos: lo bf16 plane of fp32 features split into hi + lo (NULL: bf16 features)
+  const void* feat;     // gathered features as bf16 [N][feat_rows][feat_cs]: the hi plane of split fp32, or bf16
+  const void* feat_lo;  // lo bf16 plane of fp32 features split into hi + lo (NULL: bf16 features)
   float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
   const float* gstate;  // receiver-state cotangent gS (kBwdPos, fully connected)
   float* gpos;          // position gradient (kBwdPos) or force-loss position derivative (kBwdHess), accumulated
@@ -171,7 +172,10 @@ hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 // hi[i] = bf16(x[i]), lo[i] = bf16(x[i] - hi[i]) (round to nearest even), as raw bf16 bits.
-hipError_t launch_split_bf16(const float* x, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s);
+// bf16 planes of rows x C features with channel stride CS >= C, zero-padded:
+// fp32 features split into hi + lo, bf16 features copied into hi (lo unused).
+hipError_t launch_planes(const void* x, bool x_bf16, int64_t rows, int C, int CS, uint16_t* hi, uint16_t* lo,
+                         hipStream_t s);
 hipError_t launch_cw_contract(const CwArgs& a, hipStream_t s);
 hipError_t launch_cw_gw(const CwArgs& a, hipStream_t s);
 hipError_t launch_cw_reduce(const CwArgs& a, hipStream_t s);

@@ -356,7 +356,7 @@ struct PosWave {
     const int64_t frow = a.paths[a.unit_paths[unit][0]].feat_row;
     auto gather = [&](int t, int m1, u32x4& vh, u32x4& vl) {
       const int e = min(t * 16 + i, nb - 1);
-      const int64_t off = ((int64_t)S.geo.nbr[e] * a.feat_rows + frow + m1) * C;
+      const int64_t off = ((int64_t)S.geo.nbr[e] * a.feat_rows + frow + m1) * a.feat_cs;
       vh = load_bf16x8(fhi + off, c0, C, vec);
       if constexpr (LO) vl = load_bf16x8(flo + off, c0, C, vec);
     };
@@ -605,7 +605,7 @@ hipError_t launch_pos(int lmax, int K, const StreamArgs& a, hipStream_t s) {
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   const dim3 block(64 * pos_block_waves(npairs));
   // 16-byte operand loads: whole slices, 16-byte aligned feature and state rows
-  const bool vec = a.C % kPosSlice == 0 && (reinterpret_cast<uintptr_t>(a.feat) & 15) == 0 &&
+  const bool vec = a.C % kPosSlice == 0 && a.feat_cs == a.C && (reinterpret_cast<uintptr_t>(a.feat) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.feat_lo) & 15) == 0;
 #define TPCONV_LAUNCH(LM, KK)                                                                                      \
   if (lmax == LM && K == KK) {                                                                                     \

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.s
 
 TPCONV_F32, TPCONV_BF16 = 0, 1
 FULLY_CONNECTED, CHANNELWISE = 0, 1  # tpconv_connection
-OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_GRAPH_PREPARE, OP_GRAPH_ORDER = 0, 1, 2, 3, 4
+OP_FORWARD, OP_BACKWARD, OP_DOUBLE_BACKWARD, OP_GRAPH_PREPARE, OP_GRAPH_ORDER, OP_FORWARD_SAVED = 0, 1, 2, 3, 4, 5
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "IRREPS", 3: "GRAPH", 4: "WORKSPACE", 5: "UNSUPPORTED",
           6: "DEVICE", 7: "SCRATCH"}
 STATIC_SCRATCH_BYTES = 64 << 20
@@ -296,9 +296,11 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
         _keep_for_stream(stream, out)
     _check_inputs(plan, graph, pos, x, W, out=(out, plan.feat_out))
     _require(saved_state, "saved_state", torch.float32, plan.state_size(N) // 4, dev)
-    if workspace is None and (saved_state is None or plan.ragged):  # ragged plans pad inside the workspace
-        workspace = _workspace(plan.workspace_size(OP_FORWARD, N, graph.num_edges), dev)
-        _keep_for_stream(stream, workspace)
+    if workspace is None:
+        need = plan.workspace_size(OP_FORWARD if saved_state is None else OP_FORWARD_SAVED, N, graph.num_edges)
+        if need > 0:
+            workspace = _workspace(need, dev)
+            _keep_for_stream(stream, workspace)
     _require(workspace, "workspace", None, None, dev)
     g = graph.c()
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -98,7 +98,8 @@ typedef enum {
   TPCONV_OP_BACKWARD = 1,
   TPCONV_OP_DOUBLE_BACKWARD = 2,
   TPCONV_OP_GRAPH_PREPARE = 3,
-  TPCONV_OP_GRAPH_ORDER = 4
+  TPCONV_OP_GRAPH_ORDER = 4,
+  TPCONV_OP_FORWARD_SAVED = 5     /* tpconv_forward with a saved_state */
 } tpconv_op;
 
 typedef struct {
@@ -166,9 +167,11 @@ tpconv_status tpconv_plan_cg(tpconv_plan plan, int32_t path, double* out);
  * sender state T) and the fixed-count partial sums of the weight gradient.
  * GRAPH_PREPARE needs O(N) int32 scratch for the sender sort (index
  * metadata, not tensor-product workspace), GRAPH_ORDER O(N) for the sort of
- * the nodes.  FORWARD's figure assumes
- * saved_state == NULL; with a saved state a uniform plan's forward needs none
- * and a ragged plan's at most that figure.
+ * the nodes.  FORWARD's figure is for saved_state == NULL,
+ * FORWARD_SAVED's for a forward that writes a saved state (it holds no S;
+ * zero for bf16 features with C_in a multiple of 32 and a uniform plan).  The
+ * passes also hold bf16 copies of the gathered features (fp32 split into hi
+ * and lo planes, rows padded to a multiple of 32 channels).
  * Errors: INVALID_VALUE (null plan or bytes, negative sizes, unknown op). */
 tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t num_nodes,
                                     int64_t num_edges, size_t* bytes);
@@ -210,9 +213,12 @@ tpconv_status tpconv_graph_order(tpconv_plan plan, const tpconv_graph* g, const 
 
 /* Forward: out = conv(pos, x, W) as defined at the top of this header.
  * saved_state: NULL, or device memory of tpconv_state_size bytes that receives
- * the receiver state S for a later tpconv_backward (then a uniform plan's
- * workspace may be NULL/0; a ragged plan still needs room for its padded
- * copies).  Device pointers: pos, x, W, out (and saved_state). */
+ * the receiver state S for a later tpconv_backward (then the workspace needs
+ * tpconv_workspace_size(FORWARD_SAVED) bytes, which may be 0 and then allows
+ * NULL).  Device pointers: pos, x, W, out (and saved_state).
+ * Limit of every pass: the bf16 planes of x and of grad_out
+ * (N * rows * roundup(C, 32) * 2 bytes each) stay below 4 GiB, or the call
+ * returns INVALID_VALUE. */
 tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const float* pos,
                              const void* x, const void* W, float* out, float* saved_state,
                              void* workspace, size_t workspace_bytes, void* stream);
@@ -256,10 +262,11 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
  * serving loops, harnesses that forbid hipMalloc).  The receiver state S is
  * kept in a file-scope device array of TPCONV_STATIC_SCRATCH_BYTES (64 MiB)
  * that every GPU the library runs on holds until the process ends; it fits
- * problems whose tpconv_workspace_size(FORWARD) is at most that size (for
- * example N <= 1872 nodes at 32 channels of 0e+1o+2e with K = 8, 35 KiB of
- * state per node, or N <= 32768 at 8 channels of 0e+1o, 2 KiB).  Larger
- * problems return TPCONV_ERROR_SCRATCH before any launch.  The array is looked
+ * problems whose tpconv_workspace_size(FORWARD) is at most that size (the
+ * state S and the bf16 planes of x: for example N <= 1814 nodes at 32
+ * channels of 0e+1o+2e with K = 8, 35 KiB of state and 1.1 KiB of planes per
+ * node, or N <= 26214 at 8 channels of 0e+1o, 2.5 KiB).  Larger problems
+ * return TPCONV_ERROR_SCRATCH before any launch.  The array is looked
  * up on the first call on each device (the call then needs that device
  * current).  Same arguments, results and errors as tpconv_forward otherwise.
  * All calls on one GPU share the array: calls that overlap in time on one GPU

@@ -116,9 +116,17 @@ def test_workspace_is_independent_of_edges():
     for op in (tp.OP_FORWARD, tp.OP_BACKWARD, tp.OP_DOUBLE_BACKWARD):
         sizes = {plan.workspace_size(op, 4096, E) for E in (0, 131072, 524288, 8_388_608)}
         assert len(sizes) == 1
-    # forward workspace is exactly the receiver state, K * C * sum(2l3+1) fp32 per node
-    assert plan.workspace_size(tp.OP_FORWARD, 4096, 131072) == 4096 * 8 * 32 * 35 * 4
+    # forward workspace: the receiver state, K * C * sum(2l3+1) fp32 per node, and the
+    # bf16 hi and lo planes of x (rows of 32 channels); with a saved state only the planes
+    planes = 2 * 4096 * 9 * 32 * 2
+    assert plan.workspace_size(tp.OP_FORWARD, 4096, 131072) == 4096 * 8 * 32 * 35 * 4 + planes
+    assert plan.workspace_size(tp.OP_FORWARD_SAVED, 4096, 131072) == planes
     assert plan.state_size(4096) == 4096 * 8 * 32 * 35 * 4
+    # bf16 features with 32-channel rows are gathered in place; 24 channels are padded to 32
+    bf = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis, x_dtype=tp.TPCONV_BF16, w_dtype=tp.TPCONV_BF16)
+    assert bf.workspace_size(tp.OP_FORWARD_SAVED, 4096, 0) == 0
+    bf24 = tp.Plan("24x0e+24x1o+24x2e", "24x0e+24x1o+24x2e", 2, 8, x_dtype=tp.TPCONV_BF16)
+    assert bf24.workspace_size(tp.OP_FORWARD_SAVED, 4096, 0) == 4096 * 9 * 32 * 2
 
 
 def test_argument_errors_before_any_launch():
