@@ -32,7 +32,15 @@ METRIC = "edges/sec fwd and fwd+bwd per config; % of HBM/MFMA roofline; peak byt
 HBM_GBS = 8000.0          # MI355X HBM3E
 FP32_TFLOPS = 157.3       # fp32 MFMA, and packed fp32 VALU (256 CUs x 4 SIMDs x 64 FLOP/clk x 2.4 GHz)
 BF16_TFLOPS = 2500.0      # dense bf16 MFMA
-PEAK = {"hbm": (HBM_GBS, "GB/s"), "mfma": (FP32_TFLOPS, "TFLOP/s"), "alu": (FP32_TFLOPS, "TFLOP/s")}
+PEAK = {"hbm": (HBM_GBS, "GB/s"), "alu": (FP32_TFLOPS, "TFLOP/s")}
+
+
+def gemm_peak(name, w_bf16):
+    """Peak of an fp32-accurate contraction on the bf16 matrix cores: each fp32
+    operand is split into bf16 hi + lo, so one product takes three bf16
+    products (two when the weights are bf16 already; gW multiplies two fp32
+    operands either way)."""
+    return BF16_TFLOPS / (2 if w_bf16 and name != "gemm_gw" else 3)
 CONFIG_ORDER = ("tiny", "molecular", "wide_l", "edge_scaling", "force", "molecular_uvu")
 
 
@@ -106,9 +114,10 @@ PASS_KERNELS = {
 CW_KERNEL = {"gemm_out": "cw_contract", "gemm_gx": "cw_contract", "gemm_gw": "cw_gw", "gemm_gs": None}
 
 
-def pass_bound(names, alg, channelwise, mfma_peak_tflops, nbytes):
-    """T_lb = max(bytes / HBM, VALU FLOPs / VALU peak, MFMA FLOPs / MFMA peak), perfect overlap assumed."""
+def pass_bound(names, alg, channelwise, w_bf16, nbytes):
+    """T_lb = max(bytes / HBM, VALU FLOPs / VALU peak, contraction FLOPs / their peak), perfect overlap assumed."""
     valu = mfma = 0
+    t_mfma = 0.0
     for n in names:
         if channelwise and n in CW_KERNEL:
             n = CW_KERNEL[n]
@@ -117,27 +126,27 @@ def pass_bound(names, alg, channelwise, mfma_peak_tflops, nbytes):
             valu += alg[n][0]  # channel-diagonal contractions run on the vector ALUs
         elif n.startswith("gemm"):
             mfma += alg[n][0]
+            t_mfma += alg[n][0] / (gemm_peak(n, w_bf16) * 1e12)
         else:
             valu += alg[n][0]
-    terms = {"hbm": nbytes / (HBM_GBS * 1e9), "alu": valu / (FP32_TFLOPS * 1e12),
-             "mfma": mfma / (mfma_peak_tflops * 1e12)}
+    terms = {"hbm": nbytes / (HBM_GBS * 1e9), "alu": valu / (FP32_TFLOPS * 1e12), "mfma": t_mfma}
     bind = max(terms, key=terms.get)
     return terms[bind], bind, valu, mfma
 
 
-def roofline_for(name, flops, nbytes, ms):
+def roofline_for(name, flops, nbytes, ms, w_bf16):
     sec = ms * 1e-3
     t_alu = flops / (PEAK["alu"][0] * 1e12)
     t_hbm = nbytes / (PEAK["hbm"][0] * 1e9)
     if name.startswith("gemm"):
-        bound = "mfma" if flops / (PEAK["mfma"][0] * 1e12) >= t_hbm else "hbm"
+        bound = "mfma" if flops / (gemm_peak(name, w_bf16) * 1e12) >= t_hbm else "hbm"
     else:
         bound = "alu" if t_alu >= t_hbm else "hbm"
     if bound == "hbm":
         achieved = nbytes / sec / 1e9
     else:
         achieved = flops / sec / 1e12
-    peak, unit = PEAK[bound]
+    peak, unit = (round(gemm_peak(name, w_bf16), 1), "TFLOP/s") if bound == "mfma" else PEAK[bound]
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "algorithmic_flops": int(flops), "algorithmic_bytes": int(nbytes),
             "avg_launch_us": round(ms * 1e3, 2)}
@@ -306,7 +315,7 @@ def run_workload(name, steps, warmup, detail):
     xbytes = wbytes = 2 if w.dtype == "bf16" else 4
     alg = algorithmic(plan, plan_counts(plan), N, E, xbytes, wbytes)
     z = sizes(plan, N, E, xbytes, wbytes)
-    mfma_peak = BF16_TFLOPS if w.dtype == "bf16" else FP32_TFLOPS
+    w_bf16 = w.dtype == "bf16"
 
     def bound(pass_names, measured_ms):
         ks, ts = [], set()
@@ -314,7 +323,7 @@ def run_workload(name, steps, warmup, detail):
             ks += PASS_KERNELS[pn][0]
             ts |= PASS_KERNELS[pn][1]  # a tensor several passes of one step touch counts once
         nbytes = sum(z[t] for t in ts)
-        t_lb, bind, valu, mfma = pass_bound(ks, alg, w.channelwise, mfma_peak, nbytes)
+        t_lb, bind, valu, mfma = pass_bound(ks, alg, w.channelwise, w_bf16, nbytes)
         return {"ms": round(measured_ms, 4), "edges_per_s": round(E / (measured_ms * 1e-3), 1),
                 "t_lb_us": round(t_lb * 1e6, 2), "binding": bind, "frac_of_bound": round(t_lb / (measured_ms * 1e-3), 4),
                 "valu_gflop": round(valu / 1e9, 3), "mfma_gflop": round(mfma / 1e9, 3),
@@ -352,7 +361,7 @@ def run_workload(name, steps, warmup, detail):
                           "share": round(ms / sum(v[1] for v in ktimes.values()), 4)}
     dom = max((k for k in ktimes if k in alg), key=lambda k: ktimes[k][1])
     n_dom, ms_dom = ktimes[dom]
-    roof = roofline_for(dom, alg[dom][0], alg[dom][1], ms_dom / n_dom)
+    roof = roofline_for(dom, alg[dom][0], alg[dom][1], ms_dom / n_dom, w_bf16)
     roof["traffic"] = load_traffic(w.name, dom)
     rep.update({
         "value": E / (ms_step * 1e-3),

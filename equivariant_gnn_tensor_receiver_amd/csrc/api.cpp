@@ -156,20 +156,51 @@ tpconv_status make_planes(const void* x, bool bf16, int64_t N, int rows, int C, 
   return dev(launch_planes(x, bf16, N * rows, C, out.cs, hi, lo, s));
 }
 
+// bf16 planes of W for the contractions (fully connected only): hi and, for
+// fp32 weights, lo, each in W's layout and transposed per (k, p).
+size_t w_planes(const Plan& p) {
+  if (channelwise(p)) return 0;
+  return (p.w_dtype == TPCONV_BF16 ? 2 : 4) * align_up(w_elems(p) * 2);
+}
+
+struct WPlanes {
+  const uint16_t* hi = nullptr;
+  const uint16_t* lo = nullptr;
+  const uint16_t* thi = nullptr;
+  const uint16_t* tlo = nullptr;
+};
+
+tpconv_status make_w_planes(const Plan& p, const void* W, Carver& c, WPlanes& out, hipStream_t s) {
+  if (channelwise(p)) return TPCONV_SUCCESS;
+  const size_t n = w_elems(p);
+  const bool bf16 = p.w_dtype == TPCONV_BF16;
+  uint16_t* hi = reinterpret_cast<uint16_t*>(c.take((n + 1) / 2));
+  uint16_t* thi = reinterpret_cast<uint16_t*>(c.take((n + 1) / 2));
+  uint16_t* lo = bf16 ? nullptr : reinterpret_cast<uint16_t*>(c.take((n + 1) / 2));
+  uint16_t* tlo = bf16 ? nullptr : reinterpret_cast<uint16_t*>(c.take((n + 1) / 2));
+  out.hi = hi;
+  out.lo = lo;
+  out.thi = thi;
+  out.tlo = tlo;
+  return dev(launch_w_planes(W, bf16, (int64_t)p.K * p.P, p.C_in, p.C_out, hi, lo, thi, tlo, s));
+}
+
 size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
-  return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + x_planes(p, N) + pad_bytes(p, N, TPCONV_OP_FORWARD);
+  return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + x_planes(p, N) + w_planes(p) +
+         pad_bytes(p, N, TPCONV_OP_FORWARD);
 }
 
 size_t ws_backward(const Plan& p, int64_t N) {
   // S (recomputed when not saved), gS (fully connected only), T, gW partials, planes of x and g_out
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) + pad_bytes(p, N, TPCONV_OP_BACKWARD);
+         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
+         pad_bytes(p, N, TPCONV_OP_BACKWARD);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
   // S_dot, T_dot, weight partials, gS (fully connected), planes of x and g_out
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) +
+         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
          pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD);
 }
 
@@ -345,7 +376,6 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
   a.C_in = p.C_in;
   a.C_out = p.C_out;
   a.splits = splits;
-  a.w_bf16 = p.w_dtype == TPCONV_BF16;
   const bool in_side = kind == kGemmGx;
   const auto& groups = in_side ? p.in_groups : p.out_groups;
   a.D_feat = in_side ? p.D_in : p.D_out;
@@ -381,13 +411,26 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // 16-byte operand loads need channel counts that are multiples of 16 and
-// 16-byte aligned base pointers.
+// 16-byte aligned states (the planes come from the workspace, 256-aligned).
 void set_vec(const Plan& p, GemmArgs& a) {
-  a.vec = (p.C_in % 16 == 0) && (p.C_out % 16 == 0) && aligned16(a.state) && aligned16(a.feat) && aligned16(a.W);
+  a.vec = (p.C_in % 16 == 0) && (p.C_out % 16 == 0) && aligned16(a.state);
 }
 
-tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, const float* feat,
-                       const void* W, float* out, int splits, hipStream_t s) {
+void set_planes(GemmArgs& a, const Planes* gp, const WPlanes& wp) {
+  if (gp) {
+    a.feat_hi = static_cast<const uint16_t*>(gp->hi);
+    a.feat_lo = static_cast<const uint16_t*>(gp->lo);
+    a.feat_cs = gp->cs;
+  }
+  a.w_hi = wp.hi;
+  a.w_lo = wp.lo;
+  a.wt_hi = wp.thi;
+  a.wt_lo = wp.tlo;
+}
+
+// gp: the g_out planes (gS); wp: the W planes.
+tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, const Planes* gp, const WPlanes& wp,
+                       float* out, int splits, hipStream_t s) {
   if (kind == kGemmOut || kind == kGemmGx) {  // rows of irreps that no path reaches are zero
     const bool in_side = kind == kGemmGx;
     for (const auto& g : in_side ? p.in_groups : p.out_groups) {
@@ -400,20 +443,20 @@ tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, c
   GemmArgs a;
   gemm_setup(p, kind, N, a, splits);
   a.state = state;
-  a.feat = feat;
-  a.W = W;
+  set_planes(a, gp, wp);
   a.out = out;
   set_vec(p, a);
   return dev(launch_gemm(kind, a, s));
 }
 
-tpconv_status run_gw(const Plan& p, int64_t N, const float* state, const float* gout, float* part, float* gW,
+// gW = S^T g_out from the g_out planes gp.
+tpconv_status run_gw(const Plan& p, int64_t N, const float* state, const Planes& gp, float* part, float* gW,
                      hipStream_t s) {
   const int splits = gw_splits(p, N);
   GemmArgs a;
   gemm_setup(p, kGemmGw, N, a, splits);
   a.state = state;
-  a.feat = gout;
+  set_planes(a, &gp, WPlanes{});
   a.out = part;
   set_vec(p, a);
   tpconv_status st = dev(launch_gemm(kGemmGw, a, s));
@@ -512,15 +555,15 @@ tpconv_status run_cw_gw(const Plan& p, int64_t N, const float* state, const floa
 
 // The receiver-side position streams (kBwdPos: grad_pos; kBwdHess: the
 // position derivative of the force loss along gg_pos) into out [N][3]:
-// gS = g_out W^T first (formed in registers when channel-wise); xp: the
-// bf16 planes of x.
+// gS = g_out W^T first (formed in registers when channel-wise); xp, gp, wp:
+// the bf16 planes of x, g_out and W.
 tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, const float* pos, const void* x,
-                             const Planes& xp, const void* W, const float* grad_out, const float* gg_pos, float* gS,
-                             float* out, hipStream_t s) {
+                             const Planes& xp, const Planes& gp, const WPlanes& wp, const void* W,
+                             const float* grad_out, const float* gg_pos, float* gS, float* out, hipStream_t s) {
   const int64_t N = g->num_nodes;
   const bool cw = channelwise(p);
   tpconv_status st;
-  if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, grad_out, W, gS, 1, s)) != TPCONV_SUCCESS) return st;
+  if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, 1, s)) != TPCONV_SUCCESS) return st;
   if ((st = dev(launch_fill(out, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
   StreamArgs a;
   recv_args(p, a, g, pos, x);
@@ -583,6 +626,8 @@ tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* po
   tpconv_status st;
   Planes xp;
   if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
+  WPlanes wp;
+  if ((st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
   StreamArgs a;
   recv_args(p, a, g, pos, x);
   use_planes(a, xp);
@@ -591,7 +636,7 @@ tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* po
       TPCONV_SUCCESS)
     return st;
   if (channelwise(p)) return run_cw_contract(p, true, N, S, W, out, s);
-  return run_gemm(p, kGemmOut, N, S, nullptr, W, out, 1, s);
+  return run_gemm(p, kGemmOut, N, S, nullptr, wp, out, 1, s);
 }
 
 tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x, const void* W,
@@ -621,25 +666,28 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
       return st;
     S = S_ws;
   }
+  // planes of g_out (sender stream, gS, gW) and of W, before the fork
+  Planes gp;
+  if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s)) != TPCONV_SUCCESS) return st;
+  WPlanes wp;
+  if ((grad_x || grad_pos) && (st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (grad_x) {  // side stream: sender stream, then g_x = T W^T
-    Planes gp;
-    if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s2)) != TPCONV_SUCCESS) return st;
     StreamArgs a;
     send_args(p, a, g, pos, grad_out);
     use_planes(a, gp);
     a.state = T;
     if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2) : run_gemm(p, kGemmGx, N, T, nullptr, W, grad_x, 1, s2);
+    st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2) : run_gemm(p, kGemmGx, N, T, nullptr, wp, grad_x, 1, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
   if (grad_W) {  // side stream: gW = S^T g_out
-    st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, grad_out, part, grad_W, s2);
+    st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, gp, part, grad_W, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
   if (grad_pos) {  // caller's stream
-    st = run_pos_stream(p, kBwdPos, g, pos, x, xp, W, grad_out, nullptr, gS, grad_pos, s);
+    st = run_pos_stream(p, kBwdPos, g, pos, x, xp, gp, wp, W, grad_out, nullptr, gS, grad_pos, s);
     if (st != TPCONV_SUCCESS) return st;
   }
   return fork.join();
@@ -660,18 +708,21 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   if (d_W || d_grad_out || d_pos) {
     if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
   }
+  // planes of g_out (sender tangent stream, d_W, gS) and of W, before the fork
+  Planes gp;
+  if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s)) != TPCONV_SUCCESS) return st;
+  WPlanes wp;
+  if ((d_x || d_grad_out || d_pos) && (st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
-    Planes gp;
-    if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s2)) != TPCONV_SUCCESS) return st;
     StreamArgs a;
     send_args(p, a, g, pos, grad_out);
     use_planes(a, gp);
     a.ggpos = gg_pos;
     a.state = Td;
     if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    st = cw ? run_cw_contract(p, false, N, Td, W, d_x, s2) : run_gemm(p, kGemmGx, N, Td, nullptr, W, d_x, 1, s2);
+    st = cw ? run_cw_contract(p, false, N, Td, W, d_x, s2) : run_gemm(p, kGemmGx, N, Td, nullptr, wp, d_x, 1, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
   if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
@@ -684,17 +735,17 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
         TPCONV_SUCCESS)
       return st;
     if (d_W) {
-      st = cw ? run_cw_gw(p, N, Sd, grad_out, part, d_W, s) : run_gw(p, N, Sd, grad_out, part, d_W, s);
+      st = cw ? run_cw_gw(p, N, Sd, grad_out, part, d_W, s) : run_gw(p, N, Sd, gp, part, d_W, s);
       if (st != TPCONV_SUCCESS) return st;
     }
     if (d_grad_out) {
       st = cw ? run_cw_contract(p, true, N, Sd, W, d_grad_out, s)
-              : run_gemm(p, kGemmOut, N, Sd, nullptr, W, d_grad_out, 1, s);
+              : run_gemm(p, kGemmOut, N, Sd, nullptr, wp, d_grad_out, 1, s);
       if (st != TPCONV_SUCCESS) return st;
     }
   }
   if (d_pos) {  // caller's stream: the Hessian term
-    st = run_pos_stream(p, kBwdHess, g, pos, x, xp, W, grad_out, gg_pos, gS, d_pos, s);
+    st = run_pos_stream(p, kBwdHess, g, pos, x, xp, gp, wp, W, grad_out, gg_pos, gS, d_pos, s);
     if (st != TPCONV_SUCCESS) return st;
   }
   return fork.join();

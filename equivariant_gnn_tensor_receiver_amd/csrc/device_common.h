@@ -8,6 +8,38 @@
 
 namespace tpconv {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The bf16 pairs (-1, 0) and (0, -1) for split8, held in scalar registers.
+// As literals the compiler encodes (-1, 0) as the 32-bit inline constant -1.0,
+// which the hardware reads as (0, -1); opaque register values avoid that.
+struct SplitConsts {
+  bf16x2 neg_x, neg_y;
+  __device__ __forceinline__ SplitConsts() {
+    uint32_t x = 0x0000bf80u, y = 0xbf800000u;
+    asm volatile("" : "+s"(x), "+s"(y));
+    neg_x = __builtin_bit_cast(bf16x2, x);
+    neg_y = __builtin_bit_cast(bf16x2, y);
+  }
+};
+
+// hi / lo bf16 split of eight fp32 values: hi rounds to nearest even, and
+// lo = v - hi, exact in fp32, comes from a bf16 dot product of hi with
+// (-1, 0) or (0, -1) accumulated onto v, then rounds again.
+__device__ __forceinline__ void split8(const float (&v)[8], u32x4& hi, u32x4& lo, const SplitConsts& k) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bf16x2 h = {(__bf16)v[2 * t], (__bf16)v[2 * t + 1]};
+    const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, k.neg_x, v[2 * t], false);
+    const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, k.neg_y, v[2 * t + 1], false);
+    const bf16x2 l = {(__bf16)l0, (__bf16)l1};
+    hi[t] = __builtin_bit_cast(uint32_t, h);
+    lo[t] = __builtin_bit_cast(uint32_t, l);
+  }
+}
+
 __device__ __forceinline__ float load_feat(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_feat(const uint16_t* p, int64_t i) {
   return __uint_as_float(((uint32_t)p[i]) << 16);

@@ -1,4 +1,5 @@
-// Dense contractions with the shared weights W on the fp32 matrix cores.
+// Dense contractions with the shared weights W on the bf16 matrix cores at
+// fp32 accuracy.
 //
 // After the edge stream, the remaining work of every pass is one dense
 // contraction per irrep group ("Sobek" page, abstract: the formulation keeps
@@ -9,21 +10,27 @@
 //   g_x  = T_g . W^T      rows (s, m1), reduction (k, q, co), columns ci
 //   gW   = S_g^T . g_out  rows (k, q, ci), reduction (v, m3), columns co (split, then summed in order)
 //
+// Every product runs on v_mfma_f32_32x32x16_bf16 with each fp32 operand split
+// into bf16 hi + lo and the tile formed as hi*hi' + hi*lo' + lo*hi' (each
+// exact in the fp32 accumulator; a bf16 operand has no lo part).  W and g_out
+// come pre-split into bf16 planes (W also transposed per (k, p), so that every
+// B operand is contiguous along its reduction); the node-sized states S and T
+// are split in registers as they are loaded.
+//
 // These products are skinny (32..128 columns) and stream a node-sized
 // operand once, so the kernel is built for bytes in flight rather than for
 // LDS reuse.  Every wave owns a (32*MT)-row x (32*NT)-column tile and loads its
-// operands straight into registers: for v_mfma_f32_32x32x2f32 lane (i, h)
-// (i = lane % 32, h = lane / 32) supplies A[i][kk = h] and B[kk = h][i], and
-// the reduction order inside a chunk of 2*VH indices is permuted so that lane
-// half h takes the VH consecutive indices r0 + VH*h + t (t = 0..VH-1), step t
-// of the chunk summing r0 + t and r0 + VH + t.  An operand that is contiguous
-// along the reduction is then read as 16-byte vectors per lane; one that is
-// contiguous along its row or column index is read as 128-byte coalesced
-// rows.  The next chunk is loaded while the current one is multiplied.  Small
-// problems split the reduction over the 1, 2 or 4 waves of a block (interleaved
-// chunks, so that the waves read neighbouring segments of a row); the waves'
-// partial tiles are summed in a fixed order through LDS, so results do not
-// depend on timing.
+// operands straight into registers: lane (i, h) (i = lane % 32, h = lane / 32)
+// supplies row i of A and column i of B at the reduction indices
+// r0 + VH*h + t (t = 0..VH-1) of a chunk of 2*VH, the s-th product of a chunk
+// taking t = 8s..8s+7 from both halves.  An operand that is contiguous along
+// the reduction is then read as 16-byte vectors per lane; one that is
+// contiguous along its row or column index is read as coalesced rows.  The
+// next chunks are loaded while the current one is multiplied.  Small problems
+// split the reduction over the 1, 2 or 4 waves of a block (interleaved chunks,
+// so that the waves read neighbouring segments of a row); the waves' partial
+// tiles are summed in a fixed order through LDS, so results do not depend on
+// timing.
 #include "device_common.h"
 #include "kernels.h"
 #include "timing.h"
@@ -39,17 +46,6 @@ constexpr int kTargetWaves = 4096;  // 4 waves per SIMD
 constexpr int kMaxWaveSplit = 4;
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-// Raw 32-bit pattern of one weight: the fp32 bits, or the bf16 bits
-// zero-extended (widened by a shift where the value is used).
-template <bool WBF16>
-__device__ __forceinline__ uint32_t raw_w(const void* W, int64_t i) {
-  if constexpr (WBF16)
-    return static_cast<const uint16_t*>(W)[i];
-  else
-    return __float_as_uint(static_cast<const float*>(W)[i]);
-}
-
 
 // VH consecutive floats p[0..VH) (16-byte loads when VEC).  Loads are never
 // predicated and their values are not touched here: the caller clamps `p`
@@ -119,14 +115,8 @@ __device__ __forceinline__ int64_t w_row_halves(const GemmArgs& a, const GemmGro
 template <int KIND, int VH, bool VEC>
 __device__ __forceinline__ void load_a(const GemmArgs& a, const GemmGroup& G, int m, int rs, int r_end,
                                        float (&v)[VH]) {
-  if constexpr (KIND == kGemmOut || KIND == kGemmGx || KIND == kGemmGs) {
-    const float* row;
-    if constexpr (KIND == kGemmGs) {
-      const int node = m / G.n, mm = m - node * G.n;
-      row = a.feat + ((int64_t)node * a.D_feat + G.row_off + mm) * a.C_out;
-    } else {
-      row = a.state + G.state_off + (int64_t)m * G.Kr;
-    }
+  if constexpr (KIND == kGemmOut || KIND == kGemmGx) {
+    const float* row = a.state + G.state_off + (int64_t)m * G.Kr;
     // VEC: Kr is a multiple of 16 and rs of VH, so a whole run is in or out
     const int rc = VEC ? (rs < r_end ? rs : r_end - VH) : (rs < r_end ? rs : r_end - 1);
     load_run<VH, VEC>(row + (rc > 0 ? rc : 0), r_end - rs, v);
@@ -137,95 +127,105 @@ __device__ __forceinline__ void load_a(const GemmArgs& a, const GemmGroup& G, in
   }
 }
 
-// B operand: values t = 0..VH-1 of column n at reductions rs + t, as raw bits
-// (see Bits); indices past the end of the reduction read inside the tensor.
-template <int KIND, int VH, bool WBF16, bool VEC>
-struct Bits {
-  // bf16 weights read 4 at a time (gS and g_x with 16-byte channel rows) stay
-  // packed two per word; other bf16 weights take one word each
-  static constexpr bool PACKED = WBF16 && VEC && (KIND == kGemmGs || KIND == kGemmGx);
-  static constexpr int N = PACKED ? VH / 2 : VH;
-  __device__ __forceinline__ static float get(const uint32_t (&v)[N], int t) {
-    if constexpr (!WBF16)
-      return __uint_as_float(v[t]);
-    else if constexpr (PACKED)
-      return __uint_as_float((t & 1) ? (v[t >> 1] & 0xffff0000u) : (v[t >> 1] << 16));
-    else
-      return __uint_as_float(v[t] << 16);
+// VH consecutive bf16 p[0..VH) as VH/2 packed words (16-byte loads).
+template <int VH>
+__device__ __forceinline__ void load_words(const uint16_t* p, uint32_t (&w)[VH / 2]) {
+#pragma unroll
+  for (int j = 0; j < VH / 8; ++j) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p + 8 * j);
+    w[4 * j] = u.x;
+    w[4 * j + 1] = u.y;
+    w[4 * j + 2] = u.z;
+    w[4 * j + 3] = u.w;
   }
-};
+}
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
-template <int KIND, int VH, bool WBF16, bool VEC>
+// A operand of gS from the g_out planes: values t = 0..VH-1 of row m at
+// reductions (co) rs + t.  The planes are zero past C_out up to their
+// channel stride, a multiple of 32, so a chunk never leaves its row.
+template <int VH>
+__device__ __forceinline__ void load_a_planes(const GemmArgs& a, const GemmGroup& G, int m, int rs,
+                                              uint32_t (&h)[VH / 2], uint32_t (&l)[VH / 2]) {
+  const int node = m / G.n, mm = m - node * G.n;
+  const int64_t off = ((int64_t)node * a.D_feat + G.row_off + mm) * a.feat_cs + rs;
+  load_words<VH>(a.feat_hi + off, h);
+  load_words<VH>(a.feat_lo + off, l);
+}
+
+// B operand: values t = 0..VH-1 of column n at reductions rs + t as packed
+// bf16 words (hi, and lo where LO); indices past the end of the reduction
+// read inside the tensor (their A values are zero).
+template <int KIND, int VH, bool LO, bool VEC>
 __device__ __forceinline__ void load_b(const GemmArgs& a, const GemmGroup& G, int n, int rs, int r_end, int pl,
-                                       uint32_t (&v)[Bits<KIND, VH, WBF16, VEC>::N]) {
-  if constexpr (KIND == kGemmOut) {  // B(r = (k,q,ci), n = co) = W[k][p][ci][co]
-    if constexpr (VEC) {  // the VH reductions share (k, q): C_in is a multiple of 16
-      int ci;
-      const int64_t kp = w_row_halves(a, G, rs < r_end ? rs : 0, a.C_in, pl, (int)(threadIdx.x & 63) >> 5, ci);
-      const int64_t base = (kp * a.C_in + ci) * a.C_out + n;
-#pragma unroll
-      for (int t = 0; t < VH; ++t) v[t] = raw_w<WBF16>(a.W, base + (int64_t)t * a.C_out);
-    } else {
-#pragma unroll
-      for (int t = 0; t < VH; ++t) {
-        int ci;
-        const int r = min(rs + t, G.Kr - 1);
-        const int64_t kp = w_row(a, G, r, a.C_in, pl, ci);
-        v[t] = raw_w<WBF16>(a.W, (kp * a.C_in + ci) * a.C_out + n);
-      }
-    }
-  } else if constexpr (KIND == kGemmGs || KIND == kGemmGx) {
-    // gS: B(r = co, n = (k,q,ci)) = W[k][p][ci][co];  g_x: B(r = (k,q,co), n = ci) = W[k][p][ci][co]
-    int64_t base;
-    if constexpr (KIND == kGemmGs) {
-      int ci;
-      const int64_t kp = w_row(a, G, n, a.C_in, pl, ci);
-      base = (kp * a.C_in + ci) * a.C_out + (VEC ? (rs < r_end ? rs : 0) : 0);
-    } else if constexpr (VEC) {  // the VH reductions share (k, q): C_out is a multiple of 16
-      int co;
-      const int64_t kp = w_row_halves(a, G, rs < r_end ? rs : 0, a.C_out, pl, (int)(threadIdx.x & 63) >> 5, co);
-      base = (kp * a.C_in + n) * a.C_out + co;
-    } else {
-      base = 0;
-    }
-    if constexpr (VEC) {
-#pragma unroll
-      for (int j = 0; j < VH / 4; ++j) {
-        if constexpr (WBF16) {
-          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.W) + base + 4 * j);
-          v[2 * j] = u.x;
-          v[2 * j + 1] = u.y;
-        } else {
-          const floatx4 x = *reinterpret_cast<const floatx4*>(static_cast<const float*>(a.W) + base + 4 * j);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[4 * j + e] = __float_as_uint(x[e]);
-        }
-      }
-    } else if constexpr (KIND == kGemmGs) {
-#pragma unroll
-      for (int t = 0; t < VH; ++t) v[t] = raw_w<WBF16>(a.W, base + min(rs + t, r_end - 1));
-    } else {
-#pragma unroll
-      for (int t = 0; t < VH; ++t) {
-        int co;
-        const int r = min(rs + t, G.Kr - 1);
-        const int64_t kp = w_row(a, G, r, a.C_out, pl, co);
-        v[t] = raw_w<WBF16>(a.W, (kp * a.C_in + n) * a.C_out + co);
-      }
-    }
-  } else {  // Gw: B(r = (v, m3), n = co) = g_out[v][row_off + m3][co]; rows stepped without division
+                                       uint32_t (&bh)[VH / 2], uint32_t (&bl)[LO ? VH / 2 : 1]) {
+  if constexpr (KIND == kGemmGw) {  // B(r = (v, m3), n = co) = g_out planes; rows stepped without division
     const int r0 = min(rs, G.Kr - 1);
     int node = r0 / G.n, mm = r0 - node * G.n;
-    const float* base = a.feat + (int64_t)G.row_off * a.C_out + n;
+    const int64_t col = (int64_t)G.row_off * a.feat_cs + n;
+    uint16_t vh[VH], vl[VH];
 #pragma unroll
     for (int t = 0; t < VH; ++t) {
-      v[t] = __float_as_uint(base[((int64_t)node * a.D_feat + mm) * a.C_out]);
+      const int64_t o = ((int64_t)node * a.D_feat + mm) * a.feat_cs + col;
+      vh[t] = a.feat_hi[o];
+      vl[t] = a.feat_lo[o];
       // next row; past the end of the reduction the last row is read again
       const bool adv = rs + t + 1 < G.Kr;
       const bool wrap = mm + 1 == G.n;
       const int mm2 = wrap ? 0 : mm + 1, node2 = wrap ? node + 1 : node;
       mm = adv ? mm2 : mm;
       node = adv ? node2 : node;
+    }
+#pragma unroll
+    for (int t = 0; t < VH / 2; ++t) {
+      bh[t] = pack2(vh[2 * t], vh[2 * t + 1]);
+      if constexpr (LO) bl[t] = pack2(vl[2 * t], vl[2 * t + 1]);
+    }
+  } else {
+    // out: B(r = (k,q,ci), n = co) = W^T planes [k][p][co][ci]
+    // gS:  B(r = co, n = (k,q,ci)) = W planes [k][p][ci][co]
+    // g_x: B(r = (k,q,co), n = ci) = W planes [k][p][ci][co]
+    const uint16_t* ph = KIND == kGemmOut ? a.wt_hi : a.w_hi;
+    const uint16_t* plo = KIND == kGemmOut ? a.wt_lo : a.w_lo;
+    // element index of reduction r (any r below the end of the reduction)
+    auto index = [&](int r) -> int64_t {
+      if constexpr (KIND == kGemmGs) {
+        int ci;
+        const int64_t kp = w_row(a, G, n, a.C_in, pl, ci);
+        return (kp * a.C_in + ci) * a.C_out + r;
+      } else {
+        int c;
+        const int64_t kp = w_row(a, G, r, KIND == kGemmOut ? a.C_in : a.C_out, pl, c);
+        return KIND == kGemmOut ? (kp * a.C_out + n) * a.C_in + c : (kp * a.C_in + n) * a.C_out + c;
+      }
+    };
+    if constexpr (VEC) {
+      // the VH reductions of a lane half are consecutive elements: C_in and
+      // C_out are multiples of 16, so they share (k, q)
+      int64_t base;
+      if constexpr (KIND == kGemmGs) {
+        base = index(rs < r_end ? rs : 0);
+      } else {
+        int c;
+        const int64_t kp = w_row_halves(a, G, rs < r_end ? rs : 0, KIND == kGemmOut ? a.C_in : a.C_out, pl,
+                                        (int)(threadIdx.x & 63) >> 5, c);
+        base = KIND == kGemmOut ? (kp * a.C_out + n) * a.C_in + c : (kp * a.C_in + n) * a.C_out + c;
+      }
+      load_words<VH>(ph + base, bh);
+      if constexpr (LO) load_words<VH>(plo + base, bl);
+    } else {
+      uint16_t vh[VH], vl[VH];
+#pragma unroll
+      for (int t = 0; t < VH; ++t) {
+        const int64_t o = index(min(rs + t, r_end - 1));
+        vh[t] = ph[o];
+        if constexpr (LO) vl[t] = plo[o];
+      }
+#pragma unroll
+      for (int t = 0; t < VH / 2; ++t) {
+        bh[t] = pack2(vh[2 * t], vh[2 * t + 1]);
+        if constexpr (LO) bl[t] = pack2(vl[2 * t], vl[2 * t + 1]);
+      }
     }
   }
 }
@@ -245,30 +245,67 @@ __device__ __forceinline__ void store_c(const GemmArgs& a, const GemmGroup& G, i
   }
 }
 
-template <int KIND, int MT, int NT, int VH, bool WBF16, bool VEC>
+__device__ __forceinline__ floatx16 mfma32(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// WLO: W has a lo plane (fp32 weights).  A is fp32 (split here) except for
+// gS, whose A is the g_out planes; B of gW is the g_out planes (always with lo).
+template <int KIND, int MT, int NT, int VH, bool WLO, bool VEC>
 struct Chunk {
-  using B = Bits<KIND, VH, WBF16, VEC>;
-  float a[MT][VH];
-  uint32_t b[NT][B::N];  // raw; widened in mul
+  static constexpr bool APLANE = KIND == kGemmGs;
+  static constexpr bool BLO = WLO || KIND == kGemmGw;
+  static constexpr int AW = VH / 2;
+  float a[APLANE ? 1 : MT][VH];
+  uint32_t pah[APLANE ? MT : 1][AW], pal[APLANE ? MT : 1][AW];
+  uint32_t bh[NT][AW], bl[NT][BLO ? AW : 1];
   int valid;  // reductions of this lane half inside the range (<= 0: none)
   __device__ __forceinline__ void load(const GemmArgs& ar, const GemmGroup& G, const int (&m)[MT], const int (&n)[NT],
                                        int rs, int r_end, int pl) {
     valid = r_end - rs;
 #pragma unroll
-    for (int u = 0; u < MT; ++u) load_a<KIND, VH, VEC>(ar, G, m[u], rs, r_end, a[u]);
+    for (int u = 0; u < MT; ++u) {
+      if constexpr (APLANE)
+        load_a_planes<VH>(ar, G, m[u], rs, pah[u], pal[u]);
+      else
+        load_a<KIND, VH, VEC>(ar, G, m[u], rs, r_end, a[u]);
+    }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) load_b<KIND, VH, WBF16, VEC>(ar, G, n[j], rs, r_end, pl, b[j]);
+    for (int j = 0; j < NT; ++j) load_b<KIND, VH, BLO, VEC>(ar, G, n[j], rs, r_end, pl, bh[j], bl[j]);
   }
-  __device__ __forceinline__ void mul(floatx16 (&acc)[MT][NT]) const {
+  __device__ __forceinline__ void mul(floatx16 (&acc)[MT][NT], const SplitConsts& sk) const {
 #pragma unroll
-    for (int t = 0; t < VH; ++t) {
+    for (int s = 0; s < VH / 8; ++s) {
+      u32x4 Ah[MT], Al[MT];
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        if constexpr (APLANE) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            Ah[u][t] = pah[u][4 * s + t];
+            Al[u][t] = pal[u][4 * s + t];
+          }
+        } else {
+          float v[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) v[t] = 8 * s + t < valid ? a[u][8 * s + t] : 0.f;  // past the end: zero
+          split8(v, Ah[u], Al[u], sk);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const float bv = B::get(b[j], t);
+        u32x4 Bh, Bl;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          Bh[t] = bh[j][4 * s + t];
+          if constexpr (BLO) Bl[t] = bl[j][4 * s + t];
+        }
 #pragma unroll
         for (int u = 0; u < MT; ++u) {
-          const float av = t < valid ? a[u][t] : 0.f;  // past the end of the reduction
-          acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[u][j], 0, 0, 0);
+          acc[u][j] = mfma32(Ah[u], Bh, acc[u][j]);
+          if constexpr (BLO) acc[u][j] = mfma32(Ah[u], Bl, acc[u][j]);
+          acc[u][j] = mfma32(Al[u], Bh, acc[u][j]);
         }
       }
     }
@@ -282,7 +319,7 @@ constexpr int gemm_min_waves(int mt, int nt, int vh) {
   return 16 * mt * nt + 3 * vh * (mt + nt) <= 112 ? 3 : 2;
 }
 
-template <int KIND, int MT, int NT, int VH, bool WBF16, bool VEC>
+template <int KIND, int MT, int NT, int VH, bool WLO, bool VEC>
 __global__ __launch_bounds__(64 * kMaxWaveSplit) __attribute__((amdgpu_waves_per_eu(gemm_min_waves(MT, NT, VH))))
 void gemm_kernel(const GemmArgs /*args*/) {
   // Read the arguments in place: a by-value copy indexed by a runtime group
@@ -320,6 +357,7 @@ void gemm_kernel(const GemmArgs /*args*/) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) n[j] = min(n0 + 32 * j + i, G.N - 1);
 
+  const SplitConsts sk;
   floatx16 acc[MT][NT];
 #pragma unroll
   for (int u = 0; u < MT; ++u)
@@ -332,16 +370,17 @@ void gemm_kernel(const GemmArgs /*args*/) {
   const int pl = (KIND == kGemmGw || G.npg <= 0) ? 0 : a.path_list[G.plist + min(lane, G.npg - 1)];
   const int nch = re > first ? ceil_div(re - first, stride) : 0;
   auto at = [&](int c) { return first + c * stride + VH * h; };
-  if constexpr (KIND == kGemmGs) {
-    // short reduction (C_out): one chunk ahead, loads guarded so that no
-    // chunk past the end is fetched
-    Chunk<KIND, MT, NT, VH, WBF16, VEC> c0, c1;
+  if constexpr (KIND == kGemmGs || KIND == kGemmGw) {
+    // one chunk ahead, loads guarded so that no chunk past the end is
+    // fetched (gS: a short reduction, C_out; gW: B gathered element by
+    // element, whose registers leave room for one chunk in flight only)
+    Chunk<KIND, MT, NT, VH, WLO, VEC> c0, c1;
     if (0 < nch) c0.load(a, G, m, n, at(0), re, pl);
     for (int c = 0; c < nch; c += 2) {
       if (c + 1 < nch) c1.load(a, G, m, n, at(c + 1), re, pl);
-      c0.mul(acc);
+      c0.mul(acc, sk);
       if (c + 2 < nch) c0.load(a, G, m, n, at(c + 2), re, pl);
-      if (c + 1 < nch) c1.mul(acc);
+      if (c + 1 < nch) c1.mul(acc, sk);
     }
   } else {
     // Three chunk buffers: chunks c+1 and c+2 are in flight while chunk c is
@@ -357,26 +396,26 @@ void gemm_kernel(const GemmArgs /*args*/) {
     // Scheduling barriers keep each load group ahead of the multiplies that
     // precede its use (the scheduler would otherwise sink the loads next to
     // their consumers, one chunk of prefetch at best).
-    Chunk<KIND, MT, NT, VH, WBF16, VEC> c0, c1, c2;
+    Chunk<KIND, MT, NT, VH, WLO, VEC> c0, c1, c2;
     c0.load(a, G, m, n, at(0), re, pl);
     c1.load(a, G, m, n, at(1), re, pl);
     int c = 0;
     for (; c + 3 <= nch; c += 3) {
       c2.load(a, G, m, n, at(c + 2), re, pl);
       __builtin_amdgcn_sched_barrier(0);
-      c0.mul(acc);
+      c0.mul(acc, sk);
       __builtin_amdgcn_sched_barrier(0);
       c0.load(a, G, m, n, at(c + 3), re, pl);
       __builtin_amdgcn_sched_barrier(0);
-      c1.mul(acc);
+      c1.mul(acc, sk);
       __builtin_amdgcn_sched_barrier(0);
       c1.load(a, G, m, n, at(c + 4), re, pl);
       __builtin_amdgcn_sched_barrier(0);
-      c2.mul(acc);
+      c2.mul(acc, sk);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (c < nch) c0.mul(acc);
-    if (c + 1 < nch) c1.mul(acc);
+    if (c < nch) c0.mul(acc, sk);
+    if (c + 1 < nch) c1.mul(acc, sk);
   }
 
   if (nw > 1) {  // fixed-order sum of the waves' partial tiles
@@ -398,7 +437,7 @@ void gemm_kernel(const GemmArgs /*args*/) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[u][j][r] += red[((((ww - 1) * MT + u) * NT + j) * 16 + r) * 64 + lane];
   }
-  // D layout of 32x32x2: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
+  // D layout of the 32x32 products: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
   for (int u = 0; u < MT; ++u)
 #pragma unroll
@@ -467,6 +506,28 @@ __global__ void planes_kernel(const void* x, int x_bf16, uint16_t* hi, uint16_t*
   lo[i] = __builtin_bit_cast(uint16_t, l);
 }
 
+// W [KP][Ci][Co] -> bf16 planes in its layout and transposed per (k, p) to
+// [KP][Co][Ci]: fp32 split into hi + lo, bf16 copied (lo == NULL).
+__global__ void w_planes_kernel(const void* W, int w_bf16, int64_t n, int Ci, int Co, uint16_t* hi, uint16_t* lo,
+                                uint16_t* thi, uint16_t* tlo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t per = (int64_t)Ci * Co, kp = i / per;
+  const int rem = (int)(i - kp * per), ci = rem / Co, co = rem - ci * Co;
+  const int64_t t = kp * per + (int64_t)co * Ci + ci;
+  if (w_bf16) {
+    const uint16_t v = static_cast<const uint16_t*>(W)[i];
+    hi[i] = v;
+    thi[t] = v;
+    return;
+  }
+  const float v = static_cast<const float*>(W)[i];
+  const __bf16 h = (__bf16)v;
+  const __bf16 l = (__bf16)(v - (float)h);
+  hi[i] = thi[t] = __builtin_bit_cast(uint16_t, h);
+  lo[i] = tlo[t] = __builtin_bit_cast(uint16_t, l);
+}
+
 // The nrows * C floats of rows row_off.. of a node are contiguous.
 __global__ void zero_rows_kernel(float* base, int64_t N, int D, int C, int row_off, int nrows) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -495,26 +556,32 @@ Shape gemm_shape(int kind, int max_cols, bool two_rows, int kr = 0) {
 }
 constexpr int64_t kFillWaves = 4096;
 
-template <int KIND, int MT, int NT, int VH, bool WBF16, bool VEC>
+template <int KIND, int MT, int NT, int VH, bool WLO, bool VEC>
 hipError_t launch_inst(const GemmArgs& a, dim3 grid, int waves, hipStream_t s) {
   const size_t lds = (size_t)(waves - 1) * MT * NT * 16 * 64 * sizeof(float);
-  hipLaunchKernelGGL((gemm_kernel<KIND, MT, NT, VH, WBF16, VEC>), grid, dim3(64 * waves), lds, s, a);
+  hipLaunchKernelGGL((gemm_kernel<KIND, MT, NT, VH, WLO, VEC>), grid, dim3(64 * waves), lds, s, a);
   return hipGetLastError();
 }
 
-template <int KIND, int MT, int NT, int VH, bool WBF16>
+template <int KIND, int MT, int NT, int VH, bool WLO>
 hipError_t launch_vec(const GemmArgs& a, dim3 grid, int waves, hipStream_t s) {
-  return a.vec != 0 ? launch_inst<KIND, MT, NT, VH, WBF16, true>(a, grid, waves, s)
-                    : launch_inst<KIND, MT, NT, VH, WBF16, false>(a, grid, waves, s);
+  if constexpr (VH == 8) {
+    return a.vec != 0 ? launch_inst<KIND, MT, NT, VH, WLO, true>(a, grid, waves, s)
+                      : launch_inst<KIND, MT, NT, VH, WLO, false>(a, grid, waves, s);
+  } else {  // 16 reductions per lane half only with 16-byte operand loads
+    return a.vec != 0 ? launch_inst<KIND, MT, NT, VH, WLO, true>(a, grid, waves, s) : hipErrorInvalidValue;
+  }
 }
 
-template <int KIND, bool WBF16>
+template <int KIND, bool WLO>
 hipError_t launch_kind(const GemmArgs& a, Shape sh, dim3 grid, int waves, hipStream_t s) {
-  if (sh.mt == 1 && sh.nt == 1 && sh.vh == 16) return launch_vec<KIND, 1, 1, 16, WBF16>(a, grid, waves, s);
-  if (sh.mt == 2 && sh.nt == 1 && sh.vh == 8) return launch_vec<KIND, 2, 1, 8, WBF16>(a, grid, waves, s);
-  if (sh.mt == 2 && sh.nt == 2 && sh.vh == 8) return launch_vec<KIND, 2, 2, 8, WBF16>(a, grid, waves, s);
-  if (sh.mt == 1 && sh.nt == 2 && sh.vh == 16) return launch_vec<KIND, 1, 2, 16, WBF16>(a, grid, waves, s);
-  if (KIND != kGemmGs && sh.mt == 1 && sh.nt == 4 && sh.vh == 8) return launch_vec<KIND, 1, 4, 8, WBF16>(a, grid, waves, s);
+  if (sh.mt == 1 && sh.nt == 1 && sh.vh == 8) return launch_vec<KIND, 1, 1, 8, WLO>(a, grid, waves, s);
+  if (sh.mt == 1 && sh.nt == 2 && sh.vh == 8) return launch_vec<KIND, 1, 2, 8, WLO>(a, grid, waves, s);
+  if (sh.mt == 1 && sh.nt == 1 && sh.vh == 16) return launch_vec<KIND, 1, 1, 16, WLO>(a, grid, waves, s);
+  if (sh.mt == 2 && sh.nt == 1 && sh.vh == 8) return launch_vec<KIND, 2, 1, 8, WLO>(a, grid, waves, s);
+  if (sh.mt == 2 && sh.nt == 2 && sh.vh == 8) return launch_vec<KIND, 2, 2, 8, WLO>(a, grid, waves, s);
+  if (sh.mt == 1 && sh.nt == 2 && sh.vh == 16) return launch_vec<KIND, 1, 2, 16, WLO>(a, grid, waves, s);
+  if (KIND != kGemmGs && sh.mt == 1 && sh.nt == 4 && sh.vh == 8) return launch_vec<KIND, 1, 4, 8, WLO>(a, grid, waves, s);
   return hipErrorInvalidValue;
 }
 
@@ -540,6 +607,8 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
     if (!(kind == kGemmGw || max_cols > 32) || t2 * splits * kMaxWaveSplit < kFillWaves)
       sh = gemm_shape(kind, max_cols, false, a.C_out);
   }
+  // element-by-element operands keep 8 reductions per lane half (registers)
+  if (!a.vec) sh.vh = 8;
   int64_t total = 0;
   for (int g = 0; g < a.ngroups; ++g) {
     GemmGroup& G = a.g[g];
@@ -559,12 +628,16 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
          (int64_t)max_kr >= (int64_t)splits * waves * 2 * 4 * kc)
     waves *= 2;
   const dim3 grid((unsigned)total, (unsigned)splits, 1);
-  const bool wb = a.w_bf16 != 0;
+  // gW reads no W; the other kinds take the lo plane of fp32 weights
+  const bool wlo = a.w_lo != nullptr;
+  if (kind != kGemmGw && (!a.w_hi || !a.wt_hi || (wlo != (a.wt_lo != nullptr)))) return hipErrorInvalidValue;
+  if ((kind == kGemmGs || kind == kGemmGw) && (!a.feat_hi || !a.feat_lo || a.feat_cs % 32 != 0))
+    return hipErrorInvalidValue;
   TimingScope ts(kcGemmOut + kind, s);
   switch (kind) {
-    case kGemmOut: return wb ? launch_kind<kGemmOut, true>(a, sh, grid, waves, s) : launch_kind<kGemmOut, false>(a, sh, grid, waves, s);
-    case kGemmGs: return wb ? launch_kind<kGemmGs, true>(a, sh, grid, waves, s) : launch_kind<kGemmGs, false>(a, sh, grid, waves, s);
-    case kGemmGx: return wb ? launch_kind<kGemmGx, true>(a, sh, grid, waves, s) : launch_kind<kGemmGx, false>(a, sh, grid, waves, s);
+    case kGemmOut: return wlo ? launch_kind<kGemmOut, true>(a, sh, grid, waves, s) : launch_kind<kGemmOut, false>(a, sh, grid, waves, s);
+    case kGemmGs: return wlo ? launch_kind<kGemmGs, true>(a, sh, grid, waves, s) : launch_kind<kGemmGs, false>(a, sh, grid, waves, s);
+    case kGemmGx: return wlo ? launch_kind<kGemmGx, true>(a, sh, grid, waves, s) : launch_kind<kGemmGx, false>(a, sh, grid, waves, s);
     case kGemmGw: return launch_kind<kGemmGw, false>(a, sh, grid, waves, s);
     default: return hipErrorInvalidValue;
   }
@@ -595,6 +668,17 @@ hipError_t launch_planes(const void* x, bool x_bf16, int64_t rows, int C, int CS
   TimingScope ts(kcFill, s);
   hipLaunchKernelGGL(planes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, x_bf16 ? 1 : 0, hi, lo,
                      (uint32_t)n, (uint32_t)C, (uint32_t)CS);
+  return hipGetLastError();
+}
+
+hipError_t launch_w_planes(const void* W, bool w_bf16, int64_t kp, int C_in, int C_out, uint16_t* hi, uint16_t* lo,
+                           uint16_t* thi, uint16_t* tlo, hipStream_t s) {
+  const int64_t n = kp * C_in * (int64_t)C_out;
+  if (n <= 0) return hipSuccess;
+  if (!hi || !thi || (!w_bf16 && (!lo || !tlo)) || (n + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;
+  TimingScope ts(kcFill, s);
+  hipLaunchKernelGGL(w_planes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, W, w_bf16 ? 1 : 0, n, C_in,
+                     C_out, hi, lo, thi, tlo);
   return hipGetLastError();
 }
 

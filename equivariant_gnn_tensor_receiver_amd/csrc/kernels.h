@@ -95,11 +95,15 @@ struct GemmArgs {
   int32_t ngroups;
   int32_t P, K, C_in, C_out, D_feat;  // D_feat: rows per node of the feature tensor touched
   int32_t splits;                     // kGemmGw: reduction splits
-  int32_t w_bf16;
-  int32_t vec;                        // channel counts allow float4 operand loads
+  int32_t vec;                        // channel counts allow 16-byte operand loads
+  int32_t feat_cs;                    // channel stride of the g_out planes
   const float* state;                 // S_g / T_g blocks (A for Out, Gx, Gw)
-  const float* feat;                  // g_out (A for Gs, B for Gw)
-  const void* W;                      // fp32 or bf16
+  const uint16_t* feat_hi;            // bf16 planes of g_out [N][D_out][feat_cs] (A for Gs, B for Gw)
+  const uint16_t* feat_lo;
+  const uint16_t* w_hi;               // bf16 planes of W in its layout [K][P][C_in][C_out] (B for Gs, Gx)
+  const uint16_t* w_lo;               // (NULL for bf16 weights: W is exact in bf16)
+  const uint16_t* wt_hi;              // the same transposed per (k, p): [K][P][C_out][C_in] (B for Out)
+  const uint16_t* wt_lo;
   float* out;                         // out / gS / g_x / partials
   int32_t path_list[kMaxPaths];
   GemmGroup g[kMaxGroups];
@@ -165,6 +169,10 @@ hipError_t launch_stream(int mode, int lmax, int K, bool feat_bf16, const Stream
                          hipStream_t s);
 // Fills the tiling fields of a.g[] (tiles, tiles_n, tile_begin) and launches.
 hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s);
+// bf16 planes of W [KP][C_in][C_out] (fp32 split into hi + lo; bf16 copied into
+// hi, lo unused): in its own layout and transposed per (k, p) to [KP][C_out][C_in].
+hipError_t launch_w_planes(const void* W, bool w_bf16, int64_t kp, int C_in, int C_out, uint16_t* hi, uint16_t* lo,
+                           uint16_t* thi, uint16_t* tlo, hipStream_t s);
 // Wave tiles of a C[M][N] product of the given kind (the tile shape launch_gemm uses).
 int64_t gemm_wave_tiles(int kind, int M, int N, int max_cols);
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);

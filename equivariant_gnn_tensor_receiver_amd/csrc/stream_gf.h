@@ -46,7 +46,7 @@ constexpr int kGfSlice = 32;              // channels of one wave (two 16-column
 
 template <int K, bool TAN>
 struct __attribute__((aligned(16))) GfLds {
-  int nbr[kGfBatch];                        // neighbour of each slot (past the batch: the node itself)
+  uint32_t noff[kGfBatch];                  // byte offset of each slot's neighbour in the planes (past the batch: the node's)
   float R[K][kGfStride];                    // R_e[k] (tangents: R_dot), 0 past the batch
   float Rt[TAN ? K : 1][kGfStride];         // tangents: R_e[k]
   float g[kGfMaxTot + 1][kGfStride];        // g_e of the current gathered row; row kGfMaxTot stays 0
@@ -84,22 +84,6 @@ struct GfPack {
   }
 };
 
-// hi / lo bf16 split of eight fp32 values: hi rounds to nearest even, lo is
-// v - hi (exact in fp32) rounded again.
-__device__ __forceinline__ void split8(const float (&v)[8], u32x4& hi, u32x4& lo) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const bf16x2 h = {(__bf16)v[2 * t], (__bf16)v[2 * t + 1]};
-    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-    const float l0 = v[2 * t] - __uint_as_float(hb << 16);
-    const float l1 = v[2 * t + 1] - __uint_as_float(hb & 0xffff0000u);
-    const bf16x2 l = {(__bf16)l0, (__bf16)l1};
-    hi[t] = hb;
-    lo[t] = __builtin_bit_cast(uint32_t, l);
-  }
-}
-
 // Wave-level LDS ordering: the lanes of one wave exchange values through its
 // private LDS region; LDS operations of a wave execute in order, so only the
 // compiler must keep them in program order.
@@ -122,8 +106,8 @@ struct GfWave {
   // Geometry of slot e of the batch starting at edge b0 (nb edges): LDS
   // tables and this lane's harmonics (and their tangent derivatives).
   __device__ __forceinline__ static void prep(const StreamArgs& a, int node, float psx, float psy, float psz,
-                                              int b0, int nb, int e, GfLds<K, TAN>& L, float (&y)[NSH],
-                                              float (&yd)[TAN ? NSH : 1]) {
+                                              int b0, int nb, int e, uint32_t nodebytes, GfLds<K, TAN>& L,
+                                              float (&y)[NSH], float (&yd)[TAN ? NSH : 1]) {
     if (e < nb) {
       const int nbr = a.nbr[b0 + e];
       const float qx = a.pos[3 * (int64_t)nbr], qy = a.pos[3 * (int64_t)nbr + 1], qz = a.pos[3 * (int64_t)nbr + 2];
@@ -142,7 +126,7 @@ struct GfWave {
       float R[K], dR[K];
       radial<K, TAN>(d, a.cutoff, a.inv_cutoff, a.pref, a.env_p, a.env_a, a.env_b, a.env_c, a.env_d, R, dR);
       sh_eval<LMAX>(ux, uy, uz, y);
-      L.nbr[e] = nbr;
+      L.noff[e] = (uint32_t)nbr * nodebytes;
       if constexpr (TAN) {
         float G[NSH][3];
         sh_poly_grad<LMAX>(ux, uy, uz, G);
@@ -164,7 +148,7 @@ struct GfWave {
         for (int k = 0; k < K; ++k) L.R[k][e] = R[k];
       }
     } else {
-      L.nbr[e] = node;
+      L.noff[e] = (uint32_t)node * nodebytes;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         L.R[k][e] = 0.f;
@@ -229,6 +213,7 @@ struct GfWave {
     const uint32_t nodebytes = (uint32_t)a.feat_rows * rowbytes;
     const uint32_t lanebytes = (uint32_t)a.paths[a.unit_paths[unit][0]].feat_row * rowbytes + (uint32_t)cp * 2;
 
+    const SplitConsts sk;
     floatx4 acc[TILES][2];
 #pragma unroll
     for (int T = 0; T < TILES; ++T) acc[T][0] = acc[T][1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -241,18 +226,18 @@ struct GfWave {
       const int nh = nb > 32 ? 2 : 1;
       float y[NSH], yd[TAN ? NSH : 1];
       wave_lds_sync();  // the previous batch's reads come first
-      prep(a, node, psx, psy, psz, b0, nb, lane, L, y, yd);
+      prep(a, node, psx, psy, psz, b0, nb, lane, nodebytes, L, y, yd);
       wave_lds_sync();
       // one 32-bit word (two channels) per edge and plane: row m1 of the
       // neighbours of this lane's eight edges of step h
       auto gather = [&](int m1, int h, uint32_t (&wh)[8], uint32_t (&wl)[8]) {
         const uint32_t rb = (uint32_t)m1 * rowbytes + lanebytes;
-        const int4 n0 = *reinterpret_cast<const int4*>(&L.nbr[32 * h + 8 * g]);
-        const int4 n1 = *reinterpret_cast<const int4*>(&L.nbr[32 * h + 8 * g + 4]);
-        const int nb8[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+        const uint4 n0 = *reinterpret_cast<const uint4*>(&L.noff[32 * h + 8 * g]);
+        const uint4 n1 = *reinterpret_cast<const uint4*>(&L.noff[32 * h + 8 * g + 4]);
+        const uint32_t nb8[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const uint32_t o = (uint32_t)nb8[t] * nodebytes + rb;
+          const uint32_t o = nb8[t] + rb;
           wh[t] = *reinterpret_cast<const uint32_t*>(fhi + o);
           if constexpr (LO) wl[t] = *reinterpret_cast<const uint32_t*>(flo + o);
         }
@@ -302,9 +287,10 @@ struct GfWave {
               }
             }
           }
-          static_for<TILES>([&](auto Tc) {
+          // the coupling values of tile T's rows at this lane's eight edges
+          // (rows past the unit read the zero row)
+          auto gload = [&](auto Tc, floatx4 (&gv)[TAN ? 4 : 2]) {
             constexpr int T = decltype(Tc)::value;
-            // component of row 16 T + i; rows past the unit read the zero row
             int j;
             if constexpr (K == 16) {
               j = T;
@@ -314,26 +300,38 @@ struct GfWave {
               j = (i >> 3) ? kGfMaxTot : 2 * T;
             }
             const float* gp = &L.g[j][32 * h + 8 * g];
-            const floatx4 g0 = *reinterpret_cast<const floatx4*>(gp);
-            const floatx4 g1 = *reinterpret_cast<const floatx4*>(gp + 4);
+            gv[0] = *reinterpret_cast<const floatx4*>(gp);
+            gv[1] = *reinterpret_cast<const floatx4*>(gp + 4);
+            if constexpr (TAN) {
+              const float* dp = &L.gd[j][32 * h + 8 * g];
+              gv[2] = *reinterpret_cast<const floatx4*>(dp);
+              gv[3] = *reinterpret_cast<const floatx4*>(dp + 4);
+            }
+          };
+          floatx4 gnext[TAN ? 4 : 2];
+          gload(std::integral_constant<int, 0>{}, gnext);
+          static_for<TILES>([&](auto Tc) {
+            constexpr int T = decltype(Tc)::value;
+            floatx4 gv[TAN ? 4 : 2];
+#pragma unroll
+            for (int q = 0; q < (TAN ? 4 : 2); ++q) gv[q] = gnext[q];
+            // the next tile's values, in flight during this tile
+            if constexpr (T + 1 < TILES) gload(std::integral_constant<int, T + 1>{}, gnext);
             float av[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              av[t] = r8[t] * g0[t];
-              av[4 + t] = r8[4 + t] * g1[t];
+              av[t] = r8[t] * gv[0][t];
+              av[4 + t] = r8[4 + t] * gv[1][t];
             }
             if constexpr (TAN) {
-              const float* dp = &L.gd[j][32 * h + 8 * g];
-              const floatx4 d0 = *reinterpret_cast<const floatx4*>(dp);
-              const floatx4 d1 = *reinterpret_cast<const floatx4*>(dp + 4);
 #pragma unroll
               for (int t = 0; t < 4; ++t) {
-                av[t] = __builtin_fmaf(rt8[t], d0[t], av[t]);
-                av[4 + t] = __builtin_fmaf(rt8[4 + t], d1[t], av[4 + t]);
+                av[t] = __builtin_fmaf(rt8[t], gv[2][t], av[t]);
+                av[4 + t] = __builtin_fmaf(rt8[4 + t], gv[3][t], av[4 + t]);
               }
             }
             u32x4 ah, al;
-            split8(av, ah, al);
+            split8(av, ah, al, sk);
             acc[T][0] = mfma_bf16(ah, ch0, acc[T][0]);
             acc[T][1] = mfma_bf16(ah, ch1, acc[T][1]);
             if constexpr (LO) {

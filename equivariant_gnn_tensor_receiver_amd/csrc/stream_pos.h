@@ -90,8 +90,6 @@ struct PosPack {
   }
 };
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPosSlice = 32;       // channels of one wave's reduction range
 constexpr int kPosNcl = kPosSlice / 4;  // channels per lane group (8 bf16 of one MFMA operand)

@@ -168,10 +168,11 @@ tpconv_status tpconv_plan_cg(tpconv_plan plan, int32_t path, double* out);
  * GRAPH_PREPARE needs O(N) int32 scratch for the sender sort (index
  * metadata, not tensor-product workspace), GRAPH_ORDER O(N) for the sort of
  * the nodes.  FORWARD's figure is for saved_state == NULL,
- * FORWARD_SAVED's for a forward that writes a saved state (it holds no S;
- * zero for bf16 features with C_in a multiple of 32 and a uniform plan).  The
- * passes also hold bf16 copies of the gathered features (fp32 split into hi
- * and lo planes, rows padded to a multiple of 32 channels).
+ * FORWARD_SAVED's for a forward that writes a saved state (it holds no S).
+ * The passes also hold bf16 copies of the gathered features and of W for the
+ * matrix cores (fp32 split into hi and lo planes; feature rows padded to a
+ * multiple of 32 channels, W also transposed per (k, p); bf16 features with
+ * 32-channel rows are used in place).
  * Errors: INVALID_VALUE (null plan or bytes, negative sizes, unknown op). */
 tpconv_status tpconv_workspace_size(tpconv_plan plan, int32_t op, int64_t num_nodes,
                                     int64_t num_edges, size_t* bytes);
@@ -263,9 +264,9 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
  * kept in a file-scope device array of TPCONV_STATIC_SCRATCH_BYTES (64 MiB)
  * that every GPU the library runs on holds until the process ends; it fits
  * problems whose tpconv_workspace_size(FORWARD) is at most that size (the
- * state S and the bf16 planes of x: for example N <= 1814 nodes at 32
+ * state S and the bf16 planes of x and W: for example N <= 1794 nodes at 32
  * channels of 0e+1o+2e with K = 8, 35 KiB of state and 1.1 KiB of planes per
- * node, or N <= 26214 at 8 channels of 0e+1o, 2.5 KiB).  Larger problems
+ * node, or N <= 26208 at 8 channels of 0e+1o, 2.5 KiB).  Larger problems
  * return TPCONV_ERROR_SCRATCH before any launch.  The array is looked
  * up on the first call on each device (the call then needs that device
  * current).  Same arguments, results and errors as tpconv_forward otherwise.

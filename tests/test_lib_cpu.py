@@ -116,17 +116,20 @@ def test_workspace_is_independent_of_edges():
     for op in (tp.OP_FORWARD, tp.OP_BACKWARD, tp.OP_DOUBLE_BACKWARD):
         sizes = {plan.workspace_size(op, 4096, E) for E in (0, 131072, 524288, 8_388_608)}
         assert len(sizes) == 1
-    # forward workspace: the receiver state, K * C * sum(2l3+1) fp32 per node, and the
-    # bf16 hi and lo planes of x (rows of 32 channels); with a saved state only the planes
-    planes = 2 * 4096 * 9 * 32 * 2
-    assert plan.workspace_size(tp.OP_FORWARD, 4096, 131072) == 4096 * 8 * 32 * 35 * 4 + planes
-    assert plan.workspace_size(tp.OP_FORWARD_SAVED, 4096, 131072) == planes
+    # forward workspace: the receiver state, K * C * sum(2l3+1) fp32 per node, the bf16
+    # hi and lo planes of x (rows of 32 channels) and of W (its layout and transposed);
+    # with a saved state only the planes
+    x_planes = 2 * 4096 * 9 * 32 * 2
+    w_planes = 4 * 8 * 11 * 32 * 32 * 2
+    assert plan.workspace_size(tp.OP_FORWARD, 4096, 131072) == 4096 * 8 * 32 * 35 * 4 + x_planes + w_planes
+    assert plan.workspace_size(tp.OP_FORWARD_SAVED, 4096, 131072) == x_planes + w_planes
     assert plan.state_size(4096) == 4096 * 8 * 32 * 35 * 4
-    # bf16 features with 32-channel rows are gathered in place; 24 channels are padded to 32
+    # bf16 features with 32-channel rows are gathered in place (bf16 W: hi planes only);
+    # 24 channels are padded to 32
     bf = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis, x_dtype=tp.TPCONV_BF16, w_dtype=tp.TPCONV_BF16)
-    assert bf.workspace_size(tp.OP_FORWARD_SAVED, 4096, 0) == 0
+    assert bf.workspace_size(tp.OP_FORWARD_SAVED, 4096, 0) == w_planes // 2
     bf24 = tp.Plan("24x0e+24x1o+24x2e", "24x0e+24x1o+24x2e", 2, 8, x_dtype=tp.TPCONV_BF16)
-    assert bf24.workspace_size(tp.OP_FORWARD_SAVED, 4096, 0) == 4096 * 9 * 32 * 2
+    assert bf24.workspace_size(tp.OP_FORWARD_SAVED, 4096, 0) == 4096 * 9 * 32 * 2 + 4 * 8 * 11 * 24 * 24 * 2
 
 
 def test_argument_errors_before_any_launch():
@@ -167,8 +170,10 @@ def test_channelwise_plan():
     for i in range(plan.num_paths):
         assert plan.path(i) == full.path(i)
         assert np.array_equal(plan.cg(i), full.cg(i))
-    # the state is shared; the backward needs no gS buffer
-    assert plan.workspace_size(tp.OP_FORWARD, 4096, 0) == full.workspace_size(tp.OP_FORWARD, 4096, 0)
+    # the state is shared (the channel-wise contractions read W as given: no W planes);
+    # the backward needs no gS buffer
+    w_planes = 4 * full.w_numel * 2
+    assert plan.workspace_size(tp.OP_FORWARD, 4096, 0) == full.workspace_size(tp.OP_FORWARD, 4096, 0) - w_planes
     assert plan.workspace_size(tp.OP_BACKWARD, 4096, 0) < full.workspace_size(tp.OP_BACKWARD, 4096, 0)
     for op in (tp.OP_FORWARD, tp.OP_BACKWARD, tp.OP_DOUBLE_BACKWARD):
         assert len({plan.workspace_size(op, 4096, E) for E in (0, 131072, 8_388_608)}) == 1

@@ -34,8 +34,8 @@ def test_static_forward_matches_forward_twice():
     import torch
 
     plan = tp.Plan(IRREPS, IRREPS, 2, 8)
-    assert plan.state_size(1800) <= tp.STATIC_SCRATCH_BYTES
-    for call, (N, deg, seed) in enumerate(((1800, 24, 7), (300, 12, 8))):
+    assert plan.workspace_size(tp.OP_FORWARD, 1700, 0) <= tp.STATIC_SCRATCH_BYTES
+    for call, (N, deg, seed) in enumerate(((1700, 24, 7), (300, 12, 8))):
         say(f"[case] static-scratch forward, call {call + 1}: N={N} deg~{deg}")
         graph, pos, x, W = upload(plan, N, deg, seed)
         ref = tp.tpconv_forward(plan, graph, pos, x, W)
