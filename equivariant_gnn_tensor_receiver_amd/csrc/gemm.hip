@@ -450,6 +450,214 @@ void gemm_kernel(const GemmArgs /*args*/) {
       }
 }
 
+// Products with many row tiles: a block of RW waves takes RW consecutive
+// 32-row tiles and one block of 32*NT columns.  The chunk of B
+// that all of them need is loaded once per block into LDS, in two buffers
+// (chunk c+1 is written while chunk c is read), instead of once per wave
+// from L2; each wave then reads its column fragments from LDS.  A comes
+// straight from memory into registers, one chunk ahead.  Needs 16-byte
+// operand loads (channel counts that are multiples of 16).
+template <int NT, int VH>
+struct __attribute__((aligned(16))) BStage {  // one chunk of B as bf16: [plane][column][reduction]
+  static constexpr int KC = 2 * VH;
+  static constexpr int RS = KC + 8;  // row stride: 16-byte aligned rows, spread over the banks
+  uint16_t v[2][32 * NT][RS];
+};
+
+template <int KIND, int NT, int VH, bool WLO, int RW>
+__global__ __launch_bounds__(64 * RW) __attribute__((amdgpu_waves_per_eu(NT >= 4 ? 2 : 3)))
+void gemm_lds_kernel(const GemmArgs /*args*/) {
+  const GemmArgs& a = *(const GemmArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr bool APLANE = KIND == kGemmGs;
+  constexpr bool BLO = WLO || KIND == kGemmGw;
+  constexpr int KC = 2 * VH, NC = 32 * NT;
+  constexpr int NQ = NC * KC / 8;                                  // 8-element pieces of a chunk, per plane
+  constexpr int QP = (NQ + 64 * RW - 1) / (64 * RW);  // pieces per thread
+  __shared__ BStage<NT, VH> stage[2];
+  const int b = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < a.ngroups && b >= a.g[gi + 1].tile_begin) ++gi;
+  const GemmGroup& G = a.g[gi];
+  const int tile = b - G.tile_begin;
+  if (tile >= G.tiles) return;  // uniform over the block
+  const int tm = tile / G.tiles_n, tn = tile - tm * G.tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  const int m0 = (tm * RW + w) * 32, n0 = tn * NC;
+  int rb = 0, re = G.Kr;
+  if constexpr (KIND == kGemmGw) {
+    const int per = ceil_div(ceil_div(G.Kr, a.splits), KC) * KC;
+    rb = min(G.Kr, (int)blockIdx.y * per);
+    re = min(G.Kr, rb + per);
+  }
+  const int nch = re > rb ? ceil_div(re - rb, KC) : 0;
+  const int m = min(m0 + i, G.M - 1);
+  const int pl = (KIND == kGemmGw || G.npg <= 0) ? 0 : a.path_list[G.plist + min(lane, G.npg - 1)];
+  const SplitConsts sk;
+
+  // gW: the g_out row (node, mm) of each of this thread's pieces, advanced
+  // by one chunk at a time without division; rows past the last one read the
+  // last one (their A values are zero)
+  int gnode[QP], gmm[QP];
+  const int dnode = KC / G.n, dmm = KC - dnode * G.n;
+  const int lnode = (G.Kr - 1) / G.n, lmm = (G.Kr - 1) - lnode * G.n;
+  if constexpr (KIND == kGemmGw) {
+#pragma unroll
+    for (int p = 0; p < QP; ++p) {
+      const int r = rb + (tid + p * 64 * RW) / (NC / 8);
+      gnode[p] = r / G.n;
+      gmm[p] = r - gnode[p] * G.n;
+    }
+  }
+  // piece q (the p-th of this thread) of chunk c (hi, and lo where BLO): 8
+  // consecutive reductions of one column (W planes), or for gW 8 consecutive
+  // columns of one reduction (g_out planes); clamped inside the tensors
+  // (their A values are zero)
+  auto piece_load = [&](int c, int q, int p, uint4& vh, uint4& vl) {
+    const int r0 = rb + c * KC;
+    int64_t idx;
+    const uint16_t *ph, *plo;
+    if constexpr (KIND == kGemmGw) {
+      const int red = q / (NC / 8), cg = q - red * (NC / 8);
+      const bool past = r0 + red > G.Kr - 1;
+      const int node = past ? lnode : gnode[p], mm = past ? lmm : gmm[p];
+      const int co = min(n0 + 8 * cg, a.feat_cs - 8);
+      idx = ((int64_t)node * a.D_feat + G.row_off + mm) * a.feat_cs + co;
+      ph = a.feat_hi;
+      plo = a.feat_lo;
+      // the next chunk's row
+      gmm[p] += dmm;
+      gnode[p] += dnode;
+      if (gmm[p] >= G.n) {
+        gmm[p] -= G.n;
+        gnode[p] += 1;
+      }
+    } else {
+      const int col = q / (KC / 8), part = q - col * (KC / 8);
+      const int n = min(n0 + col, G.N - 1);
+      const int r = min(r0 + 8 * part, G.Kr - 8);
+      int c2;
+      if constexpr (KIND == kGemmOut) {
+        const int64_t kp = w_row(a, G, r, a.C_in, pl, c2);
+        idx = (kp * a.C_out + n) * a.C_in + c2;
+      } else if constexpr (KIND == kGemmGs) {
+        const int64_t kp = w_row(a, G, n, a.C_in, pl, c2);
+        idx = (kp * a.C_in + c2) * a.C_out + r;
+      } else {
+        const int64_t kp = w_row(a, G, r, a.C_out, pl, c2);
+        idx = (kp * a.C_in + n) * a.C_out + c2;
+      }
+      ph = KIND == kGemmOut ? a.wt_hi : a.w_hi;
+      plo = KIND == kGemmOut ? a.wt_lo : a.w_lo;
+    }
+    vh = *reinterpret_cast<const uint4*>(ph + idx);
+    if constexpr (BLO) vl = *reinterpret_cast<const uint4*>(plo + idx);
+  };
+  auto piece_store = [&](BStage<NT, VH>& st, int q, const uint4& vh, const uint4& vl) {
+    if constexpr (KIND == kGemmGw) {
+      const int red = q / (NC / 8), cg = q - red * (NC / 8);
+      const uint32_t wh[4] = {vh.x, vh.y, vh.z, vh.w}, wl[4] = {vl.x, vl.y, vl.z, vl.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        st.v[0][8 * cg + e][red] = (uint16_t)(wh[e >> 1] >> (16 * (e & 1)));
+        st.v[1][8 * cg + e][red] = (uint16_t)(wl[e >> 1] >> (16 * (e & 1)));
+      }
+    } else {
+      const int col = q / (KC / 8), part = q - col * (KC / 8);
+      *reinterpret_cast<uint4*>(&st.v[0][col][8 * part]) = vh;
+      if constexpr (BLO) *reinterpret_cast<uint4*>(&st.v[1][col][8 * part]) = vl;
+    }
+  };
+  auto a_load = [&](int c, float (&av)[VH], uint32_t (&ah)[VH / 2], uint32_t (&al)[VH / 2]) {
+    const int rs = rb + c * KC + VH * h;
+    if constexpr (APLANE)
+      load_a_planes<VH>(a, G, m, rs, ah, al);
+    else
+      load_a<KIND, VH, true>(a, G, m, rs, re, av);
+  };
+
+  floatx16 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+  // A and the B pieces of chunk c+1 are in flight while chunk c is multiplied
+  float av[VH], avn[VH];
+  uint32_t pah[VH / 2], pal[VH / 2], pahn[VH / 2], paln[VH / 2];
+  uint4 sh[QP], sl[QP];
+  if (nch > 0) {
+#pragma unroll
+    for (int p = 0; p < QP; ++p)
+      if (tid + p * 64 * RW < NQ) piece_load(0, tid + p * 64 * RW, p, sh[p], sl[p]);
+#pragma unroll
+    for (int p = 0; p < QP; ++p)
+      if (tid + p * 64 * RW < NQ) piece_store(stage[0], tid + p * 64 * RW, sh[p], sl[p]);
+    a_load(0, av, pah, pal);
+  }
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    if (more) {
+#pragma unroll
+      for (int p = 0; p < QP; ++p)
+        if (tid + p * 64 * RW < NQ) piece_load(c + 1, tid + p * 64 * RW, p, sh[p], sl[p]);
+      a_load(c + 1, avn, pahn, paln);
+    }
+    const BStage<NT, VH>& st = stage[c & 1];
+    const int valid = re - (rb + c * KC + VH * h);
+#pragma unroll
+    for (int s2 = 0; s2 < VH / 8; ++s2) {
+      u32x4 Ah, Al;
+      if constexpr (APLANE) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          Ah[t] = pah[4 * s2 + t];
+          Al[t] = pal[4 * s2 + t];
+        }
+      } else {
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = 8 * s2 + t < valid ? av[8 * s2 + t] : 0.f;  // past the end: zero
+        split8(v, Ah, Al, sk);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const u32x4 Bh = *reinterpret_cast<const u32x4*>(&st.v[0][32 * j + i][VH * h + 8 * s2]);
+        acc[j] = mfma32(Ah, Bh, acc[j]);
+        if constexpr (BLO) {
+          const u32x4 Bl = *reinterpret_cast<const u32x4*>(&st.v[1][32 * j + i][VH * h + 8 * s2]);
+          acc[j] = mfma32(Ah, Bl, acc[j]);
+        }
+        acc[j] = mfma32(Al, Bh, acc[j]);
+      }
+    }
+    if (more) {  // chunk c+1's pieces into the other buffer
+#pragma unroll
+      for (int p = 0; p < QP; ++p)
+        if (tid + p * 64 * RW < NQ) piece_store(stage[(c + 1) & 1], tid + p * 64 * RW, sh[p], sl[p]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < VH; ++t) av[t] = avn[t];
+#pragma unroll
+    for (int t = 0; t < VH / 2; ++t) {
+      pah[t] = pahn[t];
+      pal[t] = paln[t];
+    }
+  }
+  if (m0 >= G.M) return;
+  // D layout of the 32x32 products: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int gm = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int gn = n0 + 32 * j + i;
+      if (gm < G.M && gn < G.N) store_c<KIND>(a, G, gm, gn, acc[j][r]);
+    }
+}
+
 __global__ void gw_reduce_kernel(const ReduceArgs a, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
@@ -585,6 +793,34 @@ hipError_t launch_kind(const GemmArgs& a, Shape sh, dim3 grid, int waves, hipStr
   return hipErrorInvalidValue;
 }
 
+// Waves per block (row tiles sharing a B chunk), and reductions per lane
+// half: 16 for column blocks of one or two tiles (measured faster for out,
+// g_x and gW there; not for gS, nor with four tiles, whose registers then
+// leave too little room).
+constexpr int lds_rows(int nt) { return 4; }
+
+template <int KIND, int NT, bool WLO>
+hipError_t launch_lds(const GemmArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int VH = (NT <= 2 && KIND != kGemmGs) ? 16 : 8;
+  constexpr int RW = lds_rows(NT);
+  hipLaunchKernelGGL((gemm_lds_kernel<KIND, NT, VH, WLO, RW>), grid, dim3(64 * RW), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KIND, bool WLO>
+hipError_t launch_lds_nt(const GemmArgs& a, int nt, dim3 grid, hipStream_t s) {
+  if (nt == 1) return launch_lds<KIND, 1, WLO>(a, grid, s);
+  if (nt == 2) return launch_lds<KIND, 2, WLO>(a, grid, s);
+  return launch_lds<KIND, 4, WLO>(a, grid, s);
+}
+
+// The LDS-staged kernel for launches of at least this many waves (with
+// 16-byte operand loads); smaller ones split the reduction instead.
+constexpr int64_t kLdsMinWaves = 2048;
+
+// Column tiles of the LDS-staged kernel: the whole (up to 128) columns in one block.
+int lds_nt(int max_cols) { return max_cols <= 32 ? 1 : (max_cols <= 64 ? 2 : 4); }
+
 }  // namespace
 
 int64_t gemm_wave_tiles(int kind, int M, int N, int max_cols) {
@@ -598,6 +834,39 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
   int max_cols = 0, max_kr = 0;
   for (int g = 0; g < a.ngroups; ++g) max_cols = a.g[g].N > max_cols ? a.g[g].N : max_cols;
   const int splits = kind == kGemmGw ? a.splits : 1;
+  // gW reads no W; the other kinds take the lo plane of fp32 weights
+  const bool wlo = a.w_lo != nullptr;
+  if (kind != kGemmGw && (!a.w_hi || !a.wt_hi || (wlo != (a.wt_lo != nullptr)))) return hipErrorInvalidValue;
+  if ((kind == kGemmGs || kind == kGemmGw) && (!a.feat_hi || !a.feat_lo || a.feat_cs % 32 != 0))
+    return hipErrorInvalidValue;
+  if (a.vec) {  // many row tiles: blocks of kLdsWaves row tiles sharing B through LDS
+    const int nt = lds_nt(kind == kGemmGs ? 128 : max_cols), rw = lds_rows(nt);
+    int64_t blocks = 0;
+    for (int g = 0; g < a.ngroups; ++g) {
+      const GemmGroup& G = a.g[g];
+      if (G.M > 0 && G.N > 0 && G.Kr > 0) blocks += (int64_t)ceil_div(ceil_div(G.M, 32), rw) * ceil_div(G.N, 32 * nt);
+    }
+    if (blocks * rw * splits >= kLdsMinWaves) {
+      int64_t total = 0;
+      for (int g = 0; g < a.ngroups; ++g) {
+        GemmGroup& G = a.g[g];
+        G.tiles_n = G.N > 0 ? ceil_div(G.N, 32 * nt) : 0;
+        G.tiles = (G.M > 0 && G.N > 0 && G.Kr > 0) ? ceil_div(ceil_div(G.M, 32), rw) * G.tiles_n : 0;
+        G.tile_begin = (int32_t)total;
+        total += G.tiles;
+      }
+      if (total > INT32_MAX) return hipErrorInvalidValue;
+      const dim3 grid((unsigned)total, (unsigned)splits, 1);
+      TimingScope ts(kcGemmOut + kind, s);
+      switch (kind) {
+        case kGemmOut: return wlo ? launch_lds_nt<kGemmOut, true>(a, nt, grid, s) : launch_lds_nt<kGemmOut, false>(a, nt, grid, s);
+        case kGemmGs: return wlo ? launch_lds_nt<kGemmGs, true>(a, nt, grid, s) : launch_lds_nt<kGemmGs, false>(a, nt, grid, s);
+        case kGemmGx: return wlo ? launch_lds_nt<kGemmGx, true>(a, nt, grid, s) : launch_lds_nt<kGemmGx, false>(a, nt, grid, s);
+        case kGemmGw: return launch_lds_nt<kGemmGw, false>(a, nt, grid, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   Shape sh = gemm_shape(kind, max_cols, true, a.C_out);
   {
     int64_t t2 = 0;
@@ -628,11 +897,6 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
          (int64_t)max_kr >= (int64_t)splits * waves * 2 * 4 * kc)
     waves *= 2;
   const dim3 grid((unsigned)total, (unsigned)splits, 1);
-  // gW reads no W; the other kinds take the lo plane of fp32 weights
-  const bool wlo = a.w_lo != nullptr;
-  if (kind != kGemmGw && (!a.w_hi || !a.wt_hi || (wlo != (a.wt_lo != nullptr)))) return hipErrorInvalidValue;
-  if ((kind == kGemmGs || kind == kGemmGw) && (!a.feat_hi || !a.feat_lo || a.feat_cs % 32 != 0))
-    return hipErrorInvalidValue;
   TimingScope ts(kcGemmOut + kind, s);
   switch (kind) {
     case kGemmOut: return wlo ? launch_kind<kGemmOut, true>(a, sh, grid, waves, s) : launch_kind<kGemmOut, false>(a, sh, grid, waves, s);
