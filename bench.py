@@ -160,7 +160,7 @@ def load_traffic(workload, kernel):
         t = json.load(fh)
     from equivariant_gnn_tensor_receiver_amd.profiling import kernel_source_hash
 
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash(kernel):
         return None  # the kernel changed since the counters were taken
     return t.get("hbm_bytes_per_launch")
 

@@ -46,14 +46,6 @@ struct Carver {
   }
 };
 
-// log2 of the channel tile of the edge streams: the largest power of two
-// dividing C, at most 64 and at least 4 (lanes are paired in fours by the
-// 4x4 outer products; a tile past C is masked).
-int ct_log2_of(int C) {
-  int t = 0;
-  while (t < 6 && (C % (2 << t)) == 0) ++t;
-  return t < 2 ? 2 : t;
-}
 
 // Reduction splits of the gW product over blocks: enough waves to fill the
 // chip (with up to 4 waves per block) while each split of the largest group
@@ -324,8 +316,6 @@ void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
   a.feat = x;
   a.feat_rows = p.D_in;
   a.C = p.C_in;
-  a.ct_log2 = ct_log2_of(p.C_in);
-  a.ntiles = (p.C_in + (1 << a.ct_log2) - 1) >> a.ct_log2;
   for (int i = 0; i < p.P; ++i) {
     const Path& q = p.paths[i];
     const Group& og = p.out_groups[q.i3];
@@ -345,8 +335,6 @@ void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
   a.feat = gout;
   a.feat_rows = p.D_out;
   a.C = p.C_out;
-  a.ct_log2 = ct_log2_of(p.C_out);
-  a.ntiles = (p.C_out + (1 << a.ct_log2) - 1) >> a.ct_log2;
   for (int i = 0; i < p.P; ++i) {
     const Path& q = p.paths[i];
     const Group& ig = p.in_groups[q.i1];

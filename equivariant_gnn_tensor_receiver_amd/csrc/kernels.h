@@ -40,9 +40,7 @@ struct StreamArgs {
   int32_t npaths;
   int32_t nunits;       // work units per (node, tile)
   int32_t bundled;      // units are the compile-time bundles of the natural path list
-  int32_t ct_log2;      // channel tile = 1 << ct_log2 (<= 64); edge slots per wave = 64 / tile
-  int32_t ntiles;       // channels / tile
-  int32_t nslices;      // kBwdPos: 32-channel slices of the reduction
+  int32_t nslices;      // 32-channel slices of the gathered planes (one wave, or one pair of a block, each)
   int32_t feat_rows;    // rows per node of the gathered feature tensor
   int32_t C;            // channels of the gathered features and of the state
   int32_t feat_cs;      // channel stride of the gathered planes (>= C; a multiple of 32 except bf16 used in place)

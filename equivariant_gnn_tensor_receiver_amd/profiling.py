@@ -17,8 +17,8 @@ is turned into a short Markdown table with
 
   python3 -m equivariant_gnn_tensor_receiver_amd.profiling stats DIR TITLE "COMMAND" > kernels.md
 
-The summary records the hash of the kernel sources it was taken with; bench.py
-ignores it once the sources change.
+The summary records the hash of the kernel's sources it was taken with;
+bench.py ignores it once those sources change.
 """
 from __future__ import annotations
 
@@ -33,13 +33,22 @@ from collections import defaultdict
 COPY_BYTES = 1 << 30  # 1 GiB read and 1 GiB written per copy
 COPY_REPS = 4
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("stream_impl.h", "stream_inst.hip", "stream_pos.h", "stream_pos.hip", "device_common.h", "gemm.hip",
-                  "channelwise.hip", "kernels.h", "cg_codegen.cpp")
+SHARED_SOURCES = ("stream_impl.h", "device_common.h", "kernels.h", "cg_codegen.cpp", "plan.cpp")
+KERNEL_SOURCES = {
+    "stream": ("stream_gf.h", "stream_gf.hip"),
+    "stream_bwdpos": ("stream_pos.h", "stream_pos.hip"),
+    "stream_hess": ("stream_pos.h", "stream_pos.hip"),
+    "gemm": ("gemm.hip",),
+    "cw": ("channelwise.hip",),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources a kernel class is built from (its own and the shared ones)."""
+    key = kernel if kernel in KERNEL_SOURCES else ("gemm" if kernel.startswith("gemm") else
+                                                   "cw" if kernel.startswith("cw") else "stream")
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[key] + SHARED_SOURCES:
         with open(os.path.join(HERE, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -70,7 +79,7 @@ def _per_dispatch(run_dir: str, counter: str, match) -> list[float]:
 
 def summarize(out_dir: str, workload: str, kernel_substr: str, name: str) -> dict:
     res = {"workload": workload, "kernel": name, "kernel_match": kernel_substr,
-           "source_hash": kernel_source_hash()}
+           "source_hash": kernel_source_hash(name)}
     scale = {}
     for counter, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         copy = _per_dispatch(os.path.join(out_dir, f"copy_{tag}"), counter,
