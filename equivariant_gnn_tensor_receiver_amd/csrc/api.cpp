@@ -16,6 +16,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <numeric>
 #include <new>
 #include <vector>
 
@@ -541,6 +542,54 @@ tpconv_status run_cw_gw(const Plan& p, int64_t N, const float* state, const floa
   return dev(launch_cw_reduce(a, s));
 }
 
+// Waves per block of the position streams and each wave's (slice, unit)
+// pairs.  The waves of a block meet at every 64-edge batch, so a block takes
+// as long as its most loaded wave: the pairs (cost: row tiles times gathered
+// rows, the per-batch count of matrix-core steps) are packed longest first
+// onto the least loaded wave, for the wave count (2..8) that wastes the
+// least wave time.
+bool assign_pos_pairs(const Plan& p, StreamArgs& a) {
+  const int npairs = a.nunits * a.nslices;
+  if (npairs <= 0 || npairs > kMaxPosPairs) return false;
+  std::vector<int> cost(npairs);
+  for (int pr = 0; pr < npairs; ++pr) {
+    const auto& u = p.pos_units[pr % a.nunits];
+    int tot = 0;
+    for (int q : u) tot += 2 * p.paths[q].l3 + 1;
+    cost[pr] = ((p.K * tot + 15) / 16) * (2 * p.paths[u[0]].l1 + 1) + 1;
+  }
+  std::vector<int> idx(npairs);
+  for (int i = 0; i < npairs; ++i) idx[i] = i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return cost[x] > cost[y]; });
+  double best = -1.0;
+  std::vector<std::vector<int>> best_lists;
+  for (int nw = 1; nw <= std::min(kPosMaxBlockWaves, npairs); ++nw) {
+    std::vector<std::vector<int>> lists(nw);
+    std::vector<int> load(nw, 0);
+    for (int i : idx) {
+      const int w = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+      lists[w].push_back(i);
+      load[w] += cost[i];
+    }
+    const int total = std::accumulate(load.begin(), load.end(), 0);
+    const double eff = (double)total / ((double)nw * *std::max_element(load.begin(), load.end()));
+    // at least two waves (a one-wave block leaves too little room for
+    // others in the LDS of a compute unit), otherwise the best balance
+    if ((nw >= 2 || npairs == 1) && eff > best + 1e-9) {
+      best = eff;
+      best_lists = lists;
+    }
+  }
+  a.pos_waves = (int32_t)best_lists.size();
+  int k = 0;
+  for (int w = 0; w < a.pos_waves; ++w) {
+    a.pair_begin[w] = (int16_t)k;
+    for (int pr : best_lists[w]) a.pair_order[k++] = (uint8_t)pr;
+  }
+  a.pair_begin[a.pos_waves] = (int16_t)k;
+  return true;
+}
+
 // The receiver-side position streams (kBwdPos: grad_pos; kBwdHess: the
 // position derivative of the force loss along gg_pos) into out [N][3]:
 // gS = g_out W^T first (formed in registers when channel-wise); xp, gp, wp:
@@ -557,6 +606,7 @@ tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, con
   recv_args(p, a, g, pos, x);
   set_units(p, a, p.pos_units);
   use_planes(a, xp);
+  if (!assign_pos_pairs(p, a)) return TPCONV_ERROR_INVALID_VALUE;
   a.gstate = gS;
   a.gpos = out;
   a.ggpos = gg_pos;

@@ -34,6 +34,8 @@ struct StreamPath {
 };
 
 constexpr int kMaxUnitPaths = 8;  // member paths per stream work unit
+constexpr int kPosMaxBlockWaves = 8;  // waves per block of the position streams
+constexpr int kMaxPosPairs = 256;     // (slice, unit) pairs of a position-stream launch
 
 struct StreamArgs {
   int32_t num_nodes;
@@ -64,6 +66,11 @@ struct StreamArgs {
   int32_t gout_rows;    // rows per node of grad_out
   const void* W;        // [K][P][C], fp32 or bf16
   const float* gout;    // [N][gout_rows][C]
+  // position streams: the block's waves (pos_waves) and the (slice, unit)
+  // pairs of each wave w, pair_order[pair_begin[w] .. pair_begin[w + 1])
+  int32_t pos_waves;
+  int16_t pair_begin[kPosMaxBlockWaves + 1];
+  uint8_t pair_order[kMaxPosPairs];
   StreamPath paths[kMaxPaths];
   int8_t unit_paths[kMaxPaths][kMaxUnitPaths];  // plan path indices of each unit's members
 };

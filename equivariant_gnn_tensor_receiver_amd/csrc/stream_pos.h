@@ -33,7 +33,8 @@
 //
 // Work decomposition: one block per receiver.  Its waves share the geometry
 // of a 64-edge batch (radial basis, R', harmonics and their Jacobian, written
-// to LDS once) and take the (channel slice, path bundle) pairs in turn; each
+// to LDS once) and each takes its own list of (channel slice, path bundle)
+// pairs, balanced by cost on the host since the waves meet at every batch; each
 // wave adds its per-edge share of g_r into its own LDS row, and after the
 // batch the rows are summed in a fixed order, so the sender's share goes out
 // as three fp32 atomic adds per edge.  The receiver's share is summed over
@@ -93,7 +94,7 @@ struct PosPack {
 
 constexpr int kPosSlice = 32;       // channels of one wave's reduction range
 constexpr int kPosNcl = kPosSlice / 4;  // channels per lane group (8 bf16 of one MFMA operand)
-constexpr int kPosMaxWaves = 8;     // waves per block
+constexpr int kPosMaxWaves = kPosMaxBlockWaves;  // waves per block
 constexpr int kPosBatch = 64;       // edges whose geometry is in LDS at a time
 
 // Batch geometry of the position derivative of the force loss (HESS): what
@@ -114,11 +115,13 @@ struct __attribute__((aligned(16))) HessLds {
   float phi[B][4];
 };
 
+// The batch geometry in static LDS; each wave's share of the per-edge vector,
+// gr[w][e][3], in dynamic LDS sized by the block's wave count.
 template <int K, int LMAX, bool HESS>
 struct PosLds {
   typename std::conditional<HESS, HessLds<K, LMAX>, EdgeLds<K, LMAX, kBwdPos, kPosBatch>>::type geo;
-  float gr[kPosMaxWaves][kPosBatch][3];  // per wave: its share of the per-edge vector
 };
+typedef float PosRow[kPosBatch][3];
 
 // Geometry of edge e into slot j for the position derivative of the force loss.
 //   HY phi = d^-2 [H_P(u) phi - l grad P(u) (u.phi) - l u (grad P(u).phi) - l P(u) (phi - (l+2) (u.phi) u)]
@@ -513,6 +516,8 @@ __global__ __launch_bounds__(64 * kPosMaxWaves) __attribute__((amdgpu_waves_per_
 void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
   const StreamArgs& a = *(const StreamArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ PosLds<K, LMAX, HESS> S;
+  extern __shared__ float pos_rows[];
+  PosRow* gr = reinterpret_cast<PosRow*>(pos_rows);
   const uint32_t item = (uint32_t)xcd_item(blockIdx.x, gridDim.x);
   if (item >= (uint32_t)nodes) return;  // uniform over the block
   const int node = a.order ? a.order[item] : (int)item;
@@ -533,11 +538,12 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
         edge_prep(a, node, psx, psy, psz, b0 + (int)threadIdx.x, (int)threadIdx.x, S.geo);
     }
 #pragma unroll
-    for (int cc = 0; cc < 3; ++cc) S.gr[w][lane][cc] = 0.f;
+    for (int cc = 0; cc < 3; ++cc) gr[w][lane][cc] = 0.f;
     __syncthreads();
-    for (int pr = w; pr < npairs; pr += nw) {
+    for (int k = a.pair_begin[w]; k < a.pair_begin[w + 1]; ++k) {
+      const int pr = a.pair_order[k];
       const int unit = pr % a.nunits, slice = pr / a.nunits;
-      PosUnitRunner<LMAX, K, LO, VEC, HESS> run{a, unit, node, slice, nb, S, S.gr[w]};
+      PosUnitRunner<LMAX, K, LO, VEC, HESS> run{a, unit, node, slice, nb, S, gr[w]};
       if constexpr (BUNDLED) {
         Bundles<LMAX, K, 2>::run(unit, run, a);
       } else {
@@ -559,9 +565,9 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
     if (w == 0 && lane < nb) {  // fixed-order sum over the waves, then the sender's share (+) and the receiver's (-)
       float v0 = 0.f, v1 = 0.f, v2 = 0.f;
       for (int ww = 0; ww < nw; ++ww) {
-        v0 += S.gr[ww][lane][0];
-        v1 += S.gr[ww][lane][1];
-        v2 += S.gr[ww][lane][2];
+        v0 += gr[ww][lane][0];
+        v1 += gr[ww][lane][1];
+        v2 += gr[ww][lane][2];
       }
       const int64_t s3 = 3 * (int64_t)S.geo.nbr[lane];
       atomicAdd(&a.gpos[s3 + 0], v0);
@@ -584,13 +590,6 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
   }
 }
 
-// Waves of a block: the (slice, unit) pairs spread evenly over at most
-// kPosMaxWaves waves.
-inline int pos_block_waves(int npairs) {
-  const int rounds = (npairs + kPosMaxWaves - 1) / kPosMaxWaves;
-  return (npairs + rounds - 1) / rounds;
-}
-
 // LO: the features are fp32, pre-split into the bf16 planes a.feat (hi) and
 // a.feat_lo (lo); otherwise a.feat holds them in bf16.
 template <bool LO, bool HESS>
@@ -600,21 +599,24 @@ hipError_t launch_pos(int lmax, int K, const StreamArgs& a, hipStream_t s) {
   const int npairs = a.nunits * a.nslices;
   if (nodes == 0 || npairs == 0) return hipSuccess;
   const int64_t grid = (nodes + 7) / 8 * 8;
-  if (grid > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 block(64 * pos_block_waves(npairs));
+  if (grid > INT32_MAX || a.pos_waves < 1 || a.pos_waves > kPosMaxWaves || a.pair_begin[0] != 0 ||
+      a.pair_begin[a.pos_waves] != npairs)
+    return hipErrorInvalidValue;
+  const dim3 block(64 * a.pos_waves);
+  const size_t rows = sizeof(PosRow) * (size_t)a.pos_waves;
   // 16-byte operand loads: whole slices, 16-byte aligned feature and state rows
   const bool vec = a.C % kPosSlice == 0 && a.feat_cs == a.C && (reinterpret_cast<uintptr_t>(a.feat) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.feat_lo) & 15) == 0;
 #define TPCONV_LAUNCH(LM, KK)                                                                                      \
   if (lmax == LM && K == KK) {                                                                                     \
     if (vec && a.bundled)                                                                                          \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, true, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);      \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, true, HESS>), dim3((unsigned)grid), block, rows, s, a, nodes);      \
     else if (vec)                                                                                                  \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, false, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);     \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, true, false, HESS>), dim3((unsigned)grid), block, rows, s, a, nodes);     \
     else if (a.bundled)                                                                                            \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, true, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);     \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, true, HESS>), dim3((unsigned)grid), block, rows, s, a, nodes);     \
     else                                                                                                           \
-      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, false, HESS>), dim3((unsigned)grid), block, 0, s, a, nodes);    \
+      hipLaunchKernelGGL((pos_kernel<LM, KK, LO, false, false, HESS>), dim3((unsigned)grid), block, rows, s, a, nodes);    \
     return hipGetLastError();                                                                                      \
   }
   TPCONV_LAUNCH(0, 8) TPCONV_LAUNCH(0, 16)
