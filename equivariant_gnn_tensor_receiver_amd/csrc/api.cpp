@@ -178,22 +178,25 @@ tpconv_status make_w_planes(const Plan& p, const void* W, Carver& c, WPlanes& ou
   return dev(launch_w_planes(W, bf16, (int64_t)p.K * p.P, p.C_in, p.C_out, hi, lo, thi, tlo, s));
 }
 
+size_t rows_part_elems(const Plan& p, int kind, int64_t N);
+
 size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
-  return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + x_planes(p, N) + w_planes(p) +
-         pad_bytes(p, N, TPCONV_OP_FORWARD);
+  return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + align_up(rows_part_elems(p, kGemmOut, N) * 4) +
+         x_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_FORWARD);
 }
 
 size_t ws_backward(const Plan& p, int64_t N) {
   // S (recomputed when not saved), gS (fully connected only), T, gW partials, planes of x and g_out
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
-         pad_bytes(p, N, TPCONV_OP_BACKWARD);
+         align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) +
+         g_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_BACKWARD);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
   // S_dot, T_dot, weight partials, gS (fully connected), planes of x and g_out
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
+         align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) +
+         align_up(rows_part_elems(p, kGemmOut, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
          pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD);
 }
 
@@ -399,6 +402,20 @@ int gemm_setup(const Plan& p, int kind, int64_t N, GemmArgs& a, int splits) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Partial sums of an out or g_x contraction split over blocks (floats; 0 when
+// it runs unsplit), for workspace sizing: the 16-byte load path is assumed.
+size_t rows_part_elems(const Plan& p, int kind, int64_t N) {
+  if (channelwise(p)) return 0;
+  GemmArgs a;
+  gemm_setup(p, kind, N, a, 1);
+  a.vec = (p.C_in % 16 == 0) && (p.C_out % 16 == 0);
+  const int sp = gemm_rows_splits(kind, a);
+  if (sp <= 1) return 0;
+  size_t n = 0;
+  for (int g = 0; g < a.ngroups; ++g) n += (size_t)a.g[g].M * a.g[g].N;
+  return n * sp;
+}
+
 // 16-byte operand loads need channel counts that are multiples of 16 and
 // 16-byte aligned states (the planes come from the workspace, 256-aligned).
 void set_vec(const Plan& p, GemmArgs& a) {
@@ -417,9 +434,10 @@ void set_planes(GemmArgs& a, const Planes* gp, const WPlanes& wp) {
   a.wt_lo = wp.tlo;
 }
 
-// gp: the g_out planes (gS); wp: the W planes.
+// gp: the g_out planes (gS); wp: the W planes; rows_part: room for the
+// partial sums of a split out or g_x (rows_part_elems floats).
 tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, const Planes* gp, const WPlanes& wp,
-                       float* out, int splits, hipStream_t s) {
+                       float* out, float* rows_part, hipStream_t s) {
   if (kind == kGemmOut || kind == kGemmGx) {  // rows of irreps that no path reaches are zero
     const bool in_side = kind == kGemmGx;
     for (const auto& g : in_side ? p.in_groups : p.out_groups) {
@@ -430,11 +448,24 @@ tpconv_status run_gemm(const Plan& p, int kind, int64_t N, const float* state, c
     }
   }
   GemmArgs a;
-  gemm_setup(p, kind, N, a, splits);
+  gemm_setup(p, kind, N, a, 1);
   a.state = state;
   set_planes(a, gp, wp);
   a.out = out;
   set_vec(p, a);
+  const int sp = gemm_rows_splits(kind, a);
+  if (sp > 1) {  // reduction split over blocks: partial sums, then their ordered sum
+    if (!rows_part) return TPCONV_ERROR_WORKSPACE;
+    gemm_setup(p, kind, N, a, sp);
+    a.state = state;
+    set_planes(a, gp, wp);
+    a.out = out;
+    set_vec(p, a);
+    a.part = rows_part;
+    tpconv_status st = dev(launch_gemm(kind, a, s));
+    if (st != TPCONV_SUCCESS) return st;
+    return dev(launch_rows_reduce(kind, a, s));
+  }
   return dev(launch_gemm(kind, a, s));
 }
 
@@ -600,7 +631,7 @@ tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, con
   const int64_t N = g->num_nodes;
   const bool cw = channelwise(p);
   tpconv_status st;
-  if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, 1, s)) != TPCONV_SUCCESS) return st;
+  if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
   if ((st = dev(launch_fill(out, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
   StreamArgs a;
   recv_args(p, a, g, pos, x);
@@ -661,6 +692,7 @@ tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* po
   const int64_t N = g->num_nodes;
   Carver c(ws);
   float* S = saved_state ? saved_state : c.take(state_in_elems(p, N));
+  float* rpart = c.take(rows_part_elems(p, kGemmOut, N));
   tpconv_status st;
   Planes xp;
   if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
@@ -674,7 +706,7 @@ tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* po
       TPCONV_SUCCESS)
     return st;
   if (channelwise(p)) return run_cw_contract(p, true, N, S, W, out, s);
-  return run_gemm(p, kGemmOut, N, S, nullptr, wp, out, 1, s);
+  return run_gemm(p, kGemmOut, N, S, nullptr, wp, out, rpart, s);
 }
 
 tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x, const void* W,
@@ -688,6 +720,7 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
   float* T = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
+  float* xpart = c.take(rows_part_elems(p, kGemmGx, N));
 
   const float* S = saved_state;
   Planes xp;
@@ -717,7 +750,8 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
     use_planes(a, gp);
     a.state = T;
     if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2) : run_gemm(p, kGemmGx, N, T, nullptr, wp, grad_x, 1, s2);
+    st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2)
+            : run_gemm(p, kGemmGx, N, T, nullptr, wp, grad_x, xpart, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
   if (grad_W) {  // side stream: gW = S^T g_out
@@ -742,6 +776,8 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   float* Td = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
   float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
+  float* xpart = c.take(rows_part_elems(p, kGemmGx, N));  // d_x (side stream)
+  float* opart = c.take(rows_part_elems(p, kGemmOut, N));  // d_grad_out (caller's stream)
   Planes xp;
   if (d_W || d_grad_out || d_pos) {
     if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
@@ -760,7 +796,7 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
     a.ggpos = gg_pos;
     a.state = Td;
     if ((st = dev(launch_stream(kSndT, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
-    st = cw ? run_cw_contract(p, false, N, Td, W, d_x, s2) : run_gemm(p, kGemmGx, N, Td, nullptr, wp, d_x, 1, s2);
+    st = cw ? run_cw_contract(p, false, N, Td, W, d_x, s2) : run_gemm(p, kGemmGx, N, Td, nullptr, wp, d_x, xpart, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
   if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
@@ -778,7 +814,7 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
     }
     if (d_grad_out) {
       st = cw ? run_cw_contract(p, true, N, Sd, W, d_grad_out, s)
-              : run_gemm(p, kGemmOut, N, Sd, nullptr, wp, d_grad_out, 1, s);
+              : run_gemm(p, kGemmOut, N, Sd, nullptr, wp, d_grad_out, opart, s);
       if (st != TPCONV_SUCCESS) return st;
     }
   }

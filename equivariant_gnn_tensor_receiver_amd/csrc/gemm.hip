@@ -485,7 +485,9 @@ void gemm_lds_kernel(const GemmArgs /*args*/) {
   const int i = lane & 31, h = lane >> 5;
   const int m0 = (tm * RW + w) * 32, n0 = tn * NC;
   int rb = 0, re = G.Kr;
-  if constexpr (KIND == kGemmGw) {
+  // gW, and out / g_x with too few row tiles, split the reduction over blocks
+  const bool split = KIND == kGemmGw || ((KIND == kGemmOut || KIND == kGemmGx) && a.splits > 1);
+  if (split) {
     const int per = ceil_div(ceil_div(G.Kr, a.splits), KC) * KC;
     rb = min(G.Kr, (int)blockIdx.y * per);
     re = min(G.Kr, rb + per);
@@ -647,6 +649,7 @@ void gemm_lds_kernel(const GemmArgs /*args*/) {
     }
   }
   if (m0 >= G.M) return;
+  const bool to_part = (KIND == kGemmOut || KIND == kGemmGx) && a.splits > 1;
   // D layout of the 32x32 products: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
   for (int j = 0; j < NT; ++j)
@@ -654,8 +657,37 @@ void gemm_lds_kernel(const GemmArgs /*args*/) {
     for (int r = 0; r < 16; ++r) {
       const int gm = m0 + 8 * (r >> 2) + 4 * h + (r & 3);
       const int gn = n0 + 32 * j + i;
-      if (gm < G.M && gn < G.N) store_c<KIND>(a, G, gm, gn, acc[j][r]);
+      if (gm < G.M && gn < G.N) {
+        if (to_part)
+          a.part[G.part_off + ((int64_t)blockIdx.y * G.M + gm) * G.N + gn] = acc[j][r];
+        else
+          store_c<KIND>(a, G, gm, gn, acc[j][r]);
+      }
     }
+}
+
+// out / g_x from their split partial sums, summed in split order (the
+// element's group found by a linear scan over at most kMaxGroups groups).
+template <int KIND>
+__global__ void rows_reduce_kernel(const GemmArgs /*args*/, int64_t total) {
+  const GemmArgs& a = *(const GemmArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  int64_t rem = i;
+  int gi = 0;
+  for (; gi < a.ngroups; ++gi) {
+    const int64_t sz = (int64_t)a.g[gi].M * a.g[gi].N;
+    if (rem < sz) break;
+    rem -= sz;
+  }
+  if (gi >= a.ngroups) return;
+  const GemmGroup& G = a.g[gi];
+  const int m = (int)(rem / G.N), n = (int)(rem - (int64_t)m * G.N);
+  const float* src = a.part + G.part_off + rem;
+  const int64_t step = (int64_t)G.M * G.N;
+  float v = 0.f;
+  for (int sp = 0; sp < a.splits; ++sp) v += src[sp * step];
+  store_c<KIND>(a, G, m, n, v);
 }
 
 __global__ void gw_reduce_kernel(const ReduceArgs a, int64_t total) {
@@ -846,7 +878,9 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
       const GemmGroup& G = a.g[g];
       if (G.M > 0 && G.N > 0 && G.Kr > 0) blocks += (int64_t)ceil_div(ceil_div(G.M, 32), rw) * ceil_div(G.N, 32 * nt);
     }
+    const int ysplits = (kind == kGemmOut || kind == kGemmGx) ? a.splits : splits;
     if (blocks * rw * splits >= kLdsMinWaves) {
+      if ((kind == kGemmOut || kind == kGemmGx) && ysplits > 1 && !a.part) return hipErrorInvalidValue;
       int64_t total = 0;
       for (int g = 0; g < a.ngroups; ++g) {
         GemmGroup& G = a.g[g];
@@ -856,7 +890,7 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
         total += G.tiles;
       }
       if (total > INT32_MAX) return hipErrorInvalidValue;
-      const dim3 grid((unsigned)total, (unsigned)splits, 1);
+      const dim3 grid((unsigned)total, (unsigned)ysplits, 1);
       TimingScope ts(kcGemmOut + kind, s);
       switch (kind) {
         case kGemmOut: return wlo ? launch_lds_nt<kGemmOut, true>(a, nt, grid, s) : launch_lds_nt<kGemmOut, false>(a, nt, grid, s);
@@ -905,6 +939,44 @@ hipError_t launch_gemm(int kind, GemmArgs& a, hipStream_t s) {
     case kGemmGw: return launch_kind<kGemmGw, false>(a, sh, grid, waves, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+int gemm_rows_splits(int kind, const GemmArgs& a) {
+  if ((kind != kGemmOut && kind != kGemmGx) || !a.vec || a.ngroups <= 0) return 1;
+  int max_cols = 0, max_kr = 0;
+  for (int g = 0; g < a.ngroups; ++g) {
+    max_cols = a.g[g].N > max_cols ? a.g[g].N : max_cols;
+    max_kr = a.g[g].Kr > max_kr ? a.g[g].Kr : max_kr;
+  }
+  const int nt = lds_nt(max_cols), rw = lds_rows(nt);
+  int64_t blocks = 0;
+  for (int g = 0; g < a.ngroups; ++g) {
+    const GemmGroup& G = a.g[g];
+    if (G.M > 0 && G.N > 0 && G.Kr > 0) blocks += (int64_t)ceil_div(ceil_div(G.M, 32), rw) * ceil_div(G.N, 32 * nt);
+  }
+  const int64_t waves = blocks * rw;
+  if (waves < kLdsMinWaves) return 1;  // the reduction-splitting kernel takes it
+  const int kc = 2 * (nt <= 2 ? 16 : 8);
+  // about four waves per SIMD, every split at least 64 chunks long
+  int sp = 1;
+  while (sp < 4 && waves * sp < 4096 && max_kr >= 2 * sp * 64 * kc) sp *= 2;
+  return sp;
+}
+
+hipError_t launch_rows_reduce(int kind, const GemmArgs& a, hipStream_t s) {
+  int64_t total = 0;
+  for (int g = 0; g < a.ngroups; ++g) total += (int64_t)a.g[g].M * a.g[g].N;
+  if (total <= 0 || a.splits <= 1) return hipSuccess;
+  if ((total + 255) / 256 > INT32_MAX || !a.part) return hipErrorInvalidValue;
+  TimingScope ts(kcGwReduce, s);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (kind == kGemmOut)
+    hipLaunchKernelGGL(rows_reduce_kernel<kGemmOut>, grid, dim3(256), 0, s, a, total);
+  else if (kind == kGemmGx)
+    hipLaunchKernelGGL(rows_reduce_kernel<kGemmGx>, grid, dim3(256), 0, s, a, total);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s) {

@@ -110,6 +110,7 @@ struct GemmArgs {
   const uint16_t* wt_hi;              // the same transposed per (k, p): [K][P][C_out][C_in] (B for Out)
   const uint16_t* wt_lo;
   float* out;                         // out / gS / g_x / partials
+  float* part;                        // out, g_x split over blocks (splits > 1): their partial sums
   int32_t path_list[kMaxPaths];
   GemmGroup g[kMaxGroups];
 };
@@ -180,6 +181,11 @@ hipError_t launch_w_planes(const void* W, bool w_bf16, int64_t kp, int C_in, int
                            uint16_t* thi, uint16_t* tlo, hipStream_t s);
 // Wave tiles of a C[M][N] product of the given kind (the tile shape launch_gemm uses).
 int64_t gemm_wave_tiles(int kind, int M, int N, int max_cols);
+// Reduction splits of an out or g_x contraction (1: none), for the groups of
+// `a` (set up with one split) and its vec flag; splits > 1 need partial sums
+// of splits * sum_g M * N floats in a.part and launch_rows_reduce afterwards.
+int gemm_rows_splits(int kind, const GemmArgs& a);
+hipError_t launch_rows_reduce(int kind, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 // Zeroes rows [row_off, row_off + nrows) of every node of a [N][D][C] tensor.
 hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s);

@@ -286,7 +286,7 @@ typedef enum {
   TPCONV_KERNEL_GEMM_GS = 6,       /* gS = grad_out . W^T */
   TPCONV_KERNEL_GEMM_GX = 7,       /* grad_x = T . W^T  (also d_x) */
   TPCONV_KERNEL_GEMM_GW = 8,       /* grad_W partials = S^T . grad_out  (also d_W) */
-  TPCONV_KERNEL_GW_REDUCE = 9,     /* ordered sum of the grad_W partials */
+  TPCONV_KERNEL_GW_REDUCE = 9,     /* ordered sums of split partials (grad_W; out and grad_x when split) */
   TPCONV_KERNEL_FILL = 10,         /* zero fills */
   TPCONV_KERNEL_GRAPH = 11,        /* sender-sorted view construction */
   TPCONV_KERNEL_CW_CONTRACT = 12,  /* channel-wise: out, grad_x, d_grad_out, d_x from S / T */
