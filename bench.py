@@ -266,6 +266,7 @@ def run_workload(name, steps, warmup, detail):
     dx = torch.empty((N, plan.rows_in, plan.ch_in), **f32)
     dg = torch.empty((N, plan.rows_out, plan.ch_out), **f32) if "dbwd" in w.passes else None
     dpos = torch.empty((N, 3), **f32)
+    ws_f = torch.empty(max(1, plan.workspace_size(tp.OP_FORWARD_SAVED, N, E)), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(plan.workspace_size(tp.OP_BACKWARD, N, E), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(plan.workspace_size(tp.OP_DOUBLE_BACKWARD, N, E), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -273,7 +274,7 @@ def run_workload(name, steps, warmup, detail):
     force = name == "force"
 
     def fwd():
-        tp.tpconv_forward(plan, graph, pos, x, W, out=out, saved_state=S)
+        tp.tpconv_forward(plan, graph, pos, x, W, out=out, saved_state=S, workspace=ws_f)
 
     def bwd():
         if force:  # forces: the position gradient only
@@ -371,6 +372,7 @@ def run_workload(name, steps, warmup, detail):
                    "step": "+".join(w.passes), "cutoff": inputs.CUTOFF, "box": round(data["box"], 4),
                    "connection": "channelwise" if w.channelwise else "fully_connected"},
         "peak_bytes": {"workspace_fwd": plan.workspace_size(tp.OP_FORWARD, N, E),
+                       "workspace_fwd_saved": plan.workspace_size(tp.OP_FORWARD_SAVED, N, E),
                        "workspace_bwd": plan.workspace_size(tp.OP_BACKWARD, N, E),
                        "workspace_dbwd": plan.workspace_size(tp.OP_DOUBLE_BACKWARD, N, E),
                        "saved_state": plan.state_size(N),
