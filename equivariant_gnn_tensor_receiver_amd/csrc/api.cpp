@@ -49,8 +49,10 @@ struct Carver {
 
 
 // Reduction splits of the gW product over blocks: enough waves to fill the
-// chip (with up to 4 waves per block) while each split of the largest group
-// keeps >= 512 reductions (smaller groups get shorter splits).
+// chip (with up to 4 waves per block; with channel counts that are multiples
+// of 16, about 4096 waves of the LDS-staged kernel, which shares each chunk
+// of g_out among four row tiles) while each split of the largest group keeps
+// >= 512 reductions (smaller groups get shorter splits).
 int gw_splits(const Plan& p, int64_t N) {
   int64_t tiles = 0, max_kr = 0;
   for (const auto& g : p.out_groups) {
@@ -61,6 +63,15 @@ int gw_splits(const Plan& p, int64_t N) {
   }
   if (tiles == 0) return 1;
   int64_t s = (1024 + tiles - 1) / tiles;
+  if (p.C_in % 16 == 0 && p.C_out % 16 == 0) {
+    // waves of the LDS-staged kernel (32-row tiles, up to 128 columns per block)
+    const int nt = p.C_out <= 32 ? 1 : (p.C_out <= 64 ? 2 : 4);
+    int64_t lw = 0;
+    for (const auto& g : p.out_groups)
+      if (!g.paths.empty())
+        lw += (((int64_t)p.K * g.paths.size() * p.C_in + 31) / 32) * ((p.C_out + 32 * nt - 1) / (32 * nt));
+    if (lw > 0) s = std::max<int64_t>(s, (4096 + lw - 1) / lw);
+  }
   s = std::min<int64_t>(s, 64);
   s = std::min<int64_t>(s, std::max<int64_t>(1, max_kr / 512));
   return (int)std::max<int64_t>(1, s);

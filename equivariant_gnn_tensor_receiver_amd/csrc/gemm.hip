@@ -573,7 +573,7 @@ void gemm_lds_kernel(const GemmArgs /*args*/) {
   auto a_load = [&](int c, float (&av)[VH], uint32_t (&ah)[VH / 2], uint32_t (&al)[VH / 2]) {
     const int rs = rb + c * KC + VH * h;
     if constexpr (APLANE)
-      load_a_planes<VH>(a, G, m, rs, ah, al);
+      load_a_planes<VH>(a, G, m, rs < re ? rs : re - VH, ah, al);
     else
       load_a<KIND, VH, true>(a, G, m, rs, re, av);
   };
@@ -596,16 +596,25 @@ void gemm_lds_kernel(const GemmArgs /*args*/) {
     for (int p = 0; p < QP; ++p)
       if (tid + p * 64 * RW < NQ) piece_store(stage[0], tid + p * 64 * RW, sh[p], sl[p]);
     a_load(0, av, pah, pal);
+    // chunk 0 of A has arrived before the loop: the loop is then entered
+    // with no load in flight into the registers it multiplies, as from its
+    // own back edge, and the waits the compiler places for the next chunk's
+    // loads stay after the multiplies
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    if (more) {
+    // the next chunk's loads are issued unconditionally (past the last chunk
+    // they read clamped addresses inside the tensors and are not used): a
+    // guarded load splits the loop body, and where the paths join the
+    // compiler waits for every load in flight before the multiplies
 #pragma unroll
-      for (int p = 0; p < QP; ++p)
-        if (tid + p * 64 * RW < NQ) piece_load(c + 1, tid + p * 64 * RW, p, sh[p], sl[p]);
-      a_load(c + 1, avn, pahn, paln);
-    }
+    for (int p = 0; p < QP; ++p)
+      if (tid + p * 64 * RW < NQ) piece_load(c + 1, tid + p * 64 * RW, p, sh[p], sl[p]);
+    a_load(c + 1, avn, pahn, paln);
+    // keep the loads ahead of the multiplies (the scheduler would otherwise
+    // sink them next to their use at the end of the chunk)
+    __builtin_amdgcn_sched_barrier(0);
     const BStage<NT, VH>& st = stage[c & 1];
     const int valid = re - (rb + c * KC + VH * h);
 #pragma unroll
@@ -634,11 +643,11 @@ void gemm_lds_kernel(const GemmArgs /*args*/) {
         acc[j] = mfma32(Al, Bh, acc[j]);
       }
     }
-    if (more) {  // chunk c+1's pieces into the other buffer
+    // chunk c+1's pieces into the other buffer (after the last chunk the
+    // store is unused; that buffer was last read before the previous barrier)
 #pragma unroll
-      for (int p = 0; p < QP; ++p)
-        if (tid + p * 64 * RW < NQ) piece_store(stage[(c + 1) & 1], tid + p * 64 * RW, sh[p], sl[p]);
-    }
+    for (int p = 0; p < QP; ++p)
+      if (tid + p * 64 * RW < NQ) piece_store(stage[(c + 1) & 1], tid + p * 64 * RW, sh[p], sl[p]);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < VH; ++t) av[t] = avn[t];
