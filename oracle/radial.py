@@ -95,3 +95,40 @@ def bessel_radial_deriv2(d: np.ndarray, K: int, cutoff: float, p: int = 6) -> np
     u2 = envelope_deriv2(d / cutoff, p)[..., None] / cutoff ** 2
     d2R = pref * (f2 * u + 2.0 * f1 * u1 + f * u2)
     return np.where((d > 0)[..., None], d2R, 0.0)
+
+
+# Radial MLP front end.  The pages name learned radial networks only as the
+# usual setting of the layer; the reading taken keeps the reassociation intact
+# by letting the network's last hidden layer be the K radial functions the
+# streams consume, and folding its output layer into W:
+#   R_k(d) = silu(z_k),  z_k = sum_j A[k, j] B_j(d),   silu(z) = z / (1 + exp(-z)),
+# with B_j the Bessel x envelope basis above (K functions) and A the K x K
+# weights of the hidden layer (no bias, so R vanishes with B at the cutoff).
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def silu_d1(z):
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def silu_d2(z):
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 - s) * (2.0 + z * (1.0 - 2.0 * s))
+
+
+def mlp_radial(d: np.ndarray, A: np.ndarray, K: int, cutoff: float, p: int = 6):
+    """R, dR/dd and d2R/dd2 of the radial MLP, plus (z, z', B, B') for its weight gradients."""
+    A = np.asarray(A, dtype=np.float64).reshape(K, K)
+    B = bessel_radial(d, K, cutoff, p)
+    B1 = bessel_radial_deriv(d, K, cutoff, p)
+    B2 = bessel_radial_deriv2(d, K, cutoff, p)
+    z = B @ A.T
+    z1 = B1 @ A.T
+    z2 = B2 @ A.T
+    R = silu(z)
+    R1 = silu_d1(z) * z1
+    R2 = silu_d2(z) * z1 * z1 + silu_d1(z) * z2
+    return R, R1, R2, (z, z1, B, B1)

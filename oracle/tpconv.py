@@ -8,7 +8,9 @@ implementations materialise edge-specific weights, messages and adjoints).  For
 every directed edge e = (s -> v) of the receiver-sorted graph:
 
   r_e = pos[s] - pos[v],  d = |r_e|,  r_hat = r_e / d
-  R_e[k]            radial basis (oracle.radial)
+  R_e[k]            radial basis (oracle.radial): the fixed Bessel x envelope
+                    functions, or a radial MLP on them whose last hidden width
+                    is K (oracle.radial.mlp_radial, weights radial_w)
   Y_e[l2, m2]       real spherical harmonics of r_hat (oracle.sh)
   w_e[p, ci, co]  = sum_k R_e[k] W[k, p, ci, co]                (per-edge weights)
   U_e[p, ci, m3]  = sum_{m1,m2} C^p[m1,m2,m3] x[s][l1, ci, m1] Y_e[l2, m2]
@@ -136,11 +138,21 @@ def _chunks(prob: Problem, E: int):
         yield a, min(E, a + step)
 
 
-def _edge_terms(prob, pos, s, v):
+def _radial_terms(prob, d, radial_w):
+    """R, R', R'' per edge (the fixed basis, or the radial MLP when radial_w is given) and the MLP's (z, z', B, B')."""
+    K = prob.num_basis
+    if radial_w is not None:
+        return _radial.mlp_radial(d, radial_w, K, prob.cutoff, prob.envelope_p)
+    return (_radial.bessel_radial(d, K, prob.cutoff, prob.envelope_p),
+            _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p),
+            _radial.bessel_radial_deriv2(d, K, prob.cutoff, prob.envelope_p), None)
+
+
+def _edge_terms(prob, pos, s, v, radial_w=None):
     r, d, rhat = _geometry(pos, s, v)
-    R = _radial.bessel_radial(d, prob.num_basis, prob.cutoff, prob.envelope_p)
+    R, R1, R2, mlp = _radial_terms(prob, d, radial_w)
     Y = _sh.spherical_harmonics(prob.sh_lmax, r)
-    return r, d, rhat, R, Y
+    return r, d, rhat, R, Y, R1, R2, mlp
 
 
 # Views of the flat node tensors and weights for one path.
@@ -202,8 +214,11 @@ def _as64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def forward(prob: Problem, pos, senders, receivers, x, W, num_nodes=None):
-    """out[v] = sum over edges into v of the materialised message m_e."""
+def forward(prob: Problem, pos, senders, receivers, x, W, num_nodes=None, radial_w=None):
+    """out[v] = sum over edges into v of the materialised message m_e.
+
+    radial_w: None for the fixed radial basis, or the K x K weights A of the
+    radial MLP (oracle.radial.mlp_radial)."""
     pos = _as64(pos)
     xf, Wf = _flat(prob, x, "in"), _flat_w(prob, W)
     senders = np.asarray(senders, dtype=np.int64)
@@ -213,7 +228,7 @@ def forward(prob: Problem, pos, senders, receivers, x, W, num_nodes=None):
     ops = _ops(prob)
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
-        _, _, _, R, Y = _edge_terms(prob, pos, s, v)
+        _, _, _, R, Y, _, _, _ = _edge_terms(prob, pos, s, v, radial_w)
         for p in prob.paths:
             w_e = np.einsum(ops["w"], R, _w_block(prob, Wf, p), optimize=True)       # per-edge weights
             U = _coupling(p["C"], _x_block(prob, xf, s, p), _y_block(Y, p))
@@ -222,8 +237,11 @@ def forward(prob: Problem, pos, senders, receivers, x, W, num_nodes=None):
     return out.reshape(prob.out_shape(N))
 
 
-def backward(prob: Problem, pos, senders, receivers, x, W, g_out):
-    """Materialised adjoints; returns (g_x, g_W, g_pos) for the loss <g_out, out>."""
+def backward(prob: Problem, pos, senders, receivers, x, W, g_out, radial_w=None):
+    """Materialised adjoints; returns (g_x, g_W, g_pos) for the loss <g_out, out>.
+
+    With the radial MLP (radial_w = A) also g_A, from the per-edge adjoint of
+    the radial functions: dL/dA[k, j] = sum_e g_R[e, k] silu'(z_ek) B_j(d_e)."""
     pos = _as64(pos)
     xf, Wf, gf = _flat(prob, x, "in"), _flat_w(prob, W), _flat(prob, g_out, "out")
     senders = np.asarray(senders, dtype=np.int64)
@@ -233,11 +251,11 @@ def backward(prob: Problem, pos, senders, receivers, x, W, g_out):
     g_x = np.zeros_like(xf)
     g_W = np.zeros_like(Wf)
     g_pos = np.zeros_like(pos)
+    g_A = np.zeros((K, K))
     ops = _ops(prob)
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
-        r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
-        dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
+        r, d, rhat, R, Y, dR, _, mlp = _edge_terms(prob, pos, s, v, radial_w)
         JY = _sh.sh_jacobian(prob.sh_lmax, r)                     # [e, Dsh, 3]
         g_Y = np.zeros_like(Y)
         g_R = np.zeros_like(R)
@@ -262,10 +280,14 @@ def backward(prob: Problem, pos, senders, receivers, x, W, g_out):
                + np.einsum("em,emj->ej", g_Y, JY))
         np.add.at(g_pos, s, g_r)
         np.add.at(g_pos, v, -g_r)
-    return g_x.reshape(prob.in_shape(N)), g_W.reshape(np.shape(W)), g_pos
+        if mlp is not None:
+            z, _, Bj, _ = mlp
+            g_A += np.einsum("ek,ej->kj", g_R * _radial.silu_d1(z), Bj)
+    res = (g_x.reshape(prob.in_shape(N)), g_W.reshape(np.shape(W)), g_pos)
+    return res + (g_A,) if radial_w is not None else res
 
 
-def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos):
+def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos, radial_w=None):
     """Gradients of L_F = sum_n <gg_pos[n], g_pos[n]> w.r.t. W, x and g_out.
 
     With phi_e = gg_pos[s] - gg_pos[v], L_F = sum_e <phi_e, g_r_e>, the
@@ -273,6 +295,12 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
     R_dot = R'(d) (r_hat . phi), Y_dot = J_Y phi, U_dot = CG(x_s, Y_dot) and
     w_dot = sum_k R_dot[k] W[k]; L_F is linear in W, x and g_out, so no second
     derivatives of R or Y appear (those enter only d/dpos, double_backward_pos).
+
+    With the radial MLP (radial_w = A) also d_A: L_F = sum_e sum_k
+    [R_dot[e,k] g_R[e,k] + R[e,k] h[e,k]] with g_R[e,k] = <W[k], U gm> and
+    h[e,k] = <W[k], U_dot gm>, and R_dot = R'(d)(r_hat . phi), so
+    dL_F/dA[k,j] = sum_e (r_hat . phi) g_R (silu''(z) z' B_j + silu'(z) B'_j)
+                 + h silu'(z) B_j.
     """
     pos, gg_pos = _as64(pos), _as64(gg_pos)
     xf, Wf, gf = _flat(prob, x, "in"), _flat_w(prob, W), _flat(prob, g_out, "out")
@@ -283,15 +311,18 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
     d_W = np.zeros_like(Wf)
     d_x = np.zeros_like(xf)
     d_gout = np.zeros_like(gf)
+    d_A = np.zeros((K, K))
     ops = _ops(prob)
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
-        r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
-        dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
+        r, d, rhat, R, Y, dR, _, mlp = _edge_terms(prob, pos, s, v, radial_w)
         JY = _sh.sh_jacobian(prob.sh_lmax, r)
         phi = gg_pos[s] - gg_pos[v]
-        R_dot = dR * np.einsum("ej,ej->e", rhat, phi)[:, None]
+        rphi = np.einsum("ej,ej->e", rhat, phi)
+        R_dot = dR * rphi[:, None]
         Y_dot = np.einsum("emj,ej->em", JY, phi)
+        g_R = np.zeros_like(R)
+        h_R = np.zeros_like(R)
         for p in prob.paths:
             C = p["C"]
             Wp = _w_block(prob, Wf, p)
@@ -315,10 +346,20 @@ def double_backward(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos)
             dgo = (np.einsum(ops["msg"], w_dot, U, optimize=True)
                    + np.einsum(ops["msg"], w_e, U_dot, optimize=True))
             np.add.at(d_gout[:, _out_slice(prob, p)], v, dgo.reshape(len(s), -1))
-    return d_W.reshape(np.shape(W)), d_x.reshape(prob.in_shape(N)), d_gout.reshape(prob.out_shape(N))
+            if mlp is not None:
+                g_R += np.einsum(ops["g_R"], Wp, g_w, optimize=True)
+                h_R += np.einsum(ops["g_R"], Wp, np.einsum(ops["g_w"], U_dot, gm, optimize=True), optimize=True)
+        if mlp is not None:
+            z, z1, Bj, B1 = mlp
+            s1, s2 = _radial.silu_d1(z), _radial.silu_d2(z)
+            d_A += (np.einsum("ek,ej->kj", rphi[:, None] * g_R * s2 * z1, Bj)
+                    + np.einsum("ek,ej->kj", rphi[:, None] * g_R * s1, B1)
+                    + np.einsum("ek,ej->kj", h_R * s1, Bj))
+    res = (d_W.reshape(np.shape(W)), d_x.reshape(prob.in_shape(N)), d_gout.reshape(prob.out_shape(N)))
+    return res + (d_A,) if radial_w is not None else res
 
 
-def double_backward_pos(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos):
+def double_backward_pos(prob: Problem, pos, senders, receivers, x, W, g_out, gg_pos, radial_w=None):
     """dL_F/dpos for L_F = sum_n <gg_pos[n], g_pos[n]> (the Hessian term).
 
     For an edge e, the energy <g_m_e, m_e> is eps(r) = sum_k R_k(|r|) b_k . Y(r)
@@ -341,9 +382,7 @@ def double_backward_pos(prob: Problem, pos, senders, receivers, x, W, g_out, gg_
     eye = np.eye(3)
     for a, b in _chunks(prob, len(senders)):
         s, v = senders[a:b], receivers[a:b]
-        r, d, rhat, R, Y = _edge_terms(prob, pos, s, v)
-        dR = _radial.bessel_radial_deriv(d, K, prob.cutoff, prob.envelope_p)
-        d2R = _radial.bessel_radial_deriv2(d, K, prob.cutoff, prob.envelope_p)
+        r, d, rhat, R, Y, dR, d2R, _ = _edge_terms(prob, pos, s, v, radial_w)
         JY = _sh.sh_jacobian(prob.sh_lmax, r)                       # [e, m, 3]
         HY = _sh.sh_hessian(prob.sh_lmax, r)                        # [e, m, 3, 3]
         phi = gg_pos[s] - gg_pos[v]
