@@ -191,6 +191,65 @@ tpconv_status make_w_planes(const Plan& p, const void* W, Carver& c, WPlanes& ou
 
 size_t rows_part_elems(const Plan& p, int kind, int64_t N);
 
+// The per-k dot products of two receiver states (the radial MLP's weight
+// gradient): chunks of about 1/2048 of the state's rows, at least 16 rows.
+int dot_rows_per_chunk(const Plan& p, int64_t N) {
+  int64_t rows = 0;
+  for (const auto& g : p.out_groups)
+    if (!g.paths.empty()) rows += N * (2 * g.l + 1);
+  return (int)std::max<int64_t>(16, (rows + 2047) / 2048);
+}
+
+void state_dot_setup(const Plan& p, int64_t N, StateDotArgs& d) {
+  std::memset(&d, 0, sizeof(d));
+  d.K = p.K;
+  d.rows_per_chunk = dot_rows_per_chunk(p, N);
+  d.out_stride = p.K;
+  int64_t blocks = 0, part = 0;
+  for (const auto& g : p.out_groups) {
+    if (g.paths.empty()) continue;
+    const int i = d.ngroups++;
+    d.cpk[i] = (int32_t)g.paths.size() * p.C_in;
+    d.cols[i] = p.K * d.cpk[i];
+    d.rows[i] = N * (2 * g.l + 1);
+    d.base[i] = N * g.base_per_node;
+    d.nchunks[i] = (int32_t)((d.rows[i] + d.rows_per_chunk - 1) / d.rows_per_chunk);
+    d.chunk_begin[i] = (int32_t)blocks;
+    d.part_base[i] = part;
+    blocks += d.nchunks[i];
+    part += (int64_t)d.nchunks[i] * d.cols[i];
+  }
+}
+
+size_t dot_part_elems(const Plan& p, int64_t N) {
+  if (!p.radial_mlp) return 0;
+  StateDotArgs d;
+  state_dot_setup(p, N, d);
+  size_t n = 0;
+  for (int g = 0; g < d.ngroups; ++g) n += (size_t)d.nchunks[g] * d.cols[g];
+  return n;
+}
+
+// out[k][col] = <a[k], b[k]> over the receiver-state layout, k = 0..K-1 (out: [K][K]).
+tpconv_status state_dot(const Plan& p, int64_t N, const float* a, const float* b, float* part, float* out, int col,
+                        hipStream_t s) {
+  StateDotArgs d;
+  state_dot_setup(p, N, d);
+  d.a = a;
+  d.b = b;
+  d.part = part;
+  d.out = out;
+  d.out_col = col;
+  if (d.ngroups == 0) {  // no path reaches any output irrep: the state is empty
+    for (int k = 0; k < p.K; ++k) {
+      const tpconv_status st = dev(launch_fill(out + (int64_t)k * p.K + col, 1, 0.f, s));
+      if (st != TPCONV_SUCCESS) return st;
+    }
+    return TPCONV_SUCCESS;
+  }
+  return dev(launch_state_dot(d, s));
+}
+
 size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
   return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + align_up(rows_part_elems(p, kGemmOut, N) * 4) +
          x_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_FORWARD);
@@ -200,7 +259,9 @@ size_t ws_backward(const Plan& p, int64_t N) {
   // S (recomputed when not saved), gS (fully connected only), T, gW partials, planes of x and g_out
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
          align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) +
-         g_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_BACKWARD);
+         g_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_BACKWARD) +
+         // radial MLP: the state streamed for one column of dL/dA, and the dot partials
+         (p.radial_mlp ? align_up(state_in_elems(p, N) * 4) + align_up(dot_part_elems(p, N) * 4) : 0);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
@@ -208,7 +269,7 @@ size_t ws_double_backward(const Plan& p, int64_t N) {
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
          align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) +
          align_up(rows_part_elems(p, kGemmOut, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
-         pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD);
+         pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD) + align_up(dot_part_elems(p, N) * 4);
 }
 
 // Independent chains of one call (the position gradient, the input gradient
@@ -312,6 +373,8 @@ void fill_common(const Plan& p, StreamArgs& a, const tpconv_graph* g, const floa
   a.env_c = (float)(e * (e + 1) / 2);
   a.env_d = (float)(e * (e + 1) * (e + 2) / 2);
   a.pos = pos;
+  a.mlp = nullptr;
+  a.mlp_col = -1;
 }
 
 void set_units(const Plan& p, StreamArgs& a, const std::vector<std::vector<int>>& units) {
@@ -323,9 +386,11 @@ void set_units(const Plan& p, StreamArgs& a, const std::vector<std::vector<int>>
 
 // Receiver-side stream over the CSR: gathered features x [N][D_in][C_in],
 // state S (or S_dot) in the output-group layout.
-void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const void* x) {
+void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const void* x,
+               const float* rw) {
   const int64_t N = g->num_nodes;
   fill_common(p, a, g, pos);
+  a.mlp = rw;
   a.ptr = g->rowptr;
   a.nbr = g->senders;
   a.feat = x;
@@ -342,9 +407,11 @@ void recv_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float*
 
 // Sender-side stream over the CSC view: gathered features grad_out [N][D_out][C_out],
 // state T (or T_dot) in the input-group layout.
-void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const float* gout) {
+void send_args(const Plan& p, StreamArgs& a, const tpconv_graph* g, const float* pos, const float* gout,
+               const float* rw) {
   const int64_t N = g->num_nodes;
   fill_common(p, a, g, pos);
+  a.mlp = rw;
   a.ptr = g->csc_colptr;
   a.nbr = g->csc_receivers;
   a.feat = gout;
@@ -634,18 +701,21 @@ bool assign_pos_pairs(const Plan& p, StreamArgs& a) {
 
 // The receiver-side position streams (kBwdPos: grad_pos; kBwdHess: the
 // position derivative of the force loss along gg_pos) into out [N][3]:
-// gS = g_out W^T first (formed in registers when channel-wise); xp, gp, wp:
-// the bf16 planes of x, g_out and W.
+// gS = g_out W^T first unless gs_ready (formed in registers when
+// channel-wise); xp, gp, wp: the bf16 planes of x, g_out and W; rw: the
+// radial MLP's weights or NULL.
 tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, const float* pos, const void* x,
                              const Planes& xp, const Planes& gp, const WPlanes& wp, const void* W,
-                             const float* grad_out, const float* gg_pos, float* gS, float* out, hipStream_t s) {
+                             const float* grad_out, const float* gg_pos, float* gS, bool gs_ready, const float* rw,
+                             float* out, hipStream_t s) {
   const int64_t N = g->num_nodes;
   const bool cw = channelwise(p);
   tpconv_status st;
-  if (!cw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
+  if (!cw && !gs_ready && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS)
+    return st;
   if ((st = dev(launch_fill(out, 3 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
   StreamArgs a;
-  recv_args(p, a, g, pos, x);
+  recv_args(p, a, g, pos, x, rw);
   set_units(p, a, p.pos_units);
   use_planes(a, xp);
   if (!assign_pos_pairs(p, a)) return TPCONV_ERROR_INVALID_VALUE;
@@ -699,7 +769,7 @@ RaggedWeightMap weight_map(const Plan& p) {
 
 // The passes on uniform (for ragged plans: padded) tensors.
 tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x, const void* W,
-                           float* out, float* saved_state, void* ws, hipStream_t s) {
+                           const float* rw, float* out, float* saved_state, void* ws, hipStream_t s) {
   const int64_t N = g->num_nodes;
   Carver c(ws);
   float* S = saved_state ? saved_state : c.take(state_in_elems(p, N));
@@ -710,7 +780,7 @@ tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* po
   WPlanes wp;
   if ((st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
   StreamArgs a;
-  recv_args(p, a, g, pos, x);
+  recv_args(p, a, g, pos, x, rw);
   use_planes(a, xp);
   a.state = S;
   if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
@@ -721,8 +791,8 @@ tpconv_status forward_core(const Plan& p, const tpconv_graph* g, const float* po
 }
 
 tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x, const void* W,
-                            const float* grad_out, const float* saved_state, float* grad_x, float* grad_W,
-                            float* grad_pos, void* ws, hipStream_t s) {
+                            const float* rw, const float* grad_out, const float* saved_state, float* grad_x,
+                            float* grad_W, float* grad_pos, float* grad_rw, void* ws, hipStream_t s) {
   const int64_t N = g->num_nodes;
   const bool cw = channelwise(p);
   tpconv_status st;
@@ -732,15 +802,17 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   float* T = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
   float* xpart = c.take(rows_part_elems(p, kGemmGx, N));
+  float* Sj = p.radial_mlp ? c.take(state_in_elems(p, N)) : nullptr;
+  float* dpart = c.take(dot_part_elems(p, N));
 
   const float* S = saved_state;
   Planes xp;
-  if ((grad_W && !S) || grad_pos) {
+  if ((grad_W && !S) || grad_pos || grad_rw) {
     if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
   }
   if (grad_W && !S) {  // recompute the receiver state for the weight gradient
     StreamArgs a;
-    recv_args(p, a, g, pos, x);
+    recv_args(p, a, g, pos, x, rw);
     use_planes(a, xp);
     a.state = S_ws;
     if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
@@ -752,12 +824,12 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   Planes gp;
   if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s)) != TPCONV_SUCCESS) return st;
   WPlanes wp;
-  if ((grad_x || grad_pos) && (st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
+  if ((grad_x || grad_pos || grad_rw) && (st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (grad_x) {  // side stream: sender stream, then g_x = T W^T
     StreamArgs a;
-    send_args(p, a, g, pos, grad_out);
+    send_args(p, a, g, pos, grad_out, rw);
     use_planes(a, gp);
     a.state = T;
     if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
@@ -769,16 +841,32 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
     st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, gp, part, grad_W, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
-  if (grad_pos) {  // caller's stream
-    st = run_pos_stream(p, kBwdPos, g, pos, x, xp, gp, wp, W, grad_out, nullptr, gS, grad_pos, s);
+  // caller's stream: gS, the position gradient, and dL/dA of the radial MLP
+  // one column at a time, dL/dA[k, j] = <gS[k], S^(j)[k]>
+  if (grad_rw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
+  if (grad_pos) {
+    st = run_pos_stream(p, kBwdPos, g, pos, x, xp, gp, wp, W, grad_out, nullptr, gS, grad_rw != nullptr, rw,
+                        grad_pos, s);
     if (st != TPCONV_SUCCESS) return st;
+  }
+  for (int j = 0; grad_rw && j < p.K; ++j) {
+    StreamArgs a;
+    recv_args(p, a, g, pos, x, rw);
+    a.mlp_col = j;
+    use_planes(a, xp);
+    a.state = Sj;
+    if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+        TPCONV_SUCCESS)
+      return st;
+    if ((st = state_dot(p, N, gS, Sj, dpart, grad_rw, j, s)) != TPCONV_SUCCESS) return st;
   }
   return fork.join();
 }
 
 tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const float* pos, const void* x,
-                                   const void* W, const float* grad_out, const float* gg_pos, float* d_W, float* d_x,
-                                   float* d_grad_out, float* d_pos, void* ws, hipStream_t s) {
+                                   const void* W, const float* rw, const float* grad_out, const float* gg_pos,
+                                   float* d_W, float* d_x, float* d_grad_out, float* d_pos, float* d_rw, void* ws,
+                                   hipStream_t s) {
   const int64_t N = g->num_nodes;
   const bool cw = channelwise(p);
   tpconv_status st;
@@ -789,20 +877,21 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
   float* xpart = c.take(rows_part_elems(p, kGemmGx, N));  // d_x (side stream)
   float* opart = c.take(rows_part_elems(p, kGemmOut, N));  // d_grad_out (caller's stream)
+  float* dpart = c.take(dot_part_elems(p, N));
   Planes xp;
-  if (d_W || d_grad_out || d_pos) {
+  if (d_W || d_grad_out || d_pos || d_rw) {
     if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
   }
   // planes of g_out (sender tangent stream, d_W, gS) and of W, before the fork
   Planes gp;
   if ((st = make_planes(grad_out, false, N, p.D_out, p.C_out, c, gp, s)) != TPCONV_SUCCESS) return st;
   WPlanes wp;
-  if ((d_x || d_grad_out || d_pos) && (st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
+  if ((d_x || d_grad_out || d_pos || d_rw) && (st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
   Fork fork(s);
   const hipStream_t s2 = fork.side();
   if (d_x) {  // side stream: sender tangent stream, then d_x = T_dot W^T
     StreamArgs a;
-    send_args(p, a, g, pos, grad_out);
+    send_args(p, a, g, pos, grad_out, rw);
     use_planes(a, gp);
     a.ggpos = gg_pos;
     a.state = Td;
@@ -812,7 +901,7 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   }
   if (d_W || d_grad_out) {  // caller's stream: tangent state, then its two contractions
     StreamArgs a;
-    recv_args(p, a, g, pos, x);
+    recv_args(p, a, g, pos, x, rw);
     use_planes(a, xp);
     a.ggpos = gg_pos;
     a.state = Sd;
@@ -829,9 +918,26 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
       if (st != TPCONV_SUCCESS) return st;
     }
   }
-  if (d_pos) {  // caller's stream: the Hessian term
-    st = run_pos_stream(p, kBwdHess, g, pos, x, xp, gp, wp, W, grad_out, gg_pos, gS, d_pos, s);
+  // caller's stream: gS, the Hessian term, and dL/dA of the radial MLP one
+  // column at a time, dL/dA[k, j] = <gS[k], S_dot^(j)[k]> with the tangent
+  // state streamed in the mlp_col = j mode (after d_W and d_grad_out, which
+  // read S_dot earlier on this stream)
+  if (d_rw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
+  if (d_pos) {
+    st = run_pos_stream(p, kBwdHess, g, pos, x, xp, gp, wp, W, grad_out, gg_pos, gS, d_rw != nullptr, rw, d_pos, s);
     if (st != TPCONV_SUCCESS) return st;
+  }
+  for (int j = 0; d_rw && j < p.K; ++j) {
+    StreamArgs a;
+    recv_args(p, a, g, pos, x, rw);
+    a.mlp_col = j;
+    use_planes(a, xp);
+    a.ggpos = gg_pos;
+    a.state = Sd;
+    if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+        TPCONV_SUCCESS)
+      return st;
+    if ((st = state_dot(p, N, gS, Sd, dpart, d_rw, j, s)) != TPCONV_SUCCESS) return st;
   }
   return fork.join();
 }
@@ -902,12 +1008,17 @@ tpconv_status tpconv_plan_create(tpconv_plan* out, const tpconv_desc* d) {
   try {
     auto* h = new (std::nothrow) tpconv_plan_s;
     if (!h) return TPCONV_ERROR_INVALID_VALUE;
-    const int st = build_plan(d->irreps_in, d->irreps_out, d->sh_lmax, d->num_basis, d->cutoff, d->envelope_p,
-                              d->x_dtype, d->w_dtype, d->connection, h->plan);
+    int st = build_plan(d->irreps_in, d->irreps_out, d->sh_lmax, d->num_basis, d->cutoff, d->envelope_p,
+                        d->x_dtype, d->w_dtype, d->connection, h->plan);
+    if (st == TPCONV_SUCCESS && (d->radial_mlp < 0 || d->radial_mlp > 1)) st = TPCONV_ERROR_INVALID_VALUE;
+    // the MLP's weight gradient contracts the state cotangent, which the
+    // channel-wise passes never form
+    if (st == TPCONV_SUCCESS && d->radial_mlp && d->connection == TPCONV_CHANNELWISE) st = TPCONV_ERROR_UNSUPPORTED;
     if (st != TPCONV_SUCCESS) {
       delete h;
       return (tpconv_status)st;
     }
+    h->plan.radial_mlp = d->radial_mlp;
     *out = h;
     return TPCONV_SUCCESS;
   } catch (...) {
@@ -1015,7 +1126,13 @@ tpconv_status tpconv_graph_order(tpconv_plan plan, const tpconv_graph* g, const 
 tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
                              const void* W, float* out, float* saved_state, void* ws, size_t ws_bytes,
                              void* stream) {
-  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  return tpconv_forward_mlp(plan, g, pos, x, W, nullptr, out, saved_state, ws, ws_bytes, stream);
+}
+
+tpconv_status tpconv_forward_mlp(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                                 const void* W, const float* radial_w, float* out, float* saved_state, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!plan || (plan->plan.radial_mlp != 0) != (radial_w != nullptr)) return TPCONV_ERROR_INVALID_VALUE;
   tpconv_status st = check_graph(g, false);
   if (st != TPCONV_SUCCESS) return st;
   const Plan& p = plan->plan;
@@ -1026,13 +1143,13 @@ tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const floa
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   if (N == 0) return TPCONV_SUCCESS;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!p.ragged) return forward_core(p, g, pos, x, W, out, saved_state, ws, s);
+  if (!p.ragged) return forward_core(p, g, pos, x, W, radial_w, out, saved_state, ws, s);
   Padded pd(p, ws, s);
   const void* xp = pd.pack_nodes(x, true, xbytes(p), N);
   const void* Wp = pd.pack_w(W, wbytes(p));
   float* outp = pd.out_nodes(false, N);
   if (pd.st != TPCONV_SUCCESS) return pd.st;
-  if ((st = forward_core(p, g, pos, xp, Wp, outp, saved_state, pd.rest(), s)) != TPCONV_SUCCESS) return st;
+  if ((st = forward_core(p, g, pos, xp, Wp, radial_w, outp, saved_state, pd.rest(), s)) != TPCONV_SUCCESS) return st;
   pd.unpack_nodes(outp, out, false, N);
   return pd.st;
 }
@@ -1040,10 +1157,19 @@ tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const floa
 tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
                               const void* W, const float* grad_out, const float* saved_state, float* grad_x,
                               float* grad_W, float* grad_pos, void* ws, size_t ws_bytes, void* stream) {
-  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  return tpconv_backward_mlp(plan, g, pos, x, W, nullptr, grad_out, saved_state, grad_x, grad_W, grad_pos, nullptr,
+                             ws, ws_bytes, stream);
+}
+
+tpconv_status tpconv_backward_mlp(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                                  const void* W, const float* radial_w, const float* grad_out,
+                                  const float* saved_state, float* grad_x, float* grad_W, float* grad_pos,
+                                  float* grad_radial_w, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || (plan->plan.radial_mlp != 0) != (radial_w != nullptr)) return TPCONV_ERROR_INVALID_VALUE;
+  if (grad_radial_w && !radial_w) return TPCONV_ERROR_INVALID_VALUE;
   tpconv_status st = check_graph(g, grad_x != nullptr);
   if (st != TPCONV_SUCCESS) return st;
-  if (!grad_x && !grad_W && !grad_pos) return TPCONV_ERROR_INVALID_VALUE;
+  if (!grad_x && !grad_W && !grad_pos && !grad_radial_w) return TPCONV_ERROR_INVALID_VALUE;
   const Plan& p = plan->plan;
   const int64_t N = g->num_nodes;
   if (N > 0 && (!pos || !x || !W || !grad_out)) return TPCONV_ERROR_INVALID_VALUE;
@@ -1052,10 +1178,13 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
-    if (grad_W) return dev(launch_fill(grad_W, (int64_t)w_elems_caller(p), 0.f, s));
+    if (grad_W && (st = dev(launch_fill(grad_W, (int64_t)w_elems_caller(p), 0.f, s))) != TPCONV_SUCCESS) return st;
+    if (grad_radial_w) return dev(launch_fill(grad_radial_w, (int64_t)p.K * p.K, 0.f, s));
     return TPCONV_SUCCESS;
   }
-  if (!p.ragged) return backward_core(p, g, pos, x, W, grad_out, saved_state, grad_x, grad_W, grad_pos, ws, s);
+  if (!p.ragged)
+    return backward_core(p, g, pos, x, W, radial_w, grad_out, saved_state, grad_x, grad_W, grad_pos, grad_radial_w,
+                         ws, s);
   Padded pd(p, ws, s);
   const void* xp = pd.pack_nodes(x, true, xbytes(p), N);
   const void* Wp = pd.pack_w(W, wbytes(p));
@@ -1063,8 +1192,8 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
   float* gxp = pd.out_nodes(true, N);
   float* gWp = pd.out_w();
   if (pd.st != TPCONV_SUCCESS) return pd.st;
-  if ((st = backward_core(p, g, pos, xp, Wp, gop, saved_state, grad_x ? gxp : nullptr, grad_W ? gWp : nullptr,
-                          grad_pos, pd.rest(), s)) != TPCONV_SUCCESS)
+  if ((st = backward_core(p, g, pos, xp, Wp, radial_w, gop, saved_state, grad_x ? gxp : nullptr,
+                          grad_W ? gWp : nullptr, grad_pos, grad_radial_w, pd.rest(), s)) != TPCONV_SUCCESS)
     return st;
   pd.unpack_nodes(gxp, grad_x, true, N);
   pd.unpack_w(gWp, grad_W);
@@ -1075,10 +1204,19 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
                                      const void* W, const float* grad_out, const float* gg_pos, float* d_W,
                                      float* d_x, float* d_grad_out, float* d_pos, void* ws, size_t ws_bytes,
                                      void* stream) {
-  if (!plan) return TPCONV_ERROR_INVALID_VALUE;
+  return tpconv_double_backward_mlp(plan, g, pos, x, W, nullptr, grad_out, gg_pos, d_W, d_x, d_grad_out, d_pos,
+                                    nullptr, ws, ws_bytes, stream);
+}
+
+tpconv_status tpconv_double_backward_mlp(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                                         const void* W, const float* radial_w, const float* grad_out,
+                                         const float* gg_pos, float* d_W, float* d_x, float* d_grad_out,
+                                         float* d_pos, float* d_radial_w, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || (plan->plan.radial_mlp != 0) != (radial_w != nullptr)) return TPCONV_ERROR_INVALID_VALUE;
+  if (d_radial_w && !radial_w) return TPCONV_ERROR_INVALID_VALUE;
   tpconv_status st = check_graph(g, d_x != nullptr);
   if (st != TPCONV_SUCCESS) return st;
-  if (!d_W && !d_x && !d_grad_out && !d_pos) return TPCONV_ERROR_INVALID_VALUE;
+  if (!d_W && !d_x && !d_grad_out && !d_pos && !d_radial_w) return TPCONV_ERROR_INVALID_VALUE;
   const Plan& p = plan->plan;
   const int64_t N = g->num_nodes;
   if (N > 0 && (!pos || !x || !W || !grad_out || !gg_pos)) return TPCONV_ERROR_INVALID_VALUE;
@@ -1087,11 +1225,13 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
   if (need > 0 && (!ws || ws_bytes < need)) return TPCONV_ERROR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N == 0) {
-    if (d_W) return dev(launch_fill(d_W, (int64_t)w_elems_caller(p), 0.f, s));
+    if (d_W && (st = dev(launch_fill(d_W, (int64_t)w_elems_caller(p), 0.f, s))) != TPCONV_SUCCESS) return st;
+    if (d_radial_w) return dev(launch_fill(d_radial_w, (int64_t)p.K * p.K, 0.f, s));
     return TPCONV_SUCCESS;
   }
   if (!p.ragged)
-    return double_backward_core(p, g, pos, x, W, grad_out, gg_pos, d_W, d_x, d_grad_out, d_pos, ws, s);
+    return double_backward_core(p, g, pos, x, W, radial_w, grad_out, gg_pos, d_W, d_x, d_grad_out, d_pos,
+                                d_radial_w, ws, s);
   Padded pd(p, ws, s);
   const void* xp = pd.pack_nodes(x, true, xbytes(p), N);
   const void* Wp = pd.pack_w(W, wbytes(p));
@@ -1100,8 +1240,9 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
   float* dWp = pd.out_w();
   float* dgp = pd.out_nodes(false, N);
   if (pd.st != TPCONV_SUCCESS) return pd.st;
-  if ((st = double_backward_core(p, g, pos, xp, Wp, gop, gg_pos, d_W ? dWp : nullptr, d_x ? dxp : nullptr,
-                                 d_grad_out ? dgp : nullptr, d_pos, pd.rest(), s)) != TPCONV_SUCCESS)
+  if ((st = double_backward_core(p, g, pos, xp, Wp, radial_w, gop, gg_pos, d_W ? dWp : nullptr,
+                                 d_x ? dxp : nullptr, d_grad_out ? dgp : nullptr, d_pos, d_radial_w, pd.rest(),
+                                 s)) != TPCONV_SUCCESS)
     return st;
   pd.unpack_w(dWp, d_W);
   pd.unpack_nodes(dxp, d_x, true, N);

@@ -150,6 +150,55 @@ __device__ __forceinline__ void radial2(float d, float inv_cutoff, float pref, i
   }
 }
 
+// Radial MLP on the basis, in place: the basis values B, B', B'' (from
+// radial / radial2) become those of the network's last hidden layer,
+//   z_k = sum_j A[k K + j] B_j,  R_k = silu(z_k),  R'_k = silu'(z_k) z'_k,
+//   R''_k = silu''(z_k) z'_k^2 + silu'(z_k) z''_k,   silu(z) = z sigmoid(z),
+// or, with col = j >= 0, their derivatives with respect to A[k, j] (what the
+// weight gradient of the network needs): R_k = silu'(z_k) B_j and
+// R'_k = silu''(z_k) z'_k B_j + silu'(z_k) B'_j.  ORDER: how many derivatives
+// in d are carried (0: R, 1: R and R', 2: R, R' and R'', col < 0 only).  At
+// the cutoff and beyond B = 0, so R = R' = R'' = 0; at d = 0, B' = B'' = 0.
+template <int K, int ORDER>
+__device__ __forceinline__ void mlp_radial(const float* __restrict__ A, int col, float* R, float* dR, float* d2R) {
+  float B[K], B1[ORDER >= 1 ? K : 1], B2[ORDER >= 2 ? K : 1];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    B[j] = R[j];
+    if constexpr (ORDER >= 1) B1[j] = dR[j];
+    if constexpr (ORDER >= 2) B2[j] = d2R[j];
+  }
+  // B_col and B'_col by selects (a register array is never indexed at run time)
+  float bc = 0.f, bc1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    bc = j == col ? B[j] : bc;
+    if constexpr (ORDER >= 1) bc1 = j == col ? B1[j] : bc1;
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    float z = 0.f, z1 = 0.f, z2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const float a = A[k * K + j];
+      z = __builtin_fmaf(a, B[j], z);
+      if constexpr (ORDER >= 1) z1 = __builtin_fmaf(a, B1[j], z1);
+      if constexpr (ORDER >= 2) z2 = __builtin_fmaf(a, B2[j], z2);
+    }
+    const float sg = 1.f / (1.f + __expf(-z));
+    const float s1 = sg * (1.f + z * (1.f - sg));
+    const float s2 = sg * (1.f - sg) * (2.f + z * (1.f - 2.f * sg));
+    if (col < 0) {
+      R[k] = z * sg;
+      if constexpr (ORDER >= 1) dR[k] = s1 * z1;
+      if constexpr (ORDER >= 2) d2R[k] = s2 * z1 * z1 + s1 * z2;
+    } else {
+      R[k] = s1 * bc;
+      if constexpr (ORDER >= 1) dR[k] = s2 * z1 * bc + s1 * bc1;
+    }
+  }
+}
+
 // Real harmonics of a unit vector (x, y, z), component normalised, rows l^2 + l + m.
 template <int L>
 __device__ __forceinline__ void sh_eval(float x, float y, float z, float* Y) {

@@ -54,6 +54,8 @@ struct StreamArgs {
   const int32_t* nbr;   // [E] neighbour of each edge
   const float* pos;     // [N][3]
   const float* ggpos;   // [N][3] tangent (kJvp, kSndT)
+  const float* mlp;     // [K][K] weights of the radial MLP (NULL: the fixed basis feeds W directly)
+  int32_t mlp_col;      // -1: the MLP's radial functions; j >= 0: their derivatives w.r.t. A[k][j]
   const void* feat;     // gathered features as bf16 [N][feat_rows][feat_cs]: the hi plane of split fp32, or bf16
   const void* feat_lo;  // lo bf16 plane of fp32 features split into hi + lo (NULL: bf16 features)
   float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
@@ -190,6 +192,29 @@ hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 // Zeroes rows [row_off, row_off + nrows) of every node of a [N][D][C] tensor.
 hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
+
+// Per-k dot products of two states in the receiver-state layout (group g:
+// rows (v, m), row length cols = K * cpk, column (k, q, c) = k * cpk + q * C + c):
+//   out[k * out_stride + out_col] = sum_g sum_rows sum_{col: col / cpk = k} a[..] b[..]
+// Pass 1: one block per chunk of rows_per_chunk rows of a group writes its
+// column sums to part; pass 2: one block per k sums them in a fixed order.
+struct StateDotArgs {
+  int32_t ngroups, K;
+  int32_t rows_per_chunk;
+  int32_t out_col, out_stride;
+  int32_t nchunks[kMaxGroups];
+  int32_t chunk_begin[kMaxGroups];  // first block of the group in pass 1
+  int32_t cols[kMaxGroups];
+  int32_t cpk[kMaxGroups];
+  int64_t rows[kMaxGroups];
+  int64_t base[kMaxGroups];       // element offset of the group's state
+  int64_t part_base[kMaxGroups];  // float offset of the group's column sums
+  const float* a;
+  const float* b;
+  float* part;
+  float* out;
+};
+hipError_t launch_state_dot(const StateDotArgs& a, hipStream_t s);
 // hi[i] = bf16(x[i]), lo[i] = bf16(x[i] - hi[i]) (round to nearest even), as raw bf16 bits.
 // bf16 planes of rows x C features with channel stride CS >= C, zero-padded:
 // fp32 features split into hi + lo, bf16 features copied into hi (lo unused).

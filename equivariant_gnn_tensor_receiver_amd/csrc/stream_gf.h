@@ -125,6 +125,7 @@ struct GfWave {
       }
       float R[K], dR[K];
       radial<K, TAN>(d, a.cutoff, a.inv_cutoff, a.pref, a.env_p, a.env_a, a.env_b, a.env_c, a.env_d, R, dR);
+      if (a.mlp) mlp_radial<K, TAN ? 1 : 0>(a.mlp, a.mlp_col, R, dR, nullptr);
       sh_eval<LMAX>(ux, uy, uz, y);
       L.noff[e] = (uint32_t)nbr * nodebytes;
       if constexpr (TAN) {

@@ -66,6 +66,7 @@ __device__ __forceinline__ void edge_prep(const StreamArgs& a, int self, float p
   }
   float R[K], dR[K];
   radial<K, DER>(d, a.cutoff, a.inv_cutoff, a.pref, a.env_p, a.env_a, a.env_b, a.env_c, a.env_d, R, dR);
+  if (a.mlp) mlp_radial<K, DER ? 1 : 0>(a.mlp, -1, R, dR, nullptr);
   float Y[NSH];
   sh_eval<LMAX>(ux, uy, uz, Y);
   L.nbr[j] = nb;

@@ -143,6 +143,7 @@ __device__ __forceinline__ void edge_prep_hess(const StreamArgs& a, int self, fl
   }
   float R[K], dR[K], d2R[K];
   radial2<K>(d, a.inv_cutoff, a.pref, a.env_p, a.env_a, a.env_b, a.env_c, a.env_d, R, dR, d2R);
+  if (a.mlp) mlp_radial<K, 2>(a.mlp, -1, R, dR, d2R);
   float Y[NSH], G[NSH][3], HP[NSH][3];
   sh_eval<LMAX>(ux, uy, uz, Y);
   sh_poly_grad<LMAX>(ux, uy, uz, G);

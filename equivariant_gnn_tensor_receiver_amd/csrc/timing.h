@@ -9,7 +9,7 @@ namespace tpconv {
 enum KernelClass : int {
   kcStreamFwd = 0, kcStreamJvp, kcStreamSnd, kcStreamSndT, kcStreamBwdPos,
   kcGemmOut, kcGemmGs, kcGemmGx, kcGemmGw, kcGwReduce, kcFill, kcGraph,
-  kcCwContract, kcCwGw, kcCwReduce, kcStreamHess, kcCount
+  kcCwContract, kcCwGw, kcCwReduce, kcStreamHess, kcStateDot, kcCount
 };
 
 // While timing is enabled, brackets the launches issued in its lifetime with

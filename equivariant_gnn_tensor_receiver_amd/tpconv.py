@@ -28,9 +28,10 @@ EXPORTS = ("tpconv_plan_create", "tpconv_plan_destroy", "tpconv_plan_info", "tpc
            "tpconv_plan_cg", "tpconv_workspace_size", "tpconv_state_size", "tpconv_graph_prepare",
            "tpconv_forward", "tpconv_backward", "tpconv_double_backward", "tpconv_status_string",
            "tpconv_kernel_timing", "tpconv_kernel_timing_read", "tpconv_forward_static", "tpconv_graph_order",
-           "tpconv_plan_features")
+           "tpconv_plan_features", "tpconv_forward_mlp", "tpconv_backward_mlp", "tpconv_double_backward_mlp")
 KERNELS = ("stream_fwd", "stream_jvp", "stream_snd", "stream_sndt", "stream_bwdpos", "gemm_out", "gemm_gs",
-           "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce", "stream_hess")
+           "gemm_gx", "gemm_gw", "gw_reduce", "fill", "graph", "cw_contract", "cw_gw", "cw_reduce", "stream_hess",
+           "state_dot")
 
 
 class TpconvError(RuntimeError):
@@ -42,7 +43,7 @@ class TpconvError(RuntimeError):
 class TpconvDesc(ctypes.Structure):
     _fields_ = [("irreps_in", c_char_p), ("irreps_out", c_char_p), ("sh_lmax", c_int32), ("num_basis", c_int32),
                 ("cutoff", c_float), ("envelope_p", c_int32), ("x_dtype", c_int32), ("w_dtype", c_int32),
-                ("connection", c_int32)]
+                ("connection", c_int32), ("radial_mlp", c_int32)]
 
 
 class TpconvGraph(ctypes.Structure):
@@ -75,6 +76,10 @@ def _lib():
         L.tpconv_forward_static.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P]
         L.tpconv_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, c_size_t, P]
         L.tpconv_double_backward.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, P, c_size_t, P]
+        L.tpconv_forward_mlp.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, c_size_t, P]
+        L.tpconv_backward_mlp.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]
+        L.tpconv_double_backward_mlp.argtypes = [P, POINTER(TpconvGraph), P, P, P, P, P, P, P, P, P, P, P, P,
+                                                 c_size_t, P]
         L.tpconv_kernel_timing.argtypes = [c_int32]
         L.tpconv_kernel_timing_read.argtypes = [c_int32, POINTER(c_int64), POINTER(c_double)]
         L.tpconv_status_string.argtypes = [c_int32]
@@ -107,11 +112,12 @@ class Plan:
 
     def __init__(self, irreps_in: str, irreps_out: str, sh_lmax: int, num_basis: int, cutoff: float = 5.0,
                  envelope_p: int = 6, x_dtype: int = TPCONV_F32, w_dtype: int = TPCONV_F32,
-                 connection: int = FULLY_CONNECTED):
+                 connection: int = FULLY_CONNECTED, radial_mlp: bool = False):
         self._keep = (irreps_in.encode(), irreps_out.encode())
         desc = TpconvDesc(self._keep[0], self._keep[1], sh_lmax, num_basis, cutoff, envelope_p, x_dtype, w_dtype,
-                          connection)
+                          connection, int(radial_mlp))
         self.connection = connection
+        self.radial_mlp = bool(radial_mlp)
         h = c_void_p()
         _check(_lib().tpconv_plan_create(ctypes.byref(h), ctypes.byref(desc)), "tpconv_plan_create")
         self.handle = h
@@ -286,7 +292,17 @@ def tpconv_graph_order(plan: Plan, graph: Graph, pos, stream=None) -> Graph:
     return graph._with(node_order=order)
 
 
-def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=None, workspace=None, stream=None):
+def _check_radial(plan, radial_w, dev):
+    import torch
+
+    if plan.radial_mlp != (radial_w is not None):
+        raise ValueError("radial_w must be given exactly for plans created with radial_mlp=True")
+    _require(radial_w, "radial_w", torch.float32, plan.num_basis ** 2, dev)
+
+
+def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=None, workspace=None, stream=None,
+                   radial_w=None):
+    """radial_w: the [K][K] weights of the radial MLP for plans created with radial_mlp=True."""
     import torch
 
     dev = pos.device
@@ -295,6 +311,7 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
         out = torch.empty(plan.out_shape(N), dtype=torch.float32, device=dev)
         _keep_for_stream(stream, out)
     _check_inputs(plan, graph, pos, x, W, out=(out, plan.feat_out))
+    _check_radial(plan, radial_w, dev)
     _require(saved_state, "saved_state", torch.float32, plan.state_size(N) // 4, dev)
     if workspace is None:
         need = plan.workspace_size(OP_FORWARD if saved_state is None else OP_FORWARD_SAVED, N, graph.num_edges)
@@ -304,8 +321,13 @@ def tpconv_forward(plan: Plan, graph: Graph, pos, x, W, out=None, saved_state=No
     _require(workspace, "workspace", None, None, dev)
     g = graph.c()
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib().tpconv_forward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(out),
-                                 _ptr(saved_state), _ptr(workspace), nbytes, _stream(stream)), "tpconv_forward")
+    if plan.radial_mlp:
+        _check(_lib().tpconv_forward_mlp(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(radial_w),
+                                         _ptr(out), _ptr(saved_state), _ptr(workspace), nbytes, _stream(stream)),
+               "tpconv_forward_mlp")
+    else:
+        _check(_lib().tpconv_forward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(out),
+                                     _ptr(saved_state), _ptr(workspace), nbytes, _stream(stream)), "tpconv_forward")
     return out
 
 
@@ -320,7 +342,10 @@ def tpconv_forward_static(plan: Plan, graph: Graph, pos, x, W, out, stream=None)
 
 
 def tpconv_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, saved_state=None, want=("x", "W", "pos"),
-                    workspace=None, stream=None, grad_x=None, grad_W=None, grad_pos=None):
+                    workspace=None, stream=None, grad_x=None, grad_W=None, grad_pos=None, radial_w=None,
+                    grad_radial_w=None):
+    """(grad_x, grad_W, grad_pos) for the names in `want`; with the radial MLP
+    (radial_w given) also grad_radial_w, requested as "radial_w"."""
     import torch
 
     dev = pos.device
@@ -331,26 +356,40 @@ def tpconv_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, saved_state=N
         grad_W = torch.empty(plan.w_shape, dtype=torch.float32, device=dev)
     if grad_pos is None and "pos" in want:
         grad_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
-    _keep_for_stream(stream, grad_x, grad_W, grad_pos)
+    K = plan.num_basis
+    if grad_radial_w is None and "radial_w" in want and plan.radial_mlp:
+        grad_radial_w = torch.empty((K, K), dtype=torch.float32, device=dev)
+    _keep_for_stream(stream, grad_x, grad_W, grad_pos, grad_radial_w)
     _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.feat_out), grad_x=(grad_x, plan.feat_in),
                   grad_pos=(grad_pos, 3))
+    _check_radial(plan, radial_w, dev)
     _require(grad_W, "grad_W", torch.float32, plan.w_numel, dev)
+    _require(grad_radial_w, "grad_radial_w", torch.float32, K * K, dev)
     _require(saved_state, "saved_state", torch.float32, plan.state_size(N) // 4, dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_BACKWARD, N, graph.num_edges), dev)
         _keep_for_stream(stream, workspace)
     _require(workspace, "workspace", None, None, dev)
     g = graph.c()
+    nbytes = workspace.numel() * workspace.element_size()
+    if plan.radial_mlp:
+        _check(_lib().tpconv_backward_mlp(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(radial_w),
+                                          _ptr(grad_out), _ptr(saved_state), _ptr(grad_x), _ptr(grad_W),
+                                          _ptr(grad_pos), _ptr(grad_radial_w), _ptr(workspace), nbytes,
+                                          _stream(stream)), "tpconv_backward_mlp")
+        return grad_x, grad_W, grad_pos, grad_radial_w
     _check(_lib().tpconv_backward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W), _ptr(grad_out),
                                   _ptr(saved_state), _ptr(grad_x), _ptr(grad_W), _ptr(grad_pos), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)), "tpconv_backward")
+                                  nbytes, _stream(stream)), "tpconv_backward")
     return grad_x, grad_W, grad_pos
 
 
 def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos, want=("W", "x", "grad_out", "pos"),
-                           workspace=None, stream=None, d_W=None, d_x=None, d_grad_out=None, d_pos=None):
+                           workspace=None, stream=None, d_W=None, d_x=None, d_grad_out=None, d_pos=None,
+                           radial_w=None, d_radial_w=None):
     """Gradients of sum_n <gg_pos[n], grad_pos[n]>: (d_W, d_x, d_grad_out, d_pos) for the names in
-    `want` ("W", "x", "grad_out", "pos"); the others are None."""
+    `want` ("W", "x", "grad_out", "pos"); the others are None.  With the radial
+    MLP (radial_w given) also d_radial_w, requested as "radial_w"."""
     import torch
 
     dev = pos.device
@@ -363,19 +402,30 @@ def tpconv_double_backward(plan: Plan, graph: Graph, pos, x, W, grad_out, gg_pos
         d_grad_out = torch.empty(plan.out_shape(N), dtype=torch.float32, device=dev)
     if d_pos is None and "pos" in want:
         d_pos = torch.empty((N, 3), dtype=torch.float32, device=dev)
-    _keep_for_stream(stream, d_W, d_x, d_grad_out, d_pos)
+    K = plan.num_basis
+    if d_radial_w is None and "radial_w" in want and plan.radial_mlp:
+        d_radial_w = torch.empty((K, K), dtype=torch.float32, device=dev)
+    _keep_for_stream(stream, d_W, d_x, d_grad_out, d_pos, d_radial_w)
     _check_inputs(plan, graph, pos, x, W, grad_out=(grad_out, plan.feat_out), gg_pos=(gg_pos, 3),
                   d_x=(d_x, plan.feat_in), d_grad_out=(d_grad_out, plan.feat_out), d_pos=(d_pos, 3))
+    _check_radial(plan, radial_w, dev)
     _require(d_W, "d_W", torch.float32, plan.w_numel, dev)
+    _require(d_radial_w, "d_radial_w", torch.float32, K * K, dev)
     if workspace is None:
         workspace = _workspace(plan.workspace_size(OP_DOUBLE_BACKWARD, N, graph.num_edges), dev)
         _keep_for_stream(stream, workspace)
     _require(workspace, "workspace", None, None, dev)
     g = graph.c()
+    nbytes = workspace.numel() * workspace.element_size()
+    if plan.radial_mlp:
+        _check(_lib().tpconv_double_backward_mlp(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W),
+                                                 _ptr(radial_w), _ptr(grad_out), _ptr(gg_pos), _ptr(d_W), _ptr(d_x),
+                                                 _ptr(d_grad_out), _ptr(d_pos), _ptr(d_radial_w), _ptr(workspace),
+                                                 nbytes, _stream(stream)), "tpconv_double_backward_mlp")
+        return d_W, d_x, d_grad_out, d_pos, d_radial_w
     _check(_lib().tpconv_double_backward(plan.handle, ctypes.byref(g), _ptr(pos), _ptr(x), _ptr(W),
                                          _ptr(grad_out), _ptr(gg_pos), _ptr(d_W), _ptr(d_x), _ptr(d_grad_out),
-                                         _ptr(d_pos), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                         _stream(stream)),
+                                         _ptr(d_pos), _ptr(workspace), nbytes, _stream(stream)),
            "tpconv_double_backward")
     return d_W, d_x, d_grad_out, d_pos
 

@@ -112,6 +112,8 @@ typedef struct {
   int32_t x_dtype;        /* tpconv_dtype of x */
   int32_t w_dtype;        /* tpconv_dtype of W */
   int32_t connection;     /* tpconv_connection; 0 (fully connected) when zero-initialised */
+  int32_t radial_mlp;     /* 0: the K Bessel x envelope functions are the radial functions R_e[k];
+                             1: a radial MLP in front of them (the _mlp entry points below) */
 } tpconv_desc;
 
 typedef struct {
@@ -275,6 +277,38 @@ tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, co
 tpconv_status tpconv_forward_static(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
                                     const void* W, float* out, void* stream);
 
+/* Radial MLP front end.  The pages name learned radial networks only as the
+ * usual setting of the layer; the reading taken keeps the reassociation of
+ * the Sobek page's abstract intact: the network's last hidden layer is the K
+ * radial functions the node-sized state is built from, and its output layer
+ * folds into W.  For a plan created with desc.radial_mlp = 1,
+ *   R_e[k] = silu(z_ek),  z_ek = sum_j radial_w[k][j] B_j(d_e),  silu(z) = z / (1 + exp(-z)),
+ * with B the K Bessel x envelope functions (no bias: R vanishes with B at the
+ * cutoff).  radial_w: device fp32 [K][K], row k = output function k.  These
+ * entry points are tpconv_forward / _backward / _double_backward with the
+ * network in front; the plain ones reject such a plan, and these reject a
+ * plan without it (INVALID_VALUE).  The backward also returns
+ * grad_radial_w = dL/dradial_w [K][K] and the double backward
+ * d_radial_w = dL_F/dradial_w (each may be NULL), formed one column j at a
+ * time as <gS[k], S^(j)[k]>: S^(j) is the state (tangent state) streamed with
+ * R_e[k] replaced by dR_e[k]/dradial_w[k][j], so a requested weight gradient
+ * costs K more passes of the receiver stream.  Deterministic.  Channel-wise
+ * plans do not take the network (UNSUPPORTED at plan creation).  Workspace:
+ * tpconv_workspace_size of the same op (one more node-sized state and the
+ * dot partials for such plans). */
+tpconv_status tpconv_forward_mlp(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                                 const void* W, const float* radial_w, float* out, float* saved_state,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+tpconv_status tpconv_backward_mlp(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
+                                  const void* W, const float* radial_w, const float* grad_out,
+                                  const float* saved_state, float* grad_x, float* grad_W, float* grad_pos,
+                                  float* grad_radial_w, void* workspace, size_t workspace_bytes, void* stream);
+tpconv_status tpconv_double_backward_mlp(tpconv_plan plan, const tpconv_graph* g, const float* pos,
+                                         const void* x, const void* W, const float* radial_w,
+                                         const float* grad_out, const float* gg_pos, float* d_W, float* d_x,
+                                         float* d_grad_out, float* d_pos, float* d_radial_w, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /* Kernel classes for tpconv_kernel_timing_read. */
 typedef enum {
   TPCONV_KERNEL_STREAM_FWD = 0,    /* receiver stream: S */
@@ -293,7 +327,8 @@ typedef enum {
   TPCONV_KERNEL_CW_GW = 13,        /* channel-wise: grad_W partials (also d_W) */
   TPCONV_KERNEL_CW_REDUCE = 14,    /* channel-wise: ordered sum of the partials */
   TPCONV_KERNEL_STREAM_HESS = 15,  /* receiver stream: position derivative of the force loss */
-  TPCONV_KERNEL_COUNT = 16
+  TPCONV_KERNEL_STATE_DOT = 16,    /* per-k dot products of two states (radial MLP weight gradient) */
+  TPCONV_KERNEL_COUNT = 17
 } tpconv_kernel;
 
 /* Diagnostics for roofline measurements (not needed for computing).

@@ -37,7 +37,7 @@ class DeviceCase:
     """Seeded problem uploaded to cuda:0 plus the matching oracle Problem."""
 
     def __init__(self, irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype="f32",
-                 channelwise=False, w_dtype=None, env_p=6, ordered=True):
+                 channelwise=False, w_dtype=None, env_p=6, ordered=True, radial_mlp=False):
         import torch
 
         self.dev = torch.device("cuda:0")
@@ -45,7 +45,7 @@ class DeviceCase:
         xd = tp.TPCONV_BF16 if dtype == "bf16" else tp.TPCONV_F32
         wd = tp.TPCONV_BF16 if w_dtype == "bf16" else tp.TPCONV_F32
         conn = tp.CHANNELWISE if channelwise else tp.FULLY_CONNECTED
-        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, env_p, xd, wd, conn)
+        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, env_p, xd, wd, conn, radial_mlp)
         self.prob = otp.Problem(irreps_in, irreps_out, sh_lmax, K, envelope_p=env_p, channelwise=channelwise)
         assert self.plan.num_paths == self.prob.P
         assert tuple(self.plan.w_shape) == tuple(self.prob.w_shape)
@@ -64,6 +64,9 @@ class DeviceCase:
                 t["x"] = inputs.bf16_round(t["x"])
             if w_dtype == "bf16":
                 t["W"] = inputs.bf16_round(t["W"])
+        # weights of the radial MLP, from a generator of their own (the other draws stay as they are)
+        self.A = (np.random.default_rng(1234 + N).standard_normal((K, K)).astype(np.float32)
+                  * np.float32(1.5 / K ** 0.5)) if radial_mlp else None
         self.np = dict(pos=pos, rowptr=rowptr, senders=senders, **t)
         self.receivers = otp.csr_receivers(rowptr)
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
@@ -75,6 +78,8 @@ class DeviceCase:
         self.W = tp.to_device_bf16(t["W"], self.dev) if w_dtype == "bf16" else to(t["W"])
         self.g_out = to(t["g_out"])
         self.gg = to(t["gg_pos"])
+        self.A_dev = None if self.A is None else to(self.A)
+        self.mlp = {} if self.A is None else dict(radial_w=self.A_dev)
         g = tp.Graph(self.rowptr, self.senders)
         g.num_edges = len(senders)
         self.graph = tp.tpconv_graph_prepare(self.plan, g, validate=True)
@@ -84,7 +89,7 @@ class DeviceCase:
     def forward(self, **kw):
         import torch
 
-        out = tp.tpconv_forward(self.plan, self.graph, self.pos, self.x, self.W, **kw)
+        out = tp.tpconv_forward(self.plan, self.graph, self.pos, self.x, self.W, **self.mlp, **kw)
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
@@ -92,7 +97,9 @@ class DeviceCase:
         import torch
 
         go = self.g_out if g_out is None else g_out
-        r = tp.tpconv_backward(self.plan, self.graph, self.pos, self.x, self.W, go, **kw)
+        if self.A is not None and "want" not in kw:
+            kw["want"] = ("x", "W", "pos", "radial_w")
+        r = tp.tpconv_backward(self.plan, self.graph, self.pos, self.x, self.W, go, **self.mlp, **kw)
         torch.cuda.synchronize()
         return [None if a is None else a.cpu().numpy() for a in r]
 
@@ -100,7 +107,9 @@ class DeviceCase:
         import torch
 
         go = self.g_out if g_out is None else g_out
-        r = tp.tpconv_double_backward(self.plan, self.graph, self.pos, self.x, self.W, go, self.gg, **kw)
+        if self.A is not None and "want" not in kw:
+            kw["want"] = ("W", "x", "grad_out", "pos", "radial_w")
+        r = tp.tpconv_double_backward(self.plan, self.graph, self.pos, self.x, self.W, go, self.gg, **self.mlp, **kw)
         torch.cuda.synchronize()
         return [None if a is None else a.cpu().numpy() for a in r]
 
@@ -109,21 +118,24 @@ class DeviceCase:
         n = self.np
         snd = n["senders"] if snd is None else snd
         rcv = self.receivers if rcv is None else rcv
-        return otp.forward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], num_nodes=len(n["rowptr"]) - 1)
+        return otp.forward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], num_nodes=len(n["rowptr"]) - 1,
+                           radial_w=self.A)
 
     def o_backward(self, g_out, snd=None, rcv=None):
         n = self.np
         snd = n["senders"] if snd is None else snd
         rcv = self.receivers if rcv is None else rcv
-        return otp.backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out)
+        return otp.backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, radial_w=self.A)
 
     def o_double_backward(self, g_out, snd=None, rcv=None):
-        """Oracle (d_W, d_x, d_grad_out, d_pos)."""
+        """Oracle (d_W, d_x, d_grad_out, d_pos), and d_A with the radial MLP."""
         n = self.np
         snd = n["senders"] if snd is None else snd
         rcv = self.receivers if rcv is None else rcv
-        return otp.double_backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"]) + (
-            otp.double_backward_pos(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"]),)
+        r = otp.double_backward(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"], radial_w=self.A)
+        dp = otp.double_backward_pos(self.prob, n["pos"], snd, rcv, n["x"], n["W"], g_out, n["gg_pos"],
+                                     radial_w=self.A)
+        return tuple(r[:3]) + (dp,) + tuple(r[3:])
 
 
 def small_case(irreps_in, irreps_out, sh_lmax, K, N, deg, seed, dtype="f32", channelwise=False, w_dtype=None,

@@ -29,7 +29,7 @@ def header_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(tp.LIB_PATH)
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 20
     assert sorted(names) == sorted(tp.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
