@@ -13,7 +13,9 @@ for that workload, per-pass throughput, peak workspace bytes, the dominant
 kernel's roofline (algorithmic FLOPs or bytes per launch over its HIP-event
 duration) and the CPU oracle's throughput on a bounded sample; and under
 `per_config`, every configuration's forward and fwd+bwd (Force: each stage of
-its chain) edges/s with the whole-pass lower bound T_lb and T_lb / T_measured.
+its chain) edges/s with the whole-pass lower bound T_lb and T_lb / T_measured,
+and Molecular once more with the radial MLP in front of the streams
+(`molecular_radial_mlp`, its backward including the MLP's weight gradient).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload edge_scaling]
 """
@@ -223,8 +225,12 @@ def cpu_baseline(w, data, sample_edges):
             "host": host}
 
 
-def run_workload(name, steps, warmup, detail):
-    """Time one workload; returns its report (and the oracle inputs when `detail`)."""
+def run_workload(name, steps, warmup, detail, radial_mlp=False):
+    """Time one workload; returns its report (and the oracle inputs when `detail`).
+
+    radial_mlp: put the radial MLP (one SiLU layer K wide on the basis) in
+    front of the streams; the backward and double backward then also return
+    its weight gradient."""
     import numpy as np
     import torch
 
@@ -234,7 +240,7 @@ def run_workload(name, steps, warmup, detail):
     w = inputs.WORKLOADS[name]
     dt_code = tp.TPCONV_BF16 if w.dtype == "bf16" else tp.TPCONV_F32
     plan = tp.Plan(w.irreps, w.irreps, w.lmax, w.num_basis, inputs.CUTOFF, 6, dt_code, dt_code,
-                   tp.CHANNELWISE if w.channelwise else tp.FULLY_CONNECTED)
+                   tp.CHANNELWISE if w.channelwise else tp.FULLY_CONNECTED, radial_mlp)
     t0 = time.perf_counter()
     data = inputs.make_workload(name, plan.num_paths)
     t_gen = time.perf_counter() - t0
@@ -247,6 +253,13 @@ def run_workload(name, steps, warmup, detail):
     else:
         x, W = to(data["x"]), to(data["W"])
     g_out, gg = to(data["g_out"]), to(data["gg_pos"])
+    K = w.num_basis
+    mlp = {}
+    if radial_mlp:
+        A = np.random.default_rng(w.seed + 100).standard_normal((K, K)).astype(np.float32) * np.float32(1.5 / K ** 0.5)
+        mlp = dict(radial_w=to(A), grad_radial_w=torch.empty((K, K), dtype=torch.float32, device=dev))
+    mlp_fwd = {"radial_w": mlp["radial_w"]} if mlp else {}
+    mlp_d = dict(radial_w=mlp["radial_w"], d_radial_w=torch.empty((K, K), dtype=torch.float32, device=dev)) if mlp else {}
     torch.cuda.synchronize()
     base_alloc = torch.cuda.memory_allocated()
 
@@ -274,23 +287,23 @@ def run_workload(name, steps, warmup, detail):
     force = name == "force"
 
     def fwd():
-        tp.tpconv_forward(plan, graph, pos, x, W, out=out, saved_state=S, workspace=ws_f)
+        tp.tpconv_forward(plan, graph, pos, x, W, out=out, saved_state=S, workspace=ws_f, **mlp_fwd)
 
     def bwd():
         if force:  # forces: the position gradient only
             tp.tpconv_backward(plan, graph, pos, x, W, g_out, saved_state=S, want=("pos",), workspace=ws_b,
-                               grad_pos=gp)
+                               grad_pos=gp, **mlp)
         else:
             tp.tpconv_backward(plan, graph, pos, x, W, g_out, saved_state=S, workspace=ws_b, grad_x=gx,
-                               grad_W=gW, grad_pos=gp)
+                               grad_W=gW, grad_pos=gp, **mlp)
 
     def dbwd():
         tp.tpconv_double_backward(plan, graph, pos, x, W, g_out, gg, want=("W", "x"), workspace=ws_d, d_W=dW,
-                                  d_x=dx)
+                                  d_x=dx, **mlp_d)
 
     def dbwd_all():
         tp.tpconv_double_backward(plan, graph, pos, x, W, g_out, gg, want=("W", "x", "grad_out", "pos"),
-                                  workspace=ws_d, d_W=dW, d_x=dx, d_grad_out=dg, d_pos=dpos)
+                                  workspace=ws_d, d_W=dW, d_x=dx, d_grad_out=dg, d_pos=dpos, **mlp_d)
 
     step_parts = [fwd] + ([bwd] if "bwd" in w.passes else []) + ([dbwd] if "dbwd" in w.passes else [])
 
@@ -415,6 +428,14 @@ def main():
             rep, _ = run_workload(name, max(5, args.steps // 2), 2, detail=False)
             per_config[name] = {k: rep[k] for k in ("num_edges", "step", "ms_per_step", "edges_per_s", "passes")}
             print(f"[bench] {name}: {rep['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+        # Molecular with the radial MLP in front of the streams (its backward
+        # also returns the MLP's weight gradient: K more receiver-stream
+        # passes); the bounds in `passes` are those of the plain layer
+        torch.cuda.empty_cache()
+        rep, _ = run_workload("molecular", max(5, args.steps // 2), 2, detail=False, radial_mlp=True)
+        per_config["molecular_radial_mlp"] = {k: rep[k] for k in ("num_edges", "step", "ms_per_step", "edges_per_s",
+                                                                  "passes")}
+        print(f"[bench] molecular_radial_mlp: {rep['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
 
     res = {
         "metric": METRIC,

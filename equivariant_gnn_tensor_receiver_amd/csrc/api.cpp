@@ -192,7 +192,8 @@ tpconv_status make_w_planes(const Plan& p, const void* W, Carver& c, WPlanes& ou
 size_t rows_part_elems(const Plan& p, int kind, int64_t N);
 
 // The per-k dot products of two receiver states (the radial MLP's weight
-// gradient): chunks of about 1/2048 of the state's rows, at least 16 rows.
+// gradient): chunks of about 1/2048 of the state's rows, at least 16 rows
+// (a few thousand blocks at every size).
 int dot_rows_per_chunk(const Plan& p, int64_t N) {
   int64_t rows = 0;
   for (const auto& g : p.out_groups)
@@ -205,7 +206,7 @@ void state_dot_setup(const Plan& p, int64_t N, StateDotArgs& d) {
   d.K = p.K;
   d.rows_per_chunk = dot_rows_per_chunk(p, N);
   d.out_stride = p.K;
-  int64_t blocks = 0, part = 0;
+  int64_t blocks = 0;
   for (const auto& g : p.out_groups) {
     if (g.paths.empty()) continue;
     const int i = d.ngroups++;
@@ -215,19 +216,16 @@ void state_dot_setup(const Plan& p, int64_t N, StateDotArgs& d) {
     d.base[i] = N * g.base_per_node;
     d.nchunks[i] = (int32_t)((d.rows[i] + d.rows_per_chunk - 1) / d.rows_per_chunk);
     d.chunk_begin[i] = (int32_t)blocks;
-    d.part_base[i] = part;
     blocks += d.nchunks[i];
-    part += (int64_t)d.nchunks[i] * d.cols[i];
   }
+  d.nblocks = (int32_t)blocks;
 }
 
 size_t dot_part_elems(const Plan& p, int64_t N) {
   if (!p.radial_mlp) return 0;
   StateDotArgs d;
   state_dot_setup(p, N, d);
-  size_t n = 0;
-  for (int g = 0; g < d.ngroups; ++g) n += (size_t)d.nchunks[g] * d.cols[g];
-  return n;
+  return (size_t)d.nblocks * p.K;
 }
 
 // out[k][col] = <a[k], b[k]> over the receiver-state layout, k = 0..K-1 (out: [K][K]).

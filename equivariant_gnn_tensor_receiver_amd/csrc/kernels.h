@@ -196,22 +196,22 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 // Per-k dot products of two states in the receiver-state layout (group g:
 // rows (v, m), row length cols = K * cpk, column (k, q, c) = k * cpk + q * C + c):
 //   out[k * out_stride + out_col] = sum_g sum_rows sum_{col: col / cpk = k} a[..] b[..]
-// Pass 1: one block per chunk of rows_per_chunk rows of a group writes its
-// column sums to part; pass 2: one block per k sums them in a fixed order.
+// Pass 1: one block per chunk of rows_per_chunk rows of a group writes its K
+// sums to part[block][k]; pass 2: one block per k adds them in block order.
 struct StateDotArgs {
   int32_t ngroups, K;
   int32_t rows_per_chunk;
   int32_t out_col, out_stride;
+  int32_t nblocks;                  // blocks of pass 1 (sum of nchunks)
   int32_t nchunks[kMaxGroups];
   int32_t chunk_begin[kMaxGroups];  // first block of the group in pass 1
   int32_t cols[kMaxGroups];
   int32_t cpk[kMaxGroups];
   int64_t rows[kMaxGroups];
-  int64_t base[kMaxGroups];       // element offset of the group's state
-  int64_t part_base[kMaxGroups];  // float offset of the group's column sums
+  int64_t base[kMaxGroups];  // element offset of the group's state
   const float* a;
   const float* b;
-  float* part;
+  float* part;  // [nblocks][K]
   float* out;
 };
 hipError_t launch_state_dot(const StateDotArgs& a, hipStream_t s);
