@@ -191,61 +191,11 @@ tpconv_status make_w_planes(const Plan& p, const void* W, Carver& c, WPlanes& ou
 
 size_t rows_part_elems(const Plan& p, int kind, int64_t N);
 
-// The per-k dot products of two receiver states (the radial MLP's weight
-// gradient): chunks of about 1/2048 of the state's rows, at least 16 rows
-// (a few thousand blocks at every size).
-int dot_rows_per_chunk(const Plan& p, int64_t N) {
-  int64_t rows = 0;
-  for (const auto& g : p.out_groups)
-    if (!g.paths.empty()) rows += N * (2 * g.l + 1);
-  return (int)std::max<int64_t>(16, (rows + 2047) / 2048);
-}
-
-void state_dot_setup(const Plan& p, int64_t N, StateDotArgs& d) {
-  std::memset(&d, 0, sizeof(d));
-  d.K = p.K;
-  d.rows_per_chunk = dot_rows_per_chunk(p, N);
-  d.out_stride = p.K;
-  int64_t blocks = 0;
-  for (const auto& g : p.out_groups) {
-    if (g.paths.empty()) continue;
-    const int i = d.ngroups++;
-    d.cpk[i] = (int32_t)g.paths.size() * p.C_in;
-    d.cols[i] = p.K * d.cpk[i];
-    d.rows[i] = N * (2 * g.l + 1);
-    d.base[i] = N * g.base_per_node;
-    d.nchunks[i] = (int32_t)((d.rows[i] + d.rows_per_chunk - 1) / d.rows_per_chunk);
-    d.chunk_begin[i] = (int32_t)blocks;
-    blocks += d.nchunks[i];
-  }
-  d.nblocks = (int32_t)blocks;
-}
-
+// Per-item sums of the radial MLP's weight gradient: the receiver stream in
+// its dot-out mode writes K values per work item (node, unit, slice).
 size_t dot_part_elems(const Plan& p, int64_t N) {
   if (!p.radial_mlp) return 0;
-  StateDotArgs d;
-  state_dot_setup(p, N, d);
-  return (size_t)d.nblocks * p.K;
-}
-
-// out[k][col] = <a[k], b[k]> over the receiver-state layout, k = 0..K-1 (out: [K][K]).
-tpconv_status state_dot(const Plan& p, int64_t N, const float* a, const float* b, float* part, float* out, int col,
-                        hipStream_t s) {
-  StateDotArgs d;
-  state_dot_setup(p, N, d);
-  d.a = a;
-  d.b = b;
-  d.part = part;
-  d.out = out;
-  d.out_col = col;
-  if (d.ngroups == 0) {  // no path reaches any output irrep: the state is empty
-    for (int k = 0; k < p.K; ++k) {
-      const tpconv_status st = dev(launch_fill(out + (int64_t)k * p.K + col, 1, 0.f, s));
-      if (st != TPCONV_SUCCESS) return st;
-    }
-    return TPCONV_SUCCESS;
-  }
-  return dev(launch_state_dot(d, s));
+  return (size_t)N * p.recv_units.size() * ((p.C_in + 31) / 32) * p.K;
 }
 
 size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
@@ -258,8 +208,7 @@ size_t ws_backward(const Plan& p, int64_t N) {
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
          align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) +
          g_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_BACKWARD) +
-         // radial MLP: the state streamed for one column of dL/dA, and the dot partials
-         (p.radial_mlp ? align_up(state_in_elems(p, N) * 4) + align_up(dot_part_elems(p, N) * 4) : 0);
+         align_up(dot_part_elems(p, N) * 4);  // radial MLP: per-item sums of dL/dA
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
@@ -800,7 +749,6 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   float* T = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
   float* xpart = c.take(rows_part_elems(p, kGemmGx, N));
-  float* Sj = p.radial_mlp ? c.take(state_in_elems(p, N)) : nullptr;
   float* dpart = c.take(dot_part_elems(p, N));
 
   const float* S = saved_state;
@@ -840,7 +788,8 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
     if (st != TPCONV_SUCCESS) return st;
   }
   // caller's stream: gS, the position gradient, and dL/dA of the radial MLP
-  // one column at a time, dL/dA[k, j] = <gS[k], S^(j)[k]>
+  // one column at a time, dL/dA[k, j] = <gS[k], S^(j)[k]>: the receiver
+  // stream forms S^(j) and writes only its dots with gS
   if (grad_rw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
   if (grad_pos) {
     st = run_pos_stream(p, kBwdPos, g, pos, x, xp, gp, wp, W, grad_out, nullptr, gS, grad_rw != nullptr, rw,
@@ -852,11 +801,12 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
     recv_args(p, a, g, pos, x, rw);
     a.mlp_col = j;
     use_planes(a, xp);
-    a.state = Sj;
+    a.dot_state = gS;
+    a.dot_part = dpart;
     if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
         TPCONV_SUCCESS)
       return st;
-    if ((st = state_dot(p, N, gS, Sj, dpart, grad_rw, j, s)) != TPCONV_SUCCESS) return st;
+    if ((st = dev(launch_dot_reduce(dpart, stream_items(a), p.K, grad_rw, j, p.K, s))) != TPCONV_SUCCESS) return st;
   }
   return fork.join();
 }
@@ -918,8 +868,7 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   }
   // caller's stream: gS, the Hessian term, and dL/dA of the radial MLP one
   // column at a time, dL/dA[k, j] = <gS[k], S_dot^(j)[k]> with the tangent
-  // state streamed in the mlp_col = j mode (after d_W and d_grad_out, which
-  // read S_dot earlier on this stream)
+  // state formed in the mlp_col = j mode and dotted with gS in the stream
   if (d_rw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
   if (d_pos) {
     st = run_pos_stream(p, kBwdHess, g, pos, x, xp, gp, wp, W, grad_out, gg_pos, gS, d_rw != nullptr, rw, d_pos, s);
@@ -931,11 +880,12 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
     a.mlp_col = j;
     use_planes(a, xp);
     a.ggpos = gg_pos;
-    a.state = Sd;
+    a.dot_state = gS;
+    a.dot_part = dpart;
     if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
         TPCONV_SUCCESS)
       return st;
-    if ((st = state_dot(p, N, gS, Sd, dpart, d_rw, j, s)) != TPCONV_SUCCESS) return st;
+    if ((st = dev(launch_dot_reduce(dpart, stream_items(a), p.K, d_rw, j, p.K, s))) != TPCONV_SUCCESS) return st;
   }
   return fork.join();
 }

@@ -56,6 +56,11 @@ struct StreamArgs {
   const float* ggpos;   // [N][3] tangent (kJvp, kSndT)
   const float* mlp;     // [K][K] weights of the radial MLP (NULL: the fixed basis feeds W directly)
   int32_t mlp_col;      // -1: the MLP's radial functions; j >= 0: their derivatives w.r.t. A[k][j]
+  // kFwd / kJvp: with dot_state set, each work item writes, instead of its
+  // state tile, the tile's dot with the same elements of dot_state per k to
+  // dot_part[item][k] (the radial MLP's weight gradient, one column at a time)
+  const float* dot_state;
+  float* dot_part;
   const void* feat;     // gathered features as bf16 [N][feat_rows][feat_cs]: the hi plane of split fp32, or bf16
   const void* feat_lo;  // lo bf16 plane of fp32 features split into hi + lo (NULL: bf16 features)
   float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
@@ -193,28 +198,10 @@ hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
-// Per-k dot products of two states in the receiver-state layout (group g:
-// rows (v, m), row length cols = K * cpk, column (k, q, c) = k * cpk + q * C + c):
-//   out[k * out_stride + out_col] = sum_g sum_rows sum_{col: col / cpk = k} a[..] b[..]
-// Pass 1: one block per chunk of rows_per_chunk rows of a group writes its K
-// sums to part[block][k]; pass 2: one block per k adds them in block order.
-struct StateDotArgs {
-  int32_t ngroups, K;
-  int32_t rows_per_chunk;
-  int32_t out_col, out_stride;
-  int32_t nblocks;                  // blocks of pass 1 (sum of nchunks)
-  int32_t nchunks[kMaxGroups];
-  int32_t chunk_begin[kMaxGroups];  // first block of the group in pass 1
-  int32_t cols[kMaxGroups];
-  int32_t cpk[kMaxGroups];
-  int64_t rows[kMaxGroups];
-  int64_t base[kMaxGroups];  // element offset of the group's state
-  const float* a;
-  const float* b;
-  float* part;  // [nblocks][K]
-  float* out;
-};
-hipError_t launch_state_dot(const StateDotArgs& a, hipStream_t s);
+// out[k * stride + col] = sum_b part[b * K + k] over b = 0..nblocks-1 in order
+// (one block per k): the per-item sums of the dot-out streams.
+hipError_t launch_dot_reduce(const float* part, int64_t nblocks, int K, float* out, int col, int stride,
+                             hipStream_t s);
 // hi[i] = bf16(x[i]), lo[i] = bf16(x[i] - hi[i]) (round to nearest even), as raw bf16 bits.
 // bf16 planes of rows x C features with channel stride CS >= C, zero-padded:
 // fp32 features split into hi + lo, bf16 features copied into hi (lo unused).

@@ -190,14 +190,70 @@ struct GfWave {
   // stride between consecutive k.
   template <class PK, int J>
   __device__ __forceinline__ static float* state_row(const StreamArgs& a, int unit, int node, int64_t& kstride) {
+    return state_row_of<PK, J>(a, a.state, unit, node, kstride);
+  }
+  template <class PK, int J, class F>
+  __device__ __forceinline__ static F* state_row_of(const StreamArgs& a, F* base, int unit, int node,
+                                                    int64_t& kstride) {
     constexpr int q = PK::member_of(J), o = PK::o_of(J), NO = PK::nout(q);
     const StreamPath& Q = a.paths[a.unit_paths[unit][q]];
     kstride = Q.cols_per_k;
-    return a.state + Q.state_base + (int64_t)(node * NO + o) * K * Q.cols_per_k + Q.q * a.C;
+    return base + Q.state_base + (int64_t)(node * NO + o) * K * Q.cols_per_k + Q.q * a.C;
+  }
+
+  // Radial MLP weight gradient: sum over this wave's state tile of the tile
+  // times the same elements of a.dot_state (the cotangent gS), per k, into
+  // a.dot_part[item][k] (item = this wave's work item).  Lane (i, g) holds
+  // k = kb + r, kb = 4 g (K = 16) or 4 (g & 1) (K = 8), for every tile; the
+  // lanes of one k are summed through LDS in a fixed order.
+  template <class PK, int TILES>
+  __device__ __forceinline__ static void dot_out(const StreamArgs& a, int unit, int node, int slice, uint32_t item,
+                                                 const floatx4 (&acc)[TILES][2], GfLds<K, TAN>& L) {
+    constexpr int TOT = PK::TOT;
+    const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+    const int C = a.C;
+    const int cp = slice * kGfSlice + 2 * i;
+    float d[4] = {0.f, 0.f, 0.f, 0.f};
+    static_for<TILES>([&](auto Tc) {
+      constexpr int T = decltype(Tc)::value;
+      constexpr int JA = K == 16 ? T : 2 * T;
+      constexpr int JB = K == 16 ? T : 2 * T + 1;
+      int64_t ks_a, ks_b = 0;
+      const float* pa = state_row_of<PK, JA>(a, a.dot_state, unit, node, ks_a);
+      const float* pb = nullptr;
+      if constexpr (JB < TOT) pb = state_row_of<PK, JB>(a, a.dot_state, unit, node, ks_b);
+      const bool upper = K == 8 && g >= 2;
+      if (upper && JB >= TOT) return;
+      const float* p = upper ? pb : pa;
+      const int64_t ks = upper ? ks_b : ks_a;
+      const int kb = K == 16 ? 4 * g : 4 * (g & 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (cp < C) d[r] = __builtin_fmaf(acc[T][0][r], p[(kb + r) * ks + cp], d[r]);
+        if (cp + 1 < C) d[r] = __builtin_fmaf(acc[T][1][r], p[(kb + r) * ks + cp + 1], d[r]);
+      }
+    });
+    float* red = &L.g[0][0];  // the coupling table is free after the last batch
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[4 * lane + r] = d[r];
+    wave_lds_sync();
+    if (lane < K) {
+      const int k = lane, r = k & 3;
+      float s = 0.f;
+      if constexpr (K == 16) {
+        for (int ii = 0; ii < 16; ++ii) s += red[4 * (16 * (k >> 2) + ii) + r];
+      } else {
+        for (int gg = k >> 2; gg < 4; gg += 2)
+          for (int ii = 0; ii < 16; ++ii) s += red[4 * (16 * gg + ii) + r];
+      }
+      a.dot_part[(int64_t)item * K + k] = s;
+    }
   }
 
   template <class... Ps>
-  __device__ __forceinline__ static void run(const StreamArgs& a, int node, int unit, int slice, GfLds<K, TAN>& L) {
+  __device__ __forceinline__ static void run(const StreamArgs& a, int node, int unit, int slice, uint32_t item,
+                                             GfLds<K, TAN>& L) {
     using PK = GfPack<RECV, Ps...>;
     constexpr int TOT = PK::TOT, NIN = PK::NIN;
     static_assert(TOT <= kGfMaxTot, "unit has more output components than the LDS table holds");
@@ -349,6 +405,10 @@ struct GfWave {
 
     // rows 4g..4g+3 of each tile: component j and k = (16 T + 4 g + r) % K;
     // column i of the even / odd tile: channel cp / cp + 1
+    if (a.dot_state) {  // the tile's dot with the cotangent instead of a store
+      dot_out<PK, TILES>(a, unit, node, slice, item, acc, L);
+      return;
+    }
     static_for<TILES>([&](auto Tc) {
       constexpr int T = decltype(Tc)::value;
       constexpr int JA = K == 16 ? T : 2 * T;       // rows of lane groups 0, 1 (K = 8) or all (K = 16)
@@ -380,10 +440,11 @@ struct GfWave {
 template <int LMAX, int K, int MODE, bool LO>
 struct GfUnitRunner {
   int node, unit, slice;
+  uint32_t item;
   GfLds<K, ModeTraits<MODE>::tangent>& L;
   template <class... Ps>
   __device__ __forceinline__ void run(const StreamArgs& a) {
-    GfWave<LMAX, K, MODE, LO>::template run<Ps...>(a, node, unit, slice, L);
+    GfWave<LMAX, K, MODE, LO>::template run<Ps...>(a, node, unit, slice, item, L);
   }
 };
 
@@ -411,7 +472,7 @@ void gf_kernel(const StreamArgs /*args*/, int64_t items) {
   const int lane = threadIdx.x & 63;
   L.g[kGfMaxTot][lane] = 0.f;
   if constexpr (TAN) L.gd[kGfMaxTot][lane] = 0.f;
-  GfUnitRunner<LMAX, K, MODE, LO> run{node, unit, slice, L};
+  GfUnitRunner<LMAX, K, MODE, LO> run{node, unit, slice, item, L};
   if constexpr (BUNDLED) {
     Bundles<LMAX, K, ModeTraits<MODE>::recv ? 0 : 1>::run(unit, run, a);
   } else {
