@@ -290,12 +290,13 @@ tpconv_status tpconv_forward_static(tpconv_plan plan, const tpconv_graph* g, con
  * plan without it (INVALID_VALUE).  The backward also returns
  * grad_radial_w = dL/dradial_w [K][K] and the double backward
  * d_radial_w = dL_F/dradial_w (each may be NULL), formed one column j at a
- * time as <gS[k], S^(j)[k]>: S^(j) is the state (tangent state) streamed with
- * R_e[k] replaced by dR_e[k]/dradial_w[k][j], so a requested weight gradient
- * costs K more passes of the receiver stream.  Deterministic.  Channel-wise
- * plans do not take the network (UNSUPPORTED at plan creation).  Workspace:
- * tpconv_workspace_size of the same op (one more node-sized state and the
- * dot partials for such plans). */
+ * time as <gS[k], S^(j)[k]>: S^(j) is the state (tangent state) with R_e[k]
+ * replaced by dR_e[k]/dradial_w[k][j], formed tile by tile in the receiver
+ * stream and dotted with gS there (never stored), so a requested weight
+ * gradient costs K more passes of the receiver stream.  Deterministic.
+ * Channel-wise plans do not take the network (UNSUPPORTED at plan creation).
+ * Workspace: tpconv_workspace_size of the same op (for such plans also K
+ * floats per stream work item: N x units x 32-channel slices). */
 tpconv_status tpconv_forward_mlp(tpconv_plan plan, const tpconv_graph* g, const float* pos, const void* x,
                                  const void* W, const float* radial_w, float* out, float* saved_state,
                                  void* workspace, size_t workspace_bytes, void* stream);
