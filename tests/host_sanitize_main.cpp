@@ -131,6 +131,46 @@ int main() {
   CHECK(tpconv_plan_create(&p, &d) == TPCONV_ERROR_INVALID_VALUE);
   d = desc("8x0e", "8x0e", 1, 8, 7);
   CHECK(tpconv_plan_create(&p, &d) == TPCONV_ERROR_INVALID_VALUE);
+  // radial MLP plans: the MLP entry points need radial_w, the plain ones refuse the plan
+  {
+    tpconv_desc dm = desc("8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8);
+    dm.radial_mlp = 1;
+    tpconv_plan pm = nullptr;
+    CHECK(tpconv_plan_create(&pm, &dm) == TPCONV_SUCCESS);
+    if (pm) {
+      exercise(pm);
+      tpconv_graph g{};
+      g.num_nodes = 4;
+      g.num_edges = 0;
+      float dummy[4];
+      CHECK(tpconv_forward(pm, &g, dummy, dummy, dummy, dummy, nullptr, nullptr, 0, nullptr) ==
+            TPCONV_ERROR_INVALID_VALUE);
+      CHECK(tpconv_forward_mlp(pm, &g, dummy, dummy, dummy, nullptr, dummy, nullptr, nullptr, 0, nullptr) ==
+            TPCONV_ERROR_INVALID_VALUE);
+      CHECK(tpconv_backward_mlp(pm, &g, dummy, dummy, dummy, dummy, dummy, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, 0, nullptr) == TPCONV_ERROR_INVALID_VALUE);
+      CHECK(tpconv_double_backward_mlp(pm, &g, dummy, dummy, dummy, nullptr, dummy, dummy, nullptr, nullptr,
+                                       nullptr, nullptr, dummy, nullptr, 0, nullptr) == TPCONV_ERROR_INVALID_VALUE);
+      size_t plain = 0, mlp = 0;
+      tpconv_plan pp = nullptr;
+      tpconv_desc dp = desc("8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8);
+      CHECK(tpconv_plan_create(&pp, &dp) == TPCONV_SUCCESS);
+      if (pp) {
+        CHECK(tpconv_workspace_size(pp, TPCONV_OP_BACKWARD, 1000, 5000, &plain) == TPCONV_SUCCESS);
+        CHECK(tpconv_workspace_size(pm, TPCONV_OP_BACKWARD, 1000, 5000, &mlp) == TPCONV_SUCCESS);
+        CHECK(mlp > plain);
+        CHECK(tpconv_forward_mlp(pp, &g, dummy, dummy, dummy, dummy, dummy, nullptr, nullptr, 0, nullptr) ==
+              TPCONV_ERROR_INVALID_VALUE);
+        tpconv_plan_destroy(pp);
+      }
+      tpconv_plan_destroy(pm);
+    }
+    dm.connection = TPCONV_CHANNELWISE;
+    CHECK(tpconv_plan_create(&pm, &dm) == TPCONV_ERROR_UNSUPPORTED);
+    dm.connection = 0;
+    dm.radial_mlp = 2;
+    CHECK(tpconv_plan_create(&pm, &dm) == TPCONV_ERROR_INVALID_VALUE);
+  }
   for (int s = 0; s <= 7; ++s) CHECK(tpconv_status_string((tpconv_status)s) != nullptr);
   CHECK(tpconv_status_string((tpconv_status)1234) != nullptr);
   CHECK(tpconv_plan_destroy(nullptr) != TPCONV_SUCCESS || true);
