@@ -95,3 +95,39 @@ def test_mlp_entry_point_rules():
     assert st == 1  # INVALID_VALUE
     with pytest.raises(tp.TpconvError):
         tp.Plan(ir, ir, 1, 8, connection=tp.CHANNELWISE, radial_mlp=True)
+
+
+@pytest.mark.slow
+def test_molecular_workload_with_mlp_sampled():
+    """Full-size Molecular with the radial MLP, as bench.py times it; the oracle
+    runs on the in-edges of 256 seeded receivers, with g_out masked to them
+    for the gradients (which are then exact sums over those edges)."""
+    import torch
+
+    w = inputs.WORKLOADS["molecular"]
+    say(f"[workload] molecular with radial MLP: N={w.num_nodes} deg={w.mean_degree} C={w.channels}")
+    pos, rowptr, senders, _, rng = inputs.make_graph(w)
+    case = DeviceCase(w.irreps, w.irreps, w.lmax, w.num_basis, pos, rowptr, senders, rng, w.dtype, radial_mlp=True)
+    vs = inputs.sample_receivers(w.num_nodes, 256, w.seed)
+    idx = np.concatenate([np.arange(rowptr[v], rowptr[v + 1]) for v in vs]).astype(np.int64)
+    snd = case.np["senders"][idx].astype(np.int64)
+    rcv = case.receivers[idx]
+    mask = np.zeros(w.num_nodes, dtype=np.float32)
+    mask[vs] = 1.0
+    g_masked = (case.np["g_out"] * mask[:, None, None]).astype(np.float32)
+    say(f"  sample {len(vs)} receivers / {len(idx)} edges")
+    out = case.forward()
+    e = rel_err(out[vs], case.o_forward(snd, rcv)[vs])
+    say(f"  fwd rel err {e:.2e}")
+    assert e <= FWD_TOL
+    go = torch.from_numpy(g_masked).to(case.dev)
+    got = case.backward(g_out=go)
+    ref = case.o_backward(g_masked, snd, rcv)
+    errs = [rel_err(a, b) for a, b in zip(got, ref)]
+    say("  g_x {:.2e} g_W {:.2e} g_pos {:.2e} g_A {:.2e}".format(*errs))
+    assert max(errs) <= GRAD_TOL
+    got = case.double_backward(g_out=go)
+    ref = case.o_double_backward(g_masked, snd, rcv)
+    errs = [rel_err(got[i], ref[i]) for i in (0, 1, 3, 4)] + [rel_err(got[2][vs], ref[2][vs])]
+    say("  d_W {:.2e} d_x {:.2e} d_pos {:.2e} d_A {:.2e} d_g_out {:.2e}".format(*errs))
+    assert max(errs) <= GRAD_TOL
