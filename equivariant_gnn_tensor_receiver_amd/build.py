@@ -47,7 +47,7 @@ UNITS = ([(f"stream_{n}", "stream_gf.hip", STREAM_FLAGS + [f"-DTP_MODE={m}", f"-
          + [(f"stream_{n}", "stream_pos.hip", STREAM_FLAGS + [f"-DTP_FT={t}", f"-DTP_HESS={h}",
                                                              f"-DTP_LAUNCHER=launch_stream_{n}"])
             for n, t, h in POS_VARIANTS]
-         + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("channelwise", ".hip"), ("graph", ".hip"), ("radial", ".hip"),
+         + [(u, u + ext, []) for u, ext in (("gemm", ".hip"), ("channelwise", ".hip"), ("graph", ".hip"), ("radial", ".hip"), ("fixed", ".hip"),
                                              ("scratch", ".hip"), ("ragged", ".hip"), ("api", ".cpp"),
                                              ("stream_dispatch", ".cpp"), ("plan", ".cpp"),
                                              ("timing", ".cpp"))])

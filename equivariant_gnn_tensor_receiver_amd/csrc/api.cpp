@@ -198,6 +198,23 @@ size_t dot_part_elems(const Plan& p, int64_t N) {
   return (size_t)N * p.recv_units.size() * ((p.C_in + 31) / 32) * p.K;
 }
 
+// Deterministic position gradients: 64-bit fixed-point sums [N][3] and two
+// scalars (the largest magnitude's bits and the shift).
+struct FixedBufs {
+  unsigned long long* acc = nullptr;
+  int32_t* tmp = nullptr;
+};
+size_t fixed_bytes(const Plan& p, int64_t N) {
+  return p.deterministic ? align_up((size_t)N * 3 * 8) + align_up(2 * 4) : 0;
+}
+FixedBufs take_fixed(const Plan& p, int64_t N, Carver& c) {
+  FixedBufs f;
+  if (!p.deterministic) return f;
+  f.acc = reinterpret_cast<unsigned long long*>(c.take((size_t)N * 6));
+  f.tmp = reinterpret_cast<int32_t*>(c.take(2));
+  return f;
+}
+
 size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
   return (have_saved ? 0 : align_up(state_in_elems(p, N) * 4)) + align_up(rows_part_elems(p, kGemmOut, N) * 4) +
          x_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_FORWARD);
@@ -208,7 +225,8 @@ size_t ws_backward(const Plan& p, int64_t N) {
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
          align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) +
          g_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_BACKWARD) +
-         align_up(dot_part_elems(p, N) * 4);  // radial MLP: per-item sums of dL/dA
+         align_up(dot_part_elems(p, N) * 4) +  // radial MLP: per-item sums of dL/dA
+         fixed_bytes(p, N);
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
@@ -216,7 +234,7 @@ size_t ws_double_backward(const Plan& p, int64_t N) {
   return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
          align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) +
          align_up(rows_part_elems(p, kGemmOut, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
-         pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD) + align_up(dot_part_elems(p, N) * 4);
+         pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD) + align_up(dot_part_elems(p, N) * 4) + fixed_bytes(p, N);
 }
 
 // Independent chains of one call (the position gradient, the input gradient
@@ -654,7 +672,7 @@ bool assign_pos_pairs(const Plan& p, StreamArgs& a) {
 tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, const float* pos, const void* x,
                              const Planes& xp, const Planes& gp, const WPlanes& wp, const void* W,
                              const float* grad_out, const float* gg_pos, float* gS, bool gs_ready, const float* rw,
-                             float* out, hipStream_t s) {
+                             const FixedBufs& fx, float* out, hipStream_t s) {
   const int64_t N = g->num_nodes;
   const bool cw = channelwise(p);
   tpconv_status st;
@@ -676,7 +694,23 @@ tpconv_status run_pos_stream(const Plan& p, int mode, const tpconv_graph* g, con
     a.gout = grad_out;
     a.gout_rows = p.D_out;
   }
-  return dev(launch_stream(mode, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s));
+  if ((st = dev(launch_stream(mode, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+          TPCONV_SUCCESS ||
+      !fx.acc)
+    return st;
+  // deterministic: the fp32 result sets the fixed-point shift, then the same
+  // stream again with exact 64-bit sums
+  uint32_t* maxbits = reinterpret_cast<uint32_t*>(fx.tmp);
+  int32_t* shift = fx.tmp + 1;
+  if ((st = dev(launch_fill(reinterpret_cast<float*>(maxbits), 1, 0.f, s))) != TPCONV_SUCCESS) return st;
+  if ((st = dev(launch_fixed_shift(out, 3 * N, maxbits, shift, s))) != TPCONV_SUCCESS) return st;
+  if ((st = dev(launch_fill(reinterpret_cast<float*>(fx.acc), 6 * N, 0.f, s))) != TPCONV_SUCCESS) return st;
+  a.gpos_fx = fx.acc;
+  a.fx_shift = shift;
+  if ((st = dev(launch_stream(mode, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
+      TPCONV_SUCCESS)
+    return st;
+  return dev(launch_fixed_to_float(fx.acc, shift, out, 3 * N, s));
 }
 
 RaggedNodeMap node_map(const Plan& p, bool in_side) {
@@ -750,6 +784,7 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   float* part = c.take(part_elems(p, N));
   float* xpart = c.take(rows_part_elems(p, kGemmGx, N));
   float* dpart = c.take(dot_part_elems(p, N));
+  const FixedBufs fx = take_fixed(p, N, c);
 
   const float* S = saved_state;
   Planes xp;
@@ -792,7 +827,7 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   // stream forms S^(j) and writes only its dots with gS
   if (grad_rw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
   if (grad_pos) {
-    st = run_pos_stream(p, kBwdPos, g, pos, x, xp, gp, wp, W, grad_out, nullptr, gS, grad_rw != nullptr, rw,
+    st = run_pos_stream(p, kBwdPos, g, pos, x, xp, gp, wp, W, grad_out, nullptr, gS, grad_rw != nullptr, rw, fx,
                         grad_pos, s);
     if (st != TPCONV_SUCCESS) return st;
   }
@@ -826,6 +861,7 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   float* xpart = c.take(rows_part_elems(p, kGemmGx, N));  // d_x (side stream)
   float* opart = c.take(rows_part_elems(p, kGemmOut, N));  // d_grad_out (caller's stream)
   float* dpart = c.take(dot_part_elems(p, N));
+  const FixedBufs fx = take_fixed(p, N, c);
   Planes xp;
   if (d_W || d_grad_out || d_pos || d_rw) {
     if ((st = make_planes(x, p.x_dtype == TPCONV_BF16, N, p.D_in, p.C_in, c, xp, s)) != TPCONV_SUCCESS) return st;
@@ -871,7 +907,8 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   // state formed in the mlp_col = j mode and dotted with gS in the stream
   if (d_rw && (st = run_gemm(p, kGemmGs, N, nullptr, &gp, wp, gS, nullptr, s)) != TPCONV_SUCCESS) return st;
   if (d_pos) {
-    st = run_pos_stream(p, kBwdHess, g, pos, x, xp, gp, wp, W, grad_out, gg_pos, gS, d_rw != nullptr, rw, d_pos, s);
+    st = run_pos_stream(p, kBwdHess, g, pos, x, xp, gp, wp, W, grad_out, gg_pos, gS, d_rw != nullptr, rw, fx, d_pos,
+                        s);
     if (st != TPCONV_SUCCESS) return st;
   }
   for (int j = 0; d_rw && j < p.K; ++j) {
@@ -959,6 +996,7 @@ tpconv_status tpconv_plan_create(tpconv_plan* out, const tpconv_desc* d) {
     int st = build_plan(d->irreps_in, d->irreps_out, d->sh_lmax, d->num_basis, d->cutoff, d->envelope_p,
                         d->x_dtype, d->w_dtype, d->connection, h->plan);
     if (st == TPCONV_SUCCESS && (d->radial_mlp < 0 || d->radial_mlp > 1)) st = TPCONV_ERROR_INVALID_VALUE;
+    if (st == TPCONV_SUCCESS && (d->deterministic < 0 || d->deterministic > 1)) st = TPCONV_ERROR_INVALID_VALUE;
     // the MLP's weight gradient contracts the state cotangent, which the
     // channel-wise passes never form
     if (st == TPCONV_SUCCESS && d->radial_mlp && d->connection == TPCONV_CHANNELWISE) st = TPCONV_ERROR_UNSUPPORTED;
@@ -967,6 +1005,7 @@ tpconv_status tpconv_plan_create(tpconv_plan* out, const tpconv_desc* d) {
       return (tpconv_status)st;
     }
     h->plan.radial_mlp = d->radial_mlp;
+    h->plan.deterministic = d->deterministic;
     *out = h;
     return TPCONV_SUCCESS;
   } catch (...) {

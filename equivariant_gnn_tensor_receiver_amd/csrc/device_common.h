@@ -150,6 +150,25 @@ __device__ __forceinline__ void radial2(float d, float inv_cutoff, float pref, i
   }
 }
 
+// v * 2^F as a 64-bit two's complement integer modulo 2^64: exact for the
+// bits of v at or above 2^-F, the lower ones dropped (toward zero).  Sums of
+// such values are exact modulo 2^64, so they do not depend on the order of
+// the additions; the result is right when the true sum times 2^F stays
+// within +-2^63.
+__device__ __forceinline__ unsigned long long to_fixed(float v, int F) {
+  const uint32_t bits = __float_as_uint(v);
+  const int e = (int)((bits >> 23) & 0xffu);
+  if (e == 0) return 0ull;  // zero and subnormals (far below any scale used)
+  const unsigned long long m = (unsigned long long)((bits & 0x7fffffu) | 0x800000u);
+  const int sh = e - 150 + F;  // v = m * 2^(e - 150)
+  unsigned long long q = 0ull;
+  if (sh >= 0)
+    q = sh < 64 ? m << sh : 0ull;
+  else
+    q = -sh < 64 ? m >> -sh : 0ull;
+  return (bits >> 31) ? 0ull - q : q;
+}
+
 // Radial MLP on the basis, in place: the basis values B, B', B'' (from
 // radial / radial2) become those of the network's last hidden layer,
 //   z_k = sum_j A[k K + j] B_j,  R_k = silu(z_k),  R'_k = silu'(z_k) z'_k,

@@ -61,6 +61,11 @@ struct StreamArgs {
   // dot_part[item][k] (the radial MLP's weight gradient, one column at a time)
   const float* dot_state;
   float* dot_part;
+  // position streams, deterministic mode: per-edge shares added as 64-bit
+  // fixed point (to_fixed with shift *fx_shift) to gpos_fx [N][3] instead of
+  // fp32 atomics to gpos
+  unsigned long long* gpos_fx;
+  const int32_t* fx_shift;
   const void* feat;     // gathered features as bf16 [N][feat_rows][feat_cs]: the hi plane of split fp32, or bf16
   const void* feat_lo;  // lo bf16 plane of fp32 features split into hi + lo (NULL: bf16 features)
   float* state;         // output state (kFwd, kJvp, kSnd, kSndT)
@@ -200,6 +205,12 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
 // out[k * stride + col] = sum_b part[b * K + k] over b = 0..nblocks-1 in order
 // (one block per k): the per-item sums of the dot-out streams.
+// Deterministic position gradients: the fixed-point shift from the largest
+// |g| of a first fp32 pass (F = 58 - ceil(log2 max|g|), five bits of headroom
+// for the exact sums), and the conversion of the fixed-point sums back.
+hipError_t launch_fixed_shift(const float* g, int64_t n, uint32_t* maxbits, int32_t* shift, hipStream_t s);
+hipError_t launch_fixed_to_float(const unsigned long long* acc, const int32_t* shift, float* out, int64_t n,
+                                 hipStream_t s);
 hipError_t launch_dot_reduce(const float* part, int64_t nblocks, int K, float* out, int col, int stride,
                              hipStream_t s);
 // hi[i] = bf16(x[i]), lo[i] = bf16(x[i] - hi[i]) (round to nearest even), as raw bf16 bits.

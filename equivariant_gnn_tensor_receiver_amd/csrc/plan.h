@@ -66,6 +66,7 @@ struct Plan {
   int x_dtype = 0, w_dtype = 0;
   int connection = 0;  // tpconv_connection
   int radial_mlp = 0;  // 1: the radial basis feeds a K x K SiLU layer whose outputs are the radial functions
+  int deterministic = 0;  // 1: position gradients summed in exact fixed point (bitwise reproducible)
   int C_in = 0, C_out = 0, D_in = 0, D_out = 0, P = 0;
   int lmax = 0;  // max degree over irreps and harmonics
   std::vector<Path> paths;

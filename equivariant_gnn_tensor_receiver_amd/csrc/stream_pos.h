@@ -571,9 +571,16 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
         v2 += gr[ww][lane][2];
       }
       const int64_t s3 = 3 * (int64_t)S.geo.nbr[lane];
-      atomicAdd(&a.gpos[s3 + 0], v0);
-      atomicAdd(&a.gpos[s3 + 1], v1);
-      atomicAdd(&a.gpos[s3 + 2], v2);
+      if (a.gpos_fx) {
+        const int F = *a.fx_shift;
+        atomicAdd(&a.gpos_fx[s3 + 0], to_fixed(v0, F));
+        atomicAdd(&a.gpos_fx[s3 + 1], to_fixed(v1, F));
+        atomicAdd(&a.gpos_fx[s3 + 2], to_fixed(v2, F));
+      } else {
+        atomicAdd(&a.gpos[s3 + 0], v0);
+        atomicAdd(&a.gpos[s3 + 1], v1);
+        atomicAdd(&a.gpos[s3 + 2], v2);
+      }
       vs0 -= v0;
       vs1 -= v1;
       vs2 -= v2;
@@ -584,9 +591,16 @@ void pos_kernel(const StreamArgs /*args*/, int64_t nodes) {
     vs1 = channel_sum(vs1, 6);
     vs2 = channel_sum(vs2, 6);
     if (lane == 0 && e1 > e0) {
-      atomicAdd(&a.gpos[3 * (int64_t)node + 0], vs0);
-      atomicAdd(&a.gpos[3 * (int64_t)node + 1], vs1);
-      atomicAdd(&a.gpos[3 * (int64_t)node + 2], vs2);
+      if (a.gpos_fx) {
+        const int F = *a.fx_shift;
+        atomicAdd(&a.gpos_fx[3 * (int64_t)node + 0], to_fixed(vs0, F));
+        atomicAdd(&a.gpos_fx[3 * (int64_t)node + 1], to_fixed(vs1, F));
+        atomicAdd(&a.gpos_fx[3 * (int64_t)node + 2], to_fixed(vs2, F));
+      } else {
+        atomicAdd(&a.gpos[3 * (int64_t)node + 0], vs0);
+        atomicAdd(&a.gpos[3 * (int64_t)node + 1], vs1);
+        atomicAdd(&a.gpos[3 * (int64_t)node + 2], vs2);
+      }
     }
   }
 }

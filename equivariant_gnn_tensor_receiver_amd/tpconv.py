@@ -43,7 +43,7 @@ class TpconvError(RuntimeError):
 class TpconvDesc(ctypes.Structure):
     _fields_ = [("irreps_in", c_char_p), ("irreps_out", c_char_p), ("sh_lmax", c_int32), ("num_basis", c_int32),
                 ("cutoff", c_float), ("envelope_p", c_int32), ("x_dtype", c_int32), ("w_dtype", c_int32),
-                ("connection", c_int32), ("radial_mlp", c_int32)]
+                ("connection", c_int32), ("radial_mlp", c_int32), ("deterministic", c_int32)]
 
 
 class TpconvGraph(ctypes.Structure):
@@ -112,10 +112,10 @@ class Plan:
 
     def __init__(self, irreps_in: str, irreps_out: str, sh_lmax: int, num_basis: int, cutoff: float = 5.0,
                  envelope_p: int = 6, x_dtype: int = TPCONV_F32, w_dtype: int = TPCONV_F32,
-                 connection: int = FULLY_CONNECTED, radial_mlp: bool = False):
+                 connection: int = FULLY_CONNECTED, radial_mlp: bool = False, deterministic: bool = False):
         self._keep = (irreps_in.encode(), irreps_out.encode())
         desc = TpconvDesc(self._keep[0], self._keep[1], sh_lmax, num_basis, cutoff, envelope_p, x_dtype, w_dtype,
-                          connection, int(radial_mlp))
+                          connection, int(radial_mlp), int(deterministic))
         self.connection = connection
         self.radial_mlp = bool(radial_mlp)
         h = c_void_p()

@@ -114,6 +114,10 @@ typedef struct {
   int32_t connection;     /* tpconv_connection; 0 (fully connected) when zero-initialised */
   int32_t radial_mlp;     /* 0: the K Bessel x envelope functions are the radial functions R_e[k];
                              1: a radial MLP in front of them (the _mlp entry points below) */
+  int32_t deterministic;  /* 1: grad_pos and d_pos bitwise reproducible: every per-edge share is
+                             added as an exact 64-bit fixed-point integer (shift from a first fp32
+                             pass over the same stream, so the position stream runs twice);
+                             0: fp32 atomic additions, last bits may vary between runs */
 } tpconv_desc;
 
 typedef struct {
@@ -234,7 +238,8 @@ tpconv_status tpconv_forward(tpconv_plan plan, const tpconv_graph* g, const floa
  * saved_state: S from tpconv_forward with the same inputs, or NULL to recompute it.
  * Needs g->csc_colptr / csc_receivers when grad_x is requested.  grad_pos sums
  * per-edge contributions with fp32 atomics, so its last bits may vary between
- * runs; grad_x and grad_W are deterministic. */
+ * runs unless the plan was created with desc.deterministic = 1; grad_x and
+ * grad_W are deterministic. */
 tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos,
                               const void* x, const void* W, const float* grad_out,
                               const float* saved_state, float* grad_x, float* grad_W,
@@ -252,7 +257,8 @@ tpconv_status tpconv_backward(tpconv_plan plan, const tpconv_graph* g, const flo
  * grad_out, and its position derivative is the Hessian term
  * dL/dpos[s] += H_e phi_e, dL/dpos[v] -= H_e phi_e (H_e the Hessian of eps_e
  * w.r.t. r_e, from R'' and the second derivatives of the harmonics), summed
- * with fp32 atomics like grad_pos.  Needs the CSC view when d_x is requested.
+ * like grad_pos (fp32 atomics, or exact fixed point for deterministic plans).
+ * Needs the CSC view when d_x is requested.
  * Errors as tpconv_backward. */
 tpconv_status tpconv_double_backward(tpconv_plan plan, const tpconv_graph* g, const float* pos,
                                      const void* x, const void* W, const float* grad_out,

@@ -37,7 +37,7 @@ class DeviceCase:
     """Seeded problem uploaded to cuda:0 plus the matching oracle Problem."""
 
     def __init__(self, irreps_in, irreps_out, sh_lmax, K, pos, rowptr, senders, rng, dtype="f32",
-                 channelwise=False, w_dtype=None, env_p=6, ordered=True, radial_mlp=False):
+                 channelwise=False, w_dtype=None, env_p=6, ordered=True, radial_mlp=False, deterministic=False):
         import torch
 
         self.dev = torch.device("cuda:0")
@@ -45,7 +45,8 @@ class DeviceCase:
         xd = tp.TPCONV_BF16 if dtype == "bf16" else tp.TPCONV_F32
         wd = tp.TPCONV_BF16 if w_dtype == "bf16" else tp.TPCONV_F32
         conn = tp.CHANNELWISE if channelwise else tp.FULLY_CONNECTED
-        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, env_p, xd, wd, conn, radial_mlp)
+        self.plan = tp.Plan(irreps_in, irreps_out, sh_lmax, K, inputs.CUTOFF, env_p, xd, wd, conn, radial_mlp,
+                            deterministic)
         self.prob = otp.Problem(irreps_in, irreps_out, sh_lmax, K, envelope_p=env_p, channelwise=channelwise)
         assert self.plan.num_paths == self.prob.P
         assert tuple(self.plan.w_shape) == tuple(self.prob.w_shape)

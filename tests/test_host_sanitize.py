@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "equivariant_gnn_tensor_receiver_amd", "csrc")
 BUILD = os.path.join(ROOT, "_build")
 HOST_UNITS = ("api", "plan", "timing", "stream_dispatch")
-DEVICE_UNITS = ("gemm", "channelwise", "graph", "scratch", "ragged", "radial")
+DEVICE_UNITS = ("gemm", "channelwise", "graph", "scratch", "ragged", "radial", "fixed")
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
 
 
