@@ -165,6 +165,27 @@ int main() {
       }
       tpconv_plan_destroy(pm);
     }
+    // deterministic position gradients: more workspace (the fixed-point sums), invalid flags rejected
+    tpconv_desc dd = desc("8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8);
+    dd.deterministic = 1;
+    tpconv_plan pd = nullptr;
+    CHECK(tpconv_plan_create(&pd, &dd) == TPCONV_SUCCESS);
+    if (pd) {
+      exercise(pd);
+      size_t det = 0, plain = 0;
+      tpconv_desc dp = desc("8x0e+8x1o+8x2e", "8x0e+8x1o+8x2e", 2, 8);
+      tpconv_plan pp = nullptr;
+      CHECK(tpconv_plan_create(&pp, &dp) == TPCONV_SUCCESS);
+      if (pp) {
+        CHECK(tpconv_workspace_size(pd, TPCONV_OP_DOUBLE_BACKWARD, 1000, 5000, &det) == TPCONV_SUCCESS);
+        CHECK(tpconv_workspace_size(pp, TPCONV_OP_DOUBLE_BACKWARD, 1000, 5000, &plain) == TPCONV_SUCCESS);
+        CHECK(det >= plain + 1000 * 3 * 8);
+        tpconv_plan_destroy(pp);
+      }
+      tpconv_plan_destroy(pd);
+    }
+    dd.deterministic = -1;
+    CHECK(tpconv_plan_create(&pd, &dd) == TPCONV_ERROR_INVALID_VALUE);
     dm.connection = TPCONV_CHANNELWISE;
     CHECK(tpconv_plan_create(&pm, &dm) == TPCONV_ERROR_UNSUPPORTED);
     dm.connection = 0;
