@@ -52,9 +52,10 @@ def test_deterministic_position_gradients(spec):
 
 
 @pytest.mark.slow
-def test_deterministic_molecular_full_size():
-    say("[workload] molecular, deterministic grad_pos in index and Morton order")
-    w = inputs.WORKLOADS["molecular"]
+@pytest.mark.parametrize("name", ["molecular", "edge_scaling"])
+def test_deterministic_full_size(name):
+    say(f"[workload] {name}, deterministic grad_pos in index and Morton order")
+    w = inputs.WORKLOADS[name]
     pos, rowptr, senders, _, rng = inputs.make_graph(w)
     a = DeviceCase(w.irreps, w.irreps, w.lmax, w.num_basis, pos, rowptr, senders, rng, w.dtype, ordered=False,
                    deterministic=True)
