@@ -221,9 +221,11 @@ size_t ws_forward(const Plan& p, int64_t N, bool have_saved) {
 }
 
 size_t ws_backward(const Plan& p, int64_t N) {
-  // S (recomputed when not saved), gS (fully connected only), T, gW partials, planes of x and g_out
-  return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
-         align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) +
+  // S (recomputed when not saved) and T share one buffer: the weight gradient
+  // reads S before the sender stream writes T, both on the side stream.
+  // Then gS (fully connected only), gW partials, planes of x and g_out.
+  return align_up(std::max(state_in_elems(p, N), state_out_elems(p, N)) * 4) +
+         (channelwise(p) ? 0 : align_up(state_in_elems(p, N) * 4)) + align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) +
          g_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_BACKWARD) +
          align_up(dot_part_elems(p, N) * 4) +  // radial MLP: per-item sums of dL/dA
          fixed_bytes(p, N);
@@ -778,9 +780,9 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   const bool cw = channelwise(p);
   tpconv_status st;
   Carver c(ws);
-  float* S_ws = c.take(state_in_elems(p, N));
+  float* S_ws = c.take(std::max(state_in_elems(p, N), state_out_elems(p, N)));
+  float* T = S_ws;  // written only after the weight gradient has read S (same stream)
   float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
-  float* T = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
   float* xpart = c.take(rows_part_elems(p, kGemmGx, N));
   float* dpart = c.take(dot_part_elems(p, N));
@@ -808,6 +810,10 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
   if ((grad_x || grad_pos || grad_rw) && (st = make_w_planes(p, W, c, wp, s)) != TPCONV_SUCCESS) return st;
   Fork fork(s);
   const hipStream_t s2 = fork.side();
+  if (grad_W) {  // side stream: gW = S^T g_out, first (T reuses the buffer of a recomputed S)
+    st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, gp, part, grad_W, s2);
+    if (st != TPCONV_SUCCESS) return st;
+  }
   if (grad_x) {  // side stream: sender stream, then g_x = T W^T
     StreamArgs a;
     send_args(p, a, g, pos, grad_out, rw);
@@ -816,10 +822,6 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
     if ((st = dev(launch_stream(kSnd, p.lmax, p.K, false, a, stream_items(a), s2))) != TPCONV_SUCCESS) return st;
     st = cw ? run_cw_contract(p, false, N, T, W, grad_x, s2)
             : run_gemm(p, kGemmGx, N, T, nullptr, wp, grad_x, xpart, s2);
-    if (st != TPCONV_SUCCESS) return st;
-  }
-  if (grad_W) {  // side stream: gW = S^T g_out
-    st = cw ? run_cw_gw(p, N, S, grad_out, part, grad_W, s2) : run_gw(p, N, S, gp, part, grad_W, s2);
     if (st != TPCONV_SUCCESS) return st;
   }
   // caller's stream: gS, the position gradient, and dL/dA of the radial MLP
