@@ -113,11 +113,12 @@ def stats_table(run_dir: str, title: str, command: str) -> str:
     for r in rows:
         out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-    out += ["", "Kernel template arguments: stream_kernel<LMAX, K, MODE, feature type, bundled units> with MODE",
-            "0 = receiver state (forward), 1 = tangent state, 2 = sender state, 3 = sender tangent state;",
-            "pos_kernel<LMAX, K, fp32 features split hi+lo, 16-byte loads, bundled units, Hessian term>;",
-            "gemm_kernel<KIND, row tiles, column tiles, indices per lane half, bf16 W, vector loads> with KIND",
-            "0 = out, 1 = gS, 2 = g_x, 3 = gW."]
+    out += ["", "Kernel template arguments: gf_kernel<LMAX, K, MODE, fp32 features split hi+lo, bundled units>",
+            "with MODE 0 = receiver state (forward), 1 = tangent state, 2 = sender state, 3 = sender",
+            "tangent state; pos_kernel<LMAX, K, fp32 features split hi+lo, 16-byte loads, bundled units,",
+            "Hessian term>; gemm_lds_kernel<KIND, column tiles, indices per lane half, W split hi+lo, waves",
+            "per block> and gemm_kernel<KIND, row tiles, column tiles, indices per lane half, W split hi+lo,",
+            "vector loads> with KIND 0 = out, 1 = gS, 2 = g_x, 3 = gW."]
     return "\n".join(out) + "\n"
 
 
