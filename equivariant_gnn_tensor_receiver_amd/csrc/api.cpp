@@ -232,8 +232,9 @@ size_t ws_backward(const Plan& p, int64_t N) {
 }
 
 size_t ws_double_backward(const Plan& p, int64_t N) {
-  // S_dot, T_dot, weight partials, gS (fully connected), planes of x and g_out
-  return align_up(state_in_elems(p, N) * 4) * (channelwise(p) ? 1 : 2) + align_up(state_out_elems(p, N) * 4) +
+  // S_dot (gS, fully connected, reuses it once its contractions are done; one
+  // stream), T_dot, weight partials, planes of x and g_out
+  return align_up(state_in_elems(p, N) * 4) + align_up(state_out_elems(p, N) * 4) +
          align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) +
          align_up(rows_part_elems(p, kGemmOut, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
          pad_bytes(p, N, TPCONV_OP_DOUBLE_BACKWARD) + align_up(dot_part_elems(p, N) * 4) + fixed_bytes(p, N);
@@ -859,7 +860,9 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
   float* Sd = c.take(state_in_elems(p, N));
   float* Td = c.take(state_out_elems(p, N));
   float* part = c.take(part_elems(p, N));
-  float* gS = cw ? nullptr : c.take(state_in_elems(p, N));
+  // gS is written on the caller's stream after d_W and d_grad_out have read
+  // S_dot there, and nothing reads S_dot after it: the two share one buffer
+  float* gS = cw ? nullptr : Sd;
   float* xpart = c.take(rows_part_elems(p, kGemmGx, N));  // d_x (side stream)
   float* opart = c.take(rows_part_elems(p, kGemmOut, N));  // d_grad_out (caller's stream)
   float* dpart = c.take(dot_part_elems(p, N));
