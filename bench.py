@@ -18,6 +18,8 @@ and Molecular once more with the radial MLP in front of the streams
 (`molecular_radial_mlp`, its backward including the MLP's weight gradient).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload edge_scaling]
+       [--no-all-configs] [--no-cpu-baseline] [--radial-mlp (with --no-cpu-baseline: the
+       named workload alone, with the radial MLP)]
 """
 from __future__ import annotations
 
@@ -376,14 +378,16 @@ def run_workload(name, steps, warmup, detail, radial_mlp=False):
     dom = max((k for k in ktimes if k in alg), key=lambda k: ktimes[k][1])
     n_dom, ms_dom = ktimes[dom]
     roof = roofline_for(dom, alg[dom][0], alg[dom][1], ms_dom / n_dom, w_bf16)
-    roof["traffic"] = load_traffic(w.name, dom)
+    # the counter files are taken on the plain layer
+    roof["traffic"] = None if radial_mlp else load_traffic(w.name, dom)
     rep.update({
         "value": E / (ms_step * 1e-3),
         "dtype": "f32" if w.dtype == "f32" else "bf16-in/f32",
         "config": {"workload": w.name, "num_nodes": N, "num_edges": E, "mean_degree": round(E / N, 2),
                    "irreps": w.irreps, "sh_lmax": w.lmax, "num_basis": w.num_basis, "paths": plan.num_paths,
                    "step": "+".join(w.passes), "cutoff": inputs.CUTOFF, "box": round(data["box"], 4),
-                   "connection": "channelwise" if w.channelwise else "fully_connected"},
+                   "connection": "channelwise" if w.channelwise else "fully_connected",
+                   **({"radial_mlp": True} if radial_mlp else {})},
         "peak_bytes": {"workspace_fwd": plan.workspace_size(tp.OP_FORWARD, N, E),
                        "workspace_fwd_saved": plan.workspace_size(tp.OP_FORWARD_SAVED, N, E),
                        "workspace_bwd": plan.workspace_size(tp.OP_BACKWARD, N, E),
@@ -408,17 +412,25 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-configs", action="store_true", help="time the headline workload only")
     ap.add_argument("--cpu-sample-edges", type=int, default=0, help="oracle sample size (edges); 0 = default")
+    ap.add_argument("--radial-mlp", action="store_true",
+                    help="time the headline workload with the radial MLP (needs --no-cpu-baseline)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single "
               "MI355X; sharding over several GPUs is not built)", file=sys.stderr)
         sys.exit(2)
 
+    if args.radial_mlp and not args.no_cpu_baseline:
+        print("--radial-mlp times the MLP variant only; the oracle baseline is the plain layer: add "
+              "--no-cpu-baseline", file=sys.stderr)
+        sys.exit(2)
+
     import torch
 
-    head, oracle_inputs = run_workload(args.workload, args.steps, args.warmup, detail=True)
+    head, oracle_inputs = run_workload(args.workload, args.steps, args.warmup, detail=True,
+                                       radial_mlp=args.radial_mlp)
     per_config = {}
-    if not args.no_all_configs:
+    if not args.no_all_configs and not args.radial_mlp:
         for name in CONFIG_ORDER:
             if name == args.workload:
                 per_config[name] = {k: head[k] for k in ("num_edges", "step", "ms_per_step", "edges_per_s",

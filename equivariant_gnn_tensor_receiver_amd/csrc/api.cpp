@@ -194,8 +194,8 @@ size_t rows_part_elems(const Plan& p, int kind, int64_t N);
 // Per-item sums of the radial MLP's weight gradient: the receiver stream in
 // its dot-out mode writes K values per work item (node, unit, slice).
 size_t dot_part_elems(const Plan& p, int64_t N) {
-  if (!p.radial_mlp) return 0;
-  return (size_t)N * p.recv_units.size() * ((p.C_in + 31) / 32) * p.K;
+  if (!p.radial_mlp) return 0;  // one slab of per-item sums per column of A
+  return (size_t)N * p.recv_units.size() * ((p.C_in + 31) / 32) * p.K * p.K;
 }
 
 // Deterministic position gradients: 64-bit fixed-point sums [N][3] and two
@@ -225,8 +225,9 @@ size_t ws_backward(const Plan& p, int64_t N) {
   // reads S before the sender stream writes T, both on the side stream.
   // Then gS (fully connected only), gW partials, planes of x and g_out.
   return align_up(std::max(state_in_elems(p, N), state_out_elems(p, N)) * 4) +
-         (channelwise(p) ? 0 : align_up(state_in_elems(p, N) * 4)) + align_up(part_elems(p, N) * 4) + align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) +
-         g_planes(p, N) + w_planes(p) + pad_bytes(p, N, TPCONV_OP_BACKWARD) +
+         (channelwise(p) ? 0 : align_up(state_in_elems(p, N) * 4)) + align_up(part_elems(p, N) * 4) +
+         align_up(rows_part_elems(p, kGemmGx, N) * 4) + x_planes(p, N) + g_planes(p, N) + w_planes(p) +
+         pad_bytes(p, N, TPCONV_OP_BACKWARD) +
          align_up(dot_part_elems(p, N) * 4) +  // radial MLP: per-item sums of dL/dA
          fixed_bytes(p, N);
 }
@@ -834,18 +835,21 @@ tpconv_status backward_core(const Plan& p, const tpconv_graph* g, const float* p
                         grad_pos, s);
     if (st != TPCONV_SUCCESS) return st;
   }
+  int64_t dot_items = 0;
   for (int j = 0; grad_rw && j < p.K; ++j) {
     StreamArgs a;
     recv_args(p, a, g, pos, x, rw);
     a.mlp_col = j;
     use_planes(a, xp);
+    dot_items = stream_items(a);
+    if ((size_t)dot_items * p.K * p.K > dot_part_elems(p, N)) return TPCONV_ERROR_INVALID_VALUE;
     a.dot_state = gS;
-    a.dot_part = dpart;
-    if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
-        TPCONV_SUCCESS)
+    a.dot_part = dpart + (size_t)j * dot_items * p.K;
+    if ((st = dev(launch_stream(kFwd, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, dot_items, s))) != TPCONV_SUCCESS)
       return st;
-    if ((st = dev(launch_dot_reduce(dpart, stream_items(a), p.K, grad_rw, j, p.K, s))) != TPCONV_SUCCESS) return st;
   }
+  if (grad_rw && (st = dev(launch_dot_reduce(dpart, dot_items, p.K, p.K, grad_rw, p.K, s))) != TPCONV_SUCCESS)
+    return st;
   return fork.join();
 }
 
@@ -916,19 +920,22 @@ tpconv_status double_backward_core(const Plan& p, const tpconv_graph* g, const f
                         s);
     if (st != TPCONV_SUCCESS) return st;
   }
+  int64_t dot_items = 0;
   for (int j = 0; d_rw && j < p.K; ++j) {
     StreamArgs a;
     recv_args(p, a, g, pos, x, rw);
     a.mlp_col = j;
     use_planes(a, xp);
     a.ggpos = gg_pos;
+    dot_items = stream_items(a);
+    if ((size_t)dot_items * p.K * p.K > dot_part_elems(p, N)) return TPCONV_ERROR_INVALID_VALUE;
     a.dot_state = gS;
-    a.dot_part = dpart;
-    if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, stream_items(a), s))) !=
-        TPCONV_SUCCESS)
+    a.dot_part = dpart + (size_t)j * dot_items * p.K;
+    if ((st = dev(launch_stream(kJvp, p.lmax, p.K, p.x_dtype == TPCONV_BF16, a, dot_items, s))) != TPCONV_SUCCESS)
       return st;
-    if ((st = dev(launch_dot_reduce(dpart, stream_items(a), p.K, d_rw, j, p.K, s))) != TPCONV_SUCCESS) return st;
   }
+  if (d_rw && (st = dev(launch_dot_reduce(dpart, dot_items, p.K, p.K, d_rw, p.K, s))) != TPCONV_SUCCESS)
+    return st;
   return fork.join();
 }
 

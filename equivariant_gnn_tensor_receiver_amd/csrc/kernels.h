@@ -203,15 +203,16 @@ hipError_t launch_gw_reduce(const ReduceArgs& a, int64_t total, hipStream_t s);
 hipError_t launch_zero_rows(float* base, int64_t N, int D, int C, int row_off, int nrows, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
-// out[k * stride + col] = sum_b part[b * K + k] over b = 0..nblocks-1 in order
-// (one block per k): the per-item sums of the dot-out streams.
+// out[k * stride + j] = sum over b < nitems of part[(j * nitems + b) * K + k]
+// for the columns j < ncols, in a fixed order: the per-item sums of the
+// dot-out streams, one slab per column.
 // Deterministic position gradients: the fixed-point shift from the largest
 // |g| of a first fp32 pass (F = 58 - ceil(log2 max|g|), five bits of headroom
 // for the exact sums), and the conversion of the fixed-point sums back.
 hipError_t launch_fixed_shift(const float* g, int64_t n, uint32_t* maxbits, int32_t* shift, hipStream_t s);
 hipError_t launch_fixed_to_float(const unsigned long long* acc, const int32_t* shift, float* out, int64_t n,
                                  hipStream_t s);
-hipError_t launch_dot_reduce(const float* part, int64_t nblocks, int K, float* out, int col, int stride,
+hipError_t launch_dot_reduce(const float* part, int64_t nitems, int K, int ncols, float* out, int stride,
                              hipStream_t s);
 // hi[i] = bf16(x[i]), lo[i] = bf16(x[i] - hi[i]) (round to nearest even), as raw bf16 bits.
 // bf16 planes of rows x C features with channel stride CS >= C, zero-padded:

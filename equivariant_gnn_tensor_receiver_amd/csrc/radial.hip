@@ -8,8 +8,9 @@
 // for the force loss the tangent state takes the place of S ("Sobek" page,
 // abstract: the streaming form covers the backward and double backward with
 // node-sized state only).  The receiver stream forms S^(j) tile by tile in
-// registers and writes only each tile's dot with gS per k (dot_state mode);
-// this kernel adds those per-item sums in a fixed order.
+// registers and writes only each tile's dot with gS per k (dot_state mode),
+// column j into its own slab; this kernel adds the per-item sums of all
+// columns in one launch, in a fixed order.
 #include "kernels.h"
 #include "timing.h"
 
@@ -17,30 +18,43 @@ namespace tpconv {
 
 namespace {
 
-constexpr int kDotThreads = 256;
+constexpr int kDotThreads = 1024;
 
-__global__ __launch_bounds__(kDotThreads) void dot_reduce_kernel(const float* part, int64_t nblocks, int K,
-                                                                 float* out, int col, int stride) {
+// One block per column j reads that column's slab [nitems][K] front to back
+// (coalesced).  Thread t < R*K (R a power of two) owns k = t % K and adds the
+// slab entries t, t + R*K, t + 2*R*K, ... in that order; the R partial sums
+// of each k are then added by a fixed tree.  The result depends on nothing
+// but the inputs.
+__global__ __launch_bounds__(kDotThreads) void dot_reduce_kernel(const float* part, int64_t nitems, int K, int R,
+                                                                 float* out, int stride) {
   __shared__ float red[kDotThreads];
-  const int k = blockIdx.x;
+  const int j = blockIdx.x, t = threadIdx.x, T = R * K;
+  const int64_t n = nitems * K;
+  const float* slab = part + (int64_t)j * n;
   float acc = 0.f;
-  for (int64_t b = threadIdx.x; b < nblocks; b += kDotThreads) acc += part[b * K + k];
-  red[threadIdx.x] = acc;
+  if (t < T) {
+#pragma unroll 4
+    for (int64_t i = t; i < n; i += T) acc += slab[i];
+  }
+  red[t] = acc;
   __syncthreads();
-  for (int w = kDotThreads / 2; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+  for (int w = R / 2; w > 0; w >>= 1) {
+    if (t < w * K) red[t] += red[t + w * K];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[(int64_t)k * stride + col] = red[0];
+  if (t < K) out[(int64_t)t * stride + j] = red[t];
 }
 
 }  // namespace
 
-hipError_t launch_dot_reduce(const float* part, int64_t nblocks, int K, float* out, int col, int stride,
+hipError_t launch_dot_reduce(const float* part, int64_t nitems, int K, int ncols, float* out, int stride,
                              hipStream_t s) {
-  if (K <= 0 || nblocks < 0 || col < 0 || col >= stride || !out || (nblocks > 0 && !part)) return hipErrorInvalidValue;
+  if (K <= 0 || K > kDotThreads || nitems < 0 || ncols <= 0 || ncols > stride || !out || (nitems > 0 && !part))
+    return hipErrorInvalidValue;
+  int R = 1;
+  while (2 * R * K <= kDotThreads) R *= 2;
   TimingScope ts(kcStateDot, s);
-  hipLaunchKernelGGL(dot_reduce_kernel, dim3((unsigned)K), dim3(kDotThreads), 0, s, part, nblocks, K, out, col,
+  hipLaunchKernelGGL(dot_reduce_kernel, dim3((unsigned)ncols), dim3(kDotThreads), 0, s, part, nitems, K, R, out,
                      stride);
   return hipGetLastError();
 }
