@@ -204,50 +204,59 @@ struct GfWave {
   // Radial MLP weight gradient: sum over this wave's state tile of the tile
   // times the same elements of a.dot_state (the cotangent gS), per k, into
   // a.dot_part[item][k] (item = this wave's work item).  Lane (i, g) holds
-  // k = kb + r, kb = 4 g (K = 16) or 4 (g & 1) (K = 8), for every tile; the
-  // lanes of one k are summed through LDS in a fixed order.
+  // k = kb + r, kb = 4 g (K = 16) or 4 (g & 1) (K = 8), for every tile.  All
+  // loads are issued first, unconditionally (addresses clamped inside the
+  // node's rows, out-of-range terms masked to zero), then the lanes of one k
+  // are added by a fixed pattern of lane swaps.
   template <class PK, int TILES>
   __device__ __forceinline__ static void dot_out(const StreamArgs& a, int unit, int node, int slice, uint32_t item,
-                                                 const floatx4 (&acc)[TILES][2], GfLds<K, TAN>& L) {
+                                                 const floatx4 (&acc)[TILES][2], GfLds<K, TAN>& /*L*/) {
     constexpr int TOT = PK::TOT;
     const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
     const int C = a.C;
     const int cp = slice * kGfSlice + 2 * i;
-    float d[4] = {0.f, 0.f, 0.f, 0.f};
+    const int c0 = cp < C ? cp : C - 1, c1 = cp + 1 < C ? cp + 1 : C - 1;
+    const bool upper = K == 8 && g >= 2;
+    const int kb = K == 16 ? 4 * g : 4 * (g & 1);
+    float gv[TILES][4][2];
+    bool live[TILES];
     static_for<TILES>([&](auto Tc) {
       constexpr int T = decltype(Tc)::value;
       constexpr int JA = K == 16 ? T : 2 * T;
       constexpr int JB = K == 16 ? T : 2 * T + 1;
       int64_t ks_a, ks_b = 0;
       const float* pa = state_row_of<PK, JA>(a, a.dot_state, unit, node, ks_a);
-      const float* pb = nullptr;
+      const float* pb = pa;
       if constexpr (JB < TOT) pb = state_row_of<PK, JB>(a, a.dot_state, unit, node, ks_b);
-      const bool upper = K == 8 && g >= 2;
-      if (upper && JB >= TOT) return;
-      const float* p = upper ? pb : pa;
-      const int64_t ks = upper ? ks_b : ks_a;
-      const int kb = K == 16 ? 4 * g : 4 * (g & 1);
+      live[T] = !(upper && JB >= TOT);
+      const bool use_b = upper && JB < TOT;
+      const float* p = use_b ? pb : pa;
+      const int64_t ks = use_b ? ks_b : ks_a;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (cp < C) d[r] = __builtin_fmaf(acc[T][0][r], p[(kb + r) * ks + cp], d[r]);
-        if (cp + 1 < C) d[r] = __builtin_fmaf(acc[T][1][r], p[(kb + r) * ks + cp + 1], d[r]);
+        gv[T][r][0] = p[(kb + r) * ks + c0];
+        gv[T][r][1] = p[(kb + r) * ks + c1];
       }
     });
-    float* red = &L.g[0][0];  // the coupling table is free after the last batch
-    wave_lds_sync();
+    const bool m0 = cp < C, m1 = cp + 1 < C;
+    float d[4] = {0.f, 0.f, 0.f, 0.f};
+    static_for<TILES>([&](auto Tc) {
+      constexpr int T = decltype(Tc)::value;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[4 * lane + r] = d[r];
-    wave_lds_sync();
-    if (lane < K) {
-      const int k = lane, r = k & 3;
-      float s = 0.f;
-      if constexpr (K == 16) {
-        for (int ii = 0; ii < 16; ++ii) s += red[4 * (16 * (k >> 2) + ii) + r];
-      } else {
-        for (int gg = k >> 2; gg < 4; gg += 2)
-          for (int ii = 0; ii < 16; ++ii) s += red[4 * (16 * gg + ii) + r];
+      for (int r = 0; r < 4; ++r) {
+        const float x0 = live[T] && m0 ? gv[T][r][0] : 0.f, x1 = live[T] && m1 ? gv[T][r][1] : 0.f;
+        d[r] = __builtin_fmaf(acc[T][0][r], x0, d[r]);
+        d[r] = __builtin_fmaf(acc[T][1][r], x1, d[r]);
       }
-      a.dot_part[(int64_t)item * K + k] = s;
+    });
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      d[r] = channel_sum(d[r], 4);                 // the 16 lanes of a row
+      if constexpr (K == 8) d[r] = half32_add(d[r]);  // rows g and g + 2 hold the same k
+    }
+    if (i == 0 && (K == 16 || g < 2)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a.dot_part[(int64_t)item * K + kb + r] = d[r];
     }
   }
 
